@@ -1,0 +1,110 @@
+"""Seeded synthetic embeddings for the contrastive loss, as BF16 bit patterns.
+
+This module holds no loss arithmetic: it only draws random numbers and rounds
+them to BF16.  Both the HIP path's tests/benchmarks and the FP64 oracle take
+their inputs from here; nothing else is shared between them.
+
+Every draw uses NumPy's PCG64 ``default_rng(seed)`` in FP64, in the order
+stated per workload, then FP64 -> FP32 -> BF16 with round-to-nearest-even.
+The pages name no dataset for the loss; these recipes stand in for batches of
+1024-wide embeddings (UForm README, Matryoshka paragraph; "Scaling-Up
+Contrastive Learning over NVLink Multicast", section "Bird's Eye View & the
+Results": R rows of 1024-dimensional BF16 embeddings per GPU).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+INFONCE = 0
+SIGLIP = 1
+INFONCE_ROWS = 2
+
+DEFAULT_PREFIXES = (64, 128, 256, 512, 1024)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to BF16 (round to nearest, ties to even); uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: int
+    R: int
+    N: int
+    D: int = 1024
+    prefixes: tuple = DEFAULT_PREFIXES
+    weights: tuple | None = None
+    scale: float = float(np.float32(1.0 / 0.07))
+    bias: float = 0.0
+    row_offset: int = 0
+    recipe: str = "gauss"          # gauss | clustered | student_t
+    noise: float = 0.3
+    seed: int = 0
+    extra: dict = field(default_factory=dict)
+
+
+# The five workloads the loss is specified on (sizes, noise, scale, bias, weights).
+WORKLOADS = {
+    "tiny_infonce_256": Workload("tiny_infonce_256", INFONCE, 256, 256, noise=0.3, seed=0),
+    "infonce_4096": Workload("infonce_4096", INFONCE, 4096, 4096, noise=0.5, seed=1),
+    "siglip_16384": Workload("siglip_16384", SIGLIP, 16384, 16384, scale=10.0, bias=-10.0,
+                             noise=0.5, seed=2),
+    "rows_4096x65536": Workload("rows_4096x65536", INFONCE_ROWS, 4096, 65536, recipe="clustered",
+                                noise=0.2, seed=3, extra={"centroids": 256}),
+    "infonce_32768": Workload("infonce_32768", INFONCE, 32768, 32768, weights=(1, 1, 1, 1, 2),
+                              scale=float(np.float32(1.0 / 0.05)), recipe="student_t",
+                              noise=0.4, seed=4),
+}
+
+
+def draw_f64(R: int, N: int, D: int, recipe: str = "gauss", noise: float = 0.3, seed: int = 0,
+             centroids: int = 256, row_offset: int = 0):
+    """FP64 draws (before rounding) of q [R, D] and k [N, D].
+
+    gauss:      q ~ N(0,1); k_j = q_{j-off} + noise * N(0,1) for the R paired
+                keys, fresh N(0,1) rows for any extra keys (drawn after).
+    student_t:  q ~ Student-t(3) i.i.d.; keys as for gauss.
+    clustered:  centroids C ~ N(0,1) [centroids, D]; assignment a(j) ~ U{0..C-1}
+                for every key j; k_j = C_{a(j)} + noise * N(0,1); then
+                q_i = C_{a(off+i)} + noise * N(0,1) with independent noise.
+    """
+    rng = np.random.default_rng(seed)
+    if recipe in ("gauss", "student_t"):
+        q = rng.standard_normal((R, D)) if recipe == "gauss" else rng.standard_t(3, size=(R, D))
+        k_pairs = q + noise * rng.standard_normal((R, D))
+        if N == R and row_offset == 0:
+            k = k_pairs
+        else:
+            k = rng.standard_normal((N, D)) if recipe == "gauss" else rng.standard_t(3, size=(N, D))
+            k[row_offset:row_offset + R] = k_pairs
+        return q, k
+    if recipe == "clustered":
+        C = rng.standard_normal((centroids, D))
+        assign = rng.integers(0, centroids, size=N)
+        k = C[assign] + noise * rng.standard_normal((N, D))
+        q = C[assign[row_offset:row_offset + R]] + noise * rng.standard_normal((R, D))
+        return q, k
+    raise ValueError(f"unknown recipe {recipe!r}")
+
+
+def make_inputs(R: int, N: int, D: int, recipe: str = "gauss", noise: float = 0.3, seed: int = 0,
+                centroids: int = 256, row_offset: int = 0):
+    """BF16 bit patterns (uint16) of q [R, D] and k [N, D]: FP64 -> FP32 -> BF16 (RNE)."""
+    q, k = draw_f64(R, N, D, recipe, noise, seed, centroids, row_offset)
+    return f32_to_bf16_bits(q.astype(np.float32)), f32_to_bf16_bits(k.astype(np.float32))
+
+
+def workload_inputs(w: Workload):
+    return make_inputs(w.R, w.N, w.D, w.recipe, w.noise, w.seed,
+                       w.extra.get("centroids", 256), w.row_offset)

@@ -1,0 +1,252 @@
+"""FP64 oracle: the Matryoshka contrastive loss written out from its definition.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Slow on purpose: every
+prefix is normalised on its own, every logit is formed explicitly, and the
+gradients are the textbook chain rule through the L2 normalisation.  Rows are
+processed in blocks only to bound memory; each block is the same formula
+applied to a slice of rows (or columns), and partial column statistics are
+merged in fixed block order.
+
+Sources (cited by page title and section):
+
+* "Scaling-Up Contrastive Learning over NVLink Multicast", section "One Set or
+  Two": CLIP turns each row of cosines into a softmax over the batch; the
+  SigLIP equation L = -(1/N) sum_i sum_j log sigmoid(z_ij (t cos(x_i, y_j) + b))
+  with z = +1 for the positive pair and -1 for every negative; Matryoshka
+  prefixes 64/128/256/512 plus the full width give five grids.
+* Same page, section "On the Chip: Tensor Memory & the Matryoshka Sweep":
+  every cell of every prefix needs a normalised cosine.
+* UForm README ("Multimodal Perception from 64 to 1024 Dimensions"), the
+  Matryoshka paragraph (nested prefixes {64, 128, 256, 512, 1024}) and the
+  training-stack paragraphs (BF16 storage, FP32 accumulation, FP32
+  log-sum-exps and partial-gradient slabs).
+
+Readings where the pages leave a step open (each is listed in the design doc):
+
+* two-set loss: queries q (R rows) against keys k (N rows); the positive of
+  local row i is column ``row_offset + i``;
+* symmetric InfoNCE is the CLIP convention 1/2 (row CE + column CE);
+* every kind is normalised by the global N so that row shards sum to the
+  whole loss; SigLIP's 1/N is the printed one;
+* prefixes are combined as the weighted mean sum_p w_p L^p / sum_p w_p;
+* ``scale`` multiplies the cosine as given (no exp() reparametrisation).
+"""
+
+from __future__ import annotations
+
+import contextlib
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+INFONCE = 0
+SIGLIP = 1
+INFONCE_ROWS = 2
+KIND_NAMES = {INFONCE: "infonce", SIGLIP: "siglip", INFONCE_ROWS: "infonce_rows"}
+
+
+# --------------------------------------------------------------------------
+# small numerical helpers, each a plain definition
+# --------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen BF16 bit patterns (uint16) to float64 exactly."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def prefix_normalise(x: np.ndarray, width: int):
+    """Return (x[:, :width] / ||x[:, :width]||, ||x[:, :width]||) row by row."""
+    xp = x[:, :width]
+    norm = np.sqrt(np.sum(xp * xp, axis=1))
+    return xp / norm[:, None], norm
+
+
+def logsumexp(a: np.ndarray, axis: int) -> np.ndarray:
+    """log(sum(exp(a))) along ``axis`` with the usual max shift."""
+    m = np.max(a, axis=axis, keepdims=True)
+    return np.squeeze(m + np.log(np.sum(np.exp(a - m), axis=axis, keepdims=True)), axis=axis)
+
+
+def softplus(x: np.ndarray) -> np.ndarray:
+    """log(1 + e^x) = -log sigmoid(-x), written without overflow."""
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    """1 / (1 + e^-x), written without overflow."""
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+# --------------------------------------------------------------------------
+# the loss
+# --------------------------------------------------------------------------
+
+def _positive_mask(rows: np.ndarray, cols: np.ndarray, row_offset: int) -> np.ndarray:
+    """E[a, b] = 1 where column cols[b] is the positive of row rows[a]."""
+    return (cols[None, :] == (rows[:, None] + row_offset)).astype(np.float64)
+
+
+def _default_block(n: int) -> int:
+    return int(max(16, min(512, (1 << 23) // max(n, 1))))
+
+
+def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_offset=0,
+                        grads=True, threads=None, block=None):
+    """Loss, per-prefix losses, statistics and gradients of the Matryoshka loss.
+
+    q: [R, D] queries, k: [N, D] keys (any real values; the tests pass
+    BF16-rounded values widened to float64).  ``prefixes`` are the nested
+    widths P_1 < ... < P_P <= D, ``weights`` their weights (default all 1).
+    ``kind`` is INFONCE (symmetric CLIP, needs R == N and row_offset == 0),
+    INFONCE_ROWS (row cross-entropy of the R local rows against all N keys,
+    plus the column partial log-sum-exp over the local rows), or SIGLIP.
+
+    Returns a dict with ``loss`` (float), ``prefix_losses`` [P], ``row_lse``
+    [P, R] (log-sum-exp of each row's logits; InfoNCE kinds), ``pos_logit``
+    [P, R], ``col_lse`` [P, N] (log-sum-exp over the R rows of each column's
+    logits; InfoNCE kinds) and, when ``grads``, ``dq`` [R, D] and ``dk`` [N, D].
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    if q.ndim != 2 or k.ndim != 2 or q.shape[1] != k.shape[1]:
+        raise ValueError("q and k must be [R, D] and [N, D]")
+    R, D = q.shape
+    N = k.shape[0]
+    prefixes = [int(p) for p in prefixes]
+    P = len(prefixes)
+    if P < 1 or any(b <= a for a, b in zip(prefixes, prefixes[1:])) or prefixes[0] < 1 or prefixes[-1] > D:
+        raise ValueError("prefixes must be strictly increasing widths in [1, D]")
+    if kind not in KIND_NAMES:
+        raise ValueError("unknown kind")
+    if R < 1 or R > N or row_offset < 0 or row_offset + R > N:
+        raise ValueError("need 1 <= R <= N and row_offset + R <= N")
+    if kind == INFONCE and (R != N or row_offset != 0):
+        raise ValueError("symmetric InfoNCE needs R == N and row_offset == 0")
+    w = np.ones(P) if weights is None else np.asarray(weights, dtype=np.float64)
+    W = float(np.sum(w))
+    s = float(scale)
+    b = float(bias)
+    threads = threads or len(os.sched_getaffinity(0))
+    block = block or _default_block(N)
+
+    row_blocks = [(r0, min(R, r0 + block)) for r0 in range(0, R, block)]
+    col_blocks = [(c0, min(N, c0 + block)) for c0 in range(0, N, block)]
+    all_rows = np.arange(R)
+    all_cols = np.arange(N)
+    pos_col = row_offset + all_rows
+
+    prefix_losses = np.zeros(P)
+    row_lse = np.zeros((P, R))
+    col_lse = np.zeros((P, N))
+    pos_logit = np.zeros((P, R))
+    dq = np.zeros((R, D)) if grads else None
+    dk = np.zeros((N, D)) if grads else None
+
+    with _blas_single_thread(), ThreadPoolExecutor(max_workers=threads) as pool:
+        for p, width in enumerate(prefixes):
+            qh, qnorm = prefix_normalise(q, width)
+            kh, knorm = prefix_normalise(k, width)
+
+            # ---- forward: every logit l_ij = s * cos_ij + b, one row block at a time
+            def forward_rows(rb):
+                r0, r1 = rb
+                logits = s * (qh[r0:r1] @ kh.T) + b
+                rows = all_rows[r0:r1]
+                pos = logits[rows - r0, pos_col[r0:r1]]
+                out = {"pos": pos}
+                if kind == SIGLIP:
+                    z = 2.0 * _positive_mask(rows, all_cols, row_offset) - 1.0
+                    out["siglip_rows"] = np.sum(softplus(-z * logits), axis=1)
+                else:
+                    out["row_lse"] = logsumexp(logits, axis=1)
+                    cmax = np.max(logits, axis=0)
+                    out["col_max"] = cmax
+                    out["col_sum"] = np.sum(np.exp(logits - cmax[None, :]), axis=0)
+                return out
+
+            parts = list(pool.map(forward_rows, row_blocks))
+            for (r0, r1), part in zip(row_blocks, parts):
+                pos_logit[p, r0:r1] = part["pos"]
+            if kind == SIGLIP:
+                siglip_rows = np.concatenate([part["siglip_rows"] for part in parts])
+                prefix_losses[p] = np.sum(siglip_rows) / N
+            else:
+                # merge the per-block column statistics in block order
+                m_run = np.full(N, -np.inf)
+                s_run = np.zeros(N)
+                for part in parts:
+                    m_new = np.maximum(m_run, part["col_max"])
+                    s_run = s_run * np.exp(m_run - m_new) + part["col_sum"] * np.exp(part["col_max"] - m_new)
+                    m_run = m_new
+                col_lse[p] = m_run + np.log(s_run)
+                row_lse[p] = np.concatenate([part["row_lse"] for part in parts])
+                row_ce = row_lse[p] - pos_logit[p]
+                if kind == INFONCE:
+                    # column j's positive is row j (R == N, no offset): l_jj = pos_logit[j]
+                    col_ce = col_lse[p] - pos_logit[p]
+                    prefix_losses[p] = (np.sum(row_ce) + np.sum(col_ce)) / (2.0 * N)
+                else:
+                    prefix_losses[p] = np.sum(row_ce) / N
+
+            if not grads:
+                continue
+
+            # ---- residuals g_ij = dL^p / dl_ij on a slice of the grid
+            def residual(logits, rows, cols):
+                E = _positive_mask(rows, cols, row_offset)
+                if kind == SIGLIP:
+                    return (sigmoid(logits) - E) / N
+                p_row = np.exp(logits - row_lse[p][rows][:, None])
+                if kind == INFONCE_ROWS:
+                    return (p_row - E) / N
+                p_col = np.exp(logits - col_lse[p][cols][None, :])
+                return (p_row - E + p_col - E) / (2.0 * N)
+
+            # ---- dq: u_i = sum_j g_ij * s * kh_j, then through the normalisation of q_i
+            def grad_rows(rb):
+                r0, r1 = rb
+                logits = s * (qh[r0:r1] @ kh.T) + b
+                g = residual(logits, all_rows[r0:r1], all_cols)
+                u = s * (g @ kh)
+                radial = np.sum(u * qh[r0:r1], axis=1)
+                return (u - radial[:, None] * qh[r0:r1]) / qnorm[r0:r1, None]
+
+            for (r0, r1), part in zip(row_blocks, pool.map(grad_rows, row_blocks)):
+                dq[r0:r1, :width] += (w[p] / W) * part
+
+            # ---- dk: v_j = sum_i g_ij * s * qh_i, then through the normalisation of k_j
+            def grad_cols(cb):
+                c0, c1 = cb
+                logits = s * (qh @ kh[c0:c1].T) + b
+                g = residual(logits, all_rows, all_cols[c0:c1])
+                v = s * (g.T @ qh)
+                radial = np.sum(v * kh[c0:c1], axis=1)
+                return (v - radial[:, None] * kh[c0:c1]) / knorm[c0:c1, None]
+
+            for (c0, c1), part in zip(col_blocks, pool.map(grad_cols, col_blocks)):
+                dk[c0:c1, :width] += (w[p] / W) * part
+
+    result = {
+        "loss": float(np.sum(w * prefix_losses) / W),
+        "prefix_losses": prefix_losses,
+        "pos_logit": pos_logit,
+    }
+    if kind != SIGLIP:
+        result["row_lse"] = row_lse
+        result["col_lse"] = col_lse
+    if grads:
+        result["dq"] = dq
+        result["dk"] = dk
+    return result
+
+
+def _blas_single_thread():
+    """Run BLAS single-threaded while the block pool supplies the parallelism."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # BLAS keeps its own threads
+        return contextlib.nullcontext()
+    return threadpool_limits(limits=1, user_api="blas")

@@ -1,0 +1,278 @@
+"""Pins for the FP64 oracle, each independent of the oracle's own formulas.
+
+* closed forms (identical rows, orthonormal one-hot pairs) derived by hand;
+* library routines: torch's cross_entropy / logsigmoid / normalize and its
+  autograd, in float64 on the CPU, for single and nested prefixes;
+* central finite differences of the oracle's own loss;
+* invariants: pair permutation, power-of-two row scaling, Q<->K swap, bias
+  invariance of the softmax form, the Euler identity q . dq = 0, and the
+  row-shard identity that rebuilds the symmetric loss from shards.
+
+Sources: "Scaling-Up Contrastive Learning over NVLink Multicast", section
+"One Set or Two" (CLIP row softmax; SigLIP equation; Matryoshka prefixes).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import INFONCE, INFONCE_ROWS, SIGLIP, contrastive_fwd_bwd
+
+torch = pytest.importorskip("torch")
+F = torch.nn.functional
+
+
+def _softplus(x):
+    return max(x, 0.0) + math.log1p(math.exp(-abs(x)))
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + math.exp(-x))
+
+
+# ----------------------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("N", [1, 5, 16])
+def test_identical_rows_infonce_is_ln_n(rng, N):
+    v = rng.standard_normal(128)
+    q = np.tile(v, (N, 1))
+    out = contrastive_fwd_bwd(q, q.copy(), [32, 64, 128], 1 / 0.07, 0.0, INFONCE, weights=[1, 2, 3])
+    assert out["loss"] == pytest.approx(math.log(N), abs=1e-12)
+    np.testing.assert_allclose(out["prefix_losses"], math.log(N), atol=1e-12)
+    np.testing.assert_allclose(out["dq"], 0.0, atol=1e-12)
+    np.testing.assert_allclose(out["dk"], 0.0, atol=1e-12)
+
+
+def test_identical_rows_rows_kind(rng):
+    R, N, s, b = 6, 20, 14.0, 0.5
+    v = rng.standard_normal(64)
+    out = contrastive_fwd_bwd(np.tile(v, (R, 1)), np.tile(v, (N, 1)), [32, 64], s, b, INFONCE_ROWS,
+                              row_offset=9)
+    assert out["loss"] == pytest.approx(R / N * math.log(N), abs=1e-12)
+    np.testing.assert_allclose(out["col_lse"], s + b + math.log(R), atol=1e-12)
+    np.testing.assert_allclose(out["dq"], 0.0, atol=1e-12)
+    np.testing.assert_allclose(out["dk"], 0.0, atol=1e-12)
+
+
+def test_identical_rows_siglip(rng):
+    N, s, b = 9, 10.0, -10.0
+    v = rng.standard_normal(64)
+    out = contrastive_fwd_bwd(np.tile(v, (N, 1)), np.tile(v, (N, 1)), [32, 64], s, b, SIGLIP)
+    expect = _softplus(-(s + b)) + (N - 1) * _softplus(s + b)
+    assert out["loss"] == pytest.approx(expect, rel=1e-13)
+    np.testing.assert_allclose(out["dq"], 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("s", [1.0, 14.285714149475098, 30.0])
+def test_orthonormal_pairs_infonce(s):
+    N, D = 16, 64
+    q = np.eye(N, D)
+    out = contrastive_fwd_bwd(q, q.copy(), [16, 32, 64], s, 0.25, INFONCE, weights=[2, 1, 1])
+    # LSE - l_ii cancels ~s in FP64, so the bound is absolute at the logits' rounding level
+    assert out["loss"] == pytest.approx(math.log1p((N - 1) * math.exp(-s)), rel=1e-12, abs=1e-13)
+    g = s / (N * (math.exp(s) + N - 1))
+    expect = np.zeros((N, D))
+    expect[:, :N] = g
+    expect[np.arange(N), np.arange(N)] = 0.0
+    np.testing.assert_allclose(out["dq"], expect, rtol=1e-11, atol=1e-300)
+    np.testing.assert_allclose(out["dk"], expect, rtol=1e-11, atol=1e-300)
+
+
+def test_orthonormal_pairs_siglip():
+    N, D, s, b = 12, 32, 10.0, -10.0
+    q = np.eye(N, D)
+    out = contrastive_fwd_bwd(q, q.copy(), [16, 32], s, b, SIGLIP)
+    assert out["loss"] == pytest.approx(_softplus(-(s + b)) + (N - 1) * _softplus(b), rel=1e-13)
+    expect = np.zeros((N, D))
+    expect[:, :N] = s * _sigmoid(b) / N
+    expect[np.arange(N), np.arange(N)] = 0.0
+    np.testing.assert_allclose(out["dq"], expect, rtol=1e-11)
+    np.testing.assert_allclose(out["dk"], expect, rtol=1e-11)
+
+
+# ----------------------------------------------------------------------------- library routines
+
+def _torch_loss(q, k, prefixes, s, b, kind, weights, off):
+    """Weighted mean over prefixes of the textbook loss, built from torch library calls."""
+    R, N = q.shape[0], k.shape[0]
+    w = torch.ones(len(prefixes), dtype=torch.float64) if weights is None else torch.tensor(
+        weights, dtype=torch.float64)
+    target = torch.arange(R) + off
+    total = 0.0
+    for p, width in enumerate(prefixes):
+        qh = F.normalize(q[:, :width], dim=1)
+        kh = F.normalize(k[:, :width], dim=1)
+        logits = s * qh @ kh.T + b
+        if kind == INFONCE:
+            lp = 0.5 * (F.cross_entropy(logits, target, reduction="sum")
+                        + F.cross_entropy(logits.T, target, reduction="sum")) / N
+        elif kind == INFONCE_ROWS:
+            lp = F.cross_entropy(logits, target, reduction="sum") / N
+        else:
+            z = -torch.ones(R, N, dtype=torch.float64)
+            z[torch.arange(R), target] = 1.0
+            lp = -F.logsigmoid(z * logits).sum() / N
+        total = total + w[p] * lp
+    return total / w.sum()
+
+
+CASES = [
+    (INFONCE, 10, 10, 0, [48], None),
+    (INFONCE, 10, 10, 0, [16, 32, 48], [1, 1, 2]),
+    (INFONCE_ROWS, 5, 13, 4, [16, 48], [3, 1]),
+    (SIGLIP, 7, 7, 0, [16, 32, 48], None),
+    (SIGLIP, 4, 9, 5, [32, 48], [1, 2]),
+]
+
+
+@pytest.mark.parametrize("kind,R,N,off,prefixes,weights", CASES)
+def test_matches_torch_library_loss_and_autograd(rng, kind, R, N, off, prefixes, weights):
+    D = 48
+    q = rng.standard_normal((R, D))
+    k = rng.standard_normal((N, D))
+    k[off:off + R] += 2.0 * q
+    s, b = 7.5, -1.25
+    out = contrastive_fwd_bwd(q, k, prefixes, s, b, kind, weights=weights, row_offset=off)
+    qt = torch.tensor(q, requires_grad=True)
+    kt = torch.tensor(k, requires_grad=True)
+    lt = _torch_loss(qt, kt, prefixes, s, b, kind, weights, off)
+    lt.backward()
+    assert out["loss"] == pytest.approx(lt.item(), rel=1e-12)
+    np.testing.assert_allclose(out["dq"], qt.grad.numpy(), rtol=1e-9, atol=1e-13)
+    np.testing.assert_allclose(out["dk"], kt.grad.numpy(), rtol=1e-9, atol=1e-13)
+    if kind == INFONCE_ROWS:
+        for p, width in enumerate(prefixes):
+            logits = s * F.normalize(qt[:, :width], dim=1) @ F.normalize(kt[:, :width], dim=1).T + b
+            np.testing.assert_allclose(out["col_lse"][p], torch.logsumexp(logits, 0).detach().numpy(),
+                                       rtol=1e-12)
+            np.testing.assert_allclose(out["row_lse"][p], torch.logsumexp(logits, 1).detach().numpy(),
+                                       rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- finite differences
+
+@pytest.mark.parametrize("kind,R,N,off", [(INFONCE, 6, 6, 0), (INFONCE_ROWS, 4, 7, 2), (SIGLIP, 5, 8, 3)])
+def test_gradients_match_central_differences(rng, kind, R, N, off):
+    D, prefixes, weights = 96, [32, 64, 96], [1, 2, 3]
+    q = rng.standard_normal((R, D))
+    k = rng.standard_normal((N, D))
+    k[off:off + R] += q
+    s, b = 6.0, -2.0
+    out = contrastive_fwd_bwd(q, k, prefixes, s, b, kind, weights=weights, row_offset=off)
+
+    def loss(qq, kk):
+        return contrastive_fwd_bwd(qq, kk, prefixes, s, b, kind, weights=weights, row_offset=off,
+                                   grads=False)["loss"]
+
+    picks = [(0, i, d) for i in range(R) for d in rng.choice(D, 12, replace=False)]
+    picks += [(1, j, d) for j in range(N) for d in rng.choice(D, 12, replace=False)]
+    for which, i, d in picks:
+        x = q if which == 0 else k
+        h = 1e-6 * max(1.0, abs(x[i, d]))
+        xp, xm = x.copy(), x.copy()
+        xp[i, d] += h
+        xm[i, d] -= h
+        fd = (loss(xp, k) - loss(xm, k)) / (2 * h) if which == 0 else (loss(q, xp) - loss(q, xm)) / (2 * h)
+        an = out["dq"][i, d] if which == 0 else out["dk"][i, d]
+        assert an == pytest.approx(fd, rel=1e-6, abs=1e-9), (which, i, d)
+
+
+# ----------------------------------------------------------------------------- invariants
+
+def _rand_pairs(rng, R, N, D, off=0):
+    q = rng.standard_normal((R, D))
+    k = rng.standard_normal((N, D))
+    k[off:off + R] = q + 0.5 * rng.standard_normal((R, D))
+    return q, k
+
+
+@pytest.mark.parametrize("kind", [INFONCE, SIGLIP])
+def test_pair_permutation_equivariance(rng, kind):
+    q, k = _rand_pairs(rng, 11, 11, 64)
+    perm = rng.permutation(11)
+    a = contrastive_fwd_bwd(q, k, [16, 64], 9.0, -3.0, kind)
+    c = contrastive_fwd_bwd(q[perm], k[perm], [16, 64], 9.0, -3.0, kind)
+    assert c["loss"] == pytest.approx(a["loss"], rel=1e-13)
+    np.testing.assert_allclose(c["dq"], a["dq"][perm], rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(c["dk"], a["dk"][perm], rtol=1e-10, atol=1e-15)
+
+
+def test_band_coordinate_permutation_equivariance(rng):
+    q, k = _rand_pairs(rng, 9, 9, 64)
+    perm = np.concatenate([rng.permutation(16), 16 + rng.permutation(48)])  # within bands [0,16), [16,64)
+    a = contrastive_fwd_bwd(q, k, [16, 64], 9.0, 0.0, INFONCE)
+    c = contrastive_fwd_bwd(q[:, perm], k[:, perm], [16, 64], 9.0, 0.0, INFONCE)
+    assert c["loss"] == pytest.approx(a["loss"], rel=1e-13)
+    np.testing.assert_allclose(c["dq"], a["dq"][:, perm], rtol=1e-10, atol=1e-15)
+
+
+@pytest.mark.parametrize("kind", [INFONCE, INFONCE_ROWS, SIGLIP])
+def test_power_of_two_row_scaling(rng, kind):
+    R, N = (7, 7) if kind != INFONCE_ROWS else (4, 10)
+    q, k = _rand_pairs(rng, R, N, 64)
+    a = contrastive_fwd_bwd(q, k, [32, 64], 12.0, -1.0, kind)
+    q2 = q.copy()
+    q2[3] *= 4.0
+    k2 = k.copy()
+    k2[1] *= 0.5
+    c = contrastive_fwd_bwd(q2, k2, [32, 64], 12.0, -1.0, kind)
+    assert c["loss"] == pytest.approx(a["loss"], rel=1e-13)
+    expect_dq = a["dq"].copy()
+    expect_dq[3] /= 4.0
+    expect_dk = a["dk"].copy()
+    expect_dk[1] /= 0.5
+    np.testing.assert_allclose(c["dq"], expect_dq, rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(c["dk"], expect_dk, rtol=1e-10, atol=1e-15)
+
+
+def test_qk_swap_symmetry_infonce(rng):
+    q, k = _rand_pairs(rng, 10, 10, 64)
+    a = contrastive_fwd_bwd(q, k, [32, 64], 14.0, 0.0, INFONCE)
+    c = contrastive_fwd_bwd(k, q, [32, 64], 14.0, 0.0, INFONCE)
+    assert c["loss"] == pytest.approx(a["loss"], rel=1e-13)
+    np.testing.assert_allclose(c["dq"], a["dk"], rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(c["dk"], a["dq"], rtol=1e-10, atol=1e-15)
+
+
+def test_bias_invariance_infonce(rng):
+    q, k = _rand_pairs(rng, 8, 8, 64)
+    a = contrastive_fwd_bwd(q, k, [32, 64], 14.0, 0.0, INFONCE)
+    c = contrastive_fwd_bwd(q, k, [32, 64], 14.0, 3.5, INFONCE)
+    assert c["loss"] == pytest.approx(a["loss"], rel=1e-12)
+    np.testing.assert_allclose(c["dq"], a["dq"], rtol=1e-9, atol=1e-15)
+
+
+@pytest.mark.parametrize("kind", [INFONCE, INFONCE_ROWS, SIGLIP])
+def test_euler_identity(rng, kind):
+    R, N = (8, 8) if kind != INFONCE_ROWS else (5, 12)
+    q, k = _rand_pairs(rng, R, N, 64)
+    out = contrastive_fwd_bwd(q, k, [16, 32, 64], 11.0, -2.0, kind, weights=[1, 3, 2])
+    np.testing.assert_allclose(np.sum(q * out["dq"], axis=1), 0.0, atol=1e-13)
+    np.testing.assert_allclose(np.sum(k * out["dk"], axis=1), 0.0, atol=1e-13)
+
+
+def test_row_shards_rebuild_symmetric_loss(rng):
+    """Row shards of INFONCE_ROWS (each with its row_offset) rebuild the symmetric loss."""
+    N, D, shard = 12, 64, 4
+    q, k = _rand_pairs(rng, N, N, D)
+    prefixes, s = [16, 64], 14.0
+    full = contrastive_fwd_bwd(q, k, prefixes, s, 0.0, INFONCE, grads=False)
+    parts = [contrastive_fwd_bwd(q[o:o + shard], k, prefixes, s, 0.0, INFONCE_ROWS, row_offset=o, grads=False)
+             for o in range(0, N, shard)]
+    for p in range(len(prefixes)):
+        col_lse = np.logaddexp.reduce(np.stack([part["col_lse"][p] for part in parts]), axis=0)
+        np.testing.assert_allclose(col_lse, full["col_lse"][p], rtol=1e-13)
+        pos = np.concatenate([part["pos_logit"][p] for part in parts])
+        rows = sum(part["prefix_losses"][p] for part in parts)
+        rebuilt = 0.5 * rows + np.sum(col_lse - pos) / (2 * N)
+        assert rebuilt == pytest.approx(full["prefix_losses"][p], rel=1e-13)
+
+
+def test_blocking_does_not_change_results(rng):
+    q, k = _rand_pairs(rng, 13, 13, 64)
+    a = contrastive_fwd_bwd(q, k, [32, 64], 14.0, 0.0, INFONCE, block=3, threads=3)
+    c = contrastive_fwd_bwd(q, k, [32, 64], 14.0, 0.0, INFONCE, block=64, threads=1)
+    assert c["loss"] == pytest.approx(a["loss"], rel=1e-14)
+    np.testing.assert_allclose(c["dq"], a["dq"], rtol=1e-12, atol=1e-16)
+    np.testing.assert_allclose(c["dk"], a["dk"], rtol=1e-12, atol=1e-16)
