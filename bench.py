@@ -1,0 +1,143 @@
+"""Benchmark of the fused Matryoshka contrastive loss (fwd + bwd) on one MI355X.
+
+One step = one call of the C ABI (every kernel of the forward, the statistics,
+both backward passes and the loss reduction) on inputs already resident in
+HBM.  Prints one JSON line.
+
+Metric: fwd+bwd TFLOP/s with the algorithmic count 8 R N D per step (forward
+2RND, logit recompute 2RND, dQ 2RND, dK 2RND; prefixes share one sweep), plus
+pair-scores/s = R N P per step and the fraction of the BF16 dense MFMA peak.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 FLOP/clk/CU, dense
+PEAK_HBM_GBS = 8000.0
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="infonce_32768")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=12288, help="rows of the oracle's timed sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the loss's multi-GPU "
+              "sharding is a design, not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from contrastive_embedding_loss_amd import binding
+    from contrastive_embedding_loss_amd.inputs import WORKLOADS, bf16_bits_to_f32, make_inputs, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    qb, kb = workload_inputs(w)
+    q = torch.from_numpy(bf16_bits_to_f32(qb)).to(dev).to(torch.bfloat16)
+    k = torch.from_numpy(bf16_bits_to_f32(kb)).to(dev).to(torch.bfloat16)
+    print(f"[bench] inputs {w.name} R={w.R} N={w.N} D={w.D} ready in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    R, N, D, P = w.R, w.N, w.D, len(w.prefixes)
+    f32 = dict(dtype=torch.float32, device=dev)
+    loss = torch.empty(1, **f32)
+    dq = torch.empty(R, D, **f32)
+    dk = torch.empty(N, D, **f32)
+
+    def step(profile=False):
+        return binding.fwd_bwd(q, k, w.prefixes, w.scale, w.bias, w.kind, weights=w.weights,
+                               row_offset=w.row_offset, dq=dq, dk=dk, profile=profile)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    binding.profile()  # clear
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    # timed region: K steps, each kernel bracketed by events on the launch stream
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(profile=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    kern = binding.profile()
+    ms_per_step = 1e3 * elapsed / args.steps
+
+    flops = 8.0 * R * N * D
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    pair_scores = float(R) * N * P / (ms_per_step * 1e-3)
+    kern_per_step = {n: t / args.steps for n, t in kern.items()}
+    print(f"[bench] {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s; kernels (ms/step): "
+          + ", ".join(f"{n}={t:.3f}" for n, t in sorted(kern_per_step.items(), key=lambda x: -x[1])),
+          file=sys.stderr, flush=True)
+
+    # dominant kernel: the backward pass kernel (launched twice per step: rows, columns).
+    # Algorithmic MFMA work of one launch: 4 R N D (the full-width logit recompute 2 R N D and
+    # the gradient contraction 2 R N D of its pass).
+    launches = 2
+    bwd_ms = kern_per_step.get("k_bwd", float("nan")) / launches
+    bwd_tflops = 4.0 * R * N * D / (bwd_ms * 1e-3) / 1e12
+    roofline = {"kernel": "k_bwd", "bound": "mfma", "achieved": round(bwd_tflops, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "avg_launch_ms": round(bwd_ms, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import bf16_bits_to_f64, contrastive_fwd_bwd
+
+        n_s = min(args.cpu_sample, R)
+        qs, ks = make_inputs(n_s, n_s, D, w.recipe, w.noise, w.seed, w.extra.get("centroids", 256))
+        cores = len(os.sched_getaffinity(0))
+        print(f"[bench] oracle sample {n_s}x{n_s} on {cores} cores", file=sys.stderr, flush=True)
+        kind = w.kind
+        t1 = time.perf_counter()
+        contrastive_fwd_bwd(bf16_bits_to_f64(qs), bf16_bits_to_f64(ks), w.prefixes, w.scale, w.bias, kind,
+                            weights=w.weights, threads=cores)
+        tc = time.perf_counter() - t1
+        cpu = {"value": round(8.0 * n_s * n_s * D / tc / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"FP64 oracle fwd+bwd on a {n_s}x{n_s} batch of the same recipe and prefixes "
+                         f"({tc:.1f} s), rate = 8*R*N*D/t"}
+
+    out = {
+        "metric": "fwd+bwd TFLOP/s & pair-scores/s at N=32768, 5 prefixes; % BF16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "R": R, "N": N, "D": D, "prefixes": list(w.prefixes),
+                   "kind": ["infonce", "siglip", "infonce_rows"][w.kind], "scale": w.scale, "bias": w.bias,
+                   "weights": list(w.weights) if w.weights else None, "recipe": w.recipe},
+        "pair_scores_per_s": pair_scores,
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "kernel_ms_per_step": {n: round(t, 4) for n, t in kern_per_step.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

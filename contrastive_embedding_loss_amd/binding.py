@@ -1,0 +1,188 @@
+"""ctypes binding of ``libuform_contrastive.so`` (argument marshalling only).
+
+Every step of the loss runs in the library's HIP kernels; this module only
+allocates outputs with torch on the inputs' device and passes raw pointers
+plus torch's current HIP stream.  It raises if the library is missing: there
+is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # imported before the library so both share one HIP runtime
+
+INFONCE = 0
+SIGLIP = 1
+INFONCE_ROWS = 2
+ACCUMULATE = 1
+PROFILE = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libuform_contrastive.so")
+
+STATUS_NAMES = {0: "success", 1: "invalid-argument", 2: "unsupported", 3: "out-of-memory", 4: "device-error"}
+
+
+class UformError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, 'unknown')}: {message}")
+        self.status = status
+        self.message = message
+
+
+class Options(ctypes.Structure):
+    _fields_ = [
+        ("prefix_weights", ctypes.POINTER(ctypes.c_float)),
+        ("row_offset", ctypes.c_int64),
+        ("prefix_losses_out", ctypes.c_void_p),
+        ("col_lse_out", ctypes.c_void_p),
+        ("row_lse_out", ctypes.c_void_p),
+        ("pos_logit_out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load (once) and return the HIP library; raise if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    args = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.uform_contrastive_fwd_bwd.argtypes = args
+    lib.uform_contrastive_fwd_bwd.restype = ctypes.c_int
+    lib.uform_contrastive_fwd_bwd_ex.argtypes = args + [ctypes.POINTER(Options)]
+    lib.uform_contrastive_fwd_bwd_ex.restype = ctypes.c_int
+    lib.uform_contrastive_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                      ctypes.c_int32, ctypes.c_int32]
+    lib.uform_contrastive_workspace_bytes.restype = ctypes.c_size_t
+    lib.uform_contrastive_supported.argtypes = [ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int32]
+    lib.uform_contrastive_supported.restype = ctypes.c_int
+    lib.uform_status_name.argtypes = [ctypes.c_int]
+    lib.uform_status_name.restype = ctypes.c_char_p
+    lib.uform_contrastive_last_error.argtypes = []
+    lib.uform_contrastive_last_error.restype = ctypes.c_char_p
+    lib.uform_contrastive_profile.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
+                                              ctypes.c_int32]
+    lib.uform_contrastive_profile.restype = ctypes.c_int32
+    lib.uform_contrastive_release.argtypes = []
+    lib.uform_contrastive_release.restype = None
+    _lib = lib
+    return lib
+
+
+def status_name(status: int) -> str:
+    return library().uform_status_name(status).decode()
+
+
+def last_error() -> str:
+    return library().uform_contrastive_last_error().decode()
+
+
+def supported(D: int, prefixes, kind: int, with_gradients: bool = True) -> int:
+    """Status a call with this width, ladder and kind would get from its checks (0 = runs)."""
+    pw = (ctypes.c_int32 * len(prefixes))(*[int(p) for p in prefixes])
+    return int(library().uform_contrastive_supported(D, pw, len(prefixes), kind, int(with_gradients)))
+
+
+def workspace_bytes(R: int, N: int, D: int, n_prefixes: int, kind: int) -> int:
+    return int(library().uform_contrastive_workspace_bytes(R, N, D, n_prefixes, kind))
+
+
+def profile() -> dict:
+    """Summed milliseconds per kernel over the profiled calls since the last read."""
+    cap = 64
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_float * cap)()
+    n = min(library().uform_contrastive_profile(names, ms, cap), cap)
+    return {names[i].decode(): float(ms[i]) for i in range(n)}
+
+
+def release() -> None:
+    library().uform_contrastive_release()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise UformError(status, last_error())
+
+
+def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: float, kind: int, weights=None,
+            row_offset: int = 0, want_dq: bool = True, want_dk: bool = True, extras: bool = False,
+            dq: torch.Tensor | None = None, dk: torch.Tensor | None = None, accumulate: bool = False,
+            workspace: torch.Tensor | None = None, profile: bool = False):
+    """Loss and gradients of the Matryoshka contrastive loss on q's device.
+
+    q [R, D] and k [N, D] are contiguous bfloat16 device tensors.  Returns
+    ``(loss, dq, dk)`` (float32 tensors; dq/dk None when not wanted), plus a
+    dict of ``prefix_losses``, ``row_lse``, ``col_lse`` and ``pos_logit`` when
+    ``extras``.  Everything is enqueued on torch's current stream.
+    """
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
+        raise TypeError("q and k must be bfloat16")
+    if not (q.is_cuda and k.is_cuda):
+        raise TypeError("q and k must be device tensors")
+    q = q.contiguous()
+    k = k.contiguous()
+    R, D = q.shape
+    N = k.shape[0]
+    dev = q.device
+    P = len(prefixes)
+    f32 = dict(dtype=torch.float32, device=dev)
+    loss = torch.empty(1, **f32)
+    if want_dq and dq is None:
+        dq = torch.zeros(R, D, **f32) if accumulate else torch.empty(R, D, **f32)
+    if want_dk and dk is None:
+        dk = torch.zeros(N, D, **f32) if accumulate else torch.empty(N, D, **f32)
+    if not want_dq:
+        dq = None
+    if not want_dk:
+        dk = None
+    pw = (ctypes.c_int32 * P)(*[int(p) for p in prefixes])
+    opt = Options()
+    opt.row_offset = int(row_offset)
+    wbuf = None
+    if weights is not None:
+        wbuf = (ctypes.c_float * P)(*[float(w) for w in weights])
+        opt.prefix_weights = ctypes.cast(wbuf, ctypes.POINTER(ctypes.c_float))
+    ex = None
+    if extras:
+        softmax = kind != SIGLIP
+        ex = {"prefix_losses": torch.empty(P, **f32), "pos_logit": torch.empty(P, R, **f32)}
+        if softmax:
+            ex["row_lse"] = torch.empty(P, R, **f32)
+            ex["col_lse"] = torch.empty(P, N, **f32)
+        opt.prefix_losses_out = ex["prefix_losses"].data_ptr()
+        opt.pos_logit_out = ex["pos_logit"].data_ptr()
+        if softmax:
+            opt.row_lse_out = ex["row_lse"].data_ptr()
+            opt.col_lse_out = ex["col_lse"].data_ptr()
+    if workspace is not None:
+        opt.workspace = workspace.data_ptr()
+        opt.workspace_bytes = workspace.numel() * workspace.element_size()
+    opt.flags = (ACCUMULATE if accumulate else 0) | (PROFILE if profile else 0)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    status = library().uform_contrastive_fwd_bwd_ex(
+        _ptr(q), _ptr(k), R, N, D, pw, P, float(scale), float(bias), int(kind), _ptr(loss), _ptr(dq), _ptr(dk),
+        ctypes.c_void_p(stream), ctypes.byref(opt))
+    _check(status)
+    del wbuf
+    if extras:
+        return loss, dq, dk, ex
+    return loss, dq, dk

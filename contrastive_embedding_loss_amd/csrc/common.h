@@ -1,0 +1,118 @@
+// Types and kernel argument blocks shared by the kernels and the host library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace uform {
+
+using u16 = unsigned short;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int kMaxP = 8;
+constexpr int kMaxD = 1024;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+constexpr int kInfonce = 0;
+constexpr int kSiglip = 1;
+constexpr int kRows = 2;
+
+__host__ __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+struct Prefixes {
+    int n;
+    int w[kMaxP];
+};
+
+// k_prep outputs.  sig = 2^-floor(log2 |row[:P_last]|) (exact power of two),
+// gam = |s| inv_P / den (per-row scale of the backward's band operand),
+// iyr = inv_p / sig.
+struct PrepArgs {
+    const u16 *q, *k;
+    int64_t R, N, off;
+    int D;
+    Prefixes pf;
+    float a_scale, gam_scale;
+    float *invq, *invk, *qA, *kA, *qIYR, *kIYR, *posdot, *sigq, *sigk, *gamq, *gamk;
+};
+
+// Statistics / coefficient-table kernels.  "q" tables are [P][R], "k" tables [P][N].
+struct StatsArgs {
+    int64_t R, N, off, nJt, nIt;
+    Prefixes pf;
+    int kind;
+    float scale, bias, cshift, lse_offset, inv_den, sgn;
+    float wnorm[kMaxP];  // w_p / W
+    const float *rowpart, *colpart;
+    const float *invq, *invk, *posdot, *qA;
+    float *row_lse_out, *col_lse_out, *pos_logit_out;
+    float *negfrac;           // [P][R]: (1 - p_ii) of the row softmax
+    const float *qIYR, *kIYR;
+    float *qC, *qRho, *qKap;  // query-side tables
+    float *kC, *kRho, *kKap;  // key-side tables
+    float *diagA;             // [P][R]: exact coefficient of the positive cell
+    float *lossparts;         // [slot][P]
+    int64_t slot0;
+};
+
+struct BwdArgs {
+    const u16 *X;    // outer rows, BF16 [NO][D]
+    const u16 *Y;    // inner rows scaled by sig, BF16 [NI][D]
+    const u16 *YTb;  // inner rows scaled by sig, FP16, transposed panels [NI/32][D][32]
+    int64_t NO, NI;
+    int D;
+    const float *oA, *oC, *oRho;  // outer tables [P][NO]
+    const float *iI, *iKap;       // inner tables [P][NI]: inv / sig and Kap / sig
+    float b2;                     // sigmoid form: bias * log2(e)
+    int64_t diag_shift;           // positive of outer o is inner o + diag_shift
+    int64_t blocks_per_split;
+    int do_update, want_loss;
+    float *part;   // [nsplit][NO][D]
+    float *Cpart;  // [nsplit][P][NO]
+    float *lossparts;
+    int64_t loss_slot0;
+};
+
+struct FinArgs {
+    const u16 *X, *Y;
+    int64_t NO, R;
+    int D;
+    Prefixes pf;
+    const float *part, *Cpart, *diagA, *posdot, *invx, *gam;
+    int64_t nsplit, diag_shift, pos_shift;
+    int accumulate;
+    float *out;
+};
+
+struct LossArgs {
+    Prefixes pf;
+    const float *lossparts;
+    int64_t nslots;
+    double norm;
+    float wnorm[kMaxP];
+    float *loss_out, *prefix_losses_out;
+};
+
+// launchers (kernels.hip)
+hipError_t launch_prep(const PrepArgs &a, hipStream_t s);
+hipError_t launch_scale_copy(const u16 *x, const float *sig, int64_t rows, int D, u16 *xs, u16 *xt, hipStream_t s);
+hipError_t launch_fwd(const u16 *q, const u16 *k, int64_t R, int64_t N, int D, const Prefixes &pf, int64_t off,
+                      const float *rowA, const float *colI, float cshift, float *rowpart, float *colpart,
+                      hipStream_t s);
+hipError_t launch_rowstats(const StatsArgs &a, hipStream_t s);
+hipError_t launch_colstats(const StatsArgs &a, hipStream_t s);
+hipError_t launch_siglip_tabs(const StatsArgs &a, hipStream_t s);
+bool bwd_mask_supported(uint32_t mask);
+hipError_t launch_bwd(const BwdArgs &a, uint32_t mask, bool sig, int64_t nsplit, hipStream_t s);
+hipError_t launch_finalize(const FinArgs &a, hipStream_t s);
+hipError_t launch_loss(const LossArgs &a, hipStream_t s);
+
+constexpr int kFwdTile = 128;   // forward tile (rows and columns)
+constexpr int kBwdOuter = 64;   // outer rows per backward workgroup
+constexpr int kBwdInner = 32;   // inner rows per backward block
+
+}  // namespace uform

@@ -1,0 +1,561 @@
+// Host side of the C ABI: argument checks, workspace planning, launch order.
+// Every check runs before any device call; launches go in order on the
+// caller's stream and nothing here waits for the device (except growing a
+// cached workspace, which synchronises that stream once).
+//
+// Conventions follow "UForm for Swift", sections "Errors" and "Design" (one
+// C verb per operation, statuses spelled like "invalid-argument"); the loss
+// follows "Scaling-Up Contrastive Learning over NVLink Multicast", section
+// "One Set or Two".
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "common.h"
+#include "uform_contrastive.h"
+
+namespace {
+
+using namespace uform;
+
+thread_local std::string g_last_error;
+
+uform_status_t fail(uform_status_t st, const std::string &msg) {
+    g_last_error = msg;
+    return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+    int64_t R, N, D, P, off;
+    int kind;
+    bool want_dq, want_dk;
+    uint32_t mask;
+    int64_t nIt, nJt;                  // forward tiles
+    int64_t nsplit_row, nsplit_col;    // backward inner splits
+    int64_t bps_row, bps_col;          // inner blocks per split
+    int64_t slots_a, slots_b, nslots;  // loss partial slots
+    // workspace offsets (bytes)
+    size_t o_invq, o_invk, o_qA, o_kA, o_posdot, o_qT, o_kT, o_qS, o_kS;
+    size_t o_qIYR, o_kIYR, o_sigq, o_sigk, o_gamq, o_gamk;
+    size_t o_qC, o_qRho, o_qKap, o_kC, o_kRho, o_kKap, o_negfrac, o_diagA;
+    size_t o_rowpart, o_colpart, o_part, o_Cpart, o_loss;
+    size_t total;
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Inner splits so that a pass launches enough workgroups for 256 CUs.
+void choose_split(int64_t NO, int64_t NI, int64_t &nsplit, int64_t &bps) {
+    const int64_t wgs = cdiv(NO, kBwdOuter);
+    const int64_t nblocks = cdiv(NI, kBwdInner);
+    int64_t want = cdiv(512, wgs);
+    if (want < 1) want = 1;
+    if (want > nblocks) want = nblocks;
+    bps = cdiv(nblocks, want);
+    nsplit = cdiv(nblocks, bps);
+}
+
+uint32_t ladder_mask(const int32_t *pw, int32_t n) {
+    uint32_t m = 0;
+    for (int32_t i = 0; i < n; ++i) m |= 1u << (pw[i] / 32 - 1);
+    return m;
+}
+
+Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, int kind, int64_t off, bool want_dq,
+               bool want_dk) {
+    Plan p{};
+    p.R = R;
+    p.N = N;
+    p.D = D;
+    p.P = P;
+    p.off = off;
+    p.kind = kind;
+    p.want_dq = want_dq;
+    p.want_dk = want_dk;
+    p.mask = ladder_mask(pw, P);
+    const bool softmax = kind != kSiglip;
+    p.nIt = cdiv(R, kFwdTile);
+    p.nJt = cdiv(N, kFwdTile);
+    choose_split(R, N, p.nsplit_row, p.bps_row);
+    choose_split(N, R, p.nsplit_col, p.bps_col);
+    // loss slots: softmax = row stats blocks + column stats blocks;
+    // sigmoid = positive-cell blocks + row-pass workgroups
+    if (softmax) {
+        p.slots_a = cdiv(R, 256);
+        p.slots_b = cdiv(N, 256);
+    } else {
+        p.slots_a = cdiv(R + N, 256);
+        p.slots_b = cdiv(R, kBwdOuter) * p.nsplit_row;
+    }
+    p.nslots = p.slots_a + p.slots_b;
+
+    size_t off_b = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off_b;
+        off_b += align_up(bytes);
+        return o;
+    };
+    const size_t fR = sizeof(float) * P * R, fN = sizeof(float) * P * N;
+    p.o_invq = take(fR);
+    p.o_invk = take(fN);
+    p.o_qA = take(fR);
+    p.o_kA = take(fN);
+    p.o_posdot = take(fR);
+    p.o_qIYR = take(fR);
+    p.o_kIYR = take(fN);
+    p.o_sigq = take(sizeof(float) * R);
+    p.o_sigk = take(sizeof(float) * N);
+    p.o_gamq = take(sizeof(float) * R);
+    p.o_gamk = take(sizeof(float) * N);
+    p.o_qC = take(fR);
+    p.o_qRho = take(fR);
+    p.o_qKap = take(fR);
+    p.o_kC = take(fN);
+    p.o_kRho = take(fN);
+    p.o_kKap = take(fN);
+    p.o_negfrac = take(fR);
+    p.o_diagA = take(fR);
+    p.o_qT = take((want_dk ? sizeof(u16) * cdiv(R, 32) * 32 * D : 0));
+    p.o_kT = take((want_dq || !softmax ? sizeof(u16) * cdiv(N, 32) * 32 * D : 0));
+    p.o_qS = take((want_dk ? sizeof(u16) * R * D : 0));
+    p.o_kS = take((want_dq || !softmax ? sizeof(u16) * N * D : 0));
+    p.o_rowpart = take(softmax ? sizeof(float) * p.nJt * P * R : 0);
+    p.o_colpart = take(softmax ? sizeof(float) * p.nIt * P * N : 0);
+    const size_t part_row = (want_dq || !softmax) ? sizeof(float) * p.nsplit_row * R * D : 0;
+    const size_t part_col = want_dk ? sizeof(float) * p.nsplit_col * N * D : 0;
+    p.o_part = take(part_row > part_col ? part_row : part_col);
+    const size_t c_row = sizeof(float) * p.nsplit_row * P * R, c_col = sizeof(float) * p.nsplit_col * P * N;
+    p.o_Cpart = take(c_row > c_col ? c_row : c_col);
+    p.o_loss = take(sizeof(float) * p.nslots * P);
+    p.total = off_b;
+    return p;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+uform_status_t validate(const void *q, const void *k, int64_t R, int64_t N, int64_t D, const int32_t *prefixes,
+                        int32_t n_prefixes, float scale, float bias, int32_t kind, const float *loss_out,
+                        const float *dq, const float *dk, const uform_contrastive_options_t *opt) {
+    g_last_error.clear();
+    if (!q || !k) return fail(uform_status_invalid_argument_k, "q and k must be device pointers");
+    if (!loss_out) return fail(uform_status_invalid_argument_k, "loss_out must be a device pointer");
+    if (!aligned(q, 16) || !aligned(k, 16)) return fail(uform_status_invalid_argument_k, "q and k must be 16-byte aligned");
+    if (!aligned(loss_out, 4)) return fail(uform_status_invalid_argument_k, "loss_out must be 4-byte aligned");
+    if ((dq && !aligned(dq, 16)) || (dk && !aligned(dk, 16)))
+        return fail(uform_status_invalid_argument_k, "dq and dk must be 16-byte aligned");
+    if (R < 1 || N < 1 || D < 1) return fail(uform_status_invalid_argument_k, "R, N and D must be positive");
+    if (R > N) return fail(uform_status_invalid_argument_k, "R must not exceed N");
+    if (kind != kInfonce && kind != kSiglip && kind != kRows) return fail(uform_status_invalid_argument_k, "unknown kind");
+    const int64_t off = opt ? opt->row_offset : 0;
+    if (off < 0 || off + R > N) return fail(uform_status_invalid_argument_k, "need 0 <= row_offset and row_offset + R <= N");
+    if (kind == kInfonce && (R != N || off != 0))
+        return fail(uform_status_invalid_argument_k, "symmetric InfoNCE needs R == N and row_offset == 0");
+    if (!prefixes) return fail(uform_status_invalid_argument_k, "prefixes must be a host array");
+    if (n_prefixes < 1 || n_prefixes > kMaxP) return fail(uform_status_invalid_argument_k, "n_prefixes must be in [1, 8]");
+    for (int32_t i = 0; i < n_prefixes; ++i) {
+        if (prefixes[i] < 32 || prefixes[i] % 32 != 0)
+            return fail(uform_status_invalid_argument_k, "prefix widths must be positive multiples of 32");
+        if (i > 0 && prefixes[i] <= prefixes[i - 1])
+            return fail(uform_status_invalid_argument_k, "prefix widths must be strictly increasing");
+    }
+    if (prefixes[n_prefixes - 1] > D) return fail(uform_status_invalid_argument_k, "the widest prefix exceeds D");
+    if (!std::isfinite(scale) || !std::isfinite(bias)) return fail(uform_status_invalid_argument_k, "scale and bias must be finite");
+    if (scale == 0.0f) return fail(uform_status_invalid_argument_k, "scale must be nonzero");
+    if (opt && opt->prefix_weights) {
+        for (int32_t i = 0; i < n_prefixes; ++i)
+            if (!(opt->prefix_weights[i] > 0.0f) || !std::isfinite(opt->prefix_weights[i]))
+                return fail(uform_status_invalid_argument_k, "prefix weights must be finite and positive");
+    }
+    if (opt && opt->workspace && !aligned(opt->workspace, 256))
+        return fail(uform_status_invalid_argument_k, "workspace must be 256-byte aligned");
+    if (D % 64 != 0 || D > kMaxD) return fail(uform_status_unsupported_k, "D must be a multiple of 64 and at most 1024");
+    if (kind != kSiglip && std::fabs(scale) > UFORM_CONTRASTIVE_MAX_SOFTMAX_SCALE)
+        return fail(uform_status_unsupported_k, "softmax kinds support |scale| <= 40");
+    if ((dq || dk || kind == kSiglip) && !bwd_mask_supported(ladder_mask(prefixes, n_prefixes)))
+        return fail(uform_status_unsupported_k, "this prefix ladder has no compiled backward kernel");
+    if (N > (int64_t)1 << 31) return fail(uform_status_unsupported_k, "N must be below 2^31");
+    return uform_status_success_k;
+}
+
+// ---------------------------------------------------------------- workspace cache
+
+struct Cached {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Cached> g_cache;
+
+uform_status_t get_workspace(hipStream_t s, size_t need, void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(uform_status_device_error_k, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lock(g_mu);
+    Cached &c = g_cache[{dev, s}];
+    if (c.bytes < need) {
+        if (c.ptr) {
+            if (hipStreamSynchronize(s) != hipSuccess) return fail(uform_status_device_error_k, "stream sync failed");
+            (void)hipFree(c.ptr);
+            c.ptr = nullptr;
+            c.bytes = 0;
+        }
+        void *p = nullptr;
+        if (hipMalloc(&p, need) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(uform_status_out_of_memory_k, "workspace allocation failed");
+        }
+        c.ptr = p;
+        c.bytes = need;
+    }
+    *out = c.ptr;
+    return uform_status_success_k;
+}
+
+// ---------------------------------------------------------------- opt-in kernel timing
+// With UFORM_CONTRASTIVE_PROFILE set, every launch of a call is bracketed by a
+// pair of events recorded on the caller's stream; uform_contrastive_profile()
+// waits for them and returns the summed time per kernel since the last read.
+struct ProfRec {
+    const char *name;
+    hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof_live;
+std::vector<hipEvent_t> g_prof_pool;
+bool g_prof_on = false;
+hipStream_t g_prof_stream = nullptr;
+
+hipEvent_t prof_event() {
+    if (!g_prof_pool.empty()) {
+        hipEvent_t e = g_prof_pool.back();
+        g_prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+struct ProfScope {
+    ProfRec rec{};
+    bool on;
+    ProfScope(const char *name) : on(g_prof_on) {
+        if (!on) return;
+        rec.name = name;
+        rec.a = prof_event();
+        rec.b = prof_event();
+        if (rec.a) (void)hipEventRecord(rec.a, g_prof_stream);
+    }
+    ~ProfScope() {
+        if (!on) return;
+        if (rec.b) (void)hipEventRecord(rec.b, g_prof_stream);
+        if (rec.a && rec.b) g_prof_live.push_back(rec);
+    }
+};
+
+#define LAUNCH_NAMED(name, expr)                                                                     \
+    do {                                                                                             \
+        ProfScope prof_(name);                                                                       \
+        hipError_t e_ = (expr);                                                                      \
+        if (e_ != hipSuccess) return fail(uform_status_device_error_k, std::string("launch failed: ") + \
+                                                                          hipGetErrorString(e_));      \
+    } while (0)
+#define LAUNCH(expr) LAUNCH_NAMED(#expr, expr)
+
+uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t D, const int32_t *prefixes,
+                   int32_t P, float scale, float bias, int32_t kind, float *loss_out, float *dq, float *dk,
+                   hipStream_t s, const uform_contrastive_options_t *opt) {
+    const u16 *q = (const u16 *)q_, *k = (const u16 *)k_;
+    const int64_t off = opt ? opt->row_offset : 0;
+    const bool softmax = kind != kSiglip;
+    Plan pl = make_plan(R, N, D, prefixes, P, kind, off, dq != nullptr, dk != nullptr);
+
+    void *ws = nullptr;
+    if (opt && opt->workspace) {
+        if (opt->workspace_bytes < pl.total) return fail(uform_status_invalid_argument_k, "workspace too small");
+        ws = opt->workspace;
+    } else {
+        uform_status_t st = get_workspace(s, pl.total, &ws);
+        if (st != uform_status_success_k) return st;
+    }
+    char *base = (char *)ws;
+    auto F = [&](size_t o) { return (float *)(base + o); };
+
+    Prefixes pf{};
+    pf.n = P;
+    for (int i = 0; i < P; ++i) pf.w[i] = prefixes[i];
+    float wsum = 0.f;
+    float wnorm[kMaxP] = {};
+    for (int i = 0; i < P; ++i) wsum += (opt && opt->prefix_weights) ? opt->prefix_weights[i] : 1.0f;
+    for (int i = 0; i < P; ++i) wnorm[i] = ((opt && opt->prefix_weights) ? opt->prefix_weights[i] : 1.0f) / wsum;
+
+    const float abs_s = std::fabs(scale);
+    const float cshift = -abs_s * kLog2e;
+    const float sgn = scale > 0 ? 1.0f : -1.0f;
+    const double den = kind == kInfonce ? 2.0 * (double)N : (double)N;
+    const int Di = (int)D;
+
+    float *invq = F(pl.o_invq), *invk = F(pl.o_invk), *qA = F(pl.o_qA), *kA = F(pl.o_kA), *posdot = F(pl.o_posdot);
+    float *qIYR = F(pl.o_qIYR), *kIYR = F(pl.o_kIYR), *sigq = F(pl.o_sigq), *sigk = F(pl.o_sigk);
+    float *gamq = F(pl.o_gamq), *gamk = F(pl.o_gamk);
+    u16 *qT = (u16 *)(base + pl.o_qT), *kT = (u16 *)(base + pl.o_kT);
+    u16 *qS = (u16 *)(base + pl.o_qS), *kS = (u16 *)(base + pl.o_kS);
+    float *lossparts = F(pl.o_loss);
+
+    PrepArgs pa{};
+    pa.q = q;
+    pa.k = k;
+    pa.R = R;
+    pa.N = N;
+    pa.off = off;
+    pa.D = Di;
+    pa.pf = pf;
+    pa.a_scale = scale * kLog2e;
+    pa.gam_scale = (float)(abs_s / den);
+    pa.invq = invq;
+    pa.invk = invk;
+    pa.qA = qA;
+    pa.kA = kA;
+    pa.qIYR = qIYR;
+    pa.kIYR = kIYR;
+    pa.posdot = posdot;
+    pa.sigq = sigq;
+    pa.sigk = sigk;
+    pa.gamq = gamq;
+    pa.gamk = gamk;
+    LAUNCH_NAMED("k_prep", launch_prep(pa, s));
+    if (dk) LAUNCH_NAMED("k_scale_copy", launch_scale_copy(q, sigq, R, Di, qS, qT, s));
+    if (dq || !softmax) LAUNCH_NAMED("k_scale_copy", launch_scale_copy(k, sigk, N, Di, kS, kT, s));
+
+    StatsArgs sa{};
+    sa.R = R;
+    sa.N = N;
+    sa.off = off;
+    sa.nJt = pl.nJt;
+    sa.nIt = pl.nIt;
+    sa.pf = pf;
+    sa.kind = kind;
+    sa.scale = scale;
+    sa.bias = bias;
+    sa.cshift = cshift;
+    sa.lse_offset = abs_s + bias;
+    sa.inv_den = (float)(1.0 / den);
+    sa.sgn = sgn;
+    for (int i = 0; i < kMaxP; ++i) sa.wnorm[i] = wnorm[i];
+    sa.rowpart = F(pl.o_rowpart);
+    sa.colpart = F(pl.o_colpart);
+    sa.invq = invq;
+    sa.invk = invk;
+    sa.posdot = posdot;
+    sa.qA = qA;
+    sa.qIYR = qIYR;
+    sa.kIYR = kIYR;
+    sa.row_lse_out = opt ? opt->row_lse_out : nullptr;
+    sa.col_lse_out = opt ? opt->col_lse_out : nullptr;
+    sa.pos_logit_out = opt ? opt->pos_logit_out : nullptr;
+    sa.negfrac = F(pl.o_negfrac);
+    sa.qC = F(pl.o_qC);
+    sa.qRho = F(pl.o_qRho);
+    sa.qKap = F(pl.o_qKap);
+    sa.kC = F(pl.o_kC);
+    sa.kRho = F(pl.o_kRho);
+    sa.kKap = F(pl.o_kKap);
+    sa.diagA = F(pl.o_diagA);
+    sa.lossparts = lossparts;
+
+    if (softmax) {
+        LAUNCH_NAMED("k_fwd", launch_fwd(q, k, R, N, Di, pf, off, qA, invk, cshift, F(pl.o_rowpart),
+                                         F(pl.o_colpart), s));
+        sa.slot0 = 0;
+        LAUNCH_NAMED("k_rowstats", launch_rowstats(sa, s));
+        sa.slot0 = pl.slots_a;
+        LAUNCH_NAMED("k_colstats", launch_colstats(sa, s));
+    } else {
+        sa.slot0 = 0;
+        LAUNCH_NAMED("k_siglip_tabs", launch_siglip_tabs(sa, s));
+    }
+
+    auto pass = [&](bool rowpass, float *out) -> uform_status_t {
+        BwdArgs ba{};
+        ba.X = rowpass ? q : k;
+        ba.Y = rowpass ? kS : qS;
+        ba.YTb = rowpass ? kT : qT;
+        ba.NO = rowpass ? R : N;
+        ba.NI = rowpass ? N : R;
+        ba.D = Di;
+        ba.oA = rowpass ? qA : kA;
+        ba.oC = rowpass ? sa.qC : sa.kC;
+        ba.oRho = rowpass ? sa.qRho : sa.kRho;
+        ba.iI = rowpass ? kIYR : qIYR;
+        ba.iKap = rowpass ? sa.kKap : sa.qKap;
+        ba.b2 = bias * kLog2e;
+        ba.diag_shift = rowpass ? off : -off;
+        ba.blocks_per_split = rowpass ? pl.bps_row : pl.bps_col;
+        ba.do_update = out != nullptr;
+        ba.want_loss = (!softmax && rowpass) ? 1 : 0;
+        ba.part = F(pl.o_part);
+        ba.Cpart = F(pl.o_Cpart);
+        ba.lossparts = lossparts;
+        ba.loss_slot0 = pl.slots_a;
+        const int64_t nsplit = rowpass ? pl.nsplit_row : pl.nsplit_col;
+        LAUNCH_NAMED("k_bwd", launch_bwd(ba, pl.mask, !softmax, nsplit, s));
+        if (out) {
+            FinArgs fa{};
+            fa.X = ba.X;
+            fa.Y = rowpass ? k : q;
+            fa.NO = ba.NO;
+            fa.R = R;
+            fa.D = Di;
+            fa.pf = pf;
+            fa.part = ba.part;
+            fa.Cpart = ba.Cpart;
+            fa.diagA = sa.diagA;
+            fa.posdot = posdot;
+            fa.invx = rowpass ? invq : invk;
+            fa.gam = rowpass ? gamq : gamk;
+            fa.nsplit = nsplit;
+            fa.diag_shift = ba.diag_shift;
+            fa.pos_shift = rowpass ? 0 : -off;
+            fa.accumulate = (opt && (opt->flags & UFORM_CONTRASTIVE_ACCUMULATE)) ? 1 : 0;
+            fa.out = out;
+            LAUNCH_NAMED("k_finalize", launch_finalize(fa, s));
+        }
+        return uform_status_success_k;
+    };
+    if (dq || !softmax) {
+        uform_status_t st = pass(true, dq);
+        if (st != uform_status_success_k) return st;
+    }
+    if (dk) {
+        uform_status_t st = pass(false, dk);
+        if (st != uform_status_success_k) return st;
+    }
+
+    LossArgs la{};
+    la.pf = pf;
+    la.lossparts = lossparts;
+    la.nslots = pl.nslots;
+    la.norm = 1.0 / den;
+    for (int i = 0; i < kMaxP; ++i) la.wnorm[i] = wnorm[i];
+    la.loss_out = loss_out;
+    la.prefix_losses_out = opt ? opt->prefix_losses_out : nullptr;
+    LAUNCH_NAMED("k_loss", launch_loss(la, s));
+    return uform_status_success_k;
+}
+
+}  // namespace
+
+extern "C" {
+
+uform_status_t uform_contrastive_fwd_bwd_ex(const void *q, const void *k, int64_t R, int64_t N, int64_t D,
+                                            const int32_t *prefixes, int32_t n_prefixes, float scale, float bias,
+                                            int32_t kind, float *loss_out, float *dq, float *dk, hipStream_t stream,
+                                            const uform_contrastive_options_t *options) {
+    uform_status_t st = validate(q, k, R, N, D, prefixes, n_prefixes, scale, bias, kind, loss_out, dq, dk, options);
+    if (st != uform_status_success_k) return st;
+    const bool prof = options && (options->flags & UFORM_CONTRASTIVE_PROFILE);
+    std::unique_lock<std::mutex> lock(g_prof_mu, std::defer_lock);
+    if (prof) {
+        lock.lock();
+        g_prof_on = true;
+        g_prof_stream = stream;
+    }
+    st = run(q, k, R, N, D, prefixes, n_prefixes, scale, bias, kind, loss_out, dq, dk, stream, options);
+    g_prof_on = false;
+    return st;
+}
+
+int32_t uform_contrastive_profile(const char **names, float *ms, int32_t cap) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    std::vector<std::pair<const char *, float>> sums;
+    for (const ProfRec &r : g_prof_live) {
+        float t = 0.f;
+        if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&t, r.a, r.b) == hipSuccess) {
+            bool found = false;
+            for (auto &kv : sums)
+                if (std::strcmp(kv.first, r.name) == 0) {
+                    kv.second += t;
+                    found = true;
+                }
+            if (!found) sums.emplace_back(r.name, t);
+        }
+        g_prof_pool.push_back(r.a);
+        g_prof_pool.push_back(r.b);
+    }
+    g_prof_live.clear();
+    int32_t n = 0;
+    for (auto &kv : sums) {
+        if (n < cap) {
+            if (names) names[n] = kv.first;
+            if (ms) ms[n] = kv.second;
+        }
+        ++n;
+    }
+    return n;
+}
+
+uform_status_t uform_contrastive_fwd_bwd(const void *q, const void *k, int64_t R, int64_t N, int64_t D,
+                                         const int32_t *prefixes, int32_t n_prefixes, float scale, float bias,
+                                         int32_t kind, float *loss_out, float *dq, float *dk, hipStream_t stream) {
+    return uform_contrastive_fwd_bwd_ex(q, k, R, N, D, prefixes, n_prefixes, scale, bias, kind, loss_out, dq, dk,
+                                        stream, nullptr);
+}
+
+size_t uform_contrastive_workspace_bytes(int64_t R, int64_t N, int64_t D, int32_t n_prefixes, int32_t kind) {
+    if (R < 1 || N < 1 || R > N || D < 64 || D % 64 != 0 || D > kMaxD || n_prefixes < 1 || n_prefixes > kMaxP)
+        return 0;
+    if (kind != kInfonce && kind != kSiglip && kind != kRows) return 0;
+    int32_t pw[kMaxP];
+    for (int32_t i = 0; i < n_prefixes; ++i) pw[i] = (int32_t)(D - 32 * (n_prefixes - 1 - i));  // any ladder ending at D
+    return make_plan(R, N, D, pw, n_prefixes, kind, 0, true, true).total;
+}
+
+uform_status_t uform_contrastive_supported(int64_t D, const int32_t *prefixes, int32_t n_prefixes, int32_t kind,
+                                          int32_t with_gradients) {
+    g_last_error.clear();
+    if (!prefixes || n_prefixes < 1 || n_prefixes > kMaxP)
+        return fail(uform_status_invalid_argument_k, "prefixes must be a host array of 1..8 widths");
+    if (kind != kInfonce && kind != kSiglip && kind != kRows) return fail(uform_status_invalid_argument_k, "unknown kind");
+    for (int32_t i = 0; i < n_prefixes; ++i) {
+        if (prefixes[i] < 32 || prefixes[i] % 32 != 0 || (i > 0 && prefixes[i] <= prefixes[i - 1]))
+            return fail(uform_status_invalid_argument_k, "prefix widths must be increasing multiples of 32");
+    }
+    if (D < 1 || prefixes[n_prefixes - 1] > D) return fail(uform_status_invalid_argument_k, "the widest prefix exceeds D");
+    if (D % 64 != 0 || D > kMaxD) return fail(uform_status_unsupported_k, "D must be a multiple of 64 and at most 1024");
+    if ((with_gradients || kind == kSiglip) && !bwd_mask_supported(ladder_mask(prefixes, n_prefixes)))
+        return fail(uform_status_unsupported_k, "this prefix ladder has no compiled backward kernel");
+    return uform_status_success_k;
+}
+
+const char *uform_status_name(uform_status_t status) {
+    switch (status) {
+        case uform_status_success_k: return "success";
+        case uform_status_invalid_argument_k: return "invalid-argument";
+        case uform_status_unsupported_k: return "unsupported";
+        case uform_status_out_of_memory_k: return "out-of-memory";
+        case uform_status_device_error_k: return "device-error";
+    }
+    return "unknown";
+}
+
+const char *uform_contrastive_last_error(void) { return g_last_error.c_str(); }
+
+void uform_contrastive_release(void) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    for (auto &kv : g_cache) {
+        if (kv.second.ptr) {
+            (void)hipStreamSynchronize(kv.first.second);
+            (void)hipFree(kv.second.ptr);
+        }
+    }
+    g_cache.clear();
+}
+
+}  // extern "C"

@@ -1,0 +1,929 @@
+// Device kernels of the fused Matryoshka contrastive loss for gfx950 (MI355X).
+//
+// Pages (cited by title and section):
+//  * "Scaling-Up Contrastive Learning over NVLink Multicast", "One Set or Two":
+//    CLIP row softmax, the SigLIP equation, five Matryoshka grids.
+//  * Same page, "On the Chip: Tensor Memory & the Matryoshka Sweep": one sweep
+//    over the embedding serves all prefixes; per-cell normalisation with stored
+//    inverse norms; band gradients built as running sums; the grid never leaves
+//    the chip; per-tile partials folded afterwards.
+//  * UForm README, training-stack paragraphs: BF16 operands, FP32 accumulation,
+//    FP32 log-sum-exps and partial-gradient slabs.
+//
+// Notation used throughout: outer rows X (the rows whose gradient a pass owns)
+// against inner rows Y.  The row pass has X = q, Y = k; the column pass has
+// X = k, Y = q.  S^p = <x[:P_p], y[:P_p]>, logits in base-2 units
+// u = l * log2(e); softmax kinds use one fixed shift c = -|s| log2(e) so that
+// x = (l - b - |s|) log2(e) <= 0 and one exp per cell serves row and column sums.
+#include <type_traits>
+
+#include "common.h"
+
+namespace uform {
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// small helpers
+// ----------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+__device__ __forceinline__ float bf16_lo(unsigned int v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned int v) { return __uint_as_float(v & 0xffff0000u); }
+
+__device__ __forceinline__ f16x8 pack_f16x8(const float (&v)[8]) {
+    f16x8 r;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = (_Float16)v[t];
+    return r;
+}
+
+// Sum over the 32 lanes of each wave half of v[lane & 31]: a reduce-scatter
+// butterfly (31 exchanges instead of 32 x 5).
+__device__ __forceinline__ float reduce_scatter32(float (&v)[32], int lane) {
+#pragma unroll
+    for (int h = 16; h >= 1; h >>= 1) {
+        const bool up = (lane & h) != 0;
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+            const float keep = up ? v[i + h] : v[i];
+            const float send = up ? v[i] : v[i + h];
+            v[i] = keep + __shfl_xor(send, h);
+        }
+    }
+    return v[0];
+}
+
+// Direct global -> LDS copy of 16 bytes per lane; lane l lands at lds + 16 l.
+__device__ __forceinline__ void dma16(const void *g, void *lds_base) {
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ----------------------------------------------------------------------------
+// k_prep: per-prefix inverse L2 norms of every row (and s log2(e) times
+// them), the exact power-of-two row scale sig ~ 1/|row| and the backward's
+// per-row operand scale gam; for query rows also the prefix dot products
+// with their positive key.  One wave per row.
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+    if (row >= a.R + a.N) return;
+    const bool isq = row < a.R;
+    const int D = a.D;
+    const u16 *x = isq ? a.q + row * D : a.k + (row - a.R) * D;
+    const u16 *y = isq ? a.k + (row + a.off) * D : x;
+    const int P = a.pf.n;
+    float ss_run = 0.f, dot_run = 0.f;
+    float inv[kMaxP];
+    int start = 0;
+    for (int p = 0; p < P; ++p) {
+        const int end = a.pf.w[p];
+        float ss = 0.f, dt = 0.f;
+        for (int d = start + 2 * lane; d < end; d += 128) {
+            const unsigned int xv = *(const unsigned int *)(x + d);
+            const float x0 = bf16_lo(xv), x1 = bf16_hi(xv);
+            ss = fmaf(x0, x0, fmaf(x1, x1, ss));
+            if (isq) {
+                const unsigned int yv = *(const unsigned int *)(y + d);
+                dt = fmaf(x0, bf16_lo(yv), fmaf(x1, bf16_hi(yv), dt));
+            }
+        }
+        ss_run += wave_sum(ss);
+        dot_run += wave_sum(dt);
+        inv[p] = 1.0f / sqrtf(fmaxf(ss_run, 1.17549435e-38f));
+        if (lane == 0 && isq) a.posdot[p * a.R + row] = dot_run;
+        start = end;
+    }
+    if (lane != 0) return;
+    const float norm = sqrtf(ss_run);
+    const float sig = norm > 0.f ? ldexpf(1.0f, -ilogbf(norm)) : 1.0f;
+    const int64_t r = isq ? row : row - a.R;
+    const int64_t nr = isq ? a.R : a.N;
+    float *invt = isq ? a.invq : a.invk, *At = isq ? a.qA : a.kA, *It = isq ? a.qIYR : a.kIYR;
+    for (int p = 0; p < P; ++p) {
+        invt[p * nr + r] = inv[p];
+        At[p * nr + r] = a.a_scale * inv[p];
+        It[p * nr + r] = inv[p] / sig;
+    }
+    (isq ? a.sigq : a.sigk)[r] = sig;
+    (isq ? a.gamq : a.gamk)[r] = a.gam_scale * inv[P - 1];
+}
+
+// ----------------------------------------------------------------------------
+// k_scale_copy: rows scaled by their power-of-two sig (exact), stored twice:
+// xs[r][d] in BF16, and xt[rb][d][0..31] = x[32 rb + n][d] sig in FP16 as
+// transposed 32-row panels (zero rows past the end), which give the
+// backward's second contraction contiguous 16-byte operands along the inner
+// index.  BF16 values times a power of two are exact in FP16 within range.
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_scale_copy(const u16 *__restrict__ x, const float *__restrict__ sig,
+                                                    int64_t rows, int D, u16 *__restrict__ xs,
+                                                    u16 *__restrict__ xt) {
+    __shared__ u16 tile[32][64 + 2];
+    const int rb = blockIdx.x, dc = blockIdx.y, t = threadIdx.x;
+    {
+        const int n = t >> 3, d8 = (t & 7) * 8;
+        const int64_t r = (int64_t)rb * 32 + n;
+        unsigned int w[4] = {0u, 0u, 0u, 0u};
+        unsigned int hw[4] = {0u, 0u, 0u, 0u};
+        if (r < rows) {
+            const uint4 v = *(const uint4 *)(x + r * D + dc * 64 + d8);
+            const float sc = sig[r];
+            const unsigned int in[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = bf16_lo(in[i]) * sc, hi = bf16_hi(in[i]) * sc;
+                w[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+                const _Float16 hlo = (_Float16)lo, hhi = (_Float16)hi;
+                hw[i] = (unsigned int)__builtin_bit_cast(unsigned short, hlo) |
+                        ((unsigned int)__builtin_bit_cast(unsigned short, hhi) << 16);
+            }
+            *(uint4 *)(xs + r * D + dc * 64 + d8) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            tile[n][d8 + 2 * i] = (u16)(hw[i] & 0xffffu);
+            tile[n][d8 + 2 * i + 1] = (u16)(hw[i] >> 16);
+        }
+    }
+    __syncthreads();
+    {
+        const int d = t >> 2, n8 = (t & 3) * 8;
+        unsigned int w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (unsigned int)tile[n8 + 2 * i][d] | ((unsigned int)tile[n8 + 2 * i + 1][d] << 16);
+        *(uint4 *)(xt + ((int64_t)rb * D + dc * 64 + d) * 32 + n8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// k_fwd: softmax forward.  One 128 x 128 tile of (query i, key j) per
+// workgroup, 4 waves of 64 x 64 (2 x 2 MFMA 32x32x16 blocks each), operands
+// staged through LDS in 64-wide slices of d.  At every prefix boundary the
+// FP32 accumulators are read in place ("snapshotted") and each cell's
+// e = 2^(S a_i ik_j + c) is added to a row partial and a column partial; the
+// positive cell is left out of both (the statistics kernel adds it back from
+// an exact FP32 dot product).  Writes rowpart[jt][p][i] and colpart[it][p][j].
+// ----------------------------------------------------------------------------
+constexpr int FB = 128;
+constexpr int FK = 64;
+constexpr int FPITCH = FK + 8;  // bf16 per LDS row (144 bytes): conflict-free 16-byte reads
+
+template <bool MASKED>
+__device__ __forceinline__ void fwd_snapshot(const f32x16 (&acc)[2][2], int p, int wi, int wj, int lane, int tid,
+                                             int64_t i0, int64_t j0, int64_t R, int64_t N, int64_t off, int P,
+                                             float cshift, const float (*fA)[FB], const float (*fI)[FB],
+                                             float (*racc)[FB], float (*cacc)[FB], int64_t it, int64_t jt,
+                                             float *__restrict__ rowpart, float *__restrict__ colpart) {
+    float rs[32];
+    float cs[2] = {0.f, 0.f};
+    float Ij[2];
+    int64_t gj[2];
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+        const int jl = wj * 64 + bj * 32 + (lane & 31);
+        Ij[bj] = fI[p][jl];
+        gj[bj] = j0 + jl;
+    }
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int il = wi * 64 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const float Ai = fA[p][il];
+            float rsum = 0.f;
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj) {
+                float e = __builtin_amdgcn_exp2f(fmaf(acc[bi][bj][r] * Ai, Ij[bj], cshift));
+                if (MASKED) {
+                    const int64_t gi = i0 + il;
+                    const bool ok = (gi < R) & (gj[bj] < N) & (gj[bj] != gi + off);
+                    e = ok ? e : 0.f;
+                }
+                rsum += e;
+                cs[bj] += e;
+            }
+            rs[bi * 16 + r] = rsum;
+        }
+    }
+    // row sums: lane (lane & 31) of each half ends up with row index v = lane & 31
+    const float rv = reduce_scatter32(rs, lane);
+    {
+        const int v = lane & 31, bi = v >> 4, r = v & 15;
+        const int il = wi * 64 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        racc[wj][il] = rv;
+    }
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+        const float c = cs[bj] + __shfl_xor(cs[bj], 32);
+        if (lane < 32) cacc[wi][wj * 64 + bj * 32 + lane] = c;
+    }
+    __syncthreads();
+    if (tid < FB) {
+        const int64_t gi = i0 + tid;
+        if (gi < R) rowpart[(jt * P + p) * R + gi] = racc[0][tid] + racc[1][tid];
+    } else {
+        const int c = tid - FB;
+        const int64_t g = j0 + c;
+        if (g < N) colpart[(it * P + p) * N + g] = cacc[0][c] + cacc[1][c];
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const u16 *__restrict__ k, int64_t R,
+                                                int64_t N, int D, Prefixes pf, int64_t off,
+                                                const float *__restrict__ rowA, const float *__restrict__ colI,
+                                                float cshift, float *__restrict__ rowpart,
+                                                float *__restrict__ colpart) {
+    __shared__ __attribute__((aligned(16))) u16 Xs[FB * FPITCH];
+    __shared__ __attribute__((aligned(16))) u16 Ys[FB * FPITCH];
+    __shared__ float fA[kMaxP][FB];
+    __shared__ float fI[kMaxP][FB];
+    __shared__ float racc[2][FB];
+    __shared__ float cacc[2][FB];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wi = wave >> 1, wj = wave & 1;
+    const int64_t jt = blockIdx.x, it = blockIdx.y;
+    const int64_t i0 = it * FB, j0 = jt * FB;
+    const int P = pf.n;
+    const int Dsw = pf.w[P - 1];
+
+    for (int e = tid; e < P * FB; e += 256) {
+        const int p = e / FB, r = e % FB;
+        fA[p][r] = (i0 + r < R) ? rowA[p * R + i0 + r] : 0.f;
+        fI[p][r] = (j0 + r < N) ? colI[p * N + j0 + r] : 0.f;
+    }
+    const bool masked = (i0 + FB > R) || (j0 + FB > N) || ((j0 < i0 + off + FB) && (i0 + off < j0 + FB));
+
+    uint4 xr[4], yr[4];
+    auto gload = [&](int d0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int e = tid + 256 * c, row = e >> 3, ch = e & 7;
+            const int d = d0 + ch * 8;
+            const int64_t gi = i0 + row, gj = j0 + row;
+            xr[c] = (gi < R && d < Dsw) ? *(const uint4 *)(q + gi * D + d) : make_uint4(0, 0, 0, 0);
+            yr[c] = (gj < N && d < Dsw) ? *(const uint4 *)(k + gj * D + d) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int e = tid + 256 * c, row = e >> 3, ch = e & 7;
+            *(uint4 *)&Xs[row * FPITCH + ch * 8] = xr[c];
+            *(uint4 *)&Ys[row * FPITCH + ch * 8] = yr[c];
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    const int nst = (Dsw + FK - 1) / FK;
+    int pnext = 0;
+    gload(0);
+    lstore();
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+        if (st + 1 < nst) gload((st + 1) * FK);
+#pragma unroll
+        for (int ks = 0; ks < FK / 16; ++ks) {
+            const int dk = st * FK + ks * 16;
+            if (dk < Dsw) {
+                bf16x8 av[2], bv[2];
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    av[b] = *(const bf16x8 *)&Xs[(wi * 64 + b * 32 + (lane & 31)) * FPITCH + ks * 16 + 8 * (lane >> 5)];
+                    bv[b] = *(const bf16x8 *)&Ys[(wj * 64 + b * 32 + (lane & 31)) * FPITCH + ks * 16 + 8 * (lane >> 5)];
+                }
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
+                if (pnext < P && dk + 16 == pf.w[pnext]) {
+                    if (masked)
+                        fwd_snapshot<true>(acc, pnext, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI,
+                                           racc, cacc, it, jt, rowpart, colpart);
+                    else
+                        fwd_snapshot<false>(acc, pnext, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI,
+                                            racc, cacc, it, jt, rowpart, colpart);
+                    ++pnext;
+                }
+            }
+        }
+        __syncthreads();
+        if (st + 1 < nst) {
+            lstore();
+            __syncthreads();
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Statistics for the softmax kinds (one thread per row / per column).
+// Row i: Z_i = sum_j 2^{x_ij} (negatives from the forward partials plus the
+// positive), CE_i = ln(1 + neg/e_pos), row LSE; and the per-prefix
+// coefficient tables the backward reads.  Column j likewise.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float ce_from(float neg, float epos, float x_pos, float Z) {
+    const float r = neg / epos;
+    return (r < 1e30f) ? log1pf(r) : (logf(Z) - x_pos * kLn2);
+}
+
+__device__ __forceinline__ void block_sum_write(float v, float *red /*[4]*/, float *dst) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    v = wave_sum(v);
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) *dst = ((red[0] + red[1]) + red[2]) + red[3];
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void k_rowstats(StatsArgs a) {
+    __shared__ float red[4];
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool ok = i < a.R;
+    const int P = a.pf.n;
+    for (int p = 0; p < P; ++p) {
+        float ce = 0.f;
+        if (ok) {
+            float neg = 0.f;
+            for (int64_t t = 0; t < a.nJt; ++t) neg += a.rowpart[(t * P + p) * a.R + i];
+            const float iq = a.invq[p * a.R + i], ik = a.invk[p * a.N + i + a.off];
+            const float S = a.posdot[p * a.R + i];
+            const float A = a.qA[p * a.R + i];
+            const float x = fmaf(S * A, ik, a.cshift);
+            const float epos = __builtin_amdgcn_exp2f(x);
+            const float Z = neg + epos;
+            ce = ce_from(neg, epos, x, Z);
+            if (a.row_lse_out) a.row_lse_out[p * a.R + i] = logf(Z) + a.lse_offset;
+            if (a.pos_logit_out) a.pos_logit_out[p * a.R + i] = a.scale * S * iq * ik + a.bias;
+            const float invZ = 1.0f / Z;
+            a.negfrac[p * a.R + i] = neg * invZ;
+            // band-operand scale: beta_p / gam = sgn w_p inv_p / inv_P (folded into the exponent)
+            const float iqP = a.invq[(P - 1) * a.R + i];
+            a.qC[p * a.R + i] = a.cshift + log2f(a.wnorm[p] * iq / iqP);
+            a.qRho[p * a.R + i] = a.sgn * invZ;
+            a.qKap[p * a.R + i] = a.sgn * invZ * a.qIYR[p * a.R + i];
+            if (a.kind == kRows) a.diagA[p * a.R + i] = -a.wnorm[p] * a.scale * (neg * invZ) * a.inv_den * iq * ik;
+        }
+        block_sum_write(ce, red, &a.lossparts[((int64_t)a.slot0 + blockIdx.x) * P + p]);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_colstats(StatsArgs a) {
+    __shared__ float red[4];
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool ok = j < a.N;
+    const int P = a.pf.n;
+    for (int p = 0; p < P; ++p) {
+        float ce = 0.f;
+        if (ok) {
+            float neg = 0.f;
+            for (int64_t t = 0; t < a.nIt; ++t) neg += a.colpart[(t * P + p) * a.N + j];
+            const float ik = a.invk[p * a.N + j];
+            const int64_t i = j - a.off;
+            float epos = 0.f, x = 0.f, iq = 0.f;
+            if (i >= 0 && i < a.R) {
+                iq = a.invq[p * a.R + i];
+                x = fmaf(a.posdot[p * a.R + i] * a.qA[p * a.R + i], ik, a.cshift);
+                epos = __builtin_amdgcn_exp2f(x);
+            }
+            const float Z = neg + epos;
+            if (a.col_lse_out) a.col_lse_out[p * a.N + j] = logf(Z) + a.lse_offset;
+            const float ikP = a.invk[(P - 1) * a.N + j];
+            a.kC[p * a.N + j] = a.cshift + log2f(a.wnorm[p] * ik / ikP);
+            if (a.kind == kInfonce) {
+                const float invZ = 1.0f / Z;
+                ce = ce_from(neg, epos, x, Z);
+                a.kRho[p * a.N + j] = a.sgn * invZ;
+                a.kKap[p * a.N + j] = a.sgn * invZ * a.kIYR[p * a.N + j];
+                // positive cell (j, j): g = -(neg_r / Z_r + neg_c / Z_c) / 2N
+                a.diagA[p * a.R + j] =
+                    -a.wnorm[p] * a.scale * (a.negfrac[p * a.R + j] + neg * invZ) * a.inv_den * iq * ik;
+            } else {
+                a.kRho[p * a.N + j] = 0.f;
+                a.kKap[p * a.N + j] = 0.f;
+            }
+        }
+        block_sum_write(ce, red, &a.lossparts[((int64_t)a.slot0 + blockIdx.x) * P + p]);
+    }
+}
+
+// SigLIP tables (one thread per query row, then per key row) and the
+// positive cells' loss and gradient coefficients.
+__global__ __launch_bounds__(256) void k_siglip_tabs(StatsArgs a) {
+    __shared__ float red[4];
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int P = a.pf.n;
+    for (int p = 0; p < P; ++p) {
+        float lpos = 0.f;
+        if (r < a.R) {
+            const int64_t i = r;
+            const float iq = a.invq[p * a.R + i], ik = a.invk[p * a.N + i + a.off];
+            const float S = a.posdot[p * a.R + i];
+            const float l = a.scale * S * iq * ik + a.bias;
+            // softplus(-l) and sigmoid(-l), both overflow-free
+            const float t = expf(-fabsf(l));
+            lpos = fmaxf(-l, 0.f) + log1pf(t);
+            const float sig_neg = (l >= 0.f) ? t / (1.f + t) : 1.f / (1.f + t);
+            a.qC[p * a.R + i] = a.sgn * a.wnorm[p] * iq / a.invq[(P - 1) * a.R + i];
+            a.diagA[p * a.R + i] = -a.wnorm[p] * a.scale * sig_neg * a.inv_den * iq * ik;
+            if (a.pos_logit_out) a.pos_logit_out[p * a.R + i] = l;
+        } else if (r < a.R + a.N) {
+            const int64_t j = r - a.R;
+            const float ik = a.invk[p * a.N + j];
+            a.kC[p * a.N + j] = a.sgn * a.wnorm[p] * ik / a.invk[(P - 1) * a.N + j];
+        }
+        block_sum_write(lpos, red, &a.lossparts[((int64_t)a.slot0 + blockIdx.x) * P + p]);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// k_bwd: one pass of the backward (row pass or column pass).
+//
+// Workgroup = 4 waves = 64 outer rows (16 per wave); the wave keeps its 16
+// rows of X as MFMA operands in registers and its 16 x D FP32 gradient block
+// in registers for the whole pass.  For every block of 32 inner rows:
+//  R-phase: recompute S^T (16x16x32 MFMA, inner rows in the M slot) over the
+//    prefix sweep, snapshotting at each prefix boundary (static MASK); each
+//    snapshot gives the cell coefficients a^p = dL/dS^p with all scales folded
+//    in (softmax: 2^{S A_o iy + C_o} (Rho_o iy + Kap_n); sigmoid:
+//    sigma(l) Bt_o iy), plus the radial term C^p_o += a^p S^p.
+//  U-phase: band operands A_b = sum_{p>=b} a^p, built widest band first as a
+//    running sum, rounded to BF16, contracted with transposed inner panels
+//    (16x16x32 MFMA, inner rows in the K slot) into the gradient block.
+// Inner tiles stream into LDS with direct global->LDS copies: the transposed
+// panel of block t lands during R(t), the rows of block t+1 during U(t).
+// The positive cell is left out; the finalize kernel adds its exact FP32 term.
+// ----------------------------------------------------------------------------
+constexpr int BO = 64;
+constexpr int BI = 32;
+constexpr int YROW = 1024;  // LDS row pitch of the inner tile, bf16 elements
+
+__device__ __forceinline__ int ysw(int r) { return (r & 3) | ((r >> 1) & 12); }
+
+template <uint32_t MASK>
+struct Ladder {
+    static constexpr int NP = __builtin_popcount(MASK);
+    static constexpr int NDS = 32 - __builtin_clz(MASK);  // sweep steps of 32
+    static constexpr int pos(int p) {                      // sweep step after which prefix p completes
+        int c = -1;
+        for (int ds = 0; ds < 32; ++ds)
+            if (MASK & (1u << ds)) {
+                ++c;
+                if (c == p) return ds;
+            }
+        return -1;
+    }
+};
+
+template <uint32_t MASK, bool SIG>
+__global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
+    using L = Ladder<MASK>;
+    constexpr int NP = L::NP;
+    constexpr int NDS = L::NDS;
+    constexpr int NDB = NDS * 2;  // 16-wide output blocks
+
+    __shared__ __attribute__((aligned(16))) u16 Ys[BI * YROW];
+    __shared__ __attribute__((aligned(16))) u16 YTs[NDS * 32 * 32];
+    __shared__ __attribute__((aligned(16))) float tI[NP][BI];
+    __shared__ __attribute__((aligned(16))) float tK[NP][BI];
+    __shared__ float oT[3][NP][BO];
+    __shared__ float red[4][NP];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int ol = lane & 15, g = lane >> 4;
+    const int64_t o0 = (int64_t)blockIdx.x * BO;
+    const int olocal = wave * 16 + ol;
+    const int64_t o = o0 + olocal;
+    const bool ovalid = o < a.NO;
+    const int64_t nblocks = (a.NI + BI - 1) / BI;
+    const int64_t nb_begin = (int64_t)blockIdx.y * a.blocks_per_split;
+    const int64_t nb_end = nb_begin + a.blocks_per_split < nblocks ? nb_begin + a.blocks_per_split : nblocks;
+    const int D = a.D;
+
+    // zero the inner tile once so rows past the end only ever hold finite values
+    for (int e = tid; e < BI * YROW / 8; e += 256) *(uint4 *)&Ys[e * 8] = make_uint4(0, 0, 0, 0);
+    for (int e = tid; e < 3 * NP * BO; e += 256) {
+        const int which = e / (NP * BO), p = (e / BO) % NP, r = e % BO;
+        const float *src = which == 0 ? a.oA : (which == 1 ? a.oC : a.oRho);
+        oT[which][p][r] = (o0 + r < a.NO) ? src[p * a.NO + o0 + r] : 0.f;
+    }
+
+    // this lane's 16 outer rows as B operands: row o, d = 32 ds + 8 g .. + 7
+    bf16x8 xf[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (ovalid) v = *(const uint4 *)(a.X + o * D + 32 * ds + 8 * g);
+        xf[ds] = as_bf16x8(v);
+    }
+
+    f32x4 dacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float Cacc[NP], Lacc[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) Cacc[p] = Lacc[p] = 0.f;
+
+    // issue the copy of inner rows [32 nb, 32 nb + 32) into Ys (swizzled 16-byte chunks)
+    auto issue_rows = [&](int64_t nb) {
+        constexpr int halves = (NDS * 4 + 63) / 64;
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            const int r = wave * 8 + rr;
+            const int64_t n = nb * BI + r;
+#pragma unroll
+            for (int h = 0; h < halves; ++h) {
+                const int c = (h * 64 + lane) ^ ysw(r);
+                if (n < a.NI && c < NDS * 4) dma16(a.Y + n * D + 8 * c, &Ys[r * YROW + h * 512]);
+            }
+        }
+    };
+    // issue the copy of the transposed panel rows d < 32 NDS into YTs (64 bytes per d-row)
+    auto issue_panel = [&](int64_t nb) {
+        constexpr int insts = NDS * 32 / 16;
+        for (int ins = wave; ins < insts; ins += 4) {
+            const int d = ins * 16 + (lane >> 2), pos = lane & 3;
+            const int gch = pos ^ ((d >> 2) & 3);
+            dma16(a.YTb + ((nb * D + d) * 32 + 8 * gch), &YTs[ins * 16 * 32]);
+        }
+    };
+    float tnext[2];
+    auto load_tables = [&](int64_t nb) {
+        for (int c = 0; c < 2; ++c) {
+            const int e = tid + 256 * c;
+            tnext[c] = 0.f;
+            if (e < 2 * NP * BI) {
+                const int which = e / (NP * BI), p = (e / BI) % NP, r = e % BI;
+                const int64_t n = nb * BI + r;
+                if (n < a.NI) tnext[c] = (which == 0 ? a.iI : a.iKap)[p * a.NI + n];
+            }
+        }
+    };
+    auto store_tables = [&]() {
+        for (int c = 0; c < 2; ++c) {
+            const int e = tid + 256 * c;
+            if (e < 2 * NP * BI) {
+                const int which = e / (NP * BI), p = (e / BI) % NP, r = e % BI;
+                (which == 0 ? tI : tK)[p][r] = tnext[c];
+            }
+        }
+    };
+
+    if (nb_begin < nb_end) {
+        __syncthreads();  // zero-fill of Ys done before the first copy lands
+        issue_rows(nb_begin);
+        load_tables(nb_begin);
+        store_tables();
+        wait_vm();
+        __syncthreads();
+    }
+
+    float row_scale = 0x1p126f;  // this lane's outer row: band operands are multiplied by it
+
+    // lane's inner rows for the two 16-row MFMA blocks: n = 8 (ol>>2) + 4 h + (ol&3)
+    const int nrow0 = 8 * (ol >> 2) + (ol & 3), nrow1 = nrow0 + 4;
+
+    for (int64_t nb = nb_begin; nb < nb_end; ++nb) {
+        if (a.do_update) issue_panel(nb);
+
+        // ---------------- R-phase: recompute S^T with prefix snapshots
+        f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+        float ap[NP][8];
+        const int64_t n0 = nb * BI;
+        static_for<0, NDS>([&](auto dsc) {
+            constexpr int ds = decltype(dsc)::value;
+            const int c = 4 * ds + g;
+            const bf16x8 y0 = *(const bf16x8 *)&Ys[nrow0 * YROW + 8 * (c ^ ol)];
+            const bf16x8 y1 = *(const bf16x8 *)&Ys[nrow1 * YROW + 8 * (c ^ ol)];
+            S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(y0, xf[ds], S0, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(y1, xf[ds], S1, 0, 0, 0);
+            if constexpr ((ds & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+            static_for<0, NP>([&](auto pc) {
+                constexpr int p = decltype(pc)::value;
+                if constexpr (ds == L::pos(p)) {
+                    const float A = oT[0][p][olocal], Cc = oT[1][p][olocal], Rh = oT[2][p][olocal];
+                    const float4 i0v = *(const float4 *)&tI[p][8 * g], i1v = *(const float4 *)&tI[p][8 * g + 4];
+                    const float iy[8] = {i0v.x, i0v.y, i0v.z, i0v.w, i1v.x, i1v.y, i1v.z, i1v.w};
+                    float kp[8];
+                    if constexpr (!SIG) {
+                        const float4 k0v = *(const float4 *)&tK[p][8 * g], k1v = *(const float4 *)&tK[p][8 * g + 4];
+                        kp[0] = k0v.x; kp[1] = k0v.y; kp[2] = k0v.z; kp[3] = k0v.w;
+                        kp[4] = k1v.x; kp[5] = k1v.y; kp[6] = k1v.z; kp[7] = k1v.w;
+                    }
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const float S = t < 4 ? S0[t] : S1[t - 4];
+                        const int64_t n = n0 + 8 * g + t;
+                        const bool valid = ovalid & (n < a.NI) & (n != o + a.diag_shift);
+                        float av;
+                        if constexpr (!SIG) {
+                            const float e = __builtin_amdgcn_exp2f(fmaf(S * A, iy[t], Cc));
+                            av = e * fmaf(Rh, iy[t], kp[t]);
+                        } else {
+                            const float u = fmaf(S * A, iy[t], a.b2);
+                            const float tt = __builtin_amdgcn_exp2f(-fabsf(u));
+                            const float w = 1.f + tt;
+                            const float rr = __builtin_amdgcn_rcpf(w);
+                            const float sg = u >= 0.f ? rr : tt * rr;
+                            av = sg * Cc * iy[t];  // Cc holds beta_o for the sigmoid form
+                            if (a.want_loss) {
+                                // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
+                                const float corr = (tt - (w - 1.f)) * rr * kLog2e;
+                                const float lt = fmaxf(u, 0.f) + __builtin_amdgcn_logf(w) + corr;
+                                Lacc[p] += valid ? lt : 0.f;
+                            }
+                        }
+                        av = valid ? av : 0.f;
+                        Cacc[p] = fmaf(av, S, Cacc[p]);
+                        ap[p][t] = av;
+                    }
+                }
+            });
+        });
+        wait_vm();
+        __syncthreads();  // panel nb in LDS; every wave is done reading Ys
+        if (nb + 1 < nb_end) {
+            issue_rows(nb + 1);
+            load_tables(nb + 1);
+        }
+
+        // ---------------- U-phase: dX[:, band b] += A_b Y[:, band b]
+        // Band operands A_b = sum_{p>=b} a^p (suffix sums in place, widest first),
+        // multiplied by this row's power-of-two scale and rounded to FP16.  The
+        // scale only ever decreases: it keeps |A_1| (the largest, all terms share
+        // one sign) below 2^14; when it drops, the FP32 accumulator is rescaled
+        // by the same exact power of two.  The scale is divided out at the end.
+        if (a.do_update) {
+            static_for<0, NP - 1>([&](auto bc) {
+                constexpr int b = NP - 2 - decltype(bc)::value;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) ap[b][t] += ap[b + 1][t];
+            });
+            float amax = 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) amax = fmaxf(amax, fabsf(ap[0][t]));
+            amax = fmaxf(amax, __shfl_xor(amax, 16));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            float sc = row_scale;
+            if (amax > 0.f) {
+                const int e = ilogbf(amax) + 1;  // amax < 2^e
+                sc = fminf(row_scale, ldexpf(1.0f, min(126, 14 - e)));
+            }
+            if (__any(sc < row_scale)) {
+                const float f = sc / row_scale;
+                float fr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) fr[r] = __shfl(f, 4 * g + r);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dacc[db][r] *= fr[r];
+            }
+            row_scale = sc;
+            static_for<0, NP>([&](auto bc) {
+                constexpr int b = decltype(bc)::value;
+                float v[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) v[t] = ap[b][t] * sc;
+                const f16x8 Ab = pack_f16x8(v);
+                constexpr int db_lo = b == 0 ? 0 : 2 * (L::pos(b - 1) + 1);
+                constexpr int db_hi = 2 * (L::pos(b) + 1);
+                static_for<db_lo, db_hi>([&](auto dbc) {
+                    constexpr int db = decltype(dbc)::value;
+                    const int d = 16 * db + ol;
+                    const f16x8 yt = *(const f16x8 *)&YTs[d * 32 + 8 * (g ^ ((ol >> 2) & 3))];
+                    dacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ab, yt, dacc[db], 0, 0, 0);
+                    if constexpr ((db & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+                });
+            });
+        }
+        if (nb + 1 < nb_end) store_tables();
+        wait_vm();
+        __syncthreads();  // rows nb+1 in LDS; every wave is done reading YTs
+    }
+
+    // ---------------- write the raw gradient block and the radial sums
+    const int64_t split = blockIdx.y;
+    if (a.do_update) {
+        float *dst = a.part + split * a.NO * D;
+        float inv_sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) inv_sc[r] = 1.0f / __shfl(row_scale, 4 * g + r);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t orow = o0 + wave * 16 + 4 * g + r;
+                if (orow < a.NO) dst[orow * D + 16 * db + ol] = dacc[db][r] * inv_sc[r];
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        float c = Cacc[p];
+        c += __shfl_xor(c, 16);
+        c += __shfl_xor(c, 32);
+        if (g == 0 && ovalid) a.Cpart[(split * NP + p) * a.NO + o] = c;
+    }
+    if (SIG && a.want_loss) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const float v = wave_sum(Lacc[p]);
+            if (lane == 0) red[wave][p] = v;
+        }
+        __syncthreads();
+        if (tid < NP) {
+            const float v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+            a.lossparts[((int64_t)a.loss_slot0 + split * gridDim.x + blockIdx.x) * NP + tid] = v * kLn2;
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// k_finalize: per outer row, sum the split partials and add the exact FP32
+// terms: the positive cell (left out of the band operands) and the radial
+// part of the normalisation Jacobian, -x[d] sum_{p: P_p > d} ix_p^2 C^p.
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_finalize(FinArgs a) {
+    __shared__ float DG[kMaxP], RD[kMaxP];
+    const int64_t o = blockIdx.x;
+    const int P = a.pf.n;
+    const int64_t ipos = o + a.pos_shift;  // index of the positive's query row in diagA/posdot
+    const bool has_pos = ipos >= 0 && ipos < a.R;
+    const int64_t ypos = o + a.diag_shift;  // positive's row in Y
+    if (threadIdx.x == 0) {
+        float dg = 0.f, rd = 0.f;
+        for (int p = P - 1; p >= 0; --p) {
+            float C = 0.f;
+            for (int s = 0; s < a.nsplit; ++s) C += a.Cpart[((int64_t)s * P + p) * a.NO + o];
+            float dA = 0.f, dS = 0.f;
+            if (has_pos) {
+                dA = a.diagA[p * a.R + ipos];
+                dS = a.posdot[p * a.R + ipos];
+            }
+            const float ix = a.invx[p * a.NO + o];
+            dg += dA;
+            rd += ix * ix * fmaf(dA, dS, C * a.gam[o]);
+            DG[p] = dg;
+            RD[p] = rd;
+        }
+    }
+    __syncthreads();
+    const int D = a.D;
+    const int Dw = a.pf.w[P - 1];
+    float *dst = a.out + o * D;
+    for (int d = threadIdx.x; d < D; d += 256) {
+        float v = 0.f;
+        if (d < Dw) {
+            int b = 0;
+            while (d >= a.pf.w[b]) ++b;
+            for (int s = 0; s < a.nsplit; ++s) v += a.part[((int64_t)s * a.NO + o) * D + d];
+            v *= a.gam[o];
+            const float xv = __uint_as_float((unsigned int)a.X[o * D + d] << 16);
+            const float yv = has_pos ? __uint_as_float((unsigned int)a.Y[ypos * D + d] << 16) : 0.f;
+            v = fmaf(DG[b], yv, fmaf(-RD[b], xv, v));
+        }
+        dst[d] = a.accumulate ? dst[d] + v : v;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// k_loss: fixed-order sum of every loss partial slot -> loss and L^p.
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_loss(LossArgs a) {
+    __shared__ double red[256];
+    __shared__ double lp[kMaxP];
+    const int P = a.pf.n;
+    for (int p = 0; p < P; ++p) {
+        double v = 0.0;
+        for (int64_t s = threadIdx.x; s < a.nslots; s += 256) v += (double)a.lossparts[s * P + p];
+        red[threadIdx.x] = v;
+        __syncthreads();
+        for (int h = 128; h >= 1; h >>= 1) {
+            if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) lp[p] = red[0] * a.norm;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        double tot = 0.0;
+        for (int p = 0; p < P; ++p) {
+            tot += (double)a.wnorm[p] * lp[p];
+            if (a.prefix_losses_out) a.prefix_losses_out[p] = (float)lp[p];
+        }
+        *a.loss_out = (float)tot;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// launch wrappers (host side of this translation unit)
+// ----------------------------------------------------------------------------
+hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
+    const int64_t rows = a.R + a.N;
+    hipLaunchKernelGGL(k_prep, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_copy(const u16 *x, const float *sig, int64_t rows, int D, u16 *xs, u16 *xt, hipStream_t s) {
+    hipLaunchKernelGGL(k_scale_copy, dim3((unsigned)((rows + 31) / 32), (unsigned)(D / 64)), dim3(256), 0, s, x,
+                       sig, rows, D, xs, xt);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd(const u16 *q, const u16 *k, int64_t R, int64_t N, int D, const Prefixes &pf, int64_t off,
+                      const float *rowA, const float *colI, float cshift, float *rowpart, float *colpart,
+                      hipStream_t s) {
+    const int64_t nIt = (R + FB - 1) / FB, nJt = (N + FB - 1) / FB;
+    hipLaunchKernelGGL(k_fwd, dim3((unsigned)nJt, (unsigned)nIt), dim3(256), 0, s, q, k, R, N, D, pf, off, rowA,
+                       colI, cshift, rowpart, colpart);
+    return hipGetLastError();
+}
+
+hipError_t launch_rowstats(const StatsArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_rowstats, dim3((unsigned)((a.R + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_colstats(const StatsArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_colstats, dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_siglip_tabs(const StatsArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_siglip_tabs, dim3((unsigned)((a.R + a.N + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <uint32_t MASK>
+static hipError_t launch_bwd_mask(const BwdArgs &a, bool sig, dim3 grid, hipStream_t s) {
+    if (sig)
+        hipLaunchKernelGGL((k_bwd<MASK, true>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_bwd<MASK, false>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// Prefix ladders with a compiled backward (bit ds set: a prefix ends at 32 (ds + 1)).
+#define UFORM_LADDERS(X)                                                        \
+    X(0x8000808Au) /* 64, 128, 256, 512, 1024 */                                \
+    X(0x0000808Au) /* 64, 128, 256, 512 */                                      \
+    X(0x0000008Au) /* 64, 128, 256 */                                           \
+    X(0x0000000Au) /* 64, 128 */                                                \
+    X(0x80000000u) /* 1024 */                                                   \
+    X(0x00008000u) /* 512 */                                                    \
+    X(0x00000080u) /* 256 */                                                    \
+    X(0x00000008u) /* 128 */
+
+bool bwd_mask_supported(uint32_t mask) {
+#define UFORM_CASE(m) if (mask == (m)) return true;
+    UFORM_LADDERS(UFORM_CASE)
+#undef UFORM_CASE
+    return false;
+}
+
+hipError_t launch_bwd(const BwdArgs &a, uint32_t mask, bool sig, int64_t nsplit, hipStream_t s) {
+    const dim3 grid((unsigned)((a.NO + BO - 1) / BO), (unsigned)nsplit);
+#define UFORM_CASE(m) \
+    if (mask == (m)) return launch_bwd_mask<(m)>(a, sig, grid, s);
+    UFORM_LADDERS(UFORM_CASE)
+#undef UFORM_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_finalize(const FinArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_finalize, dim3((unsigned)a.NO), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_loss(const LossArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_loss, dim3(1), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace uform

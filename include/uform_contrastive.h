@@ -1,0 +1,162 @@
+/*
+ * uform_contrastive.h -- C ABI of the fused Matryoshka contrastive loss on
+ * AMD Instinct MI355X (gfx950): forward and backward in one asynchronous call.
+ *
+ * What it computes (pages cited by title and section):
+ *  - "Scaling-Up Contrastive Learning over NVLink Multicast", section "One Set
+ *    or Two": CLIP's row softmax over the batch and SigLIP's pairwise sigmoid
+ *    loss L = -(1/N) sum_i sum_j log sigmoid(z_ij (t cos(x_i, y_j) + b)), with
+ *    z = +1 for the positive pair and -1 for every negative; Matryoshka
+ *    prefixes make every nested prefix of the embedding its own grid.
+ *  - Same page, section "On the Chip: Tensor Memory & the Matryoshka Sweep":
+ *    one sweep over the embedding serves every prefix; each cell's cosine is
+ *    normalised with stored inverse norms; the N x N grid never reaches memory.
+ *  - UForm README ("Multimodal Perception from 64 to 1024 Dimensions"),
+ *    Matryoshka paragraph: nested prefixes {64, 128, 256, 512, 1024}; its
+ *    training-stack paragraphs: BF16 storage, FP32 accumulation, FP32
+ *    log-sum-exps and FP32 partial-gradient slabs.
+ *  - "UForm for Swift", sections "Errors" and "Design": one C verb per
+ *    operation named uform_<noun>_<verb>, statuses uform_status_*_k whose
+ *    names read like "invalid-argument".
+ *
+ * Definitions (q: R query rows, k: N key rows, both D wide; prefix widths
+ * P_1 < ... < P_n; weights w_p, W = sum w_p; s = scale, b = bias; the positive
+ * of local row i is key row_offset + i):
+ *   cos^p_ij = <q_i[:P_p], k_j[:P_p]> / (|q_i[:P_p]| |k_j[:P_p]|),
+ *   l^p_ij   = s * cos^p_ij + b,
+ *   INFONCE       (R == N, row_offset == 0): L^p = (1/2N) [ sum_i (LSE_j l_ij - l_ii)
+ *                                                        + sum_j (LSE_i l_ij - l_jj) ]
+ *   INFONCE_ROWS  L^p = (1/N) sum_{i<R} (LSE_{j<N} l_ij - l_{i,off+i}); also the
+ *                 column partial log-sum-exp PLSE^p_j = LSE_{i<R} l_ij
+ *   SIGLIP        L^p = (1/N) sum_{i<R} sum_{j<N} log(1 + exp(-z_ij l_ij))
+ *   loss = sum_p w_p L^p / W.  Gradients dq = dloss/dq, dk = dloss/dk (FP32);
+ *   entries beyond the widest prefix are 0.
+ *
+ * Ownership: the caller owns every buffer and the stream; the library never
+ * frees caller memory.  Without a caller workspace the library keeps one
+ * grow-only device workspace per (device, stream), allocated on first use
+ * (synchronising that stream once when it grows) and freed by
+ * uform_contrastive_release().
+ *
+ * Errors: every argument check runs on the host before any launch or write;
+ * a failed check returns invalid-argument or unsupported and touches nothing.
+ * A failed launch returns device-error.  Faults inside kernels surface at the
+ * caller's next synchronisation.  No call synchronises the host with the
+ * device except a workspace growth.  Calls that share a library workspace
+ * must be ordered on one stream.
+ */
+#ifndef UFORM_CONTRASTIVE_H
+#define UFORM_CONTRASTIVE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t; /* NULL = the device's default stream */
+
+typedef enum {
+    uform_contrastive_infonce_k = 0,      /* symmetric CLIP 1/2 (row CE + column CE) */
+    uform_contrastive_siglip_k = 1,       /* pairwise sigmoid, z = +1 at (i, off + i) */
+    uform_contrastive_infonce_rows_k = 2, /* row CE of the R local rows + column PLSE */
+} uform_contrastive_kind_t;
+
+typedef enum {
+    uform_status_success_k = 0,
+    uform_status_invalid_argument_k = 1, /* a null or misaligned pointer, a bad size or prefix list */
+    uform_status_unsupported_k = 2,      /* valid request outside this build's limits */
+    uform_status_out_of_memory_k = 3,    /* workspace allocation failed */
+    uform_status_device_error_k = 4,     /* a HIP call or a kernel launch failed */
+} uform_status_t;
+
+/* Limits of this build. */
+#define UFORM_CONTRASTIVE_MAX_PREFIXES 8
+#define UFORM_CONTRASTIVE_MAX_DIM 1024
+/* Softmax kinds use one fixed log-sum-exp shift per call, exact while
+ * 2 * |scale| * log2(e) stays inside FP32's normal exponent range. */
+#define UFORM_CONTRASTIVE_MAX_SOFTMAX_SCALE 40.0f
+
+/*
+ * uform_contrastive_fwd_bwd -- loss and gradients in one call.
+ *
+ *  q, k        device, BF16 bit patterns, row-major [R][D] and [N][D] with
+ *              leading dimension D, 16-byte aligned.
+ *  R, N, D     1 <= R <= N; D % 64 == 0 and D <= 1024 (else unsupported).
+ *  prefixes    HOST array of n_prefixes widths, read during the call only:
+ *              strictly increasing multiples of 32, last <= D;
+ *              1 <= n_prefixes <= 8.
+ *  scale, bias finite; softmax kinds need |scale| <= 40 (else unsupported).
+ *  kind        a uform_contrastive_kind_t; INFONCE needs R == N.
+ *  loss_out    device, 1 float: the weighted loss (written asynchronously).
+ *  dq, dk      device FP32 [R][D] and [N][D], 16-byte aligned, overwritten;
+ *              NULL skips that gradient.
+ *  stream      every launch is enqueued on it in order; nothing waits.
+ * Prefix weights default to 1 and the positive of row i is key i.
+ */
+uform_status_t uform_contrastive_fwd_bwd(const void *q, const void *k, int64_t R, int64_t N, int64_t D,
+                                         const int32_t *prefixes, int32_t n_prefixes, float scale,
+                                         float bias, int32_t kind, float *loss_out, float *dq, float *dk,
+                                         hipStream_t stream);
+
+typedef struct {
+    const float *prefix_weights; /* host [n_prefixes], finite and > 0; NULL = all 1            */
+    int64_t row_offset;          /* key index of local row 0's positive; 0 <= off, off + R <= N */
+    float *prefix_losses_out;    /* device [n_prefixes]: unweighted L^p; nullable               */
+    float *col_lse_out;          /* device [n_prefixes][N]: LSE over the R rows of column j
+                                    (INFONCE: full column LSE; INFONCE_ROWS: the PLSE);
+                                    softmax kinds only; nullable                                */
+    float *row_lse_out;          /* device [n_prefixes][R]: LSE over the N keys of row i;
+                                    softmax kinds only; nullable                                */
+    float *pos_logit_out;        /* device [n_prefixes][R]: l^p_{i, off+i}; nullable            */
+    void *workspace;             /* device, 256-byte aligned; NULL = library workspace          */
+    size_t workspace_bytes;      /* >= uform_contrastive_workspace_bytes(...) when given        */
+    uint32_t flags;              /* bit 0: add into dq/dk instead of overwriting them           */
+} uform_contrastive_options_t;
+
+#define UFORM_CONTRASTIVE_ACCUMULATE 1u
+/* Diagnostics: bracket each kernel launch of the call with a pair of events
+ * on the stream (read them with uform_contrastive_profile). */
+#define UFORM_CONTRASTIVE_PROFILE 2u
+
+/* As uform_contrastive_fwd_bwd, with the options above (options may be NULL). */
+uform_status_t uform_contrastive_fwd_bwd_ex(const void *q, const void *k, int64_t R, int64_t N, int64_t D,
+                                            const int32_t *prefixes, int32_t n_prefixes, float scale,
+                                            float bias, int32_t kind, float *loss_out, float *dq, float *dk,
+                                            hipStream_t stream, const uform_contrastive_options_t *options);
+
+/* Device workspace a call of this shape needs, in bytes (gradients included);
+ * 0 for arguments the call would reject. */
+size_t uform_contrastive_workspace_bytes(int64_t R, int64_t N, int64_t D, int32_t n_prefixes, int32_t kind);
+
+/* Whether a call with this width, prefix ladder and kind can run, without
+ * touching any device: success, invalid-argument or unsupported (the reason
+ * is in uform_contrastive_last_error()).  The backward is compiled for the
+ * ladders {64,128,256,512,1024}, {64,128,256,512}, {64,128,256}, {64,128}
+ * and the single widths {128}, {256}, {512}, {1024}; a softmax call without
+ * gradients accepts any valid ladder. */
+uform_status_t uform_contrastive_supported(int64_t D, const int32_t *prefixes, int32_t n_prefixes, int32_t kind,
+                                          int32_t with_gradients);
+
+/* "success", "invalid-argument", "unsupported", "out-of-memory", "device-error";
+ * "unknown" otherwise.  Static strings. */
+const char *uform_status_name(uform_status_t status);
+
+/* Human-readable reason of this thread's last non-success status ("" if none). */
+const char *uform_contrastive_last_error(void);
+
+/* Diagnostics for calls made with UFORM_CONTRASTIVE_PROFILE: waits for their
+ * events and writes up to cap (kernel name, summed milliseconds) pairs, one
+ * per kernel, covering every profiled call since the previous read (which it
+ * clears).  Returns the number of distinct kernels.  Names are static. */
+int32_t uform_contrastive_profile(const char **names, float *ms, int32_t cap);
+
+/* Frees the library's cached workspaces (waits for their streams first). */
+void uform_contrastive_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UFORM_CONTRASTIVE_H */

@@ -1,0 +1,122 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects every invalid argument on the host before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from contrastive_embedding_loss_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uform_contrastive.h")
+PREFIXES = [64, 128, 256, 512, 1024]
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(uform_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 8, names
+    lib = binding.library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_names():
+    assert [binding.status_name(s) for s in range(5)] == [
+        "success", "invalid-argument", "unsupported", "out-of-memory", "device-error"]
+    assert binding.status_name(17) == "unknown"
+
+
+def _call(q=0x10000, k=0x20000, R=256, N=256, D=1024, prefixes=PREFIXES, scale=14.0, bias=0.0, kind=0,
+          loss=0x30000, dq=0x40000, dk=0x50000, opt=None, n_prefixes=None):
+    """Call the ABI with fake device addresses: argument checks must fail before any device call."""
+    lib = binding.library()
+    P = (len(prefixes) if prefixes is not None else 5) if n_prefixes is None else n_prefixes
+    pw = (ctypes.c_int32 * max(1, len(prefixes)))(*prefixes) if prefixes is not None else None
+    args = [ctypes.c_void_p(q), ctypes.c_void_p(k), R, N, D, pw, P, scale, bias, kind, ctypes.c_void_p(loss),
+            ctypes.c_void_p(dq), ctypes.c_void_p(dk), None]
+    if opt is None:
+        return lib.uform_contrastive_fwd_bwd(*args)
+    return lib.uform_contrastive_fwd_bwd_ex(*args, ctypes.byref(opt))
+
+
+INVALID = [
+    dict(q=0), dict(k=0), dict(loss=0), dict(q=0x10008), dict(dq=0x40004), dict(loss=0x30002),
+    dict(R=0), dict(N=0), dict(D=0), dict(R=300, N=256, kind=2), dict(kind=3), dict(kind=-1),
+    dict(R=128, N=256, kind=0), dict(prefixes=None), dict(prefixes=[64, 64, 1024]),
+    dict(prefixes=[64, 48, 1024]), dict(prefixes=[100, 1024]), dict(prefixes=[64, 2048]),
+    dict(prefixes=PREFIXES, n_prefixes=0), dict(prefixes=[32 * (i + 1) for i in range(9)]),
+    dict(scale=float("inf")), dict(scale=float("nan")), dict(bias=float("nan")), dict(scale=0.0),
+]
+
+
+@pytest.mark.parametrize("kw", INVALID)
+def test_invalid_arguments_are_rejected_on_the_host(kw):
+    assert _call(**kw) == 1, binding.last_error()
+    assert binding.last_error() != ""
+
+
+UNSUPPORTED = [
+    dict(D=1000, prefixes=[64, 992]), dict(D=2048, prefixes=[64, 2048]), dict(scale=50.0),
+    dict(prefixes=[96, 1024]),  # no compiled backward for this ladder
+]
+
+
+@pytest.mark.parametrize("kw", UNSUPPORTED)
+def test_unsupported_requests_are_reported(kw):
+    assert _call(**kw) == 2, binding.last_error()
+
+
+def test_softmax_scale_limit_names_the_scale():
+    assert _call(scale=100.0, kind=0) == 2
+    assert "scale" in binding.last_error()
+
+
+def test_option_checks():
+    opt = binding.Options()
+    opt.row_offset = 10
+    assert _call(R=250, N=256, kind=2, opt=opt) == 1  # off + R > N
+    opt.row_offset = -1
+    assert _call(R=100, N=256, kind=2, opt=opt) == 1
+    opt.row_offset = 0
+    w = (ctypes.c_float * 5)(1, 1, 0, 1, 1)
+    opt.prefix_weights = ctypes.cast(w, ctypes.POINTER(ctypes.c_float))
+    assert _call(opt=opt) == 1
+    opt.prefix_weights = None
+    opt.workspace = 0x1000010
+    assert _call(opt=opt) == 1
+
+
+def test_workspace_bytes():
+    small = binding.workspace_bytes(256, 256, 1024, 5, 0)
+    big = binding.workspace_bytes(32768, 32768, 1024, 5, 0)
+    assert 0 < small < big
+    assert binding.workspace_bytes(300, 256, 1024, 5, 0) == 0
+    assert binding.workspace_bytes(256, 256, 1000, 5, 0) == 0
+    assert binding.workspace_bytes(256, 256, 1024, 9, 0) == 0
+
+
+COMPILED = [(1024, (64, 128, 256, 512, 1024)), (512, (64, 128, 256, 512)), (256, (64, 128, 256)),
+            (128, (64, 128)), (1024, (1024,)), (512, (512,)), (256, (256,)), (128, (128,)),
+            (1024, (64, 128, 256, 512)), (768, (64, 128))]
+
+
+@pytest.mark.parametrize("D,prefixes", COMPILED)
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_compiled_ladders_are_supported(D, prefixes, kind):
+    assert binding.supported(D, prefixes, kind) == 0, binding.last_error()
+
+
+@pytest.mark.parametrize("prefixes", [(96, 1024), (64, 256, 1024), (32, 64), (64, 128, 256, 512, 768)])
+def test_other_ladders_need_the_forward_only(prefixes):
+    assert binding.supported(1024, prefixes, 0) == 2
+    assert binding.supported(1024, prefixes, 1, with_gradients=False) == 2  # SigLIP's loss needs the backward
+    assert binding.supported(1024, prefixes, 0, with_gradients=False) == 0

@@ -1,0 +1,155 @@
+"""GPU parity: the HIP path through the C ABI against the FP64 oracle.
+
+Tolerances: relative loss error <= 1e-3; per tensor max|g - g_ref| <=
+2e-3 * max|g_ref| for dq and dk; log-domain statistics (row and column
+log-sum-exps, positive logits) max-abs <= 1e-3; per-prefix losses rel 1e-3.
+Inputs are the seeded BF16 draws of ``contrastive_embedding_loss_amd.inputs``.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from contrastive_embedding_loss_amd import binding  # noqa: E402
+from contrastive_embedding_loss_amd.inputs import (  # noqa: E402
+    INFONCE, INFONCE_ROWS, SIGLIP, WORKLOADS, bf16_bits_to_f32, make_inputs, workload_inputs)
+from oracle import bf16_bits_to_f64, contrastive_fwd_bwd  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+LADDER = (64, 128, 256, 512, 1024)
+
+
+def to_dev(bits):
+    return torch.from_numpy(bf16_bits_to_f32(bits)).to("cuda").to(torch.bfloat16)
+
+
+def run_both(qb, kb, prefixes, scale, bias, kind, weights=None, off=0, label=""):
+    print(f"[case] {label} R={qb.shape[0]} N={kb.shape[0]} D={qb.shape[1]} kind={kind} prefixes={prefixes}",
+          flush=True)
+    q, k = to_dev(qb), to_dev(kb)
+    loss, dq, dk, ex = binding.fwd_bwd(q, k, prefixes, scale, bias, kind, weights=weights, row_offset=off,
+                                       extras=True)
+    torch.cuda.synchronize()
+    ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), prefixes, scale, bias, kind,
+                              weights=weights, row_offset=off)
+    got = {"loss": loss.item(), "dq": dq.cpu().numpy(), "dk": dk.cpu().numpy(),
+           **{n: t.cpu().numpy() for n, t in ex.items()}}
+    return got, ref
+
+
+def check(got, ref, kind, loss_abs=0.0):
+    err = abs(got["loss"] - ref["loss"])
+    assert err <= max(1e-3 * abs(ref["loss"]), loss_abs), (got["loss"], ref["loss"])
+    for name in ("dq", "dk"):
+        scale = np.abs(ref[name]).max()
+        e = np.abs(got[name] - ref[name]).max()
+        assert e <= 2e-3 * scale + 1e-30, (name, e, scale)
+    np.testing.assert_allclose(got["prefix_losses"], ref["prefix_losses"], rtol=1e-3, atol=loss_abs)
+    assert np.abs(got["pos_logit"] - ref["pos_logit"]).max() <= 1e-3
+    if kind != SIGLIP:
+        assert np.abs(got["row_lse"] - ref["row_lse"]).max() <= 1e-3
+        assert np.abs(got["col_lse"] - ref["col_lse"]).max() <= 1e-3
+
+
+def test_tiny_infonce_256_workload():
+    w = WORKLOADS["tiny_infonce_256"]
+    qb, kb = workload_inputs(w)
+    got, ref = run_both(qb, kb, w.prefixes, w.scale, w.bias, w.kind, w.weights, label=w.name)
+    check(got, ref, w.kind)
+
+
+@pytest.mark.parametrize("R", [300, 129])
+def test_infonce_ragged(R):
+    qb, kb = make_inputs(R, R, 1024, noise=0.5, seed=11 + R)
+    got, ref = run_both(qb, kb, LADDER, 1 / 0.07, 0.0, INFONCE, weights=(1, 1, 1, 1, 2), label="ragged")
+    check(got, ref, INFONCE)
+
+
+def test_siglip_ragged():
+    qb, kb = make_inputs(200, 200, 1024, noise=0.5, seed=21)
+    got, ref = run_both(qb, kb, LADDER, 10.0, -10.0, SIGLIP, label="siglip")
+    check(got, ref, SIGLIP)
+
+
+def test_siglip_offset_rows():
+    qb, kb = make_inputs(90, 250, 1024, noise=0.5, seed=22, row_offset=100)
+    got, ref = run_both(qb, kb, LADDER, 10.0, -10.0, SIGLIP, off=100, label="siglip-offset")
+    check(got, ref, SIGLIP)
+
+
+def test_rows_clustered_with_offset():
+    qb, kb = make_inputs(96, 352, 1024, recipe="clustered", noise=0.2, seed=23, centroids=16, row_offset=128)
+    got, ref = run_both(qb, kb, LADDER, 1 / 0.07, 0.0, INFONCE_ROWS, off=128, label="rows-offset")
+    check(got, ref, INFONCE_ROWS)
+
+
+@pytest.mark.parametrize("D,prefixes,kind", [
+    (512, (64, 128, 256, 512), INFONCE), (256, (256,), SIGLIP), (256, (64, 128, 256), INFONCE_ROWS),
+    (128, (64, 128), INFONCE), (1024, (1024,), INFONCE), (512, (512,), SIGLIP), (128, (128,), INFONCE)])
+def test_other_ladders(D, prefixes, kind):
+    R, N = (160, 160) if kind != INFONCE_ROWS else (70, 200)
+    qb, kb = make_inputs(R, N, D, noise=0.4, seed=31 + D)
+    got, ref = run_both(qb, kb, prefixes, 12.0, -2.0 if kind == SIGLIP else 0.0, kind, label="ladder")
+    check(got, ref, kind)
+
+
+def test_single_pair_infonce_is_zero():
+    qb, kb = make_inputs(1, 1, 1024, seed=41)
+    got, ref = run_both(qb, kb, LADDER, 14.0, 0.0, INFONCE, label="N=1")
+    assert abs(got["loss"]) <= 1e-6
+    assert np.abs(got["dq"]).max() <= 1e-6 and np.abs(got["dk"]).max() <= 1e-6
+
+
+def test_identical_rows_closed_form():
+    v = np.random.default_rng(5).standard_normal(1024).astype(np.float32)
+    from contrastive_embedding_loss_amd.inputs import f32_to_bf16_bits
+    bits = np.tile(f32_to_bf16_bits(v), (64, 1))
+    q = to_dev(bits)
+    loss, dq, dk = binding.fwd_bwd(q, q.clone(), LADDER, 14.0, 0.0, INFONCE)
+    assert loss.item() == pytest.approx(math.log(64), rel=1e-4)
+    assert dq.abs().max().item() <= 1e-5 and dk.abs().max().item() <= 1e-5
+
+
+def test_orthonormal_closed_form():
+    N, s = 64, 20.0
+    q = torch.zeros(N, 1024, dtype=torch.bfloat16, device="cuda")
+    q[torch.arange(N), torch.arange(N)] = 1.0
+    loss, dq, dk = binding.fwd_bwd(q, q.clone(), LADDER, s, 0.0, INFONCE)
+    assert loss.item() == pytest.approx(math.log1p((N - 1) * math.exp(-s)), rel=1e-3)
+    g = s / (N * (math.exp(s) + N - 1))
+    expect = torch.zeros(N, 1024, device="cuda")
+    expect[:, :N] = g
+    expect[torch.arange(N), torch.arange(N)] = 0.0
+    assert (dq - expect).abs().max().item() <= 2e-3 * g
+
+
+def test_deterministic_and_partial_outputs():
+    qb, kb = make_inputs(192, 192, 1024, noise=0.5, seed=51)
+    q, k = to_dev(qb), to_dev(kb)
+    a = binding.fwd_bwd(q, k, LADDER, 14.0, 0.0, INFONCE)
+    b = binding.fwd_bwd(q, k, LADDER, 14.0, 0.0, INFONCE)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    l1, dq1, dk1 = binding.fwd_bwd(q, k, LADDER, 14.0, 0.0, INFONCE, want_dk=False)
+    l2, dq2, dk2 = binding.fwd_bwd(q, k, LADDER, 14.0, 0.0, INFONCE, want_dq=False)
+    assert dk1 is None and dq2 is None
+    assert torch.equal(l1, a[0]) and torch.equal(l2, a[0])
+    assert torch.equal(dq1, a[1]) and torch.equal(dk2, a[2])
+    # accumulate adds into the given gradients
+    dq0 = torch.full_like(a[1], 0.5)
+    dk0 = torch.full_like(a[2], -0.25)
+    _, dq3, dk3 = binding.fwd_bwd(q, k, LADDER, 14.0, 0.0, INFONCE, dq=dq0.clone(), dk=dk0.clone(),
+                                  accumulate=True)
+    assert torch.allclose(dq3, a[1] + 0.5, atol=1e-6) and torch.allclose(dk3, a[2] - 0.25, atol=1e-6)
+
+
+def test_loss_only_calls():
+    qb, kb = make_inputs(130, 130, 1024, noise=0.5, seed=61)
+    q, k = to_dev(qb), to_dev(kb)
+    for kind, s, b in ((INFONCE, 14.0, 0.0), (SIGLIP, 10.0, -10.0)):
+        full = binding.fwd_bwd(q, k, LADDER, s, b, kind)
+        only = binding.fwd_bwd(q, k, LADDER, s, b, kind, want_dq=False, want_dk=False)
+        assert torch.equal(full[0], only[0])
