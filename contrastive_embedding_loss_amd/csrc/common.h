@@ -9,6 +9,7 @@ namespace uform {
 using u16 = unsigned short;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
@@ -51,6 +52,7 @@ struct StatsArgs {
     const float *invq, *invk, *posdot, *qA;
     float *row_lse_out, *col_lse_out, *pos_logit_out;
     float *negfrac;           // [P][R]: (1 - p_ii) of the row softmax
+    float *kNegfrac;          // [P][N]: negative mass fraction of each column's softmax
     const float *qIYR, *kIYR;
     float *qC, *qRho, *qKap;  // query-side tables
     float *kC, *kRho, *kKap;  // key-side tables
@@ -62,12 +64,18 @@ struct StatsArgs {
 struct BwdArgs {
     const u16 *X;    // outer rows, BF16 [NO][D]
     const u16 *Y;    // inner rows scaled by sig, BF16 [NI][D]
-    const u16 *YTb;  // inner rows scaled by sig, FP16, transposed panels [NI/32][D][32]
+    const u16 *YTb;  // inner rows scaled by sig, FP16, transposed panels [NI/16][D][16]
     int64_t NO, NI;
     int D;
     const float *oA, *oC, *oRho;  // outer tables [P][NO]
     const float *iI, *iKap;       // inner tables [P][NI]: inv / sig and Kap / sig
     float b2;                     // sigmoid form: bias * log2(e)
+    // operand-scale bound: U_o = sum_p wnorm_p (inv_p / inv_P)_o iyrmax_p (oNeg_p,o + gterm_p)
+    const float *oInv, *oNeg;     // outer inverse norms and negative-mass fractions [P][NO] (oNeg nullable)
+    const float *iyrmax;          // [P] device: max over inner rows of inv_p / sig
+    const float *gterm;           // [P] device global term per prefix, or nullptr to use gterm_val
+    float gterm_val[kMaxP];
+    float wnorm[kMaxP];
     int64_t diag_shift;           // positive of outer o is inner o + diag_shift
     int64_t blocks_per_split;
     int do_update, want_loss;
@@ -108,11 +116,13 @@ hipError_t launch_colstats(const StatsArgs &a, hipStream_t s);
 hipError_t launch_siglip_tabs(const StatsArgs &a, hipStream_t s);
 bool bwd_mask_supported(uint32_t mask);
 hipError_t launch_bwd(const BwdArgs &a, uint32_t mask, bool sig, int64_t nsplit, hipStream_t s);
+hipError_t launch_maxes(const float *t0, const float *t1, const float *t2, const float *t3, int64_t n0, int64_t n1,
+                        int64_t n2, int64_t n3, int P, float *gmax, hipStream_t s);
 hipError_t launch_finalize(const FinArgs &a, hipStream_t s);
 hipError_t launch_loss(const LossArgs &a, hipStream_t s);
 
 constexpr int kFwdTile = 128;   // forward tile (rows and columns)
 constexpr int kBwdOuter = 64;   // outer rows per backward workgroup
-constexpr int kBwdInner = 32;   // inner rows per backward block
+constexpr int kBwdInner = 16;   // inner rows per backward block
 
 }  // namespace uform

@@ -45,7 +45,7 @@ struct Plan {
     // workspace offsets (bytes)
     size_t o_invq, o_invk, o_qA, o_kA, o_posdot, o_qT, o_kT, o_qS, o_kS;
     size_t o_qIYR, o_kIYR, o_sigq, o_sigk, o_gamq, o_gamk;
-    size_t o_qC, o_qRho, o_qKap, o_kC, o_kRho, o_kKap, o_negfrac, o_diagA;
+    size_t o_qC, o_qRho, o_qKap, o_kC, o_kRho, o_kKap, o_negfrac, o_kNegfrac, o_diagA, o_gmax;
     size_t o_rowpart, o_colpart, o_part, o_Cpart, o_loss;
     size_t total;
 };
@@ -122,9 +122,11 @@ Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, in
     p.o_kRho = take(fN);
     p.o_kKap = take(fN);
     p.o_negfrac = take(fR);
+    p.o_kNegfrac = take(fN);
+    p.o_gmax = take(sizeof(float) * 4 * P);
     p.o_diagA = take(fR);
-    p.o_qT = take((want_dk ? sizeof(u16) * cdiv(R, 32) * 32 * D : 0));
-    p.o_kT = take((want_dq || !softmax ? sizeof(u16) * cdiv(N, 32) * 32 * D : 0));
+    p.o_qT = take((want_dk ? sizeof(u16) * cdiv(R, 16) * 16 * D : 0));
+    p.o_kT = take((want_dq || !softmax ? sizeof(u16) * cdiv(N, 16) * 16 * D : 0));
     p.o_qS = take((want_dk ? sizeof(u16) * R * D : 0));
     p.o_kS = take((want_dq || !softmax ? sizeof(u16) * N * D : 0));
     p.o_rowpart = take(softmax ? sizeof(float) * p.nJt * P * R : 0);
@@ -361,6 +363,7 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     sa.col_lse_out = opt ? opt->col_lse_out : nullptr;
     sa.pos_logit_out = opt ? opt->pos_logit_out : nullptr;
     sa.negfrac = F(pl.o_negfrac);
+    sa.kNegfrac = F(pl.o_kNegfrac);
     sa.qC = F(pl.o_qC);
     sa.qRho = F(pl.o_qRho);
     sa.qKap = F(pl.o_qKap);
@@ -381,6 +384,9 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
         sa.slot0 = 0;
         LAUNCH_NAMED("k_siglip_tabs", launch_siglip_tabs(sa, s));
     }
+    float *gmax = F(pl.o_gmax);  // [4][P]: max q inv/sig, max k inv/sig, max row neg mass, max column neg mass
+    LAUNCH_NAMED("k_maxes", launch_maxes(qIYR, kIYR, softmax ? sa.negfrac : nullptr,
+                                         kind == kInfonce ? sa.kNegfrac : nullptr, R, N, R, N, P, gmax, s));
 
     auto pass = [&](bool rowpass, float *out) -> uform_status_t {
         BwdArgs ba{};
@@ -396,6 +402,24 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
         ba.iI = rowpass ? kIYR : qIYR;
         ba.iKap = rowpass ? sa.kKap : sa.qKap;
         ba.b2 = bias * kLog2e;
+        ba.oInv = rowpass ? invq : invk;
+        ba.iyrmax = gmax + (rowpass ? 1 : 0) * P;
+        for (int i = 0; i < kMaxP; ++i) ba.wnorm[i] = wnorm[i];
+        if (!softmax) {  // sigmoid: every cell is bounded by sigma(|s| + b)
+            const float smax = 1.0f / (1.0f + std::exp(-(abs_s + bias)));
+            ba.oNeg = nullptr;
+            ba.gterm = nullptr;
+            for (int i = 0; i < kMaxP; ++i) ba.gterm_val[i] = smax;
+        } else if (kind == kInfonce) {  // row and column softmax terms
+            ba.oNeg = rowpass ? sa.negfrac : sa.kNegfrac;
+            ba.gterm = gmax + (rowpass ? 3 : 2) * P;
+        } else if (rowpass) {  // rows: the row softmax only
+            ba.oNeg = sa.negfrac;
+            ba.gterm = nullptr;
+        } else {  // rows, column pass: the inner rows' softmax only
+            ba.oNeg = nullptr;
+            ba.gterm = gmax + 2 * P;
+        }
         ba.diag_shift = rowpass ? off : -off;
         ba.blocks_per_split = rowpass ? pl.bps_row : pl.bps_col;
         ba.do_update = out != nullptr;

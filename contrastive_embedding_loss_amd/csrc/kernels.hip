@@ -127,25 +127,25 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
 
 // ----------------------------------------------------------------------------
 // k_scale_copy: rows scaled by their power-of-two sig (exact), stored twice:
-// xs[r][d] in BF16, and xt[rb][d][0..31] = x[32 rb + n][d] sig in FP16 as
-// transposed 32-row panels (zero rows past the end), which give the
+// xs[r][d] in BF16, and xt[rb][d][0..15] = x[16 rb + n][d] sig in FP16 as
+// transposed 16-row panels (zero rows past the end), which give the
 // backward's second contraction contiguous 16-byte operands along the inner
 // index.  BF16 values times a power of two are exact in FP16 within range.
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_scale_copy(const u16 *__restrict__ x, const float *__restrict__ sig,
                                                     int64_t rows, int D, u16 *__restrict__ xs,
                                                     u16 *__restrict__ xt) {
-    __shared__ u16 tile[32][64 + 2];
-    const int rb = blockIdx.x, dc = blockIdx.y, t = threadIdx.x;
+    __shared__ u16 tile[16][128 + 2];
+    const int rb = blockIdx.x, dc = blockIdx.y, t = threadIdx.x;  // 16 rows x 128 d per block
     {
-        const int n = t >> 3, d8 = (t & 7) * 8;
-        const int64_t r = (int64_t)rb * 32 + n;
-        unsigned int w[4] = {0u, 0u, 0u, 0u};
+        const int n = t >> 4, d8 = (t & 15) * 8;
+        const int64_t r = (int64_t)rb * 16 + n;
         unsigned int hw[4] = {0u, 0u, 0u, 0u};
-        if (r < rows) {
-            const uint4 v = *(const uint4 *)(x + r * D + dc * 64 + d8);
+        if (r < rows && dc * 128 + d8 < D) {
+            const uint4 v = *(const uint4 *)(x + r * D + dc * 128 + d8);
             const float sc = sig[r];
             const unsigned int in[4] = {v.x, v.y, v.z, v.w};
+            unsigned int w[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float lo = bf16_lo(in[i]) * sc, hi = bf16_hi(in[i]) * sc;
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void k_scale_copy(const u16 *__restrict__ x, c
                 hw[i] = (unsigned int)__builtin_bit_cast(unsigned short, hlo) |
                         ((unsigned int)__builtin_bit_cast(unsigned short, hhi) << 16);
             }
-            *(uint4 *)(xs + r * D + dc * 64 + d8) = make_uint4(w[0], w[1], w[2], w[3]);
+            *(uint4 *)(xs + r * D + dc * 128 + d8) = make_uint4(w[0], w[1], w[2], w[3]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -164,11 +164,14 @@ __global__ __launch_bounds__(256) void k_scale_copy(const u16 *__restrict__ x, c
     }
     __syncthreads();
     {
-        const int d = t >> 2, n8 = (t & 3) * 8;
-        unsigned int w[4];
+        const int d = t >> 1, n8 = (t & 1) * 8;
+        if (dc * 128 + d < D) {
+            unsigned int w[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = (unsigned int)tile[n8 + 2 * i][d] | ((unsigned int)tile[n8 + 2 * i + 1][d] << 16);
-        *(uint4 *)(xt + ((int64_t)rb * D + dc * 64 + d) * 32 + n8) = make_uint4(w[0], w[1], w[2], w[3]);
+            for (int i = 0; i < 4; ++i)
+                w[i] = (unsigned int)tile[n8 + 2 * i][d] | ((unsigned int)tile[n8 + 2 * i + 1][d] << 16);
+            *(uint4 *)(xt + ((int64_t)rb * D + dc * 128 + d) * 16 + n8) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
     }
 }
 
@@ -418,6 +421,7 @@ __global__ __launch_bounds__(256) void k_colstats(StatsArgs a) {
             if (a.kind == kInfonce) {
                 const float invZ = 1.0f / Z;
                 ce = ce_from(neg, epos, x, Z);
+                a.kNegfrac[p * a.N + j] = neg * invZ;
                 a.kRho[p * a.N + j] = a.sgn * invZ;
                 a.kKap[p * a.N + j] = a.sgn * invZ * a.kIYR[p * a.N + j];
                 // positive cell (j, j): g = -(neg_r / Z_r + neg_c / Z_c) / 2N
@@ -426,6 +430,7 @@ __global__ __launch_bounds__(256) void k_colstats(StatsArgs a) {
             } else {
                 a.kRho[p * a.N + j] = 0.f;
                 a.kKap[p * a.N + j] = 0.f;
+                a.kNegfrac[p * a.N + j] = 0.f;
             }
         }
         block_sum_write(ce, red, &a.lossparts[((int64_t)a.slot0 + blockIdx.x) * P + p]);
@@ -464,26 +469,33 @@ __global__ __launch_bounds__(256) void k_siglip_tabs(StatsArgs a) {
 // ----------------------------------------------------------------------------
 // k_bwd: one pass of the backward (row pass or column pass).
 //
-// Workgroup = 4 waves = 64 outer rows (16 per wave); the wave keeps its 16
-// rows of X as MFMA operands in registers and its 16 x D FP32 gradient block
-// in registers for the whole pass.  For every block of 32 inner rows:
-//  R-phase: recompute S^T (16x16x32 MFMA, inner rows in the M slot) over the
-//    prefix sweep, snapshotting at each prefix boundary (static MASK); each
-//    snapshot gives the cell coefficients a^p = dL/dS^p with all scales folded
-//    in (softmax: 2^{S A_o iy + C_o} (Rho_o iy + Kap_n); sigmoid:
-//    sigma(l) Bt_o iy), plus the radial term C^p_o += a^p S^p.
-//  U-phase: band operands A_b = sum_{p>=b} a^p, built widest band first as a
-//    running sum, rounded to BF16, contracted with transposed inner panels
-//    (16x16x32 MFMA, inner rows in the K slot) into the gradient block.
-// Inner tiles stream into LDS with direct global->LDS copies: the transposed
-// panel of block t lands during R(t), the rows of block t+1 during U(t).
-// The positive cell is left out; the finalize kernel adds its exact FP32 term.
+// Workgroup = 4 waves = 64 outer rows, one wave per SIMD.  X rows stay on chip
+// for the whole pass: d < 512 as MFMA operands in registers, the rest in LDS.
+// For every block of 16 inner rows:
+//  R-phase: each wave recomputes S^T for its own 16 outer rows over the prefix
+//    sweep (16x16x32 MFMA, inner rows in the M slot) and, at each prefix
+//    boundary (static MASK), forms the cell coefficients a^p = dL/dS^p with
+//    every scale folded in (softmax: 2^{S A_o iy + C_o} (Rho_o iy + Kap_n);
+//    sigmoid: sigma(l) Bt_o iy) and the radial sums C^p_o += a^p S^p.  The band
+//    operands A_b = sum_{p>=b} a^p (suffix sums, widest band first) are stored
+//    to LDS in FP16.
+//  U-phase: the gradient block is split by d-quarters: each wave owns all 64
+//    outer rows x its quarter of d in FP32 registers and contracts the band
+//    operands with the transposed inner panel (32x32x16 FP16 MFMA).
+// Every outer row carries a power-of-two scale fixed before the pass from an
+// upper bound of |A_1| over all inner rows (the statistics bound every
+// probability by the row's and the column's negative mass), so the FP16
+// operands stay below 2^14; the scale is folded into the row's exponent (or
+// beta) term and divided out when the block is written.  Inner tiles stream into LDS with
+// direct global->LDS copies: the transposed panel of block t lands during
+// R(t), the rows of block t+1 during U(t).  The positive cell is left out;
+// the finalize kernel adds its exact FP32 term.
 // ----------------------------------------------------------------------------
 constexpr int BO = 64;
-constexpr int BI = 32;
-constexpr int YROW = 1024;  // LDS row pitch of the inner tile, bf16 elements
-
-__device__ __forceinline__ int ysw(int r) { return (r & 3) | ((r >> 1) & 12); }
+constexpr int BI = 16;
+constexpr int YROW = 1024 + 8;  // LDS row pitch of the inner tile (one spare 16-byte chunk: rows rotate banks)
+constexpr int APITCH = 24;  // FP16 elements per band-operand row (48 bytes: conflict-free reads)
+constexpr int XREG = 16;    // sweep steps of 32 whose X operands live in registers
 
 template <uint32_t MASK>
 struct Ladder {
@@ -505,17 +517,24 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     using L = Ladder<MASK>;
     constexpr int NP = L::NP;
     constexpr int NDS = L::NDS;
-    constexpr int NDB = NDS * 2;  // 16-wide output blocks
+    constexpr int NXR = NDS < XREG ? NDS : XREG;  // register-held sweep steps
+    constexpr int NXL = NDS - NXR;                // LDS-held sweep steps
+    constexpr int NJ = (NDS + 3) / 4;             // 32-wide output blocks per wave in the U-phase
 
     __shared__ __attribute__((aligned(16))) u16 Ys[BI * YROW];
-    __shared__ __attribute__((aligned(16))) u16 YTs[NDS * 32 * 32];
+    __shared__ __attribute__((aligned(16))) u16 YTs[NDS * 32 * BI];
+    constexpr int XROW = NXL * 32 + 8;  // one spare 16-byte chunk per row: consecutive rows rotate banks
+    __shared__ __attribute__((aligned(16))) u16 Xs[NXL > 0 ? BO * XROW : 8];
+    __shared__ __attribute__((aligned(16))) u16 At[NP][BO * APITCH];
     __shared__ __attribute__((aligned(16))) float tI[NP][BI];
     __shared__ __attribute__((aligned(16))) float tK[NP][BI];
     __shared__ float oT[3][NP][BO];
+    __shared__ float sfinal[BO];
     __shared__ float red[4][NP];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ol = lane & 15, g = lane >> 4;
+    const int l32 = lane & 31, h32 = lane >> 5;
     const int64_t o0 = (int64_t)blockIdx.x * BO;
     const int olocal = wave * 16 + ol;
     const int64_t o = o0 + olocal;
@@ -524,6 +543,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     const int64_t nb_begin = (int64_t)blockIdx.y * a.blocks_per_split;
     const int64_t nb_end = nb_begin + a.blocks_per_split < nblocks ? nb_begin + a.blocks_per_split : nblocks;
     const int D = a.D;
+    const int jlo = (wave * NDS) / 4, jhi = ((wave + 1) * NDS) / 4;  // this wave's 32-wide d-blocks
 
     // zero the inner tile once so rows past the end only ever hold finite values
     for (int e = tid; e < BI * YROW / 8; e += 256) *(uint4 *)&Ys[e * 8] = make_uint4(0, 0, 0, 0);
@@ -532,125 +552,156 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         const float *src = which == 0 ? a.oA : (which == 1 ? a.oC : a.oRho);
         oT[which][p][r] = (o0 + r < a.NO) ? src[p * a.NO + o0 + r] : 0.f;
     }
-
-    // this lane's 16 outer rows as B operands: row o, d = 32 ds + 8 g .. + 7
-    bf16x8 xf[NDS];
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (ovalid) v = *(const uint4 *)(a.X + o * D + 32 * ds + 8 * g);
-        xf[ds] = as_bf16x8(v);
+    // per-row power-of-two operand scale: 2^14 / (bound of |A_1| over every inner row)
+    if (tid < BO) {
+        const int64_t orow = o0 + tid;
+        float sc = 1.0f;
+        if (orow < a.NO) {
+            const float ixP = a.oInv[(NP - 1) * a.NO + orow];
+            float U = 0.f;
+            for (int p = 0; p < NP; ++p) {
+                const float own = a.oNeg ? a.oNeg[p * a.NO + orow] : 0.f;
+                const float gt = a.gterm ? a.gterm[p] : a.gterm_val[p];
+                U += a.wnorm[p] * (a.oInv[p * a.NO + orow] / ixP) * a.iyrmax[p] * (own + gt);
+            }
+            if (U > 0.f) sc = ldexpf(1.0f, max(-126, min(126, 14 - (ilogbf(U) + 1))));
+        }
+        sfinal[tid] = sc;
+    }
+    __syncthreads();
+    for (int e = tid; e < NP * BO; e += 256) {
+        const int p = e / BO, r = e % BO;
+        if (SIG) oT[1][p][r] *= sfinal[r];
+        else oT[1][p][r] += log2f(sfinal[r]);
+    }
+    // outer rows, d >= 32 NXR, into LDS
+    if constexpr (NXL > 0) {
+        for (int r = wave; r < BO; r += 4) {
+            const int64_t orow = o0 + r;
+            if (orow < a.NO && lane < NXL * 4) dma16(a.X + orow * D + 32 * NXR + 8 * lane, &Xs[r * XROW]);
+        }
     }
 
-    f32x4 dacc[NDB];
+    // this lane's outer row as B operands for the register-held part: d = 32 ds + 8 g .. + 7
+    bf16x8 xf[NXR];
+    {
+        const u16 *xrow = a.X + (ovalid ? o : 0) * D + 8 * g;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) dacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ds = 0; ds < NXR; ++ds) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (ovalid) v = *(const uint4 *)(xrow + 32 * ds);
+            xf[ds] = as_bf16x8(v);
+        }
+    }
+
+    f32x16 dacc[2][NJ];
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dacc[ob][j][r] = 0.f;
     float Cacc[NP], Lacc[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) Cacc[p] = Lacc[p] = 0.f;
-
-    // issue the copy of inner rows [32 nb, 32 nb + 32) into Ys (swizzled 16-byte chunks)
+    // copies of inner rows [16 nb, 16 nb + 16) into Ys
     auto issue_rows = [&](int64_t nb) {
         constexpr int halves = (NDS * 4 + 63) / 64;
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            const int r = wave * 8 + rr;
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = wave * 4 + rr;
             const int64_t n = nb * BI + r;
+            if (n < a.NI) {
 #pragma unroll
-            for (int h = 0; h < halves; ++h) {
-                const int c = (h * 64 + lane) ^ ysw(r);
-                if (n < a.NI && c < NDS * 4) dma16(a.Y + n * D + 8 * c, &Ys[r * YROW + h * 512]);
+                for (int h = 0; h < halves; ++h) {
+                    const int c = h * 64 + lane;
+                    if (c < NDS * 4) dma16(a.Y + n * D + 8 * c, &Ys[r * YROW + h * 512]);
+                }
             }
         }
     };
-    // issue the copy of the transposed panel rows d < 32 NDS into YTs (64 bytes per d-row)
+    // copies of the transposed 16-row panel, d-rows d < 32 NDS of 32 bytes; chunk
+    // position = chunk ^ ((d >> 3) & 1), which for these copies depends on the lane only
+    const int panel_lane_off = (lane >> 1) * BI + 8 * ((lane & 1) ^ ((lane >> 4) & 1));
     auto issue_panel = [&](int64_t nb) {
-        constexpr int insts = NDS * 32 / 16;
-        for (int ins = wave; ins < insts; ins += 4) {
-            const int d = ins * 16 + (lane >> 2), pos = lane & 3;
-            const int gch = pos ^ ((d >> 2) & 3);
-            dma16(a.YTb + ((nb * D + d) * 32 + 8 * gch), &YTs[ins * 16 * 32]);
-        }
+        constexpr int insts = NDS;  // 32 d-rows (1 KB) per copy
+        const u16 *base = a.YTb + nb * D * BI + panel_lane_off;
+        for (int ins = wave; ins < insts; ins += 4) dma16(base + ins * 512, &YTs[ins * 512]);
     };
-    float tnext[2];
+    float tnext;
     auto load_tables = [&](int64_t nb) {
-        for (int c = 0; c < 2; ++c) {
-            const int e = tid + 256 * c;
-            tnext[c] = 0.f;
-            if (e < 2 * NP * BI) {
-                const int which = e / (NP * BI), p = (e / BI) % NP, r = e % BI;
-                const int64_t n = nb * BI + r;
-                if (n < a.NI) tnext[c] = (which == 0 ? a.iI : a.iKap)[p * a.NI + n];
-            }
+        tnext = 0.f;
+        if (tid < 2 * NP * BI) {
+            const int which = tid / (NP * BI), p = (tid / BI) % NP, r = tid % BI;
+            const int64_t n = nb * BI + r;
+            if (n < a.NI) tnext = (which == 0 ? a.iI : a.iKap)[p * a.NI + n];
         }
     };
     auto store_tables = [&]() {
-        for (int c = 0; c < 2; ++c) {
-            const int e = tid + 256 * c;
-            if (e < 2 * NP * BI) {
-                const int which = e / (NP * BI), p = (e / BI) % NP, r = e % BI;
-                (which == 0 ? tI : tK)[p][r] = tnext[c];
-            }
+        if (tid < 2 * NP * BI) {
+            const int which = tid / (NP * BI), p = (tid / BI) % NP, r = tid % BI;
+            (which == 0 ? tI : tK)[p][r] = tnext;
         }
     };
 
+    __syncthreads();  // zero-fill and tables done before the first copy lands
     if (nb_begin < nb_end) {
-        __syncthreads();  // zero-fill of Ys done before the first copy lands
         issue_rows(nb_begin);
         load_tables(nb_begin);
         store_tables();
-        wait_vm();
-        __syncthreads();
     }
-
-    float row_scale = 0x1p126f;  // this lane's outer row: band operands are multiplied by it
-
-    // lane's inner rows for the two 16-row MFMA blocks: n = 8 (ol>>2) + 4 h + (ol&3)
-    const int nrow0 = 8 * (ol >> 2) + (ol & 3), nrow1 = nrow0 + 4;
+    wait_vm();
+    __syncthreads();
 
     for (int64_t nb = nb_begin; nb < nb_end; ++nb) {
         if (a.do_update) issue_panel(nb);
 
         // ---------------- R-phase: recompute S^T with prefix snapshots
-        f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
-        float ap[NP][8];
+        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+        float ap[NP][4];
         const int64_t n0 = nb * BI;
+        bool vm[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int64_t n = n0 + 4 * g + t;
+            vm[t] = ovalid & (n < a.NI) & (n != o + a.diag_shift);
+        }
+        const u16 *yrow = &Ys[ol * YROW + 8 * g];
+        const u16 *xrow_l = &Xs[(NXL > 0 ? olocal * XROW : 0) + 8 * g];
         static_for<0, NDS>([&](auto dsc) {
             constexpr int ds = decltype(dsc)::value;
-            const int c = 4 * ds + g;
-            const bf16x8 y0 = *(const bf16x8 *)&Ys[nrow0 * YROW + 8 * (c ^ ol)];
-            const bf16x8 y1 = *(const bf16x8 *)&Ys[nrow1 * YROW + 8 * (c ^ ol)];
-            S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(y0, xf[ds], S0, 0, 0, 0);
-            S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(y1, xf[ds], S1, 0, 0, 0);
-            if constexpr ((ds & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+            const bf16x8 yv = *(const bf16x8 *)(yrow + 32 * ds);
+            bf16x8 xv;
+            if constexpr (ds < NXR) {
+                xv = xf[ds];
+            } else {
+                xv = *(const bf16x8 *)(xrow_l + 32 * (ds - NXR));
+            }
+            S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yv, xv, S, 0, 0, 0);
             static_for<0, NP>([&](auto pc) {
                 constexpr int p = decltype(pc)::value;
                 if constexpr (ds == L::pos(p)) {
                     const float A = oT[0][p][olocal], Cc = oT[1][p][olocal], Rh = oT[2][p][olocal];
-                    const float4 i0v = *(const float4 *)&tI[p][8 * g], i1v = *(const float4 *)&tI[p][8 * g + 4];
-                    const float iy[8] = {i0v.x, i0v.y, i0v.z, i0v.w, i1v.x, i1v.y, i1v.z, i1v.w};
-                    float kp[8];
-                    if constexpr (!SIG) {
-                        const float4 k0v = *(const float4 *)&tK[p][8 * g], k1v = *(const float4 *)&tK[p][8 * g + 4];
-                        kp[0] = k0v.x; kp[1] = k0v.y; kp[2] = k0v.z; kp[3] = k0v.w;
-                        kp[4] = k1v.x; kp[5] = k1v.y; kp[6] = k1v.z; kp[7] = k1v.w;
-                    }
+                    const float4 iy = *(const float4 *)&tI[p][4 * g];
+                    float4 kp = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (!SIG) kp = *(const float4 *)&tK[p][4 * g];
+                    const float iya[4] = {iy.x, iy.y, iy.z, iy.w};
+                    const float kpa[4] = {kp.x, kp.y, kp.z, kp.w};
 #pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const float S = t < 4 ? S0[t] : S1[t - 4];
-                        const int64_t n = n0 + 8 * g + t;
-                        const bool valid = ovalid & (n < a.NI) & (n != o + a.diag_shift);
+                    for (int t = 0; t < 4; ++t) {
+                        const float Sv = S[t];
+                        const bool valid = vm[t];
                         float av;
                         if constexpr (!SIG) {
-                            const float e = __builtin_amdgcn_exp2f(fmaf(S * A, iy[t], Cc));
-                            av = e * fmaf(Rh, iy[t], kp[t]);
+                            const float e = __builtin_amdgcn_exp2f(fmaf(Sv * A, iya[t], Cc));
+                            av = e * fmaf(Rh, iya[t], kpa[t]);
                         } else {
-                            const float u = fmaf(S * A, iy[t], a.b2);
+                            const float u = fmaf(Sv * A, iya[t], a.b2);
                             const float tt = __builtin_amdgcn_exp2f(-fabsf(u));
                             const float w = 1.f + tt;
                             const float rr = __builtin_amdgcn_rcpf(w);
                             const float sg = u >= 0.f ? rr : tt * rr;
-                            av = sg * Cc * iy[t];  // Cc holds beta_o for the sigmoid form
+                            av = sg * Cc * iya[t];  // Cc holds beta_o for the sigmoid form
                             if (a.want_loss) {
                                 // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
                                 const float corr = (tt - (w - 1.f)) * rr * kLog2e;
@@ -659,96 +710,91 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
                             }
                         }
                         av = valid ? av : 0.f;
-                        Cacc[p] = fmaf(av, S, Cacc[p]);
+                        Cacc[p] = fmaf(av, Sv, Cacc[p]);
                         ap[p][t] = av;
                     }
                 }
             });
+            if constexpr ((ds & 1) == 1) __builtin_amdgcn_sched_barrier(0);
         });
+
+        // band operands: suffix sums in place (widest band first), FP16 into LDS
+        if (a.do_update) {
+            static_for<0, NP - 1>([&](auto bc) {
+                constexpr int b = NP - 2 - decltype(bc)::value;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) ap[b][t] += ap[b + 1][t];
+            });
+            static_for<0, NP>([&](auto bc) {
+                constexpr int b = decltype(bc)::value;
+                f16x4 v;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = (_Float16)ap[b][t];
+                *(f16x4 *)&At[b][olocal * APITCH + 4 * g] = v;
+            });
+        }
         wait_vm();
-        __syncthreads();  // panel nb in LDS; every wave is done reading Ys
+        __syncthreads();  // panel nb and band operands in LDS; every wave is done reading Ys
         if (nb + 1 < nb_end) {
             issue_rows(nb + 1);
             load_tables(nb + 1);
         }
 
-        // ---------------- U-phase: dX[:, band b] += A_b Y[:, band b]
-        // Band operands A_b = sum_{p>=b} a^p (suffix sums in place, widest first),
-        // multiplied by this row's power-of-two scale and rounded to FP16.  The
-        // scale only ever decreases: it keeps |A_1| (the largest, all terms share
-        // one sign) below 2^14; when it drops, the FP32 accumulator is rescaled
-        // by the same exact power of two.  The scale is divided out at the end.
+        // ---------------- U-phase: dX[:, quarter] += A_band . Y[:, quarter]
         if (a.do_update) {
-            static_for<0, NP - 1>([&](auto bc) {
-                constexpr int b = NP - 2 - decltype(bc)::value;
+            int cur_band = -1;
+            f16x8 af[2];
+            static_for<0, NJ>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                const int db = jlo + j;
+                if (db < jhi) {
+                    int band = 0;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) ap[b][t] += ap[b + 1][t];
-            });
-            float amax = 0.f;
+                    for (int p = 0; p < NP - 1; ++p) band += (db >= L::pos(p) + 1) ? 1 : 0;
+                    if (band != cur_band) {
+                        cur_band = band;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) amax = fmaxf(amax, fabsf(ap[0][t]));
-            amax = fmaxf(amax, __shfl_xor(amax, 16));
-            amax = fmaxf(amax, __shfl_xor(amax, 32));
-            float sc = row_scale;
-            if (amax > 0.f) {
-                const int e = ilogbf(amax) + 1;  // amax < 2^e
-                sc = fminf(row_scale, ldexpf(1.0f, min(126, 14 - e)));
-            }
-            if (__any(sc < row_scale)) {
-                const float f = sc / row_scale;
-                float fr[4];
+                        for (int ob = 0; ob < 2; ++ob)
+                            af[ob] = *(const f16x8 *)&At[band][(ob * 32 + l32) * APITCH + 8 * h32];
+                    }
+                    const int d = 32 * db + l32;
+                    const f16x8 bfr = *(const f16x8 *)&YTs[d * BI + 8 * (h32 ^ ((d >> 3) & 1))];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) fr[r] = __shfl(f, 4 * g + r);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) dacc[db][r] *= fr[r];
-            }
-            row_scale = sc;
-            static_for<0, NP>([&](auto bc) {
-                constexpr int b = decltype(bc)::value;
-                float v[8];
-#pragma unroll
-                for (int t = 0; t < 8; ++t) v[t] = ap[b][t] * sc;
-                const f16x8 Ab = pack_f16x8(v);
-                constexpr int db_lo = b == 0 ? 0 : 2 * (L::pos(b - 1) + 1);
-                constexpr int db_hi = 2 * (L::pos(b) + 1);
-                static_for<db_lo, db_hi>([&](auto dbc) {
-                    constexpr int db = decltype(dbc)::value;
-                    const int d = 16 * db + ol;
-                    const f16x8 yt = *(const f16x8 *)&YTs[d * 32 + 8 * (g ^ ((ol >> 2) & 3))];
-                    dacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ab, yt, dacc[db], 0, 0, 0);
-                    if constexpr ((db & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-                });
+                    for (int ob = 0; ob < 2; ++ob)
+                        dacc[ob][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ob], bfr, dacc[ob][j], 0, 0, 0);
+                }
             });
         }
         if (nb + 1 < nb_end) store_tables();
         wait_vm();
-        __syncthreads();  // rows nb+1 in LDS; every wave is done reading YTs
+        __syncthreads();  // rows nb+1 in LDS; every wave is done reading YTs and At
     }
 
-    // ---------------- write the raw gradient block and the radial sums
+    // ---------------- write the raw gradient block (scale divided out) and the radial sums
     const int64_t split = blockIdx.y;
     if (a.do_update) {
         float *dst = a.part + split * a.NO * D;
-        float inv_sc[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) inv_sc[r] = 1.0f / __shfl(row_scale, 4 * g + r);
+        for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+            for (int r = 0; r < 16; ++r) {
+                const int orow = ob * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+                const float inv_sc = 1.0f / sfinal[orow];
+                if (o0 + orow < a.NO) {
+                    float *rowp = dst + (o0 + orow) * D + l32;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t orow = o0 + wave * 16 + 4 * g + r;
-                if (orow < a.NO) dst[orow * D + 16 * db + ol] = dacc[db][r] * inv_sc[r];
+                    for (int j = 0; j < NJ; ++j)
+                        if (jlo + j < jhi) rowp[32 * (jlo + j)] = dacc[ob][j][r] * inv_sc;
+                }
             }
-        }
     }
+    const float inv_own = 1.0f / sfinal[olocal];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         float c = Cacc[p];
         c += __shfl_xor(c, 16);
         c += __shfl_xor(c, 32);
-        if (g == 0 && ovalid) a.Cpart[(split * NP + p) * a.NO + o] = c;
+        if (g == 0 && ovalid) a.Cpart[(split * NP + p) * a.NO + o] = c * inv_own;
     }
     if (SIG && a.want_loss) {
 #pragma unroll
@@ -762,6 +808,29 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             a.lossparts[((int64_t)a.loss_slot0 + split * gridDim.x + blockIdx.x) * NP + tid] = v * kLn2;
         }
     }
+}
+
+// ----------------------------------------------------------------------------
+// k_maxes: gmax[t][p] = max over the rows of table t, prefix p (one block each;
+// a fixed tree, so the result does not depend on scheduling).
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_maxes(const float *t0, const float *t1, const float *t2, const float *t3,
+                                               int64_t n0, int64_t n1, int64_t n2, int64_t n3, int P,
+                                               float *gmax) {
+    __shared__ float red[256];
+    const int t = blockIdx.x / P, p = blockIdx.x % P;
+    const float *src = t == 0 ? t0 : t == 1 ? t1 : t == 2 ? t2 : t3;
+    const int64_t n = t == 0 ? n0 : t == 1 ? n1 : t == 2 ? n2 : n3;
+    float m = 0.f;
+    if (src)
+        for (int64_t i = threadIdx.x; i < n; i += 256) m = fmaxf(m, src[p * n + i]);
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int h = 128; h >= 1; h >>= 1) {
+        if ((int)threadIdx.x < h) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + h]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) gmax[t * P + p] = red[0];
 }
 
 // ----------------------------------------------------------------------------
@@ -851,7 +920,7 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_scale_copy(const u16 *x, const float *sig, int64_t rows, int D, u16 *xs, u16 *xt, hipStream_t s) {
-    hipLaunchKernelGGL(k_scale_copy, dim3((unsigned)((rows + 31) / 32), (unsigned)(D / 64)), dim3(256), 0, s, x,
+    hipLaunchKernelGGL(k_scale_copy, dim3((unsigned)((rows + 15) / 16), (unsigned)((D + 127) / 128)), dim3(256), 0, s, x,
                        sig, rows, D, xs, xt);
     return hipGetLastError();
 }
@@ -914,6 +983,12 @@ hipError_t launch_bwd(const BwdArgs &a, uint32_t mask, bool sig, int64_t nsplit,
     UFORM_LADDERS(UFORM_CASE)
 #undef UFORM_CASE
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_maxes(const float *t0, const float *t1, const float *t2, const float *t3, int64_t n0, int64_t n1,
+                        int64_t n2, int64_t n3, int P, float *gmax, hipStream_t s) {
+    hipLaunchKernelGGL(k_maxes, dim3((unsigned)(4 * P)), dim3(256), 0, s, t0, t1, t2, t3, n0, n1, n2, n3, P, gmax);
+    return hipGetLastError();
 }
 
 hipError_t launch_finalize(const FinArgs &a, hipStream_t s) {

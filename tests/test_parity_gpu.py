@@ -88,7 +88,8 @@ def test_rows_clustered_with_offset():
 
 @pytest.mark.parametrize("D,prefixes,kind", [
     (512, (64, 128, 256, 512), INFONCE), (256, (256,), SIGLIP), (256, (64, 128, 256), INFONCE_ROWS),
-    (128, (64, 128), INFONCE), (1024, (1024,), INFONCE), (512, (512,), SIGLIP), (128, (128,), INFONCE)])
+    (128, (64, 128), INFONCE), (1024, (1024,), INFONCE), (512, (512,), SIGLIP), (128, (128,), INFONCE),
+    (192, (64, 128), SIGLIP), (320, (64, 128, 256), INFONCE)])
 def test_other_ladders(D, prefixes, kind):
     R, N = (160, 160) if kind != INFONCE_ROWS else (70, 200)
     qb, kb = make_inputs(R, N, D, noise=0.4, seed=31 + D)
