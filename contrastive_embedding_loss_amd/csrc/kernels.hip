@@ -53,8 +53,8 @@ __device__ __forceinline__ f16x8 pack_f16x8(const float (&v)[8]) {
 // Sum over the 32 lanes of each wave half of v[lane & 31]: a reduce-scatter
 // butterfly (31 exchanges instead of 32 x 5).
 __device__ __forceinline__ float reduce_scatter32(float (&v)[32], int lane) {
-#pragma unroll
-    for (int h = 16; h >= 1; h >>= 1) {
+    static_for<0, 5>([&](auto sc) {
+        constexpr int h = 16 >> decltype(sc)::value;
         const bool up = (lane & h) != 0;
 #pragma unroll
         for (int i = 0; i < h; ++i) {
@@ -62,7 +62,7 @@ __device__ __forceinline__ float reduce_scatter32(float (&v)[32], int lane) {
             const float send = up ? v[i] : v[i + h];
             v[i] = keep + __shfl_xor(send, h);
         }
-    }
+    });
     return v[0];
 }
 
