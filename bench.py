@@ -22,6 +22,27 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 FLOP/clk/CU, dense
 PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "contrastive_embedding_loss_amd", "csrc", "kernels.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per backward launch from the committed counter summary, or None.
+
+    The summary's record names the sha256 of the kernel source it was measured
+    on; a record for other source (the kernels changed since) is not used.
+    """
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    for line in open(path):
+        if line.startswith("traffic-record "):
+            kv = dict(f.split("=", 1) for f in line.split()[1:])
+            if kv.get("kernel") == "k_bwd" and kv.get("source_sha256_16") == sha:
+                return int(kv["read_bytes"]) + int(kv["write_bytes"])
+    return None
 
 
 def main():
@@ -31,7 +52,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="infonce_32768")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=12288, help="rows of the oracle's timed sample")
+    ap.add_argument("--cpu-sample", type=int, default=24576, help="rows of the oracle's timed sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (a known-size kernel "
+                         "against which the HBM byte counters are scaled) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the loss's multi-GPU "
@@ -44,8 +68,18 @@ def main():
     from contrastive_embedding_loss_amd import binding
     from contrastive_embedding_loss_amd.inputs import WORKLOADS, bf16_bits_to_f32, make_inputs, workload_inputs
 
-    w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}), flush=True)
+        return
+
+    w = WORKLOADS[args.workload]
     t0 = time.time()
     qb, kb = workload_inputs(w)
     q = torch.from_numpy(bf16_bits_to_f32(qb)).to(dev).to(torch.bfloat16)
@@ -87,14 +121,16 @@ def main():
           file=sys.stderr, flush=True)
 
     # dominant kernel: the backward pass kernel (launched twice per step: rows, columns).
-    # Algorithmic MFMA work of one launch: 4 R N D (the full-width logit recompute 2 R N D and
-    # the gradient contraction 2 R N D of its pass).
+    # Algorithmic MFMA work credited to one launch: 3 R N D = its gradient contraction 2 R N D
+    # plus half of the single logit recompute 2 R N D that the step's count includes (each
+    # launch actually executes a full recompute, 4 R N D in all; the extra is not credited).
     launches = 2
     bwd_ms = kern_per_step.get("k_bwd", float("nan")) / launches
-    bwd_tflops = 4.0 * R * N * D / (bwd_ms * 1e-3) / 1e12
+    bwd_tflops = 3.0 * R * N * D / (bwd_ms * 1e-3) / 1e12
     roofline = {"kernel": "k_bwd", "bound": "mfma", "achieved": round(bwd_tflops, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "avg_launch_ms": round(bwd_ms, 4)}
+                "traffic": measured_traffic(w.name), "avg_launch_ms": round(bwd_ms, 4),
+                "executed_tflops": round(4.0 * R * N * D / (bwd_ms * 1e-3) / 1e12, 1)}
 
     cpu = None
     if not args.no_cpu_baseline:
