@@ -62,12 +62,12 @@ struct StatsArgs {
 };
 
 struct BwdArgs {
-    const u16 *X;    // outer rows, BF16 [NO][D]
-    const u16 *Y;    // inner rows scaled by sig, BF16 [NI][D]
-    const u16 *YTb;  // inner rows scaled by sig, FP16, transposed panels [NI/16][D][16]
+    const _Float16 *X16;  // outer rows scaled by their sig, FP16 [NO][D]
+    const _Float16 *Y16;  // inner rows scaled by their sig, FP16 [NI][D]
     int64_t NO, NI;
     int D;
     const float *oA, *oC, *oRho;  // outer tables [P][NO]
+    const float *oSig;            // outer rows' sig [NO]
     const float *iI, *iKap;       // inner tables [P][NI]: inv / sig and Kap / sig
     float b2;                     // sigmoid form: bias * log2(e)
     // operand-scale bound: U_o = sum_p wnorm_p (inv_p / inv_P)_o iyrmax_p (oNeg_p,o + gterm_p)
@@ -107,7 +107,7 @@ struct LossArgs {
 
 // launchers (kernels.hip)
 hipError_t launch_prep(const PrepArgs &a, hipStream_t s);
-hipError_t launch_scale_copy(const u16 *x, const float *sig, int64_t rows, int D, u16 *xs, u16 *xt, hipStream_t s);
+hipError_t launch_half_copy(const u16 *x, const float *sig, int64_t rows, int D, _Float16 *xh, hipStream_t s);
 hipError_t launch_fwd(const u16 *q, const u16 *k, int64_t R, int64_t N, int D, const Prefixes &pf, int64_t off,
                       const float *rowA, const float *colI, float cshift, float *rowpart, float *colpart,
                       hipStream_t s);

@@ -43,7 +43,7 @@ struct Plan {
     int64_t bps_row, bps_col;          // inner blocks per split
     int64_t slots_a, slots_b, nslots;  // loss partial slots
     // workspace offsets (bytes)
-    size_t o_invq, o_invk, o_qA, o_kA, o_posdot, o_qT, o_kT, o_qS, o_kS;
+    size_t o_invq, o_invk, o_qA, o_kA, o_posdot, o_qH, o_kH;
     size_t o_qIYR, o_kIYR, o_sigq, o_sigk, o_gamq, o_gamk;
     size_t o_qC, o_qRho, o_qKap, o_kC, o_kRho, o_kKap, o_negfrac, o_kNegfrac, o_diagA, o_gmax;
     size_t o_rowpart, o_colpart, o_part, o_Cpart, o_loss;
@@ -125,10 +125,9 @@ Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, in
     p.o_kNegfrac = take(fN);
     p.o_gmax = take(sizeof(float) * 4 * P);
     p.o_diagA = take(fR);
-    p.o_qT = take((want_dk ? sizeof(u16) * cdiv(R, 16) * 16 * D : 0));
-    p.o_kT = take((want_dq || !softmax ? sizeof(u16) * cdiv(N, 16) * 16 * D : 0));
-    p.o_qS = take((want_dk ? sizeof(u16) * R * D : 0));
-    p.o_kS = take((want_dq || !softmax ? sizeof(u16) * N * D : 0));
+    const bool bwd = want_dq || want_dk || !softmax;  // some backward pass runs
+    p.o_qH = take(bwd ? sizeof(u16) * R * D : 0);
+    p.o_kH = take(bwd ? sizeof(u16) * N * D : 0);
     p.o_rowpart = take(softmax ? sizeof(float) * p.nJt * P * R : 0);
     p.o_colpart = take(softmax ? sizeof(float) * p.nIt * P * N : 0);
     const size_t part_row = (want_dq || !softmax) ? sizeof(float) * p.nsplit_row * R * D : 0;
@@ -307,8 +306,7 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     float *invq = F(pl.o_invq), *invk = F(pl.o_invk), *qA = F(pl.o_qA), *kA = F(pl.o_kA), *posdot = F(pl.o_posdot);
     float *qIYR = F(pl.o_qIYR), *kIYR = F(pl.o_kIYR), *sigq = F(pl.o_sigq), *sigk = F(pl.o_sigk);
     float *gamq = F(pl.o_gamq), *gamk = F(pl.o_gamk);
-    u16 *qT = (u16 *)(base + pl.o_qT), *kT = (u16 *)(base + pl.o_kT);
-    u16 *qS = (u16 *)(base + pl.o_qS), *kS = (u16 *)(base + pl.o_kS);
+    _Float16 *qH = (_Float16 *)(base + pl.o_qH), *kH = (_Float16 *)(base + pl.o_kH);
     float *lossparts = F(pl.o_loss);
 
     PrepArgs pa{};
@@ -333,8 +331,10 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     pa.gamq = gamq;
     pa.gamk = gamk;
     LAUNCH_NAMED("k_prep", launch_prep(pa, s));
-    if (dk) LAUNCH_NAMED("k_scale_copy", launch_scale_copy(q, sigq, R, Di, qS, qT, s));
-    if (dq || !softmax) LAUNCH_NAMED("k_scale_copy", launch_scale_copy(k, sigk, N, Di, kS, kT, s));
+    if (dq || dk || !softmax) {
+        LAUNCH_NAMED("k_half_copy", launch_half_copy(q, sigq, R, Di, qH, s));
+        LAUNCH_NAMED("k_half_copy", launch_half_copy(k, sigk, N, Di, kH, s));
+    }
 
     StatsArgs sa{};
     sa.R = R;
@@ -390,9 +390,9 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
 
     auto pass = [&](bool rowpass, float *out) -> uform_status_t {
         BwdArgs ba{};
-        ba.X = rowpass ? q : k;
-        ba.Y = rowpass ? kS : qS;
-        ba.YTb = rowpass ? kT : qT;
+        ba.X16 = rowpass ? qH : kH;
+        ba.Y16 = rowpass ? kH : qH;
+        ba.oSig = rowpass ? sigq : sigk;
         ba.NO = rowpass ? R : N;
         ba.NI = rowpass ? N : R;
         ba.D = Di;
@@ -432,7 +432,7 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
         LAUNCH_NAMED("k_bwd", launch_bwd(ba, pl.mask, !softmax, nsplit, s));
         if (out) {
             FinArgs fa{};
-            fa.X = ba.X;
+            fa.X = rowpass ? q : k;
             fa.Y = rowpass ? k : q;
             fa.NO = ba.NO;
             fa.R = R;

@@ -126,53 +126,24 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// k_scale_copy: rows scaled by their power-of-two sig (exact), stored twice:
-// xs[r][d] in BF16, and xt[rb][d][0..15] = x[16 rb + n][d] sig in FP16 as
-// transposed 16-row panels (zero rows past the end), which give the
-// backward's second contraction contiguous 16-byte operands along the inner
-// index.  BF16 values times a power of two are exact in FP16 within range.
+// k_half_copy: xh[r][d] = x[r][d] * sig_r in FP16.  sig is a power of two
+// that brings the row norm into [1, 2), so the BF16 -> FP16 conversion is exact
+// for every element above FP16's subnormal range.  8 elements per thread.
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_scale_copy(const u16 *__restrict__ x, const float *__restrict__ sig,
-                                                    int64_t rows, int D, u16 *__restrict__ xs,
-                                                    u16 *__restrict__ xt) {
-    __shared__ u16 tile[16][128 + 2];
-    const int rb = blockIdx.x, dc = blockIdx.y, t = threadIdx.x;  // 16 rows x 128 d per block
-    {
-        const int n = t >> 4, d8 = (t & 15) * 8;
-        const int64_t r = (int64_t)rb * 16 + n;
-        unsigned int hw[4] = {0u, 0u, 0u, 0u};
-        if (r < rows && dc * 128 + d8 < D) {
-            const uint4 v = *(const uint4 *)(x + r * D + dc * 128 + d8);
-            const float sc = sig[r];
-            const unsigned int in[4] = {v.x, v.y, v.z, v.w};
-            unsigned int w[4];
+__global__ __launch_bounds__(256) void k_half_copy(const u16 *__restrict__ x, const float *__restrict__ sig,
+                                                   int64_t rows, int D, _Float16 *__restrict__ xh) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (e >= rows * D) return;
+    const float sc = sig[e / D];
+    const uint4 v = *(const uint4 *)(x + e);
+    const unsigned int in[4] = {v.x, v.y, v.z, v.w};
+    f16x8 h;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float lo = bf16_lo(in[i]) * sc, hi = bf16_hi(in[i]) * sc;
-                w[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
-                const _Float16 hlo = (_Float16)lo, hhi = (_Float16)hi;
-                hw[i] = (unsigned int)__builtin_bit_cast(unsigned short, hlo) |
-                        ((unsigned int)__builtin_bit_cast(unsigned short, hhi) << 16);
-            }
-            *(uint4 *)(xs + r * D + dc * 128 + d8) = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            tile[n][d8 + 2 * i] = (u16)(hw[i] & 0xffffu);
-            tile[n][d8 + 2 * i + 1] = (u16)(hw[i] >> 16);
-        }
+    for (int i = 0; i < 4; ++i) {
+        h[2 * i] = (_Float16)(bf16_lo(in[i]) * sc);
+        h[2 * i + 1] = (_Float16)(bf16_hi(in[i]) * sc);
     }
-    __syncthreads();
-    {
-        const int d = t >> 1, n8 = (t & 1) * 8;
-        if (dc * 128 + d < D) {
-            unsigned int w[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                w[i] = (unsigned int)tile[n8 + 2 * i][d] | ((unsigned int)tile[n8 + 2 * i + 1][d] << 16);
-            *(uint4 *)(xt + ((int64_t)rb * D + dc * 128 + d) * 16 + n8) = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-    }
+    *(f16x8 *)(xh + e) = h;
 }
 
 // ----------------------------------------------------------------------------
@@ -469,94 +440,123 @@ __global__ __launch_bounds__(256) void k_siglip_tabs(StatsArgs a) {
 // ----------------------------------------------------------------------------
 // k_bwd: one pass of the backward (row pass or column pass).
 //
-// Workgroup = 4 waves = 64 outer rows, one wave per SIMD.  X rows stay on chip
-// for the whole pass: d < 512 as MFMA operands in registers, the rest in LDS.
-// For every block of 16 inner rows:
-//  R-phase: each wave recomputes S^T for its own 16 outer rows over the prefix
-//    sweep (16x16x32 MFMA, inner rows in the M slot) and, at each prefix
-//    boundary (static MASK), forms the cell coefficients a^p = dL/dS^p with
-//    every scale folded in (softmax: 2^{S A_o iy + C_o} (Rho_o iy + Kap_n);
-//    sigmoid: sigma(l) Bt_o iy) and the radial sums C^p_o += a^p S^p.  The band
-//    operands A_b = sum_{p>=b} a^p (suffix sums, widest band first) are stored
-//    to LDS in FP16.
-//  U-phase: the gradient block is split by d-quarters: each wave owns all 64
-//    outer rows x its quarter of d in FP32 registers and contracts the band
-//    operands with the transposed inner panel (32x32x16 FP16 MFMA).
-// Every outer row carries a power-of-two scale fixed before the pass from an
-// upper bound of |A_1| over all inner rows (the statistics bound every
-// probability by the row's and the column's negative mass), so the FP16
-// operands stay below 2^14; the scale is folded into the row's exponent (or
-// beta) term and divided out when the block is written.  Inner tiles stream into LDS with
-// direct global->LDS copies: the transposed panel of block t lands during
-// R(t), the rows of block t+1 during U(t).  The positive cell is left out;
-// the finalize kernel adds its exact FP32 term.
+// Workgroup = 64 outer rows (the rows whose gradient the pass owns), 4 waves,
+// one per SIMD; wave w owns the w-th quarter of the prefix width Dw, both for
+// the logit recompute and for the gradient, so every inner element it reads
+// from LDS feeds four MFMAs and is read by one wave only.  The outer rows'
+// quarter stays in registers as FP16 MFMA operands for the whole pass, the
+// gradient quarter (64 x Dw/4) in FP32 accumulators.  For every block of 16
+// inner rows (one FP16 row-major tile in LDS, copied global->LDS two blocks
+// ahead into a ring of three):
+//  R: each wave forms its partial S^T over its quarter (16x16x32 FP16 MFMA)
+//     and stores it, plus snapshots at prefix ends inside the quarter, to
+//     LDS slots; S^p is the sum of the quarters below P_p plus the snapshot.
+//  E: lane o of wave w forms, for outer row o and inner rows 4w..4w+3, the
+//     cell coefficients a^p = dL/dS^p with every scale folded in (softmax:
+//     2^{S A_o iy_n + C_o} (Rho_o iy_n + Kap_n); sigmoid: sigma(l) Bt_o iy_n),
+//     the radial sums C^p_o += a^p S^p, and the band operands
+//     A_b = sum_{p>=b} a^p (suffix sums, widest band first), stored in FP16.
+//  U: dX[:, quarter] += A_band . Y[:, quarter] with 32x32x16 FP16 MFMA; the
+//     inner tile is read transposed (ds_read_b64_tr_b16), so one copy serves
+//     both contractions.
+// Operands are exact power-of-two rescalings: inner and outer rows by their
+// sig (BF16 -> FP16 is exact in range), and every outer row's band operand by
+// a static scale fixed before the pass from an upper bound of |A_1| over all
+// inner rows (the statistics bound every probability by the row's and the
+// column's negative mass), so FP16 operands stay below 2^14; the scale is
+// folded into the row's exponent (or beta) term and divided out at the write.
+// The positive cell is left out; the finalize kernel adds its exact FP32 term.
+// Barriers wait for LDS only: each wave waits for its own copies explicitly,
+// so the copies of the next blocks stay in flight across barriers.
 // ----------------------------------------------------------------------------
 constexpr int BO = 64;
 constexpr int BI = 16;
-constexpr int YROW = 1024 + 8;  // LDS row pitch of the inner tile (one spare 16-byte chunk: rows rotate banks)
-constexpr int APITCH = 24;  // FP16 elements per band-operand row (48 bytes: conflict-free reads)
-constexpr int XREG = 16;    // sweep steps of 32 whose X operands live in registers
+constexpr int NYBUF = 3;    // inner tiles in flight
+constexpr int SLOTP = 20;   // floats per outer row of an S slot (16 + 4: conflict-free 16-byte accesses)
+constexpr int APITCH = 24;  // FP16 per outer row of a band operand (16 + 8: conflict-free 16-byte reads)
 
 template <uint32_t MASK>
 struct Ladder {
     static constexpr int NP = __builtin_popcount(MASK);
-    static constexpr int NDS = 32 - __builtin_clz(MASK);  // sweep steps of 32
-    static constexpr int pos(int p) {                      // sweep step after which prefix p completes
+    static constexpr int NDS = 32 - __builtin_clz(MASK);  // 32-wide steps of the widest prefix
+    static constexpr int NQ = NDS / 4;                    // 32-wide steps per wave quarter
+    static constexpr int DW = 32 * NDS;
+    static constexpr int YP = DW + 16;                    // FP16 per LDS row of an inner tile
+    static constexpr int end(int p) {                     // steps covered by prefix p
         int c = -1;
         for (int ds = 0; ds < 32; ++ds)
             if (MASK & (1u << ds)) {
                 ++c;
-                if (c == p) return ds;
+                if (c == p) return ds + 1;
             }
         return -1;
     }
+    // prefixes that end strictly inside a wave's quarter need a snapshot slot
+    static constexpr uint32_t interior() {
+        uint32_t m = 0;
+        for (int p = 0; p < NP; ++p)
+            if (end(p) % NQ != 0) m |= 1u << (end(p) - 1);
+        return m;
+    }
+    static constexpr uint32_t INT_MASK = interior();
+    static constexpr int NSLOT = 4 + __builtin_popcount(INT_MASK);
+    static constexpr int wave_of(int p) { return (end(p) - 1) / NQ; }
+    static constexpr int snap_slot(int p) {  // slot holding S^p's last quarter
+        return (end(p) % NQ == 0) ? wave_of(p) : 4 + __builtin_popcount(INT_MASK & ((1u << (end(p) - 1)) - 1));
+    }
 };
 
-template <uint32_t MASK, bool SIG>
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+
+__device__ __forceinline__ f16x4 ds_read_tr(const _Float16 *p) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
+    return __builtin_bit_cast(f16x4, v);
+}
+
+template <uint32_t MASK, bool SIG, bool UPD>
 __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     using L = Ladder<MASK>;
     constexpr int NP = L::NP;
-    constexpr int NDS = L::NDS;
-    constexpr int NXR = NDS < XREG ? NDS : XREG;  // register-held sweep steps
-    constexpr int NXL = NDS - NXR;                // LDS-held sweep steps
-    constexpr int NJ = (NDS + 3) / 4;             // 32-wide output blocks per wave in the U-phase
+    constexpr int NQ = L::NQ;
+    constexpr int DW = L::DW;
+    constexpr int YP = L::YP;
+    constexpr int NSLOT = L::NSLOT;
+    constexpr int IPR = (DW / 8 + 63) / 64;  // 16-byte copy instructions per inner row
+    constexpr int NCW = BI * IPR / 4;        // copy instructions per wave per block
+    static_assert(NQ >= 1 && L::NDS % 4 == 0, "the widest prefix must be a multiple of 128");
 
-    __shared__ __attribute__((aligned(16))) u16 Ys[BI * YROW];
-    __shared__ __attribute__((aligned(16))) u16 YTs[NDS * 32 * BI];
-    constexpr int XROW = NXL * 32 + 8;  // one spare 16-byte chunk per row: consecutive rows rotate banks
-    __shared__ __attribute__((aligned(16))) u16 Xs[NXL > 0 ? BO * XROW : 8];
-    __shared__ __attribute__((aligned(16))) u16 At[NP][BO * APITCH];
-    __shared__ __attribute__((aligned(16))) float tI[NP][BI];
-    __shared__ __attribute__((aligned(16))) float tK[NP][BI];
-    __shared__ float oT[3][NP][BO];
-    __shared__ float sfinal[BO];
-    __shared__ float red[4][NP];
+    __shared__ __attribute__((aligned(16))) _Float16 Ys[NYBUF][BI * YP];
+    __shared__ __attribute__((aligned(16))) float Sl[NSLOT][BO * SLOTP];
+    __shared__ __attribute__((aligned(16))) _Float16 At[NP][BO * APITCH];
+    __shared__ __attribute__((aligned(16))) float tabs[2][2][NP][BI];  // [buffer][iI | iKap][p][inner row]
+    __shared__ float inv_sc[BO];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int ol = lane & 15, g = lane >> 4;
-    const int l32 = lane & 31, h32 = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4, l32 = lane & 31, h32 = lane >> 5;
     const int64_t o0 = (int64_t)blockIdx.x * BO;
-    const int olocal = wave * 16 + ol;
-    const int64_t o = o0 + olocal;
+    const int64_t o = o0 + lane;  // the outer row of this lane in the E-phase
     const bool ovalid = o < a.NO;
     const int64_t nblocks = (a.NI + BI - 1) / BI;
     const int64_t nb_begin = (int64_t)blockIdx.y * a.blocks_per_split;
     const int64_t nb_end = nb_begin + a.blocks_per_split < nblocks ? nb_begin + a.blocks_per_split : nblocks;
     const int D = a.D;
-    const int jlo = (wave * NDS) / 4, jhi = ((wave + 1) * NDS) / 4;  // this wave's 32-wide d-blocks
+    const int dq0 = w * (DW / 4);  // first column of this wave's quarter
 
-    // zero the inner tile once so rows past the end only ever hold finite values
-    for (int e = tid; e < BI * YROW / 8; e += 256) *(uint4 *)&Ys[e * 8] = make_uint4(0, 0, 0, 0);
-    for (int e = tid; e < 3 * NP * BO; e += 256) {
-        const int which = e / (NP * BO), p = (e / BO) % NP, r = e % BO;
-        const float *src = which == 0 ? a.oA : (which == 1 ? a.oC : a.oRho);
-        oT[which][p][r] = (o0 + r < a.NO) ? src[p * a.NO + o0 + r] : 0.f;
-    }
-    // per-row power-of-two operand scale: 2^14 / (bound of |A_1| over every inner row)
-    if (tid < BO) {
-        const int64_t orow = o0 + tid;
+    // ---- this lane's outer-row terms (every wave holds the same 64 rows)
+    float Ao[NP], Co[NP], Ro[NP];
+    float csc = 1.0f;  // 1 / (static scale * sig) of this lane's row, for the radial sums
+    {
+        const int64_t orow = ovalid ? o : 0;
         float sc = 1.0f;
-        if (orow < a.NO) {
+        if (ovalid) {
             const float ixP = a.oInv[(NP - 1) * a.NO + orow];
             float U = 0.f;
             for (int p = 0; p < NP; ++p) {
@@ -566,247 +566,248 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             }
             if (U > 0.f) sc = ldexpf(1.0f, max(-126, min(126, 14 - (ilogbf(U) + 1))));
         }
-        sfinal[tid] = sc;
-    }
-    __syncthreads();
-    for (int e = tid; e < NP * BO; e += 256) {
-        const int p = e / BO, r = e % BO;
-        if (SIG) oT[1][p][r] *= sfinal[r];
-        else oT[1][p][r] += log2f(sfinal[r]);
-    }
-    // outer rows, d >= 32 NXR, into LDS
-    if constexpr (NXL > 0) {
-        for (int r = wave; r < BO; r += 4) {
-            const int64_t orow = o0 + r;
-            if (orow < a.NO && lane < NXL * 4) dma16(a.X + orow * D + 32 * NXR + 8 * lane, &Xs[r * XROW]);
-        }
-    }
-
-    // this lane's outer row as B operands for the register-held part: d = 32 ds + 8 g .. + 7
-    bf16x8 xf[NXR];
-    {
-        const u16 *xrow = a.X + (ovalid ? o : 0) * D + 8 * g;
+        const float rsig = 1.0f / a.oSig[orow];  // exact: sig is a power of two
 #pragma unroll
-        for (int ds = 0; ds < NXR; ++ds) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (ovalid) v = *(const uint4 *)(xrow + 32 * ds);
-            xf[ds] = as_bf16x8(v);
+        for (int p = 0; p < NP; ++p) {
+            Ao[p] = a.oA[p * a.NO + orow] * rsig;
+            const float c = a.oC[p * a.NO + orow];
+            Co[p] = SIG ? c * sc : c + log2f(sc);
+            Ro[p] = SIG ? 0.f : a.oRho[p * a.NO + orow];
+        }
+        csc = rsig / sc;
+        if (w == 0) inv_sc[lane] = 1.0f / sc;
+    }
+
+    // ---- tables of inner block nb (plain loads; one value per thread)
+    auto load_tab = [&](int64_t nb) {
+        float v = 0.f;
+        if (tid < 2 * NP * BI) {
+            const int which = tid / (NP * BI), p = (tid / BI) % NP, r = tid % BI;
+            const int64_t n = nb * BI + r;
+            if (n < a.NI) v = (which == 0 ? a.iI : a.iKap)[p * a.NI + n];
+        }
+        return v;
+    };
+    auto store_tab = [&](int buf, float v) {
+        if (tid < 2 * NP * BI) {
+            const int which = tid / (NP * BI), p = (tid / BI) % NP, r = tid % BI;
+            tabs[buf][which][p][r] = v;
+        }
+    };
+    // ---- copy of inner block nb (rows clamped to the last row: always NCW copies per wave)
+    auto issue_y = [&](int64_t nb, int buf) {
+        static_for<0, NCW>([&](auto ic) {
+            const int inst = w * NCW + decltype(ic)::value;
+            const int r = inst / IPR, i = inst % IPR;
+            int64_t n = nb * BI + r;
+            if (n >= a.NI) n = a.NI - 1;
+            const int c = 64 * i + lane;
+            if (c < DW / 8) dma16(a.Y16 + n * D + 8 * c, &Ys[buf][r * YP + 512 * i]);
+        });
+    };
+
+    float t0 = 0.f;
+    if (nb_begin < nb_end) t0 = load_tab(nb_begin);
+
+    // ---- outer rows' quarter as B operands: rows 16 ob + l16, columns dq0 + 32 ks + 8 g4
+    f16x8 xr[4][NQ];
+#pragma unroll
+    for (int ob = 0; ob < 4; ++ob) {
+        const int64_t orow = o0 + 16 * ob + l16;
+        const _Float16 *src = a.X16 + (orow < a.NO ? orow : 0) * D + dq0 + 8 * g4;
+#pragma unroll
+        for (int ks = 0; ks < NQ; ++ks) {
+            f16x8 v = {};
+            if (orow < a.NO) v = *(const f16x8 *)(src + 32 * ks);
+            xr[ob][ks] = v;
         }
     }
 
-    f32x16 dacc[2][NJ];
+    f32x16 dacc[2][NQ];
 #pragma unroll
     for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+        for (int j = 0; j < NQ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) dacc[ob][j][r] = 0.f;
     float Cacc[NP], Lacc[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) Cacc[p] = Lacc[p] = 0.f;
-    // copies of inner rows [16 nb, 16 nb + 16) into Ys
-    auto issue_rows = [&](int64_t nb) {
-        constexpr int halves = (NDS * 4 + 63) / 64;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int r = wave * 4 + rr;
-            const int64_t n = nb * BI + r;
-            if (n < a.NI) {
-#pragma unroll
-                for (int h = 0; h < halves; ++h) {
-                    const int c = h * 64 + lane;
-                    if (c < NDS * 4) dma16(a.Y + n * D + 8 * c, &Ys[r * YROW + h * 512]);
-                }
-            }
-        }
-    };
-    // copies of the transposed 16-row panel, d-rows d < 32 NDS of 32 bytes; chunk
-    // position = chunk ^ ((d >> 3) & 1), which for these copies depends on the lane only
-    const int panel_lane_off = (lane >> 1) * BI + 8 * ((lane & 1) ^ ((lane >> 4) & 1));
-    auto issue_panel = [&](int64_t nb) {
-        constexpr int insts = NDS;  // 32 d-rows (1 KB) per copy
-        const u16 *base = a.YTb + nb * D * BI + panel_lane_off;
-        for (int ins = wave; ins < insts; ins += 4) dma16(base + ins * 512, &YTs[ins * 512]);
-    };
-    float tnext;
-    auto load_tables = [&](int64_t nb) {
-        tnext = 0.f;
-        if (tid < 2 * NP * BI) {
-            const int which = tid / (NP * BI), p = (tid / BI) % NP, r = tid % BI;
-            const int64_t n = nb * BI + r;
-            if (n < a.NI) tnext = (which == 0 ? a.iI : a.iKap)[p * a.NI + n];
-        }
-    };
-    auto store_tables = [&]() {
-        if (tid < 2 * NP * BI) {
-            const int which = tid / (NP * BI), p = (tid / BI) % NP, r = tid % BI;
-            (which == 0 ? tI : tK)[p][r] = tnext;
-        }
-    };
 
-    __syncthreads();  // zero-fill and tables done before the first copy lands
     if (nb_begin < nb_end) {
-        issue_rows(nb_begin);
-        load_tables(nb_begin);
-        store_tables();
+        issue_y(nb_begin, 0);
+        if (nb_begin + 1 < nb_end) {
+            issue_y(nb_begin + 1, 1);
+            wait_vm_n<NCW>();
+        } else {
+            wait_vm();
+        }
+        store_tab(0, t0);
     }
-    wait_vm();
-    __syncthreads();
+    lds_barrier();
 
-    for (int64_t nb = nb_begin; nb < nb_end; ++nb) {
-        if (a.do_update) issue_panel(nb);
+    int it = 0;
+    for (int64_t nb = nb_begin; nb < nb_end; ++nb, ++it) {
+        const int buf = it % NYBUF, tb = it & 1;
+        const _Float16 *Yb = Ys[buf];
 
-        // ---------------- R-phase: recompute S^T with prefix snapshots
-        f32x4 S = {0.f, 0.f, 0.f, 0.f};
-        float ap[NP][4];
-        const int64_t n0 = nb * BI;
-        bool vm[4];
+        // ---------------- R: partial S^T over this wave's quarter, 16 inner x 64 outer
+        {
+            f32x4 acc[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int64_t n = n0 + 4 * g + t;
-            vm[t] = ovalid & (n < a.NI) & (n != o + a.diag_shift);
+            for (int ob = 0; ob < 4; ++ob) acc[ob] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const _Float16 *yrow = Yb + l16 * YP + dq0 + 8 * g4;
+            auto put = [&](int slot) {
+#pragma unroll
+                for (int ob = 0; ob < 4; ++ob) *(f32x4 *)&Sl[slot][(16 * ob + l16) * SLOTP + 4 * g4] = acc[ob];
+            };
+            static_for<0, NQ>([&](auto kc) {
+                constexpr int ks = decltype(kc)::value;
+                const f16x8 yv = *(const f16x8 *)(yrow + 32 * ks);
+#pragma unroll
+                for (int ob = 0; ob < 4; ++ob)
+                    acc[ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(yv, xr[ob][ks], acc[ob], 0, 0, 0);
+                if constexpr (L::INT_MASK != 0 && ks + 1 < NQ) {
+                    const int J = w * NQ + ks;
+                    if ((L::INT_MASK >> J) & 1u) put(4 + __builtin_popcount(L::INT_MASK & ((1u << J) - 1u)));
+                }
+            });
+            put(w);
         }
-        const u16 *yrow = &Ys[ol * YROW + 8 * g];
-        const u16 *xrow_l = &Xs[(NXL > 0 ? olocal * XROW : 0) + 8 * g];
-        static_for<0, NDS>([&](auto dsc) {
-            constexpr int ds = decltype(dsc)::value;
-            const bf16x8 yv = *(const bf16x8 *)(yrow + 32 * ds);
-            bf16x8 xv;
-            if constexpr (ds < NXR) {
-                xv = xf[ds];
-            } else {
-                xv = *(const bf16x8 *)(xrow_l + 32 * (ds - NXR));
+        lds_barrier();  // slots complete; every wave is done with U of the previous block
+
+        const bool more = nb + 1 < nb_end, pre = nb + 2 < nb_end;
+        const float tn = more ? load_tab(nb + 1) : 0.f;
+        if (pre) issue_y(nb + 2, (it + 2) % NYBUF);
+
+        // ---------------- E: lane = outer row, inner rows 4 w .. 4 w + 3
+        {
+            const int64_t nw = nb * BI + 4 * w;
+            bool vm[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int64_t n = nw + t;
+                vm[t] = ovalid & (n < a.NI) & (n != o + a.diag_shift);
             }
-            S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yv, xv, S, 0, 0, 0);
+            // widest prefix first: the band operand A_p = sum_{p' >= p} a^p' is a running sum
+            float run[4] = {0.f, 0.f, 0.f, 0.f};
+            const float *slot_row = &Sl[0][lane * SLOTP + 4 * w];
             static_for<0, NP>([&](auto pc) {
-                constexpr int p = decltype(pc)::value;
-                if constexpr (ds == L::pos(p)) {
-                    const float A = oT[0][p][olocal], Cc = oT[1][p][olocal], Rh = oT[2][p][olocal];
-                    const float4 iy = *(const float4 *)&tI[p][4 * g];
-                    float4 kp = {0.f, 0.f, 0.f, 0.f};
-                    if constexpr (!SIG) kp = *(const float4 *)&tK[p][4 * g];
-                    const float iya[4] = {iy.x, iy.y, iy.z, iy.w};
-                    const float kpa[4] = {kp.x, kp.y, kp.z, kp.w};
+                constexpr int p = NP - 1 - decltype(pc)::value;
+                f32x4 Sp = *(const f32x4 *)(slot_row + L::snap_slot(p) * (BO * SLOTP));
+                static_for<0, L::wave_of(p)>([&](auto qc) {
+                    Sp += *(const f32x4 *)(slot_row + decltype(qc)::value * (BO * SLOTP));
+                });
+                const f32x4 iy = *(const f32x4 *)&tabs[tb][0][p][4 * w];
+                f32x4 kp = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (!SIG) kp = *(const f32x4 *)&tabs[tb][1][p][4 * w];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const float Sv = S[t];
-                        const bool valid = vm[t];
-                        float av;
-                        if constexpr (!SIG) {
-                            const float e = __builtin_amdgcn_exp2f(fmaf(Sv * A, iya[t], Cc));
-                            av = e * fmaf(Rh, iya[t], kpa[t]);
-                        } else {
-                            const float u = fmaf(Sv * A, iya[t], a.b2);
-                            const float tt = __builtin_amdgcn_exp2f(-fabsf(u));
-                            const float w = 1.f + tt;
-                            const float rr = __builtin_amdgcn_rcpf(w);
-                            const float sg = u >= 0.f ? rr : tt * rr;
-                            av = sg * Cc * iya[t];  // Cc holds beta_o for the sigmoid form
-                            if (a.want_loss) {
-                                // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
-                                const float corr = (tt - (w - 1.f)) * rr * kLog2e;
-                                const float lt = fmaxf(u, 0.f) + __builtin_amdgcn_logf(w) + corr;
-                                Lacc[p] += valid ? lt : 0.f;
-                            }
+                for (int t = 0; t < 4; ++t) {
+                    const float Sv = Sp[t];
+                    float av;
+                    if constexpr (!SIG) {
+                        const float e = __builtin_amdgcn_exp2f(fmaf(Sv * Ao[p], iy[t], Co[p]));
+                        av = e * fmaf(Ro[p], iy[t], kp[t]);
+                    } else {
+                        const float u = fmaf(Sv * Ao[p], iy[t], a.b2);
+                        const float tt = __builtin_amdgcn_exp2f(-fabsf(u));
+                        const float wq = 1.f + tt;
+                        const float rr = __builtin_amdgcn_rcpf(wq);
+                        const float sg = u >= 0.f ? rr : tt * rr;
+                        av = sg * Co[p] * iy[t];  // Co holds beta_o for the sigmoid form
+                        if (a.want_loss) {
+                            // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
+                            const float corr = (tt - (wq - 1.f)) * rr * kLog2e;
+                            const float lt = fmaxf(u, 0.f) + __builtin_amdgcn_logf(wq) + corr;
+                            Lacc[p] += vm[t] ? lt : 0.f;
                         }
-                        av = valid ? av : 0.f;
-                        Cacc[p] = fmaf(av, Sv, Cacc[p]);
-                        ap[p][t] = av;
                     }
+                    av = vm[t] ? av : 0.f;
+                    Cacc[p] = fmaf(av, Sv, Cacc[p]);
+                    run[t] += av;
                 }
-            });
-            if constexpr ((ds & 1) == 1) __builtin_amdgcn_sched_barrier(0);
-        });
-
-        // band operands: suffix sums in place (widest band first), FP16 into LDS
-        if (a.do_update) {
-            static_for<0, NP - 1>([&](auto bc) {
-                constexpr int b = NP - 2 - decltype(bc)::value;
+                if constexpr (UPD) {
+                    f16x4 v;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) ap[b][t] += ap[b + 1][t];
+                    for (int t = 0; t < 4; ++t) v[t] = (_Float16)run[t];
+                    *(f16x4 *)&At[p][lane * APITCH + 4 * w] = v;
+                }
+                __builtin_amdgcn_sched_barrier(0);
             });
-            static_for<0, NP>([&](auto bc) {
-                constexpr int b = decltype(bc)::value;
-                f16x4 v;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = (_Float16)ap[b][t];
-                *(f16x4 *)&At[b][olocal * APITCH + 4 * g] = v;
-            });
-        }
-        wait_vm();
-        __syncthreads();  // panel nb and band operands in LDS; every wave is done reading Ys
-        if (nb + 1 < nb_end) {
-            issue_rows(nb + 1);
-            load_tables(nb + 1);
         }
 
-        // ---------------- U-phase: dX[:, quarter] += A_band . Y[:, quarter]
-        if (a.do_update) {
-            int cur_band = -1;
-            f16x8 af[2];
-            static_for<0, NJ>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                const int db = jlo + j;
-                if (db < jhi) {
-                    int band = 0;
+        // every copy but the newest block's has landed (block nb + 1 in particular)
+        if (pre)
+            wait_vm_n<NCW>();
+        else
+            wait_vm();
+        if (more) store_tab(tb ^ 1, tn);
+        lds_barrier();  // band operands, tables and tile of block nb + 1 visible
+
+        // ---------------- U: dX[:, quarter] += A_band . Y[:, quarter]
+        if constexpr (UPD) {
+            const int G = lane >> 4, j = lane & 15;
+            const _Float16 *ysrc = Yb + (8 * (G >> 1) + (j >> 2)) * YP + 16 * (G & 1) + 4 * (j & 3);
+            static_for<0, NQ>([&](auto jc) {
+                constexpr int jb = decltype(jc)::value;
+                const int J = w * NQ + jb;
+                const int band = __builtin_popcount(MASK & ((1u << J) - 1u));
+                f16x8 af[2];
 #pragma unroll
-                    for (int p = 0; p < NP - 1; ++p) band += (db >= L::pos(p) + 1) ? 1 : 0;
-                    if (band != cur_band) {
-                        cur_band = band;
+                for (int ob = 0; ob < 2; ++ob) af[ob] = *(const f16x8 *)&At[band][(32 * ob + l32) * APITCH + 8 * h32];
+                const f16x4 lo = ds_read_tr(ysrc + 32 * J);
+                const f16x4 hi = ds_read_tr(ysrc + 32 * J + 4 * YP);
+                const f16x8 bf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-                        for (int ob = 0; ob < 2; ++ob)
-                            af[ob] = *(const f16x8 *)&At[band][(ob * 32 + l32) * APITCH + 8 * h32];
-                    }
-                    const int d = 32 * db + l32;
-                    const f16x8 bfr = *(const f16x8 *)&YTs[d * BI + 8 * (h32 ^ ((d >> 3) & 1))];
-#pragma unroll
-                    for (int ob = 0; ob < 2; ++ob)
-                        dacc[ob][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ob], bfr, dacc[ob][j], 0, 0, 0);
-                }
+                for (int ob = 0; ob < 2; ++ob)
+                    dacc[ob][jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ob], bf, dacc[ob][jb], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             });
         }
-        if (nb + 1 < nb_end) store_tables();
-        wait_vm();
-        __syncthreads();  // rows nb+1 in LDS; every wave is done reading YTs and At
     }
 
     // ---------------- write the raw gradient block (scale divided out) and the radial sums
     const int64_t split = blockIdx.y;
-    if (a.do_update) {
+    if constexpr (UPD) {
         float *dst = a.part + split * a.NO * D;
 #pragma unroll
         for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int orow = ob * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-                const float inv_sc = 1.0f / sfinal[orow];
+                const float s = inv_sc[orow];
                 if (o0 + orow < a.NO) {
-                    float *rowp = dst + (o0 + orow) * D + l32;
+                    float *rowp = dst + (o0 + orow) * D + dq0 + l32;
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j)
-                        if (jlo + j < jhi) rowp[32 * (jlo + j)] = dacc[ob][j][r] * inv_sc;
+                    for (int jb = 0; jb < NQ; ++jb) rowp[32 * jb] = dacc[ob][jb][r] * s;
                 }
             }
     }
-    const float inv_own = 1.0f / sfinal[olocal];
+    // radial sums and sigmoid loss: add the four waves' inner rows (slots are free now)
+    lds_barrier();
+    float *red = &Sl[0][0];  // [4][NP][BO] then [4][NP]
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        float c = Cacc[p];
-        c += __shfl_xor(c, 16);
-        c += __shfl_xor(c, 32);
-        if (g == 0 && ovalid) a.Cpart[(split * NP + p) * a.NO + o] = c * inv_own;
-    }
+    for (int p = 0; p < NP; ++p) red[(w * NP + p) * BO + lane] = Cacc[p];
     if (SIG && a.want_loss) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const float v = wave_sum(Lacc[p]);
-            if (lane == 0) red[wave][p] = v;
+            if (lane == 0) red[4 * NP * BO + w * NP + p] = v;
         }
-        __syncthreads();
-        if (tid < NP) {
-            const float v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-            a.lossparts[((int64_t)a.loss_slot0 + split * gridDim.x + blockIdx.x) * NP + tid] = v * kLn2;
+    }
+    lds_barrier();
+    if (w == 0 && ovalid) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const float c = ((red[(0 * NP + p) * BO + lane] + red[(1 * NP + p) * BO + lane]) +
+                             red[(2 * NP + p) * BO + lane]) + red[(3 * NP + p) * BO + lane];
+            a.Cpart[(split * NP + p) * a.NO + o] = c * csc;
         }
+    }
+    if (SIG && a.want_loss && tid < NP) {
+        const float *lr = red + 4 * NP * BO;
+        const float v = ((lr[0 * NP + tid] + lr[1 * NP + tid]) + lr[2 * NP + tid]) + lr[3 * NP + tid];
+        a.lossparts[((int64_t)a.loss_slot0 + split * gridDim.x + blockIdx.x) * NP + tid] = v * kLn2;
     }
 }
 
@@ -919,9 +920,9 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_scale_copy(const u16 *x, const float *sig, int64_t rows, int D, u16 *xs, u16 *xt, hipStream_t s) {
-    hipLaunchKernelGGL(k_scale_copy, dim3((unsigned)((rows + 15) / 16), (unsigned)((D + 127) / 128)), dim3(256), 0, s, x,
-                       sig, rows, D, xs, xt);
+hipError_t launch_half_copy(const u16 *x, const float *sig, int64_t rows, int D, _Float16 *xh, hipStream_t s) {
+    const int64_t chunks = rows * D / 8;  // D is a multiple of 64
+    hipLaunchKernelGGL(k_half_copy, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, x, sig, rows, D, xh);
     return hipGetLastError();
 }
 
@@ -951,10 +952,12 @@ hipError_t launch_siglip_tabs(const StatsArgs &a, hipStream_t s) {
 
 template <uint32_t MASK>
 static hipError_t launch_bwd_mask(const BwdArgs &a, bool sig, dim3 grid, hipStream_t s) {
-    if (sig)
-        hipLaunchKernelGGL((k_bwd<MASK, true>), grid, dim3(256), 0, s, a);
+    if (!sig)
+        hipLaunchKernelGGL((k_bwd<MASK, false, true>), grid, dim3(256), 0, s, a);
+    else if (a.do_update)
+        hipLaunchKernelGGL((k_bwd<MASK, true, true>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((k_bwd<MASK, false>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_bwd<MASK, true, false>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -1,0 +1,90 @@
+"""GPU parity at the full workload sizes, in the launch configuration the bench times.
+
+``infonce_4096`` is compared with a live oracle run element by element.  The
+three large workloads are compared with the oracle's stored values
+(``tests/golden/<workload>.npz``, written by ``tests/golden/make_golden.py``
+from ``oracle/`` alone): the loss and every prefix loss (rel <= 1e-3), 16
+sampled rows of dq and dk against 2e-3 x max|grad| of the whole oracle
+tensor, and 256 sampled row/column log-sum-exps and positive logits
+(max-abs <= 1e-3).  Properties that hold at any size are checked on the whole
+GPU output: finiteness, zeros beyond the widest prefix, and the Euler
+identity x . dx = 0 of the scale-invariant loss, per row (within 1e-2 of
+sum |x||dx|: a dropped radial term breaks it by O(1)).
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from contrastive_embedding_loss_amd import binding  # noqa: E402
+from contrastive_embedding_loss_amd.inputs import SIGLIP, WORKLOADS, bf16_bits_to_f32, workload_inputs  # noqa: E402
+from oracle import bf16_bits_to_f64, contrastive_fwd_bwd  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def run_gpu(w):
+    print(f"[case] {w.name} R={w.R} N={w.N} D={w.D} kind={w.kind}", flush=True)
+    qb, kb = workload_inputs(w)
+    q = torch.from_numpy(bf16_bits_to_f32(qb)).to("cuda").to(torch.bfloat16)
+    k = torch.from_numpy(bf16_bits_to_f32(kb)).to("cuda").to(torch.bfloat16)
+    loss, dq, dk, ex = binding.fwd_bwd(q, k, w.prefixes, w.scale, w.bias, w.kind, weights=w.weights,
+                                       row_offset=w.row_offset, extras=True)
+    torch.cuda.synchronize()
+    return qb, kb, q, k, loss.item(), dq, dk, ex
+
+
+def check_properties(w, q, k, dq, dk):
+    Dw = w.prefixes[-1]
+    for x, g in ((q, dq), (k, dk)):
+        assert torch.isfinite(g).all()
+        if Dw < w.D:
+            assert (g[:, Dw:] == 0).all()
+        # scale invariance of every prefix's cosine: <x[:P_p], dx-contribution> sums to 0 per row
+        xf = x.float()[:, :Dw]
+        euler = (xf * g[:, :Dw]).sum(dim=1).abs().max().item()
+        scale = (xf.abs() * g[:, :Dw].abs()).sum(dim=1).max().item()
+        print(f"[euler] max |x.dx| = {euler:.3e}, max sum |x||dx| = {scale:.3e}", flush=True)
+        assert euler <= 1e-2 * scale + 1e-30, (euler, scale)
+
+
+def test_infonce_4096_full_oracle():
+    w = WORKLOADS["infonce_4096"]
+    qb, kb, q, k, loss, dq, dk, ex = run_gpu(w)
+    ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), w.prefixes, w.scale, w.bias, w.kind,
+                              weights=w.weights)
+    assert abs(loss - ref["loss"]) <= 1e-3 * abs(ref["loss"])
+    np.testing.assert_allclose(ex["prefix_losses"].cpu().numpy(), ref["prefix_losses"], rtol=1e-3)
+    for name, g in (("dq", dq), ("dk", dk)):
+        e = np.abs(g.cpu().numpy() - ref[name]).max()
+        assert e <= 2e-3 * np.abs(ref[name]).max(), (name, e)
+    for name in ("row_lse", "col_lse", "pos_logit"):
+        assert np.abs(ex[name].cpu().numpy() - ref[name]).max() <= 1e-3, name
+    check_properties(w, q, k, dq, dk)
+
+
+@pytest.mark.parametrize("name", ["siglip_16384", "rows_4096x65536", "infonce_32768"])
+def test_large_workload_against_stored_oracle(name):
+    path = os.path.join(GOLDEN, f"{name}.npz")
+    g = np.load(path)
+    w = WORKLOADS[name]
+    qb, kb, q, k, loss, dq, dk, ex = run_gpu(w)
+    assert abs(loss - float(g["loss"])) <= 1e-3 * abs(float(g["loss"])), (loss, float(g["loss"]))
+    np.testing.assert_allclose(ex["prefix_losses"].cpu().numpy(), g["prefix_losses"], rtol=1e-3)
+    for name_g, t in (("dq", dq), ("dk", dk)):
+        rows = torch.from_numpy(g[f"{name_g}_rows"]).to("cuda")
+        got = t.index_select(0, rows).cpu().numpy()
+        e = np.abs(got - g[name_g]).max()
+        assert e <= 2e-3 * float(g[f"{name_g}_absmax"]), (name_g, e, float(g[f"{name_g}_absmax"]))
+        # the whole tensor's scale agrees too
+        assert abs(t.abs().max().item() - float(g[f"{name_g}_absmax"])) <= 2e-3 * float(g[f"{name_g}_absmax"])
+    idx = g["tab_idx"]
+    assert np.abs(ex["pos_logit"].cpu().numpy()[:, idx] - g["pos_logit"]).max() <= 1e-3
+    if w.kind != SIGLIP:
+        assert np.abs(ex["row_lse"].cpu().numpy()[:, idx] - g["row_lse"]).max() <= 1e-3
+        assert np.abs(ex["col_lse"].cpu().numpy()[:, g["col_idx"]] - g["col_lse"]).max() <= 1e-3
+    check_properties(w, q, k, dq, dk)
