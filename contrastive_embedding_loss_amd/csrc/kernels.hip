@@ -74,6 +74,19 @@ __device__ __forceinline__ void dma16(const void *g, void *lds_base) {
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// The same copies issued from inline assembly, 16 or 4 bytes per lane: the
+// compiler does not see them, so it adds no waits of its own before LDS
+// accesses; the caller waits for them with s_waitcnt vmcnt.  lds must be
+// wave-uniform (it goes to M0).
+__device__ __forceinline__ void dma16_async(const void *g, const void *lds) {
+    const uint32_t l = (uint32_t)(uintptr_t)lds;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory");
+}
+__device__ __forceinline__ void dma4_async(const void *g, const void *lds) {
+    const uint32_t l = (uint32_t)(uintptr_t)lds;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(l) : "memory");
+}
+
 // ----------------------------------------------------------------------------
 // k_prep: per-prefix inverse L2 norms of every row (and s log2(e) times
 // them), the exact power-of-two row scale sig ~ 1/|row| and the backward's
@@ -499,7 +512,25 @@ struct Ladder {
         return m;
     }
     static constexpr uint32_t INT_MASK = interior();
-    static constexpr int NSLOT = 4 + __builtin_popcount(INT_MASK);
+    static constexpr int NSLOT = 4 + __builtin_popcount(INT_MASK) + 1;  // the last one takes unused snapshots
+    static constexpr int DUMMY = NSLOT - 1;
+    // local steps (within a quarter) after which some wave takes a snapshot
+    static constexpr uint32_t local_snaps() {
+        uint32_t m = 0;
+        for (int J = 0; J < NDS; ++J)
+            if (INT_MASK & (1u << J)) m |= 1u << (J % NQ);
+        return m;
+    }
+    static constexpr uint32_t LPOS = local_snaps();
+    // local steps at which the band of some wave's 32-wide output block changes (step 0 always)
+    static constexpr int band_at(int J) { return __builtin_popcount(MASK & ((1u << J) - 1u)); }
+    static constexpr uint32_t band_steps() {
+        uint32_t m = 1u;
+        for (int J = 1; J < NDS; ++J)
+            if (J % NQ != 0 && band_at(J) != band_at(J - 1)) m |= 1u << (J % NQ);
+        return m;
+    }
+    static constexpr uint32_t BAND_STEPS = band_steps();
     static constexpr int wave_of(int p) { return (end(p) - 1) / NQ; }
     static constexpr int snap_slot(int p) {  // slot holding S^p's last quarter
         return (end(p) % NQ == 0) ? wave_of(p) : 4 + __builtin_popcount(INT_MASK & ((1u << (end(p) - 1)) - 1));
@@ -534,8 +565,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
 
     __shared__ __attribute__((aligned(16))) _Float16 Ys[NYBUF][BI * YP];
     __shared__ __attribute__((aligned(16))) float Sl[NSLOT][BO * SLOTP];
+    __shared__ __attribute__((aligned(16))) float tabs[NYBUF][256];  // per tile: [iI | iKap][p][inner row]
     __shared__ __attribute__((aligned(16))) _Float16 At[NP][BO * APITCH];
-    __shared__ __attribute__((aligned(16))) float tabs[2][2][NP][BI];  // [buffer][iI | iKap][p][inner row]
     __shared__ float inv_sc[BO];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -578,36 +609,37 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         if (w == 0) inv_sc[lane] = 1.0f / sc;
     }
 
-    // ---- tables of inner block nb (plain loads; one value per thread)
-    auto load_tab = [&](int64_t nb) {
-        float v = 0.f;
-        if (tid < 2 * NP * BI) {
-            const int which = tid / (NP * BI), p = (tid / BI) % NP, r = tid % BI;
-            const int64_t n = nb * BI + r;
-            if (n < a.NI) v = (which == 0 ? a.iI : a.iKap)[p * a.NI + n];
-        }
-        return v;
+    // ---- copies of inner block nb into ring slot buf: the FP16 tile (rows clamped
+    // to the last row) and its two tables; every wave issues NCW + 1 copies
+    auto copy_inst = [&](int64_t nb, int buf, auto ic) {  // copy instruction ic (< NCW) of this wave
+        const int inst = w * NCW + decltype(ic)::value;
+        const int r = inst / IPR, i = inst % IPR;
+        int64_t n = nb * BI + r;
+        if (n >= a.NI) n = a.NI - 1;
+        const int c = 64 * i + lane;
+        if constexpr ((DW / 8) % 64 == 0)  // whole rows of 1 KB copies: every lane active
+            dma16_async(a.Y16 + n * D + 8 * c, &Ys[buf][r * YP + 512 * i]);
+        else if (c < DW / 8)
+            dma16_async(a.Y16 + n * D + 8 * c, &Ys[buf][r * YP + 512 * i]);
     };
-    auto store_tab = [&](int buf, float v) {
-        if (tid < 2 * NP * BI) {
-            const int which = tid / (NP * BI), p = (tid / BI) % NP, r = tid % BI;
-            tabs[buf][which][p][r] = v;
-        }
+    auto copy_tables = [&](int64_t nb, int buf) {
+        const int e = 64 * w + lane;  // table entry [which][p][r]; lanes past the end copy a harmless float
+        const int which = e / (NP * BI), p = (e / BI) % NP, r = e % BI;
+        int64_t n = nb * BI + r;
+        if (n >= a.NI) n = a.NI - 1;
+        const float *tsrc = which == 0 ? a.iI : a.iKap;
+        const float *src = e < 2 * NP * BI ? tsrc + p * a.NI + n : a.iI;
+        dma4_async(src, &tabs[buf][64 * w]);
     };
-    // ---- copy of inner block nb (rows clamped to the last row: always NCW copies per wave)
-    auto issue_y = [&](int64_t nb, int buf) {
-        static_for<0, NCW>([&](auto ic) {
-            const int inst = w * NCW + decltype(ic)::value;
-            const int r = inst / IPR, i = inst % IPR;
-            int64_t n = nb * BI + r;
-            if (n >= a.NI) n = a.NI - 1;
-            const int c = 64 * i + lane;
-            if (c < DW / 8) dma16(a.Y16 + n * D + 8 * c, &Ys[buf][r * YP + 512 * i]);
-        });
+    auto issue_block = [&](int64_t nb, int buf) {
+        static_for<0, NCW>([&](auto ic) { copy_inst(nb, buf, ic); });
+        copy_tables(nb, buf);
     };
 
-    float t0 = 0.f;
-    if (nb_begin < nb_end) t0 = load_tab(nb_begin);
+    // zero the ring once so that every LDS word the kernel reads was written
+    for (int e = tid; e < NYBUF * BI * YP / 8; e += 256) *(uint4 *)&Ys[0][e * 8] = make_uint4(0, 0, 0, 0);
+    for (int e = tid; e < NYBUF * 256; e += 256) tabs[0][e] = 0.f;
+    lds_barrier();
 
     // ---- outer rows' quarter as B operands: rows 16 ob + l16, columns dq0 + 32 ks + 8 g4
     f16x8 xr[4][NQ];
@@ -634,136 +666,186 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) Cacc[p] = Lacc[p] = 0.f;
 
-    if (nb_begin < nb_end) {
-        issue_y(nb_begin, 0);
-        if (nb_begin + 1 < nb_end) {
-            issue_y(nb_begin + 1, 1);
-            wait_vm_n<NCW>();
-        } else {
-            wait_vm();
-        }
-        store_tab(0, t0);
-    }
-    lds_barrier();
-
-    int it = 0;
-    for (int64_t nb = nb_begin; nb < nb_end; ++nb, ++it) {
-        const int buf = it % NYBUF, tb = it & 1;
-        const _Float16 *Yb = Ys[buf];
-
-        // ---------------- R: partial S^T over this wave's quarter, 16 inner x 64 outer
-        {
-            f32x4 acc[4];
+    // ---- One region per block: the recompute R of the tile in ring slot rbuf (partial S^T
+    // over this wave's quarter, 16 inner x 64 outer, into the S slots) with the epilogue E
+    // of block nb (ring slot ebuf) spread over its steps, so that the MFMA pipe and the
+    // VALU work side by side.  E: lane = outer row, inner rows 4 w .. 4 w + 3; a^p for every
+    // prefix from the slot values sv, widest prefix first, so that the band operand
+    // A_p = sum_{p' >= p} a^p' is a running sum.
+    f32x4 sv[NSLOT - 1];
+    auto read_slots = [&]() {
 #pragma unroll
-            for (int ob = 0; ob < 4; ++ob) acc[ob] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const _Float16 *yrow = Yb + l16 * YP + dq0 + 8 * g4;
-            auto put = [&](int slot) {
+        for (int s = 0; s < NSLOT - 1; ++s) sv[s] = *(const f32x4 *)&Sl[s][lane * SLOTP + 4 * w];
+    };
+    auto r_and_e = [&](auto masked, auto with_e, int rbuf, int64_t nb, int ebuf, int64_t cnb, int cbuf) {
+        constexpr bool MK = decltype(masked)::value;
+        constexpr bool WE = decltype(with_e)::value;
+        f32x4 acc[4];
 #pragma unroll
-                for (int ob = 0; ob < 4; ++ob) *(f32x4 *)&Sl[slot][(16 * ob + l16) * SLOTP + 4 * g4] = acc[ob];
-            };
-            static_for<0, NQ>([&](auto kc) {
-                constexpr int ks = decltype(kc)::value;
-                const f16x8 yv = *(const f16x8 *)(yrow + 32 * ks);
+        for (int ob = 0; ob < 4; ++ob) acc[ob] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const _Float16 *yrow = Ys[rbuf] + l16 * YP + dq0 + 8 * g4;
+        auto put = [&](int slot) {
 #pragma unroll
-                for (int ob = 0; ob < 4; ++ob)
-                    acc[ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(yv, xr[ob][ks], acc[ob], 0, 0, 0);
-                if constexpr (L::INT_MASK != 0 && ks + 1 < NQ) {
-                    const int J = w * NQ + ks;
-                    if ((L::INT_MASK >> J) & 1u) put(4 + __builtin_popcount(L::INT_MASK & ((1u << J) - 1u)));
-                }
-            });
-            put(w);
-        }
-        lds_barrier();  // slots complete; every wave is done with U of the previous block
-
-        const bool more = nb + 1 < nb_end, pre = nb + 2 < nb_end;
-        const float tn = more ? load_tab(nb + 1) : 0.f;
-        if (pre) issue_y(nb + 2, (it + 2) % NYBUF);
-
-        // ---------------- E: lane = outer row, inner rows 4 w .. 4 w + 3
+            for (int ob = 0; ob < 4; ++ob) *(f32x4 *)&Sl[slot][(16 * ob + l16) * SLOTP + 4 * g4] = acc[ob];
+        };
+        bool vm[4];
         {
             const int64_t nw = nb * BI + 4 * w;
-            bool vm[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int64_t n = nw + t;
-                vm[t] = ovalid & (n < a.NI) & (n != o + a.diag_shift);
+                vm[t] = MK ? (ovalid & (n < a.NI) & (n != o + a.diag_shift)) : true;
             }
-            // widest prefix first: the band operand A_p = sum_{p' >= p} a^p' is a running sum
-            float run[4] = {0.f, 0.f, 0.f, 0.f};
-            const float *slot_row = &Sl[0][lane * SLOTP + 4 * w];
-            static_for<0, NP>([&](auto pc) {
-                constexpr int p = NP - 1 - decltype(pc)::value;
-                f32x4 Sp = *(const f32x4 *)(slot_row + L::snap_slot(p) * (BO * SLOTP));
-                static_for<0, L::wave_of(p)>([&](auto qc) {
-                    Sp += *(const f32x4 *)(slot_row + decltype(qc)::value * (BO * SLOTP));
-                });
-                const f32x4 iy = *(const f32x4 *)&tabs[tb][0][p][4 * w];
-                f32x4 kp = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (!SIG) kp = *(const f32x4 *)&tabs[tb][1][p][4 * w];
+        }
+        // one epilogue unit = one prefix for the 4 inner rows (4 independent chains)
+        float run[4] = {0.f, 0.f, 0.f, 0.f};
+        auto unit = [&](auto uc) {
+            constexpr int p = NP - 1 - decltype(uc)::value;
+            f32x4 Sp = sv[L::snap_slot(p)];
+            static_for<0, L::wave_of(p)>([&](auto qc) { Sp += sv[decltype(qc)::value]; });
+            const f32x4 iy = *(const f32x4 *)&tabs[ebuf][p * BI + 4 * w];
+            float av[4];
+            if constexpr (!SIG) {
+                const f32x4 kp = *(const f32x4 *)&tabs[ebuf][(NP + p) * BI + 4 * w];
+                float x[4], e[4], g[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) x[t] = Sp[t] * Ao[p];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) x[t] = fmaf(x[t], iy[t], Co[p]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) e[t] = __builtin_amdgcn_exp2f(x[t]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) g[t] = fmaf(Ro[p], iy[t], kp[t]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) av[t] = e[t] * g[t];
+            } else {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const float Sv = Sp[t];
-                    float av;
-                    if constexpr (!SIG) {
-                        const float e = __builtin_amdgcn_exp2f(fmaf(Sv * Ao[p], iy[t], Co[p]));
-                        av = e * fmaf(Ro[p], iy[t], kp[t]);
-                    } else {
-                        const float u = fmaf(Sv * Ao[p], iy[t], a.b2);
-                        const float tt = __builtin_amdgcn_exp2f(-fabsf(u));
-                        const float wq = 1.f + tt;
-                        const float rr = __builtin_amdgcn_rcpf(wq);
-                        const float sg = u >= 0.f ? rr : tt * rr;
-                        av = sg * Co[p] * iy[t];  // Co holds beta_o for the sigmoid form
-                        if (a.want_loss) {
-                            // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
-                            const float corr = (tt - (wq - 1.f)) * rr * kLog2e;
-                            const float lt = fmaxf(u, 0.f) + __builtin_amdgcn_logf(wq) + corr;
-                            Lacc[p] += vm[t] ? lt : 0.f;
-                        }
+                    const float uu = fmaf(Sp[t] * Ao[p], iy[t], a.b2);
+                    const float tt = __builtin_amdgcn_exp2f(-fabsf(uu));
+                    const float wq = 1.f + tt;
+                    const float rr = __builtin_amdgcn_rcpf(wq);
+                    const float sg = uu >= 0.f ? rr : tt * rr;
+                    av[t] = sg * Co[p] * iy[t];  // Co holds beta_o for the sigmoid form
+                    if (a.want_loss) {
+                        // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
+                        const float corr = (tt - (wq - 1.f)) * rr * kLog2e;
+                        const float lt = fmaxf(uu, 0.f) + __builtin_amdgcn_logf(wq) + corr;
+                        Lacc[p] += (!MK || vm[t]) ? lt : 0.f;
                     }
-                    av = vm[t] ? av : 0.f;
-                    Cacc[p] = fmaf(av, Sv, Cacc[p]);
-                    run[t] += av;
                 }
-                if constexpr (UPD) {
-                    f16x4 v;
+            }
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = (_Float16)run[t];
-                    *(f16x4 *)&At[p][lane * APITCH + 4 * w] = v;
-                }
-                __builtin_amdgcn_sched_barrier(0);
+            for (int t = 0; t < 4; ++t) {
+                if constexpr (MK) av[t] = vm[t] ? av[t] : 0.f;
+                if constexpr (p == NP - 1)
+                    run[t] = av[t];
+                else
+                    run[t] += av[t];
+            }
+            Cacc[p] = fmaf(av[0], Sp[0], fmaf(av[1], Sp[1], fmaf(av[2], Sp[2], fmaf(av[3], Sp[3], Cacc[p]))));
+            if constexpr (UPD) {
+                f16x4 v;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = (_Float16)run[t];
+                *(f16x4 *)&At[p][lane * APITCH + 4 * w] = v;
+            }
+        };
+        f16x8 yv[2];
+        yv[0] = *(const f16x8 *)yrow;
+        static_for<0, NQ>([&](auto kc) {
+            constexpr int ks = decltype(kc)::value;
+            if constexpr (ks + 1 < NQ) yv[(ks + 1) & 1] = *(const f16x8 *)(yrow + 32 * (ks + 1));
+            if constexpr (WE) {  // the copies of block cnb, spread over the steps
+                if constexpr (ks == 0) copy_tables(cnb, cbuf);
+                static_for<0, NCW>([&](auto ic) {
+                    if constexpr ((decltype(ic)::value * NQ) / NCW == ks) copy_inst(cnb, cbuf, ic);
+                });
+            }
+#pragma unroll
+            for (int ob = 0; ob < 4; ++ob)
+                acc[ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(yv[ks & 1], xr[ob][ks], acc[ob], 0, 0, 0);
+            if constexpr (((L::LPOS >> ks) & 1u) != 0 && ks + 1 < NQ) {
+                // every wave stores here (no branch); waves without a prefix end at this step use the spare slot
+                const int J = w * NQ + ks;
+                const int slot = ((L::INT_MASK >> J) & 1u) ? 4 + __builtin_popcount(L::INT_MASK & ((1u << J) - 1u))
+                                                           : L::DUMMY;
+                put(slot);
+            }
+            if constexpr (WE) static_for<0, NP>([&](auto uc) {
+                if constexpr ((decltype(uc)::value * NQ) / NP == ks) unit(uc);
             });
-        }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        put(w);
+    };
 
-        // every copy but the newest block's has landed (block nb + 1 in particular)
-        if (pre)
-            wait_vm_n<NCW>();
-        else
-            wait_vm();
-        if (more) store_tab(tb ^ 1, tn);
-        lds_barrier();  // band operands, tables and tile of block nb + 1 visible
-
-        // ---------------- U: dX[:, quarter] += A_band . Y[:, quarter]
-        if constexpr (UPD) {
-            const int G = lane >> 4, j = lane & 15;
-            const _Float16 *ysrc = Yb + (8 * (G >> 1) + (j >> 2)) * YP + 16 * (G & 1) + 4 * (j & 3);
-            static_for<0, NQ>([&](auto jc) {
-                constexpr int jb = decltype(jc)::value;
-                const int J = w * NQ + jb;
-                const int band = __builtin_popcount(MASK & ((1u << J) - 1u));
-                f16x8 af[2];
+    // ---- U: dX[:, quarter] += A_band . Y[:, quarter] for the tile in ring slot buf.
+    // The band operand is read only at the steps where some wave's band changes
+    // (the same code for every wave, no branches); the inner tile's operands of
+    // step jb + 1 are read while the MFMAs of step jb run.
+    auto uphase = [&](int buf) {
+        const int G = lane >> 4, j = lane & 15;
+        const _Float16 *ysrc = Ys[buf] + (8 * (G >> 1) + (j >> 2)) * YP + 16 * (G & 1) + 4 * (j & 3) + 32 * w * NQ;
+        f16x8 af[2], bf[2];
+        auto load_b = [&](auto jc) {
+            constexpr int jb = decltype(jc)::value;
+            const f16x4 lo = ds_read_tr(ysrc + 32 * jb);
+            const f16x4 hi = ds_read_tr(ysrc + 32 * jb + 4 * YP);
+            bf[jb & 1] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        load_b(std::integral_constant<int, 0>{});
+        static_for<0, NQ>([&](auto jc) {
+            constexpr int jb = decltype(jc)::value;
+            if constexpr ((L::BAND_STEPS >> jb) & 1u) {
+                const int band = __builtin_popcount(MASK & ((1u << (w * NQ + jb)) - 1u));
 #pragma unroll
                 for (int ob = 0; ob < 2; ++ob) af[ob] = *(const f16x8 *)&At[band][(32 * ob + l32) * APITCH + 8 * h32];
-                const f16x4 lo = ds_read_tr(ysrc + 32 * J);
-                const f16x4 hi = ds_read_tr(ysrc + 32 * J + 4 * YP);
-                const f16x8 bf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            if constexpr (jb + 1 < NQ) load_b(std::integral_constant<int, jb + 1>{});
 #pragma unroll
-                for (int ob = 0; ob < 2; ++ob)
-                    dacc[ob][jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ob], bf, dacc[ob][jb], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            });
+            for (int ob = 0; ob < 2; ++ob)
+                dacc[ob][jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ob], bf[jb & 1], dacc[ob][jb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    // Software pipeline, per block t: the epilogue of t runs beside the recompute
+    // of t + 1 (independent: the MFMA pipe and the VALU overlap), then the update
+    // of t.  Ring slot of block t = t mod 3; the copy of t + 2 is issued once
+    // every wave is past the update of t - 1, whose slot it reuses.
+    if (nb_begin < nb_end) {
+        issue_block(nb_begin, 0);
+        if (nb_begin + 1 < nb_end) {
+            issue_block(nb_begin + 1, 1);
+            wait_vm_n<NCW + 1>();
+        } else {
+            wait_vm();
         }
+        lds_barrier();  // block 0 visible
+        r_and_e(std::false_type{}, std::false_type{}, 0, nb_begin, 0, 0, 0);  // recompute of block 0 alone
+        lds_barrier();  // slots of block 0 visible
+        read_slots();
+    }
+
+    int it = 0;
+    for (int64_t nb = nb_begin; nb < nb_end; ++nb, ++it) {
+        const int buf = it % NYBUF, buf1 = (it + 1) % NYBUF;
+        wait_vm();      // block nb + 1 landed (issued a full block earlier)
+        lds_barrier();  // every wave holds block nb's slot values and is past the update of nb - 1; block nb + 1 visible
+
+        // recompute of nb + 1 (past the end it reads a stale tile and its slots go unread) beside the
+        // epilogue of nb and the copies of nb + 2 (past the end: clamped rows into a free ring slot)
+        const int64_t n0 = nb * BI;
+        const bool needmask = (n0 + BI > a.NI) || (o0 + BO > a.NO) ||
+                              ((n0 < o0 + a.diag_shift + BO) && (o0 + a.diag_shift < n0 + BI));
+        if (needmask)
+            r_and_e(std::true_type{}, std::true_type{}, buf1, nb, buf, nb + 2, (it + 2) % NYBUF);
+        else
+            r_and_e(std::false_type{}, std::true_type{}, buf1, nb, buf, nb + 2, (it + 2) % NYBUF);
+        lds_barrier();  // band operands of nb and slots of nb + 1 visible
+        read_slots();
+        if constexpr (UPD) uphase(buf);
     }
 
     // ---------------- write the raw gradient block (scale divided out) and the radial sums
