@@ -82,6 +82,11 @@ __device__ __forceinline__ void dma16_async(const void *g, const void *lds) {
     const uint32_t l = (uint32_t)(uintptr_t)lds;
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory");
 }
+// Same, wave-uniform base (SGPR pair) plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16_async_s(const void *base, uint32_t voff, const void *lds) {
+    const uint32_t l = (uint32_t)(uintptr_t)lds;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(l) : "memory");
+}
 __device__ __forceinline__ void dma4_async(const void *g, const void *lds) {
     const uint32_t l = (uint32_t)(uintptr_t)lds;
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(l) : "memory");
@@ -615,12 +620,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         const int inst = w * NCW + decltype(ic)::value;
         const int r = inst / IPR, i = inst % IPR;
         int64_t n = nb * BI + r;
-        if (n >= a.NI) n = a.NI - 1;
-        const int c = 64 * i + lane;
+        n = __builtin_amdgcn_readfirstlane((int)(n < a.NI ? n : a.NI - 1));
+        const _Float16 *rowp = a.Y16 + n * D + 512 * i;  // wave-uniform
         if constexpr ((DW / 8) % 64 == 0)  // whole rows of 1 KB copies: every lane active
-            dma16_async(a.Y16 + n * D + 8 * c, &Ys[buf][r * YP + 512 * i]);
-        else if (c < DW / 8)
-            dma16_async(a.Y16 + n * D + 8 * c, &Ys[buf][r * YP + 512 * i]);
+            dma16_async_s(rowp, 16u * lane, &Ys[buf][r * YP + 512 * i]);
+        else if (64 * i + lane < DW / 8)
+            dma16_async_s(rowp, 16u * lane, &Ys[buf][r * YP + 512 * i]);
     };
     auto copy_tables = [&](int64_t nb, int buf) {
         const int e = 64 * w + lane;  // table entry [which][p][r]; lanes past the end copy a harmless float
@@ -784,17 +789,24 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     // The band operand is read only at the steps where some wave's band changes
     // (the same code for every wave, no branches); the inner tile's operands of
     // step jb + 1 are read while the MFMAs of step jb run.
-    auto uphase = [&](int buf) {
+    // transposed inner-tile operands, two steps ahead; the first two are read before
+    // the barrier that publishes the band operands (the tile itself is already stable)
+    f16x8 bf[3];
+    auto load_b = [&](int buf, auto jc) {
+        constexpr int jb = decltype(jc)::value;
         const int G = lane >> 4, j = lane & 15;
-        const _Float16 *ysrc = Ys[buf] + (8 * (G >> 1) + (j >> 2)) * YP + 16 * (G & 1) + 4 * (j & 3) + 32 * w * NQ;
-        f16x8 af[2], bf[2];
-        auto load_b = [&](auto jc) {
-            constexpr int jb = decltype(jc)::value;
-            const f16x4 lo = ds_read_tr(ysrc + 32 * jb);
-            const f16x4 hi = ds_read_tr(ysrc + 32 * jb + 4 * YP);
-            bf[jb & 1] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        };
-        load_b(std::integral_constant<int, 0>{});
+        const _Float16 *ysrc =
+            Ys[buf] + (8 * (G >> 1) + (j >> 2)) * YP + 16 * (G & 1) + 4 * (j & 3) + 32 * (w * NQ + jb);
+        const f16x4 lo = ds_read_tr(ysrc);
+        const f16x4 hi = ds_read_tr(ysrc + 4 * YP);
+        bf[jb % 3] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto u_pre = [&](int buf) {
+        load_b(buf, std::integral_constant<int, 0>{});
+        if constexpr (NQ > 1) load_b(buf, std::integral_constant<int, 1>{});
+    };
+    auto uphase = [&](int buf) {
+        f16x8 af[2];
         static_for<0, NQ>([&](auto jc) {
             constexpr int jb = decltype(jc)::value;
             if constexpr ((L::BAND_STEPS >> jb) & 1u) {
@@ -802,10 +814,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
 #pragma unroll
                 for (int ob = 0; ob < 2; ++ob) af[ob] = *(const f16x8 *)&At[band][(32 * ob + l32) * APITCH + 8 * h32];
             }
-            if constexpr (jb + 1 < NQ) load_b(std::integral_constant<int, jb + 1>{});
+            if constexpr (jb + 2 < NQ) load_b(buf, std::integral_constant<int, jb + 2>{});
 #pragma unroll
             for (int ob = 0; ob < 2; ++ob)
-                dacc[ob][jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ob], bf[jb & 1], dacc[ob][jb], 0, 0, 0);
+                dacc[ob][jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ob], bf[jb % 3], dacc[ob][jb], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         });
     };
@@ -843,6 +855,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             r_and_e(std::true_type{}, std::true_type{}, buf1, nb, buf, nb + 2, (it + 2) % NYBUF);
         else
             r_and_e(std::false_type{}, std::true_type{}, buf1, nb, buf, nb + 2, (it + 2) % NYBUF);
+        if constexpr (UPD) u_pre(buf);
         lds_barrier();  // band operands of nb and slots of nb + 1 visible
         read_slots();
         if constexpr (UPD) uphase(buf);
