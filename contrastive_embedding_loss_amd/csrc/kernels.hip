@@ -252,7 +252,21 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wi = wave >> 1, wj = wave & 1;
-    const int64_t jt = blockIdx.x, it = blockIdx.y;
+    int64_t it, jt;
+    {
+        // Workgroups are dealt to the 8 XCDs in turn (id mod 8).  Give each XCD a contiguous
+        // run of tiles in grouped order (8 row tiles, then the next column), so that the tiles
+        // resident on one XCD share 8 row tiles and 8 column tiles in its L2.
+        const int64_t nIt = (R + FB - 1) / FB, nJt = (N + FB - 1) / FB, T = nIt * nJt;
+        const int64_t L = blockIdx.x, x = L % 8, idx = L / 8;
+        const int64_t base = (T / 8) * x + (x < T % 8 ? x : T % 8);  // tiles of the XCDs before x
+        const int64_t t = base + idx;
+        constexpr int64_t GM = 8;
+        const int64_t per_group = GM * nJt, g = t / per_group, i0g = g * GM;
+        const int64_t gsz = nIt - i0g < GM ? nIt - i0g : GM;
+        it = i0g + (t % per_group) % gsz;
+        jt = (t % per_group) / gsz;
+    }
     const int64_t i0 = it * FB, j0 = jt * FB;
     const int P = pf.n;
     const int Dsw = pf.w[P - 1];
@@ -1025,8 +1039,8 @@ hipError_t launch_fwd(const u16 *q, const u16 *k, int64_t R, int64_t N, int D, c
                       const float *rowA, const float *colI, float cshift, float *rowpart, float *colpart,
                       hipStream_t s) {
     const int64_t nIt = (R + FB - 1) / FB, nJt = (N + FB - 1) / FB;
-    hipLaunchKernelGGL(k_fwd, dim3((unsigned)nJt, (unsigned)nIt), dim3(256), 0, s, q, k, R, N, D, pf, off, rowA,
-                       colI, cshift, rowpart, colpart);
+    hipLaunchKernelGGL(k_fwd, dim3((unsigned)(nIt * nJt)), dim3(256), 0, s, q, k, R, N, D, pf, off, rowA, colI,
+                       cshift, rowpart, colpart);
     return hipGetLastError();
 }
 
