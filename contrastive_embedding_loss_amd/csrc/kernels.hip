@@ -685,19 +685,94 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) Cacc[p] = Lacc[p] = 0.f;
 
-    // ---- One region per block: the recompute R of the tile in ring slot rbuf (partial S^T
-    // over this wave's quarter, 16 inner x 64 outer, into the S slots) with the epilogue E
-    // of block nb (ring slot ebuf) spread over its steps, so that the MFMA pipe and the
-    // VALU work side by side.  E: lane = outer row, inner rows 4 w .. 4 w + 3; a^p for every
-    // prefix from the slot values sv, widest prefix first, so that the band operand
-    // A_p = sum_{p' >= p} a^p' is a running sum.
+    // ---- Two-phase software pipeline.  Epilogue E of a block = one unit per prefix
+    // (lane = outer row, inner rows 4 w .. 4 w + 3, four independent chains), widest
+    // prefix first so that the band operand A_p = sum_{p' >= p} a^p' is a running sum.
+    // Its NA widest units (E_a) run in phase B beside the update MFMAs of the block
+    // before; the rest (E_b) in phase A beside the recompute MFMAs of the block after:
+    //   phase A(t): recompute of t + 1 | E_b(t) | copies of t + 2      -> barrier
+    //   phase B(t): update of t         | E_a(t + 1)                   -> barrier
+    // E_a's band operands are held in registers until phase A writes them, because
+    // the update of t reads the band operand buffer during phase B.
+    constexpr int NA = NP / 2;  // prefixes NP - NA .. NP - 1 belong to E_a
     f32x4 sv[NSLOT - 1];
     auto read_slots = [&]() {
 #pragma unroll
         for (int s = 0; s < NSLOT - 1; ++s) sv[s] = *(const f32x4 *)&Sl[s][lane * SLOTP + 4 * w];
     };
-    auto r_and_e = [&](auto masked, auto with_e, int rbuf, int64_t nb, int ebuf, int64_t cnb, int cbuf) {
+    float run[4] = {0.f, 0.f, 0.f, 0.f};
+    f16x4 hv[NA > 0 ? NA : 1];
+    auto masks = [&](auto masked, int64_t nb, bool (&vm)[4]) {
         constexpr bool MK = decltype(masked)::value;
+        const int64_t nw = nb * BI + 4 * w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int64_t n = nw + t;
+            vm[t] = MK ? (ovalid & (n < a.NI) & (n < nb_end * BI) & (n != o + a.diag_shift)) : true;
+        }
+    };
+    // epilogue unit of prefix p for the block whose tables sit in ring slot ebuf
+    auto unit = [&](auto pc, auto masked, const bool (&vm)[4], int ebuf) {
+        constexpr int p = decltype(pc)::value;
+        constexpr bool MK = decltype(masked)::value;
+        f32x4 Sp = sv[L::snap_slot(p)];
+        static_for<0, L::wave_of(p)>([&](auto qc) { Sp += sv[decltype(qc)::value]; });
+        const f32x4 iy = *(const f32x4 *)&tabs[ebuf][p * BI + 4 * w];
+        float av[4];
+        if constexpr (!SIG) {
+            const f32x4 kp = *(const f32x4 *)&tabs[ebuf][(NP + p) * BI + 4 * w];
+            float x[4], e[4], g[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) x[t] = Sp[t] * Ao[p];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) x[t] = fmaf(x[t], iy[t], Co[p]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) e[t] = __builtin_amdgcn_exp2f(x[t]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) g[t] = fmaf(Ro[p], iy[t], kp[t]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) av[t] = e[t] * g[t];
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float uu = fmaf(Sp[t] * Ao[p], iy[t], a.b2);
+                const float tt = __builtin_amdgcn_exp2f(-fabsf(uu));
+                const float wq = 1.f + tt;
+                const float rr = __builtin_amdgcn_rcpf(wq);
+                const float sg = uu >= 0.f ? rr : tt * rr;
+                av[t] = sg * Co[p] * iy[t];  // Co holds beta_o for the sigmoid form
+                if (a.want_loss) {
+                    // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
+                    const float corr = (tt - (wq - 1.f)) * rr * kLog2e;
+                    const float lt = fmaxf(uu, 0.f) + __builtin_amdgcn_logf(wq) + corr;
+                    Lacc[p] += (!MK || vm[t]) ? lt : 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if constexpr (MK) av[t] = vm[t] ? av[t] : 0.f;
+            if constexpr (p == NP - 1)
+                run[t] = av[t];
+            else
+                run[t] += av[t];
+        }
+        Cacc[p] = fmaf(av[0], Sp[0], fmaf(av[1], Sp[1], fmaf(av[2], Sp[2], fmaf(av[3], Sp[3], Cacc[p]))));
+        if constexpr (UPD) {
+            f16x4 v;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = (_Float16)run[t];
+            if constexpr (p >= NP - NA)
+                hv[NP - 1 - p] = v;  // E_a: held until phase A
+            else
+                *(f16x4 *)&At[p][lane * APITCH + 4 * w] = v;
+        }
+    };
+
+    // phase A: recompute of the tile in ring slot rbuf (partial S^T over this wave's quarter,
+    // 16 inner x 64 outer, into the S slots) | E_b of block nb (tables in ebuf) | copies of
+    // block cnb into cbuf, each spread over the recompute steps
+    auto phase_a = [&](auto masked, auto with_e, int rbuf, int64_t nb, int ebuf, int64_t cnb, int cbuf) {
         constexpr bool WE = decltype(with_e)::value;
         f32x4 acc[4];
 #pragma unroll
@@ -708,74 +783,20 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             for (int ob = 0; ob < 4; ++ob) *(f32x4 *)&Sl[slot][(16 * ob + l16) * SLOTP + 4 * g4] = acc[ob];
         };
         bool vm[4];
-        {
-            const int64_t nw = nb * BI + 4 * w;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int64_t n = nw + t;
-                vm[t] = MK ? (ovalid & (n < a.NI) & (n != o + a.diag_shift)) : true;
-            }
+        if constexpr (WE) {
+            masks(masked, nb, vm);
+            if constexpr (UPD)
+                static_for<0, NA>([&](auto ic) {
+                    constexpr int p = NP - 1 - decltype(ic)::value;
+                    *(f16x4 *)&At[p][lane * APITCH + 4 * w] = hv[decltype(ic)::value];
+                });
         }
-        // one epilogue unit = one prefix for the 4 inner rows (4 independent chains)
-        float run[4] = {0.f, 0.f, 0.f, 0.f};
-        auto unit = [&](auto uc) {
-            constexpr int p = NP - 1 - decltype(uc)::value;
-            f32x4 Sp = sv[L::snap_slot(p)];
-            static_for<0, L::wave_of(p)>([&](auto qc) { Sp += sv[decltype(qc)::value]; });
-            const f32x4 iy = *(const f32x4 *)&tabs[ebuf][p * BI + 4 * w];
-            float av[4];
-            if constexpr (!SIG) {
-                const f32x4 kp = *(const f32x4 *)&tabs[ebuf][(NP + p) * BI + 4 * w];
-                float x[4], e[4], g[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) x[t] = Sp[t] * Ao[p];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) x[t] = fmaf(x[t], iy[t], Co[p]);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) e[t] = __builtin_amdgcn_exp2f(x[t]);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) g[t] = fmaf(Ro[p], iy[t], kp[t]);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) av[t] = e[t] * g[t];
-            } else {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const float uu = fmaf(Sp[t] * Ao[p], iy[t], a.b2);
-                    const float tt = __builtin_amdgcn_exp2f(-fabsf(uu));
-                    const float wq = 1.f + tt;
-                    const float rr = __builtin_amdgcn_rcpf(wq);
-                    const float sg = uu >= 0.f ? rr : tt * rr;
-                    av[t] = sg * Co[p] * iy[t];  // Co holds beta_o for the sigmoid form
-                    if (a.want_loss) {
-                        // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
-                        const float corr = (tt - (wq - 1.f)) * rr * kLog2e;
-                        const float lt = fmaxf(uu, 0.f) + __builtin_amdgcn_logf(wq) + corr;
-                        Lacc[p] += (!MK || vm[t]) ? lt : 0.f;
-                    }
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                if constexpr (MK) av[t] = vm[t] ? av[t] : 0.f;
-                if constexpr (p == NP - 1)
-                    run[t] = av[t];
-                else
-                    run[t] += av[t];
-            }
-            Cacc[p] = fmaf(av[0], Sp[0], fmaf(av[1], Sp[1], fmaf(av[2], Sp[2], fmaf(av[3], Sp[3], Cacc[p]))));
-            if constexpr (UPD) {
-                f16x4 v;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = (_Float16)run[t];
-                *(f16x4 *)&At[p][lane * APITCH + 4 * w] = v;
-            }
-        };
         f16x8 yv[2];
         yv[0] = *(const f16x8 *)yrow;
         static_for<0, NQ>([&](auto kc) {
             constexpr int ks = decltype(kc)::value;
             if constexpr (ks + 1 < NQ) yv[(ks + 1) & 1] = *(const f16x8 *)(yrow + 32 * (ks + 1));
-            if constexpr (WE) {  // the copies of block cnb, spread over the steps
+            if constexpr (WE) {
                 if constexpr (ks == 0) copy_tables(cnb, cbuf);
                 static_for<0, NCW>([&](auto ic) {
                     if constexpr ((decltype(ic)::value * NQ) / NCW == ks) copy_inst(cnb, cbuf, ic);
@@ -791,20 +812,18 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
                                                            : L::DUMMY;
                 put(slot);
             }
-            if constexpr (WE) static_for<0, NP>([&](auto uc) {
-                if constexpr ((decltype(uc)::value * NQ) / NP == ks) unit(uc);
-            });
+            if constexpr (WE)  // E_b units: prefixes NP - NA - 1 .. 0
+                static_for<0, NP - NA>([&](auto uc) {
+                    if constexpr ((decltype(uc)::value * NQ) / (NP - NA) == ks)
+                        unit(std::integral_constant<int, NP - NA - 1 - decltype(uc)::value>{}, masked, vm, ebuf);
+                });
             __builtin_amdgcn_sched_barrier(0);
         });
         put(w);
     };
 
-    // ---- U: dX[:, quarter] += A_band . Y[:, quarter] for the tile in ring slot buf.
-    // The band operand is read only at the steps where some wave's band changes
-    // (the same code for every wave, no branches); the inner tile's operands of
-    // step jb + 1 are read while the MFMAs of step jb run.
-    // transposed inner-tile operands, two steps ahead; the first two are read before
-    // the barrier that publishes the band operands (the tile itself is already stable)
+    // transposed inner-tile operands of the update, two steps ahead; the first two are
+    // read before the barrier that publishes the band operands (the tile is stable)
     f16x8 bf[3];
     auto load_b = [&](int buf, auto jc) {
         constexpr int jb = decltype(jc)::value;
@@ -819,27 +838,46 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         load_b(buf, std::integral_constant<int, 0>{});
         if constexpr (NQ > 1) load_b(buf, std::integral_constant<int, 1>{});
     };
-    auto uphase = [&](int buf) {
+    // phase B: dX[:, quarter] += A_band . Y[:, quarter] for the tile in ring slot ubuf | E_a of
+    // block nb1 (tables in ebuf1).  The band operand is read only at the
+    // steps where some wave's band changes (the same code for every wave, no branches).
+    // (No branches in here: the gradient accumulators must not meet at a join.  E_a always
+    // runs with masks; a block past the end has every cell masked.)
+    auto phase_b = [&](auto with_u, int ubuf, int64_t nb1, int ebuf1) {
+        constexpr bool WE = NA > 0;
+        constexpr bool WU = decltype(with_u)::value && UPD;
+        constexpr std::true_type masked{};
+        bool vm[4];
+        if constexpr (WE) masks(masked, nb1, vm);
         f16x8 af[2];
         static_for<0, NQ>([&](auto jc) {
             constexpr int jb = decltype(jc)::value;
-            if constexpr ((L::BAND_STEPS >> jb) & 1u) {
-                const int band = __builtin_popcount(MASK & ((1u << (w * NQ + jb)) - 1u));
+            if constexpr (WU) {
+                if constexpr ((L::BAND_STEPS >> jb) & 1u) {
+                    const int band = __builtin_popcount(MASK & ((1u << (w * NQ + jb)) - 1u));
 #pragma unroll
-                for (int ob = 0; ob < 2; ++ob) af[ob] = *(const f16x8 *)&At[band][(32 * ob + l32) * APITCH + 8 * h32];
+                    for (int ob = 0; ob < 2; ++ob)
+                        af[ob] = *(const f16x8 *)&At[band][(32 * ob + l32) * APITCH + 8 * h32];
+                }
+                if constexpr (jb + 2 < NQ) load_b(ubuf, std::integral_constant<int, jb + 2>{});
+#pragma unroll
+                for (int ob = 0; ob < 2; ++ob)
+                    dacc[ob][jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ob], bf[jb % 3], dacc[ob][jb], 0, 0, 0);
             }
-            if constexpr (jb + 2 < NQ) load_b(buf, std::integral_constant<int, jb + 2>{});
-#pragma unroll
-            for (int ob = 0; ob < 2; ++ob)
-                dacc[ob][jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ob], bf[jb % 3], dacc[ob][jb], 0, 0, 0);
+            if constexpr (WE)  // E_a units: prefixes NP - 1 .. NP - NA
+                static_for<0, NA>([&](auto uc) {
+                    if constexpr ((decltype(uc)::value * NQ) / NA == jb)
+                        unit(std::integral_constant<int, NP - 1 - decltype(uc)::value>{}, masked, vm, ebuf1);
+                });
             __builtin_amdgcn_sched_barrier(0);
         });
     };
+    auto needmask = [&](int64_t nb) {  // cells that need masks: ragged rows, or the positives of these outer rows
+        const int64_t n0 = nb * BI;
+        return (n0 + BI > a.NI) || (o0 + BO > a.NO) ||
+               ((n0 < o0 + a.diag_shift + BO) && (o0 + a.diag_shift < n0 + BI));
+    };
 
-    // Software pipeline, per block t: the epilogue of t runs beside the recompute
-    // of t + 1 (independent: the MFMA pipe and the VALU overlap), then the update
-    // of t.  Ring slot of block t = t mod 3; the copy of t + 2 is issued once
-    // every wave is past the update of t - 1, whose slot it reuses.
     if (nb_begin < nb_end) {
         issue_block(nb_begin, 0);
         if (nb_begin + 1 < nb_end) {
@@ -849,30 +887,27 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             wait_vm();
         }
         lds_barrier();  // block 0 visible
-        r_and_e(std::false_type{}, std::false_type{}, 0, nb_begin, 0, 0, 0);  // recompute of block 0 alone
+        phase_a(std::false_type{}, std::false_type{}, 0, nb_begin, 0, 0, 0);  // recompute of block 0 alone
         lds_barrier();  // slots of block 0 visible
         read_slots();
+        phase_b(std::false_type{}, 0, nb_begin, 0);  // E_a of block 0 alone
     }
 
     int it = 0;
     for (int64_t nb = nb_begin; nb < nb_end; ++nb, ++it) {
-        const int buf = it % NYBUF, buf1 = (it + 1) % NYBUF;
+        const int buf = it % NYBUF, buf1 = (it + 1) % NYBUF, buf2 = (it + 2) % NYBUF;
         wait_vm();      // block nb + 1 landed (issued a full block earlier)
-        lds_barrier();  // every wave holds block nb's slot values and is past the update of nb - 1; block nb + 1 visible
-
-        // recompute of nb + 1 (past the end it reads a stale tile and its slots go unread) beside the
-        // epilogue of nb and the copies of nb + 2 (past the end: clamped rows into a free ring slot)
-        const int64_t n0 = nb * BI;
-        const bool needmask = (n0 + BI > a.NI) || (o0 + BO > a.NO) ||
-                              ((n0 < o0 + a.diag_shift + BO) && (o0 + a.diag_shift < n0 + BI));
-        if (needmask)
-            r_and_e(std::true_type{}, std::true_type{}, buf1, nb, buf, nb + 2, (it + 2) % NYBUF);
+        lds_barrier();  // slots of nb consumed, every wave past the update of nb - 1; block nb + 1 visible
+        // phase A: recompute of nb + 1 (past the end: a stale tile) | E_b(nb) | copies of nb + 2
+        // (past the end: clamped rows into a free ring slot)
+        if (needmask(nb))
+            phase_a(std::true_type{}, std::true_type{}, buf1, nb, buf, nb + 2, buf2);
         else
-            r_and_e(std::false_type{}, std::true_type{}, buf1, nb, buf, nb + 2, (it + 2) % NYBUF);
+            phase_a(std::false_type{}, std::true_type{}, buf1, nb, buf, nb + 2, buf2);
         if constexpr (UPD) u_pre(buf);
         lds_barrier();  // band operands of nb and slots of nb + 1 visible
         read_slots();
-        if constexpr (UPD) uphase(buf);
+        phase_b(std::true_type{}, buf, nb + 1, buf1);  // update of nb | E_a(nb + 1)
     }
 
     // ---------------- write the raw gradient block (scale divided out) and the radial sums
