@@ -124,5 +124,6 @@ hipError_t launch_loss(const LossArgs &a, hipStream_t s);
 constexpr int kFwdTile = 128;   // forward tile (rows and columns)
 constexpr int kBwdOuter = 64;   // outer rows per backward workgroup
 constexpr int kBwdInner = 16;   // inner rows per backward block
+constexpr int kStatRows = 64;   // rows per block of the statistics kernels
 
 }  // namespace uform

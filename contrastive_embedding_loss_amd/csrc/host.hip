@@ -89,8 +89,8 @@ Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, in
     // loss slots: softmax = row stats blocks + column stats blocks;
     // sigmoid = positive-cell blocks + row-pass workgroups
     if (softmax) {
-        p.slots_a = cdiv(R, 256);
-        p.slots_b = cdiv(N, 256);
+        p.slots_a = cdiv(R, kStatRows);
+        p.slots_b = cdiv(N, kStatRows);
     } else {
         p.slots_a = cdiv(R + N, 256);
         p.slots_b = cdiv(R, kBwdOuter) * p.nsplit_row;

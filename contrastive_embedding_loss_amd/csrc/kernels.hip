@@ -367,16 +367,33 @@ __device__ __forceinline__ void block_sum_write(float v, float *red /*[4]*/, flo
     __syncthreads();
 }
 
+// Sum of the per-tile partials of row (or column) r, prefix p: the 4 waves of a
+// block each take every 4th tile (kStatRows consecutive rows per wave, so the
+// loads coalesce), then the four sums are added in a fixed order.
+__device__ __forceinline__ float fold_partials(const float *part, int64_t ntiles, int P, int p, int64_t len,
+                                               int64_t r, bool ok, float (*fold)[kStatRows]) {
+    const int g = threadIdx.x / kStatRows, rl = threadIdx.x % kStatRows;
+    float v = 0.f;
+    if (ok)
+        for (int64_t t = g; t < ntiles; t += 4) v += part[(t * P + p) * len + r];
+    fold[g][rl] = v;
+    __syncthreads();
+    const float s = (fold[0][rl] + fold[1][rl]) + (fold[2][rl] + fold[3][rl]);
+    __syncthreads();
+    return s;
+}
+
 __global__ __launch_bounds__(256) void k_rowstats(StatsArgs a) {
     __shared__ float red[4];
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const bool ok = i < a.R;
+    __shared__ float fold[4][kStatRows];
+    const int64_t i = (int64_t)blockIdx.x * kStatRows + threadIdx.x % kStatRows;
+    const bool lead = threadIdx.x < kStatRows;
     const int P = a.pf.n;
     for (int p = 0; p < P; ++p) {
         float ce = 0.f;
-        if (ok) {
-            float neg = 0.f;
-            for (int64_t t = 0; t < a.nJt; ++t) neg += a.rowpart[(t * P + p) * a.R + i];
+        const float negsum = fold_partials(a.rowpart, a.nJt, P, p, a.R, i, i < a.R, fold);
+        if (lead && i < a.R) {
+            const float neg = negsum;
             const float iq = a.invq[p * a.R + i], ik = a.invk[p * a.N + i + a.off];
             const float S = a.posdot[p * a.R + i];
             const float A = a.qA[p * a.R + i];
@@ -401,14 +418,15 @@ __global__ __launch_bounds__(256) void k_rowstats(StatsArgs a) {
 
 __global__ __launch_bounds__(256) void k_colstats(StatsArgs a) {
     __shared__ float red[4];
-    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const bool ok = j < a.N;
+    __shared__ float fold[4][kStatRows];
+    const int64_t j = (int64_t)blockIdx.x * kStatRows + threadIdx.x % kStatRows;
+    const bool lead = threadIdx.x < kStatRows;
     const int P = a.pf.n;
     for (int p = 0; p < P; ++p) {
         float ce = 0.f;
-        if (ok) {
-            float neg = 0.f;
-            for (int64_t t = 0; t < a.nIt; ++t) neg += a.colpart[(t * P + p) * a.N + j];
+        const float negsum = fold_partials(a.colpart, a.nIt, P, p, a.N, j, j < a.N, fold);
+        if (lead && j < a.N) {
+            const float neg = negsum;
             const float ik = a.invk[p * a.N + j];
             const int64_t i = j - a.off;
             float epos = 0.f, x = 0.f, iq = 0.f;
@@ -1080,12 +1098,12 @@ hipError_t launch_fwd(const u16 *q, const u16 *k, int64_t R, int64_t N, int D, c
 }
 
 hipError_t launch_rowstats(const StatsArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_rowstats, dim3((unsigned)((a.R + 255) / 256)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_rowstats, dim3((unsigned)((a.R + kStatRows - 1) / kStatRows)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_colstats(const StatsArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_colstats, dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_colstats, dim3((unsigned)((a.N + kStatRows - 1) / kStatRows)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
