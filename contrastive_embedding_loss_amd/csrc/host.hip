@@ -128,8 +128,9 @@ Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, in
     const bool bwd = want_dq || want_dk || !softmax;  // some backward pass runs
     p.o_qH = take(bwd ? sizeof(u16) * R * D : 0);
     p.o_kH = take(bwd ? sizeof(u16) * N * D : 0);
-    p.o_rowpart = take(softmax ? sizeof(float) * p.nJt * P * R : 0);
-    p.o_colpart = take(softmax ? sizeof(float) * p.nIt * P * N : 0);
+    // forward partials: one per wave column (row partials) / wave row (column partials) of a tile
+    p.o_rowpart = take(softmax ? sizeof(float) * 2 * p.nJt * P * R : 0);
+    p.o_colpart = take(softmax ? sizeof(float) * 2 * p.nIt * P * N : 0);
     const size_t part_row = (want_dq || !softmax) ? sizeof(float) * p.nsplit_row * R * D : 0;
     const size_t part_col = want_dk ? sizeof(float) * p.nsplit_col * N * D : 0;
     p.o_part = take(part_row > part_col ? part_row : part_col);
@@ -340,8 +341,8 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     sa.R = R;
     sa.N = N;
     sa.off = off;
-    sa.nJt = pl.nJt;
-    sa.nIt = pl.nIt;
+    sa.nJt = 2 * pl.nJt;  // partials per row: two per column tile
+    sa.nIt = 2 * pl.nIt;
     sa.pf = pf;
     sa.kind = kind;
     sa.scale = scale;

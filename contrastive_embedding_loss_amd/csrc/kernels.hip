@@ -51,18 +51,35 @@ __device__ __forceinline__ f16x8 pack_f16x8(const float (&v)[8]) {
 }
 
 // Sum over the 32 lanes of each wave half of v[lane & 31]: a reduce-scatter
-// butterfly (31 exchanges instead of 32 x 5).
+// butterfly (31 exchanges instead of 32 x 5) without LDS traffic.  Stage 16
+// uses v_permlane16_swap (rows of 16 lanes trade halves); stages 8 and 4 pair
+// lane i with 15 - i and 7 - i (DPP row mirror and half mirror), stages 2 and
+// 1 use quad permutes.  Each stage pairs lanes that differ in the stage's bit
+// and agree on the bits of the stages before, so lane l keeps slot l & 31.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float reduce_scatter32(float (&v)[32], int lane) {
-    static_for<0, 5>([&](auto sc) {
-        constexpr int h = 16 >> decltype(sc)::value;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 16]), false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    auto stage = [&](auto hc, auto cc) {
+        constexpr int h = decltype(hc)::value, C = decltype(cc)::value;
         const bool up = (lane & h) != 0;
 #pragma unroll
         for (int i = 0; i < h; ++i) {
             const float keep = up ? v[i + h] : v[i];
             const float send = up ? v[i] : v[i + h];
-            v[i] = keep + __shfl_xor(send, h);
+            v[i] = keep + dpp<C>(send);
         }
-    });
+    };
+    stage(std::integral_constant<int, 8>{}, std::integral_constant<int, 0x140>{});  // row_mirror
+    stage(std::integral_constant<int, 4>{}, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    stage(std::integral_constant<int, 2>{}, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+    stage(std::integral_constant<int, 1>{}, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
     return v[0];
 }
 
@@ -181,7 +198,7 @@ template <bool MASKED>
 __device__ __forceinline__ void fwd_snapshot(const f32x16 (&acc)[2][2], int p, int wi, int wj, int lane, int tid,
                                              int64_t i0, int64_t j0, int64_t R, int64_t N, int64_t off, int P,
                                              float cshift, const float (*fA)[FB], const float (*fI)[FB],
-                                             float (*racc)[FB], float (*cacc)[FB], int64_t it, int64_t jt,
+                                             int64_t it, int64_t jt,
                                              float *__restrict__ rowpart, float *__restrict__ colpart) {
     float rs[32];
     float cs[2] = {0.f, 0.f};
@@ -217,25 +234,19 @@ __device__ __forceinline__ void fwd_snapshot(const f32x16 (&acc)[2][2], int p, i
     // row sums: lane (lane & 31) of each half ends up with row index v = lane & 31
     const float rv = reduce_scatter32(rs, lane);
     {
+        // row partial of this wave's 64 columns: rowpart[2 jt + wj][p][row]
         const int v = lane & 31, bi = v >> 4, r = v & 15;
         const int il = wi * 64 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        racc[wj][il] = rv;
+        const int64_t gi = i0 + il;
+        if (gi < R) rowpart[((2 * jt + wj) * P + p) * R + gi] = rv;
     }
-#pragma unroll
-    for (int bj = 0; bj < 2; ++bj) {
-        const float c = cs[bj] + __shfl_xor(cs[bj], 32);
-        if (lane < 32) cacc[wi][wj * 64 + bj * 32 + lane] = c;
+    {
+        // column partial of this wave's 64 rows: lanes 0..31 column block 0, 32..63 block 1
+        const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(cs[0]), __float_as_uint(cs[1]), false, false);
+        const float cv = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+        const int64_t g = j0 + wj * 64 + lane;
+        if (g < N) colpart[((2 * it + wi) * P + p) * N + g] = cv;
     }
-    __syncthreads();
-    if (tid < FB) {
-        const int64_t gi = i0 + tid;
-        if (gi < R) rowpart[(jt * P + p) * R + gi] = racc[0][tid] + racc[1][tid];
-    } else {
-        const int c = tid - FB;
-        const int64_t g = j0 + c;
-        if (g < N) colpart[(it * P + p) * N + g] = cacc[0][c] + cacc[1][c];
-    }
-    __syncthreads();
 }
 
 __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const u16 *__restrict__ k, int64_t R,
@@ -247,8 +258,6 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
     __shared__ __attribute__((aligned(16))) u16 Ys[FB * FPITCH];
     __shared__ float fA[kMaxP][FB];
     __shared__ float fI[kMaxP][FB];
-    __shared__ float racc[2][FB];
-    __shared__ float cacc[2][FB];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wi = wave >> 1, wj = wave & 1;
@@ -330,11 +339,11 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
                         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
                 if (pnext < P && dk + 16 == pf.w[pnext]) {
                     if (masked)
-                        fwd_snapshot<true>(acc, pnext, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI,
-                                           racc, cacc, it, jt, rowpart, colpart);
+                        fwd_snapshot<true>(acc, pnext, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, it,
+                                           jt, rowpart, colpart);
                     else
-                        fwd_snapshot<false>(acc, pnext, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI,
-                                            racc, cacc, it, jt, rowpart, colpart);
+                        fwd_snapshot<false>(acc, pnext, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, it,
+                                            jt, rowpart, colpart);
                     ++pnext;
                 }
             }
@@ -843,11 +852,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     // transposed inner-tile operands of the update, two steps ahead; the first two are
     // read before the barrier that publishes the band operands (the tile is stable)
     f16x8 bf[3];
+    // per-lane part of the transposed reads (loop invariant); ring slot and step are immediates
+    const _Float16 *ytr = &Ys[0][0] + (8 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * YP + 16 * ((lane >> 4) & 1) +
+                          4 * (lane & 3) + 32 * w * NQ;
     auto load_b = [&](int buf, auto jc) {
         constexpr int jb = decltype(jc)::value;
-        const int G = lane >> 4, j = lane & 15;
-        const _Float16 *ysrc =
-            Ys[buf] + (8 * (G >> 1) + (j >> 2)) * YP + 16 * (G & 1) + 4 * (j & 3) + 32 * (w * NQ + jb);
+        const _Float16 *ysrc = ytr + buf * (BI * YP) + 32 * jb;
         const f16x4 lo = ds_read_tr(ysrc);
         const f16x4 hi = ds_read_tr(ysrc + 4 * YP);
         bf[jb % 3] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
