@@ -383,8 +383,16 @@ __device__ __forceinline__ float fold_partials(const float *part, int64_t ntiles
                                                int64_t r, bool ok, float (*fold)[kStatRows]) {
     const int g = threadIdx.x / kStatRows, rl = threadIdx.x % kStatRows;
     float v = 0.f;
-    if (ok)
-        for (int64_t t = g; t < ntiles; t += 4) v += part[(t * P + p) * len + r];
+    if (ok) {
+        // four independent running sums (loads in flight), added in a fixed order
+        float u[4] = {0.f, 0.f, 0.f, 0.f};
+        int64_t t = g;
+        for (; t + 12 < ntiles; t += 16)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) u[k] += part[((t + 4 * k) * P + p) * len + r];
+        for (; t < ntiles; t += 4) u[0] += part[(t * P + p) * len + r];
+        v = (u[0] + u[1]) + (u[2] + u[3]);
+    }
     fold[g][rl] = v;
     __syncthreads();
     const float s = (fold[0][rl] + fold[1][rl]) + (fold[2][rl] + fold[3][rl]);
@@ -558,8 +566,7 @@ struct Ladder {
         return m;
     }
     static constexpr uint32_t INT_MASK = interior();
-    static constexpr int NSLOT = 4 + __builtin_popcount(INT_MASK) + 1;  // the last one takes unused snapshots
-    static constexpr int DUMMY = NSLOT - 1;
+    static constexpr int NSLOT = 4 + __builtin_popcount(INT_MASK);
     // local steps (within a quarter) after which some wave takes a snapshot
     static constexpr uint32_t local_snaps() {
         uint32_t m = 0;
@@ -722,10 +729,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     // E_a's band operands are held in registers until phase A writes them, because
     // the update of t reads the band operand buffer during phase B.
     constexpr int NA = NP / 2;  // prefixes NP - NA .. NP - 1 belong to E_a
-    f32x4 sv[NSLOT - 1];
+    f32x4 sv[NSLOT];
     auto read_slots = [&]() {
 #pragma unroll
-        for (int s = 0; s < NSLOT - 1; ++s) sv[s] = *(const f32x4 *)&Sl[s][lane * SLOTP + 4 * w];
+        for (int s = 0; s < NSLOT; ++s) sv[s] = *(const f32x4 *)&Sl[s][lane * SLOTP + 4 * w];
     };
     float run[4] = {0.f, 0.f, 0.f, 0.f};
     f16x4 hv[NA > 0 ? NA : 1];
@@ -833,11 +840,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             for (int ob = 0; ob < 4; ++ob)
                 acc[ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(yv[ks & 1], xr[ob][ks], acc[ob], 0, 0, 0);
             if constexpr (((L::LPOS >> ks) & 1u) != 0 && ks + 1 < NQ) {
-                // every wave stores here (no branch); waves without a prefix end at this step use the spare slot
+                // waves with a prefix end at this step store a snapshot (a wave-uniform branch)
                 const int J = w * NQ + ks;
-                const int slot = ((L::INT_MASK >> J) & 1u) ? 4 + __builtin_popcount(L::INT_MASK & ((1u << J) - 1u))
-                                                           : L::DUMMY;
-                put(slot);
+                if ((L::INT_MASK >> J) & 1u) put(4 + __builtin_popcount(L::INT_MASK & ((1u << J) - 1u)));
             }
             if constexpr (WE)  // E_b units: prefixes NP - NA - 1 .. 0
                 static_for<0, NP - NA>([&](auto uc) {
