@@ -124,6 +124,9 @@ hipError_t launch_loss(const LossArgs &a, hipStream_t s);
 constexpr int kFwdTile = 128;   // forward tile (rows and columns)
 constexpr int kBwdOuter = 64;   // outer rows per backward workgroup
 constexpr int kBwdInner = 16;   // inner rows per backward block
+// rows of a backward operand copy: whole blocks plus two zero blocks, which the
+// backward's copies run into past the last block
+inline int64_t bwd_padded_rows(int64_t rows) { return ((rows + kBwdInner - 1) / kBwdInner + 2) * kBwdInner; }
 constexpr int kStatRows = 64;   // rows per block of the statistics kernels
 
 }  // namespace uform

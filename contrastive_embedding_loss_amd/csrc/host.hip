@@ -126,8 +126,8 @@ Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, in
     p.o_gmax = take(sizeof(float) * 4 * P);
     p.o_diagA = take(fR);
     const bool bwd = want_dq || want_dk || !softmax;  // some backward pass runs
-    p.o_qH = take(bwd ? sizeof(u16) * R * D : 0);
-    p.o_kH = take(bwd ? sizeof(u16) * N * D : 0);
+    p.o_qH = take(bwd ? sizeof(u16) * bwd_padded_rows(R) * D : 0);
+    p.o_kH = take(bwd ? sizeof(u16) * bwd_padded_rows(N) * D : 0);
     // forward partials: one per wave column (row partials) / wave row (column partials) of a tile
     p.o_rowpart = take(softmax ? sizeof(float) * 2 * p.nJt * P * R : 0);
     p.o_colpart = take(softmax ? sizeof(float) * 2 * p.nIt * P * N : 0);

@@ -83,30 +83,25 @@ __device__ __forceinline__ float reduce_scatter32(float (&v)[32], int lane) {
     return v[0];
 }
 
-// Direct global -> LDS copy of 16 bytes per lane; lane l lands at lds + 16 l.
-__device__ __forceinline__ void dma16(const void *g, void *lds_base) {
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)g,
-                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
-}
-
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// The same copies issued from inline assembly, 16 or 4 bytes per lane: the
-// compiler does not see them, so it adds no waits of its own before LDS
-// accesses; the caller waits for them with s_waitcnt vmcnt.  lds must be
-// wave-uniform (it goes to M0).
-__device__ __forceinline__ void dma16_async(const void *g, const void *lds) {
-    const uint32_t l = (uint32_t)(uintptr_t)lds;
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory");
+// Direct global -> LDS copies issued from inline assembly: the compiler does not
+// see them, so it adds no waits of its own before LDS accesses; the caller waits
+// for them with s_waitcnt vmcnt.  The LDS destination (M0) must be wave-uniform.
+// dma_row1 / dma_row2: one inner row of 1 KB or 2 KB, 16 bytes per lane from
+// base + voff into LDS at m0v + 16 lane (the instruction offset moves the source
+// and the LDS destination alike).  dma4_m0: 4 bytes per lane from g into m0v + 4 lane.
+__device__ __forceinline__ void dma_row1(const void *base, uint32_t voff, uint32_t m0v) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0v) : "memory");
 }
-// Same, wave-uniform base (SGPR pair) plus a 32-bit per-lane byte offset.
-__device__ __forceinline__ void dma16_async_s(const void *base, uint32_t voff, const void *lds) {
-    const uint32_t l = (uint32_t)(uintptr_t)lds;
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(l) : "memory");
+__device__ __forceinline__ void dma_row2(const void *base, uint32_t voff, uint32_t m0v) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1\n\tglobal_load_lds_dwordx4 %0, %1 offset:1024" ::"v"(
+                     voff),
+                 "s"(base), "s"(m0v)
+                 : "memory");
 }
-__device__ __forceinline__ void dma4_async(const void *g, const void *lds) {
-    const uint32_t l = (uint32_t)(uintptr_t)lds;
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(l) : "memory");
+__device__ __forceinline__ void dma4_m0(const void *g, uint32_t m0v) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0v) : "memory");
 }
 
 // ----------------------------------------------------------------------------
@@ -163,20 +158,23 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
 // ----------------------------------------------------------------------------
 // k_half_copy: xh[r][d] = x[r][d] * sig_r in FP16.  sig is a power of two
 // that brings the row norm into [1, 2), so the BF16 -> FP16 conversion is exact
-// for every element above FP16's subnormal range.  8 elements per thread.
+// for every element above FP16's subnormal range.  Rows rows .. rows_pad - 1 are
+// zeros (the backward streams whole blocks past the last row).  8 elements per thread.
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_half_copy(const u16 *__restrict__ x, const float *__restrict__ sig,
-                                                   int64_t rows, int D, _Float16 *__restrict__ xh) {
+                                                   int64_t rows, int64_t rows_pad, int D, _Float16 *__restrict__ xh) {
     const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-    if (e >= rows * D) return;
-    const float sc = sig[e / D];
-    const uint4 v = *(const uint4 *)(x + e);
-    const unsigned int in[4] = {v.x, v.y, v.z, v.w};
-    f16x8 h;
+    if (e >= rows_pad * D) return;
+    f16x8 h = {};
+    if (e < rows * D) {
+        const float sc = sig[e / D];
+        const uint4 v = *(const uint4 *)(x + e);
+        const unsigned int in[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        h[2 * i] = (_Float16)(bf16_lo(in[i]) * sc);
-        h[2 * i + 1] = (_Float16)(bf16_hi(in[i]) * sc);
+        for (int i = 0; i < 4; ++i) {
+            h[2 * i] = (_Float16)(bf16_lo(in[i]) * sc);
+            h[2 * i + 1] = (_Float16)(bf16_hi(in[i]) * sc);
+        }
     }
     *(f16x8 *)(xh + e) = h;
 }
@@ -612,9 +610,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     constexpr int DW = L::DW;
     constexpr int YP = L::YP;
     constexpr int NSLOT = L::NSLOT;
-    constexpr int IPR = (DW / 8 + 63) / 64;  // 16-byte copy instructions per inner row
-    constexpr int NCW = BI * IPR / 4;        // copy instructions per wave per block
+    constexpr int RPW = BI / 4;                // inner rows this wave copies per block
+    constexpr int IPR = (DW / 8 + 63) / 64;    // 1 KB pieces per inner row
+    constexpr bool FULLP = (DW / 8) % 64 == 0;  // every lane of every piece active
+    constexpr int NCW = RPW * IPR;             // row copy instructions per wave per block
     static_assert(NQ >= 1 && L::NDS % 4 == 0, "the widest prefix must be a multiple of 128");
+    static_assert(IPR == 1 || (FULLP && IPR == 2), "an inner row is one partial or one or two whole 1 KB pieces");
 
     __shared__ __attribute__((aligned(16))) _Float16 Ys[NYBUF][BI * YP];
     __shared__ __attribute__((aligned(16))) float Sl[NSLOT][BO * SLOTP];
@@ -625,12 +626,13 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4, l32 = lane & 31, h32 = lane >> 5;
-    const int64_t o0 = (int64_t)blockIdx.x * BO;
-    const int64_t o = o0 + lane;  // the outer row of this lane in the E-phase
-    const bool ovalid = o < a.NO;
-    const int64_t nblocks = (a.NI + BI - 1) / BI;
-    const int64_t nb_begin = (int64_t)blockIdx.y * a.blocks_per_split;
-    const int64_t nb_end = nb_begin + a.blocks_per_split < nblocks ? nb_begin + a.blocks_per_split : nblocks;
+    const int NO = (int)a.NO, NI = (int)a.NI, dsh = (int)a.diag_shift;
+    const int o0 = (int)blockIdx.x * BO;
+    const int o = o0 + lane;  // the outer row of this lane in the E-phase
+    const bool ovalid = o < NO;
+    const int nblocks = (NI + BI - 1) / BI;
+    const int nb_begin = (int)blockIdx.y * (int)a.blocks_per_split;
+    const int nb_end = min(nb_begin + (int)a.blocks_per_split, nblocks);
     const int D = a.D;
     const int dq0 = w * (DW / 4);  // first column of this wave's quarter
 
@@ -662,31 +664,35 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         if (w == 0) inv_sc[lane] = 1.0f / sc;
     }
 
-    // ---- copies of inner block nb into ring slot buf: the FP16 tile (rows clamped
-    // to the last row) and its two tables; every wave issues NCW + 1 copies
-    auto copy_inst = [&](int64_t nb, int buf, auto ic) {  // copy instruction ic (< NCW) of this wave
-        const int inst = w * NCW + decltype(ic)::value;
-        const int r = inst / IPR, i = inst % IPR;
-        int64_t n = nb * BI + r;
-        n = __builtin_amdgcn_readfirstlane((int)(n < a.NI ? n : a.NI - 1));
-        const _Float16 *rowp = a.Y16 + n * D + 512 * i;  // wave-uniform
-        if constexpr ((DW / 8) % 64 == 0)  // whole rows of 1 KB copies: every lane active
-            dma16_async_s(rowp, 16u * lane, &Ys[buf][r * YP + 512 * i]);
-        else if (64 * i + lane < DW / 8)
-            dma16_async_s(rowp, 16u * lane, &Ys[buf][r * YP + 512 * i]);
+    // ---- copies of an inner block into a ring slot.  This wave copies inner rows
+    // 4 w .. 4 w + 3 (the FP16 inner matrix carries two zero blocks past its last row,
+    // so no row index is clamped) and one float of the block's tables per lane.
+    uint32_t cvo[RPW];  // this lane's byte offset in each of its rows, from the block start
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) cvo[k] = (uint32_t)(4 * w + k) * (uint32_t)D * 2u + 16u * (uint32_t)lane;
+    const uint32_t ys_lds = (uint32_t)(uintptr_t)&Ys[0][0], tab_lds = (uint32_t)(uintptr_t)&tabs[0][0];
+    auto copy_row = [&](const _Float16 *gblk, int ybo, auto kc) {  // row 4 w + k of the block at gblk into slot ybo
+        constexpr int k = decltype(kc)::value;
+        const uint32_t m0v = ys_lds + 2u * (uint32_t)(ybo + (4 * w + k) * YP);
+        if constexpr (IPR == 2)
+            dma_row2(gblk, cvo[k], m0v);
+        else if constexpr (FULLP)
+            dma_row1(gblk, cvo[k], m0v);
+        else if (lane < DW / 8)
+            dma_row1(gblk, cvo[k], m0v);
     };
-    auto copy_tables = [&](int64_t nb, int buf) {
-        const int e = 64 * w + lane;  // table entry [which][p][r]; lanes past the end copy a harmless float
-        const int which = e / (NP * BI), p = (e / BI) % NP, r = e % BI;
-        int64_t n = nb * BI + r;
-        if (n >= a.NI) n = a.NI - 1;
-        const float *tsrc = which == 0 ? a.iI : a.iKap;
-        const float *src = e < 2 * NP * BI ? tsrc + p * a.NI + n : a.iI;
-        dma4_async(src, &tabs[buf][64 * w]);
-    };
-    auto issue_block = [&](int64_t nb, int buf) {
-        static_for<0, NCW>([&](auto ic) { copy_inst(nb, buf, ic); });
-        copy_tables(nb, buf);
+    // table entry [which][p][r] of this lane (lanes past the end copy a harmless float)
+    const int te = 64 * w + lane;
+    const bool tact = te < 2 * NP * BI;
+    const int tr = te % BI;
+    const float *tbase = tact ? ((te / (NP * BI)) == 0 ? a.iI : a.iKap) + (int64_t)((te / BI) % NP) * NI + tr : a.iI;
+    const int tlim = tact ? NI - 1 - tr : 0;  // rows past the end read the last row
+    auto copy_tables = [&](int nb, int tbo) { dma4_m0(tbase + min(nb * BI, tlim), tab_lds + 4u * (uint32_t)(tbo + 64 * w)); };
+    const _Float16 *gcp = a.Y16 + (int64_t)nb_begin * BI * D;  // the next block to copy
+    auto issue_block = [&](int nb, int ybo, int tbo) {
+        static_for<0, RPW>([&](auto kc) { copy_row(gcp, ybo, kc); });
+        copy_tables(nb, tbo);
+        gcp += (int64_t)BI * D;
     };
 
     // zero the ring once so that every LDS word the kernel reads was written
@@ -736,25 +742,48 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     };
     float run[4] = {0.f, 0.f, 0.f, 0.f};
     f16x4 hv[NA > 0 ? NA : 1];
-    auto masks = [&](auto masked, int64_t nb, bool (&vm)[4]) {
-        constexpr bool MK = decltype(masked)::value;
-        const int64_t nw = nb * BI + 4 * w;
+    // cells that need masks: ragged rows, or the positives of these outer rows
+    auto needmask = [&](int nb) {
+        const int n0 = nb * BI;
+        return (n0 + BI > NI) || (o0 + BO > NO) || ((n0 < o0 + dsh + BO) && (o0 + dsh < n0 + BI));
+    };
+    // lane masks of block nb's cells for inner rows 4 w + t (wave-uniform 64-bit masks;
+    // a block past the split's end has every cell masked)
+    const uint64_t ovm = __builtin_amdgcn_ballot_w64(ovalid);
+    auto block_masks = [&](int nb, uint64_t(&mk)[4]) {
+        if (nb >= nb_end) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int64_t n = nw + t;
-            vm[t] = MK ? (ovalid & (n < a.NI) & (n < nb_end * BI) & (n != o + a.diag_shift)) : true;
+            for (int t = 0; t < 4; ++t) mk[t] = 0;
+        } else if (needmask(nb)) {
+            const int nw = nb * BI + 4 * w;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) mk[t] = __builtin_amdgcn_ballot_w64(ovalid && nw + t < NI && nw + t != o + dsh);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) mk[t] = ovm;
         }
     };
     // epilogue unit of prefix p for the block whose tables sit in ring slot ebuf
-    auto unit = [&](auto pc, auto masked, const bool (&vm)[4], int ebuf) {
+    const float *tabs0 = &tabs[0][0];
+    auto unit = [&](auto pc, auto masked, const uint64_t(&mk)[4], int eto) {
         constexpr int p = decltype(pc)::value;
         constexpr bool MK = decltype(masked)::value;
-        f32x4 Sp = sv[L::snap_slot(p)];
-        static_for<0, L::wave_of(p)>([&](auto qc) { Sp += sv[decltype(qc)::value]; });
-        const f32x4 iy = *(const f32x4 *)&tabs[ebuf][p * BI + 4 * w];
+        // S^p = quarters below wave_of(p), lowest first (shared by the prefixes), plus the snapshot
+        f32x4 Sp;
+        if constexpr (L::wave_of(p) == 0) {
+            Sp = sv[L::snap_slot(p)];
+        } else {
+            Sp = sv[0];
+            static_for<1, L::wave_of(p)>([&](auto qc) { Sp += sv[decltype(qc)::value]; });
+            Sp += sv[L::snap_slot(p)];
+        }
+        bool vm[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) vm[t] = MK ? __builtin_amdgcn_inverse_ballot_w64(mk[t]) : true;
+        const f32x4 iy = *(const f32x4 *)&tabs0[eto + p * BI + 4 * w];
         float av[4];
         if constexpr (!SIG) {
-            const f32x4 kp = *(const f32x4 *)&tabs[ebuf][(NP + p) * BI + 4 * w];
+            const f32x4 kp = *(const f32x4 *)&tabs0[eto + (NP + p) * BI + 4 * w];
             float x[4], e[4], g[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) x[t] = Sp[t] * Ao[p];
@@ -806,19 +835,17 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     // phase A: recompute of the tile in ring slot rbuf (partial S^T over this wave's quarter,
     // 16 inner x 64 outer, into the S slots) | E_b of block nb (tables in ebuf) | copies of
     // block cnb into cbuf, each spread over the recompute steps
-    auto phase_a = [&](auto masked, auto with_e, int rbuf, int64_t nb, int ebuf, int64_t cnb, int cbuf) {
+    auto phase_a = [&](auto masked, auto with_e, int ryo, const uint64_t(&mk)[4], int eto, int cnb, int cyo, int cto) {
         constexpr bool WE = decltype(with_e)::value;
         f32x4 acc[4];
 #pragma unroll
         for (int ob = 0; ob < 4; ++ob) acc[ob] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const _Float16 *yrow = Ys[rbuf] + l16 * YP + dq0 + 8 * g4;
+        const _Float16 *yrow = &Ys[0][0] + ryo + l16 * YP + dq0 + 8 * g4;
         auto put = [&](int slot) {
 #pragma unroll
             for (int ob = 0; ob < 4; ++ob) *(f32x4 *)&Sl[slot][(16 * ob + l16) * SLOTP + 4 * g4] = acc[ob];
         };
-        bool vm[4];
         if constexpr (WE) {
-            masks(masked, nb, vm);
             if constexpr (UPD)
                 static_for<0, NA>([&](auto ic) {
                     constexpr int p = NP - 1 - decltype(ic)::value;
@@ -831,9 +858,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             constexpr int ks = decltype(kc)::value;
             if constexpr (ks + 1 < NQ) yv[(ks + 1) & 1] = *(const f16x8 *)(yrow + 32 * (ks + 1));
             if constexpr (WE) {
-                if constexpr (ks == 0) copy_tables(cnb, cbuf);
-                static_for<0, NCW>([&](auto ic) {
-                    if constexpr ((decltype(ic)::value * NQ) / NCW == ks) copy_inst(cnb, cbuf, ic);
+                if constexpr (ks == 0) copy_tables(cnb, cto);
+                static_for<0, RPW>([&](auto kc) {
+                    if constexpr ((decltype(kc)::value * NQ) / RPW == ks) copy_row(gcp, cyo, kc);
                 });
             }
 #pragma unroll
@@ -847,7 +874,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             if constexpr (WE)  // E_b units: prefixes NP - NA - 1 .. 0
                 static_for<0, NP - NA>([&](auto uc) {
                     if constexpr ((decltype(uc)::value * NQ) / (NP - NA) == ks)
-                        unit(std::integral_constant<int, NP - NA - 1 - decltype(uc)::value>{}, masked, vm, ebuf);
+                        unit(std::integral_constant<int, NP - NA - 1 - decltype(uc)::value>{}, masked, mk, eto);
                 });
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -860,28 +887,26 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     // per-lane part of the transposed reads (loop invariant); ring slot and step are immediates
     const _Float16 *ytr = &Ys[0][0] + (8 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * YP + 16 * ((lane >> 4) & 1) +
                           4 * (lane & 3) + 32 * w * NQ;
-    auto load_b = [&](int buf, auto jc) {
+    auto load_b = [&](int uyo, auto jc) {
         constexpr int jb = decltype(jc)::value;
-        const _Float16 *ysrc = ytr + buf * (BI * YP) + 32 * jb;
+        const _Float16 *ysrc = ytr + uyo + 32 * jb;
         const f16x4 lo = ds_read_tr(ysrc);
         const f16x4 hi = ds_read_tr(ysrc + 4 * YP);
         bf[jb % 3] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    auto u_pre = [&](int buf) {
-        load_b(buf, std::integral_constant<int, 0>{});
-        if constexpr (NQ > 1) load_b(buf, std::integral_constant<int, 1>{});
+    auto u_pre = [&](int uyo) {
+        load_b(uyo, std::integral_constant<int, 0>{});
+        if constexpr (NQ > 1) load_b(uyo, std::integral_constant<int, 1>{});
     };
     // phase B: dX[:, quarter] += A_band . Y[:, quarter] for the tile in ring slot ubuf | E_a of
     // block nb1 (tables in ebuf1).  The band operand is read only at the
     // steps where some wave's band changes (the same code for every wave, no branches).
     // (No branches in here: the gradient accumulators must not meet at a join.  E_a always
     // runs with masks; a block past the end has every cell masked.)
-    auto phase_b = [&](auto with_u, int ubuf, int64_t nb1, int ebuf1) {
+    auto phase_b = [&](auto with_u, int uyo, const uint64_t(&mk1)[4], int eto1) {
         constexpr bool WE = NA > 0;
         constexpr bool WU = decltype(with_u)::value && UPD;
         constexpr std::true_type masked{};
-        bool vm[4];
-        if constexpr (WE) masks(masked, nb1, vm);
         f16x8 af[2];
         static_for<0, NQ>([&](auto jc) {
             constexpr int jb = decltype(jc)::value;
@@ -892,7 +917,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
                     for (int ob = 0; ob < 2; ++ob)
                         af[ob] = *(const f16x8 *)&At[band][(32 * ob + l32) * APITCH + 8 * h32];
                 }
-                if constexpr (jb + 2 < NQ) load_b(ubuf, std::integral_constant<int, jb + 2>{});
+                if constexpr (jb + 2 < NQ) load_b(uyo, std::integral_constant<int, jb + 2>{});
 #pragma unroll
                 for (int ob = 0; ob < 2; ++ob)
                     dacc[ob][jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ob], bf[jb % 3], dacc[ob][jb], 0, 0, 0);
@@ -900,47 +925,47 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             if constexpr (WE)  // E_a units: prefixes NP - 1 .. NP - NA
                 static_for<0, NA>([&](auto uc) {
                     if constexpr ((decltype(uc)::value * NQ) / NA == jb)
-                        unit(std::integral_constant<int, NP - 1 - decltype(uc)::value>{}, masked, vm, ebuf1);
+                        unit(std::integral_constant<int, NP - 1 - decltype(uc)::value>{}, masked, mk1, eto1);
                 });
             __builtin_amdgcn_sched_barrier(0);
         });
     };
-    auto needmask = [&](int64_t nb) {  // cells that need masks: ragged rows, or the positives of these outer rows
-        const int64_t n0 = nb * BI;
-        return (n0 + BI > a.NI) || (o0 + BO > a.NO) ||
-               ((n0 < o0 + a.diag_shift + BO) && (o0 + a.diag_shift < n0 + BI));
-    };
-
+    // ring slots (FP16 elements) and table slots (floats) of blocks nb, nb + 1, nb + 2
+    int yo0 = 0, yo1 = BI * YP, yo2 = 2 * BI * YP;
+    int to0 = 0, to1 = 256, to2 = 512;
+    uint64_t mk_cur[4], mk_nxt[4];  // lane masks of blocks nb and nb + 1
+    block_masks(nb_begin, mk_cur);
     if (nb_begin < nb_end) {
-        issue_block(nb_begin, 0);
-        if (nb_begin + 1 < nb_end) {
-            issue_block(nb_begin + 1, 1);
-            wait_vm_n<NCW + 1>();
-        } else {
-            wait_vm();
-        }
+        issue_block(nb_begin, yo0, to0);
+        issue_block(nb_begin + 1, yo1, to1);  // past the split's end: rows of the next split or the zero blocks
+        wait_vm_n<NCW + 1>();
         lds_barrier();  // block 0 visible
-        phase_a(std::false_type{}, std::false_type{}, 0, nb_begin, 0, 0, 0);  // recompute of block 0 alone
+        phase_a(std::false_type{}, std::false_type{}, yo0, mk_cur, 0, 0, 0, 0);  // recompute of block 0 alone
         lds_barrier();  // slots of block 0 visible
         read_slots();
-        phase_b(std::false_type{}, 0, nb_begin, 0);  // E_a of block 0 alone
+        phase_b(std::false_type{}, 0, mk_cur, to0);  // E_a of block 0 alone
     }
 
-    int it = 0;
-    for (int64_t nb = nb_begin; nb < nb_end; ++nb, ++it) {
-        const int buf = it % NYBUF, buf1 = (it + 1) % NYBUF, buf2 = (it + 2) % NYBUF;
+    for (int nb = nb_begin; nb < nb_end; ++nb) {
         wait_vm();      // block nb + 1 landed (issued a full block earlier)
         lds_barrier();  // slots of nb consumed, every wave past the update of nb - 1; block nb + 1 visible
-        // phase A: recompute of nb + 1 (past the end: a stale tile) | E_b(nb) | copies of nb + 2
-        // (past the end: clamped rows into a free ring slot)
+        // phase A: recompute of nb + 1 (past the end: a block of zeros or of the next split) | E_b(nb) |
+        // copies of nb + 2
         if (needmask(nb))
-            phase_a(std::true_type{}, std::true_type{}, buf1, nb, buf, nb + 2, buf2);
+            phase_a(std::true_type{}, std::true_type{}, yo1, mk_cur, to0, nb + 2, yo2, to2);
         else
-            phase_a(std::false_type{}, std::true_type{}, buf1, nb, buf, nb + 2, buf2);
-        if constexpr (UPD) u_pre(buf);
+            phase_a(std::false_type{}, std::true_type{}, yo1, mk_cur, to0, nb + 2, yo2, to2);
+        gcp += (int64_t)BI * D;
+        block_masks(nb + 1, mk_nxt);
+        if constexpr (UPD) u_pre(yo0);
         lds_barrier();  // band operands of nb and slots of nb + 1 visible
         read_slots();
-        phase_b(std::true_type{}, buf, nb + 1, buf1);  // update of nb | E_a(nb + 1)
+        phase_b(std::true_type{}, yo0, mk_nxt, to1);  // update of nb | E_a(nb + 1)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) mk_cur[t] = mk_nxt[t];
+        const int y = yo0, tt = to0;
+        yo0 = yo1, yo1 = yo2, yo2 = y;
+        to0 = to1, to1 = to2, to2 = tt;
     }
 
     // ---------------- write the raw gradient block (scale divided out) and the radial sums
@@ -953,8 +978,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             for (int r = 0; r < 16; ++r) {
                 const int orow = ob * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
                 const float s = inv_sc[orow];
-                if (o0 + orow < a.NO) {
-                    float *rowp = dst + (o0 + orow) * D + dq0 + l32;
+                if (o0 + orow < NO) {
+                    float *rowp = dst + (int64_t)(o0 + orow) * D + dq0 + l32;
 #pragma unroll
                     for (int jb = 0; jb < NQ; ++jb) rowp[32 * jb] = dacc[ob][jb][r] * s;
                 }
@@ -1098,8 +1123,10 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_half_copy(const u16 *x, const float *sig, int64_t rows, int D, _Float16 *xh, hipStream_t s) {
-    const int64_t chunks = rows * D / 8;  // D is a multiple of 64
-    hipLaunchKernelGGL(k_half_copy, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, x, sig, rows, D, xh);
+    const int64_t rows_pad = bwd_padded_rows(rows);
+    const int64_t chunks = rows_pad * D / 8;  // D is a multiple of 64
+    hipLaunchKernelGGL(k_half_copy, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, x, sig, rows, rows_pad,
+                       D, xh);
     return hipGetLastError();
 }
 
