@@ -617,9 +617,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     static_assert(NQ >= 1 && L::NDS % 4 == 0, "the widest prefix must be a multiple of 128");
     static_assert(IPR == 1 || (FULLP && IPR == 2), "an inner row is one partial or one or two whole 1 KB pieces");
 
-    __shared__ __attribute__((aligned(16))) _Float16 Ys[NYBUF][BI * YP];
+    constexpr int RSL = BI * YP + 512;  // FP16 elements per ring slot: the tile, then its tables [iI | iKap][p][row]
+    __shared__ __attribute__((aligned(16))) _Float16 Ys[NYBUF][RSL];
     __shared__ __attribute__((aligned(16))) float Sl[NSLOT][BO * SLOTP];
-    __shared__ __attribute__((aligned(16))) float tabs[NYBUF][256];  // per tile: [iI | iKap][p][inner row]
     __shared__ __attribute__((aligned(16))) _Float16 At[NP][BO * APITCH];
     __shared__ float inv_sc[BO];
 
@@ -670,7 +670,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     uint32_t cvo[RPW];  // this lane's byte offset in each of its rows, from the block start
 #pragma unroll
     for (int k = 0; k < RPW; ++k) cvo[k] = (uint32_t)(4 * w + k) * (uint32_t)D * 2u + 16u * (uint32_t)lane;
-    const uint32_t ys_lds = (uint32_t)(uintptr_t)&Ys[0][0], tab_lds = (uint32_t)(uintptr_t)&tabs[0][0];
+    const uint32_t ys_lds = (uint32_t)(uintptr_t)&Ys[0][0];
     auto copy_row = [&](const _Float16 *gblk, int ybo, auto kc) {  // row 4 w + k of the block at gblk into slot ybo
         constexpr int k = decltype(kc)::value;
         const uint32_t m0v = ys_lds + 2u * (uint32_t)(ybo + (4 * w + k) * YP);
@@ -687,17 +687,18 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     const int tr = te % BI;
     const float *tbase = tact ? ((te / (NP * BI)) == 0 ? a.iI : a.iKap) + (int64_t)((te / BI) % NP) * NI + tr : a.iI;
     const int tlim = tact ? NI - 1 - tr : 0;  // rows past the end read the last row
-    auto copy_tables = [&](int nb, int tbo) { dma4_m0(tbase + min(nb * BI, tlim), tab_lds + 4u * (uint32_t)(tbo + 64 * w)); };
+    auto copy_tables = [&](int nb, int ybo) {
+        dma4_m0(tbase + min(nb * BI, tlim), ys_lds + 2u * (uint32_t)(ybo + BI * YP) + 4u * (uint32_t)(64 * w));
+    };
     const _Float16 *gcp = a.Y16 + (int64_t)nb_begin * BI * D;  // the next block to copy
-    auto issue_block = [&](int nb, int ybo, int tbo) {
+    auto issue_block = [&](int nb, int ybo) {
         static_for<0, RPW>([&](auto kc) { copy_row(gcp, ybo, kc); });
-        copy_tables(nb, tbo);
+        copy_tables(nb, ybo);
         gcp += (int64_t)BI * D;
     };
 
     // zero the ring once so that every LDS word the kernel reads was written
-    for (int e = tid; e < NYBUF * BI * YP / 8; e += 256) *(uint4 *)&Ys[0][e * 8] = make_uint4(0, 0, 0, 0);
-    for (int e = tid; e < NYBUF * 256; e += 256) tabs[0][e] = 0.f;
+    for (int e = tid; e < NYBUF * RSL / 8; e += 256) *(uint4 *)&Ys[0][e * 8] = make_uint4(0, 0, 0, 0);
     lds_barrier();
 
     // ---- outer rows' quarter as B operands: rows 16 ob + l16, columns dq0 + 32 ks + 8 g4
@@ -742,34 +743,44 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     };
     float run[4] = {0.f, 0.f, 0.f, 0.f};
     f16x4 hv[NA > 0 ? NA : 1];
-    // cells that need masks: ragged rows, or the positives of these outer rows
-    auto needmask = [&](int nb) {
-        const int n0 = nb * BI;
-        return (n0 + BI > NI) || (o0 + BO > NO) || ((n0 < o0 + dsh + BO) && (o0 + dsh < n0 + BI));
-    };
-    // lane masks of block nb's cells for inner rows 4 w + t (wave-uniform 64-bit masks;
-    // a block past the split's end has every cell masked)
+    // blocks whose cells need masks: from nb_sp on (ragged or past the split's end; every
+    // block if the outer rows are ragged), and those holding positives of these outer rows
+    const int nb_sp = o0 + BO > NO ? 0 : min(NI / BI, nb_end);
+    const int c_hi = o0 + dsh + BO, c_lo = o0 + dsh - BI;
+    auto needmask = [&](int nb) { return nb >= nb_sp || (nb * BI < c_hi && nb * BI > c_lo); };
+    // lane masks of block nb's cells for inner rows 4 w + t (wave-uniform 64-bit masks)
     const uint64_t ovm = __builtin_amdgcn_ballot_w64(ovalid);
     auto block_masks = [&](int nb, uint64_t(&mk)[4]) {
-        if (nb >= nb_end) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) mk[t] = 0;
-        } else if (needmask(nb)) {
-            const int nw = nb * BI + 4 * w;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) mk[t] = __builtin_amdgcn_ballot_w64(ovalid && nw + t < NI && nw + t != o + dsh);
-        } else {
+        if (!needmask(nb)) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) mk[t] = ovm;
+        } else {
+            const int nw = nb * BI + 4 * w;
+            const int lim = min(NI, nb_end * BI);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) mk[t] = __builtin_amdgcn_ballot_w64(ovalid && nw + t < lim && nw + t != o + dsh);
         }
     };
-    // epilogue unit of prefix p for the block whose tables sit in ring slot ebuf
-    const float *tabs0 = &tabs[0][0];
-    auto unit = [&](auto pc, auto masked, const uint64_t(&mk)[4], int eto) {
+    // Epilogue unit of prefix p for the block in ring slot eyo (its tables follow the tile), in
+    // three parts that the phases spread over their MFMA steps: the table reads (utab), the
+    // logits and exponentials (uchunk_a), the coefficients, radial sums and band operands (uchunk_b).
+    const float *tabs0 = (const float *)&Ys[0][BI * YP];
+    struct UTab {
+        f32x4 iy, kp;
+    };
+    auto utab = [&](auto pc, int eyo) {
+        constexpr int p = decltype(pc)::value;
+        const int eto = eyo / 2;  // the slot's tables, in floats from the first slot's
+        UTab tb;
+        tb.iy = *(const f32x4 *)&tabs0[eto + p * BI + 4 * w];
+        if constexpr (!SIG) tb.kp = *(const f32x4 *)&tabs0[eto + (NP + p) * BI + 4 * w];
+        return tb;
+    };
+    // S^p (quarters below wave_of(p), lowest first, shared by the prefixes, plus the snapshot) and
+    // e = 2^(S A_o iy + C_o) (softmax) or the unmasked coefficient sigma(l) beta_o iy (sigmoid)
+    auto uchunk_a = [&](auto pc, auto masked, const uint64_t(&mk)[4], const UTab &tb, f32x4 &Sp, f32x4 &e) {
         constexpr int p = decltype(pc)::value;
         constexpr bool MK = decltype(masked)::value;
-        // S^p = quarters below wave_of(p), lowest first (shared by the prefixes), plus the snapshot
-        f32x4 Sp;
         if constexpr (L::wave_of(p) == 0) {
             Sp = sv[L::snap_slot(p)];
         } else {
@@ -777,44 +788,43 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             static_for<1, L::wave_of(p)>([&](auto qc) { Sp += sv[decltype(qc)::value]; });
             Sp += sv[L::snap_slot(p)];
         }
-        bool vm[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) vm[t] = MK ? __builtin_amdgcn_inverse_ballot_w64(mk[t]) : true;
-        const f32x4 iy = *(const f32x4 *)&tabs0[eto + p * BI + 4 * w];
-        float av[4];
         if constexpr (!SIG) {
-            const f32x4 kp = *(const f32x4 *)&tabs0[eto + (NP + p) * BI + 4 * w];
-            float x[4], e[4], g[4];
+            float x[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) x[t] = Sp[t] * Ao[p];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) x[t] = fmaf(x[t], iy[t], Co[p]);
+            for (int t = 0; t < 4; ++t) x[t] = fmaf(x[t], tb.iy[t], Co[p]);
 #pragma unroll
             for (int t = 0; t < 4; ++t) e[t] = __builtin_amdgcn_exp2f(x[t]);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) g[t] = fmaf(Ro[p], iy[t], kp[t]);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) av[t] = e[t] * g[t];
         } else {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const float uu = fmaf(Sp[t] * Ao[p], iy[t], a.b2);
+                const float uu = fmaf(Sp[t] * Ao[p], tb.iy[t], a.b2);
                 const float tt = __builtin_amdgcn_exp2f(-fabsf(uu));
                 const float wq = 1.f + tt;
                 const float rr = __builtin_amdgcn_rcpf(wq);
                 const float sg = uu >= 0.f ? rr : tt * rr;
-                av[t] = sg * Co[p] * iy[t];  // Co holds beta_o for the sigmoid form
+                e[t] = sg * Co[p] * tb.iy[t];  // Co holds beta_o for the sigmoid form
                 if (a.want_loss) {
                     // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
                     const float corr = (tt - (wq - 1.f)) * rr * kLog2e;
                     const float lt = fmaxf(uu, 0.f) + __builtin_amdgcn_logf(wq) + corr;
-                    Lacc[p] += (!MK || vm[t]) ? lt : 0.f;
+                    Lacc[p] += (!MK || __builtin_amdgcn_inverse_ballot_w64(mk[t])) ? lt : 0.f;
                 }
             }
         }
+    };
+    // a^p = e (Rho_o iy + Kap) (softmax) or e (sigmoid), masked; radial sums; band operand suffix sums
+    auto uchunk_b = [&](auto pc, auto masked, const uint64_t(&mk)[4], const UTab &tb, const f32x4 &Sp,
+                        const f32x4 &e) {
+        constexpr int p = decltype(pc)::value;
+        constexpr bool MK = decltype(masked)::value;
+        float av[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) av[t] = SIG ? e[t] : e[t] * fmaf(Ro[p], tb.iy[t], tb.kp[t]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            if constexpr (MK) av[t] = vm[t] ? av[t] : 0.f;
+            if constexpr (MK) av[t] = __builtin_amdgcn_inverse_ballot_w64(mk[t]) ? av[t] : 0.f;
             if constexpr (p == NP - 1)
                 run[t] = av[t];
             else
@@ -831,54 +841,17 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
                 *(f16x4 *)&At[p][lane * APITCH + 4 * w] = v;
         }
     };
-
-    // phase A: recompute of the tile in ring slot rbuf (partial S^T over this wave's quarter,
-    // 16 inner x 64 outer, into the S slots) | E_b of block nb (tables in ebuf) | copies of
-    // block cnb into cbuf, each spread over the recompute steps
-    auto phase_a = [&](auto masked, auto with_e, int ryo, const uint64_t(&mk)[4], int eto, int cnb, int cyo, int cto) {
-        constexpr bool WE = decltype(with_e)::value;
-        f32x4 acc[4];
-#pragma unroll
-        for (int ob = 0; ob < 4; ++ob) acc[ob] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const _Float16 *yrow = &Ys[0][0] + ryo + l16 * YP + dq0 + 8 * g4;
-        auto put = [&](int slot) {
-#pragma unroll
-            for (int ob = 0; ob < 4; ++ob) *(f32x4 *)&Sl[slot][(16 * ob + l16) * SLOTP + 4 * g4] = acc[ob];
-        };
-        if constexpr (WE) {
-            if constexpr (UPD)
-                static_for<0, NA>([&](auto ic) {
-                    constexpr int p = NP - 1 - decltype(ic)::value;
-                    *(f16x4 *)&At[p][lane * APITCH + 4 * w] = hv[decltype(ic)::value];
-                });
+    // Schedules (compile time): unit u's two chunks and its table reads, by MFMA step.
+    // Phase A runs E_b (units u = 0 .. NUB - 1 are prefixes NUB - 1 - u), phase B runs E_a
+    // (units u = 0 .. NA - 1 are prefixes NP - 1 - u); a table step of -1 is before the first step.
+    constexpr int NUB = NP - NA;
+    struct Sched {
+        static constexpr int chunk_a(int k) { return NUB > 0 ? (k * NQ) / (2 * NUB) : 0; }
+        static constexpr int tab_a(int u) { return chunk_a(2 * u) - 1; }
+        static constexpr int chunk_b(int k) {
+            return NA > 0 ? ((k * NQ) / (2 * NA) + 1 < NQ ? (k * NQ) / (2 * NA) + 1 : NQ - 1) : 0;
         }
-        f16x8 yv[2];
-        yv[0] = *(const f16x8 *)yrow;
-        static_for<0, NQ>([&](auto kc) {
-            constexpr int ks = decltype(kc)::value;
-            if constexpr (ks + 1 < NQ) yv[(ks + 1) & 1] = *(const f16x8 *)(yrow + 32 * (ks + 1));
-            if constexpr (WE) {
-                if constexpr (ks == 0) copy_tables(cnb, cto);
-                static_for<0, RPW>([&](auto kc) {
-                    if constexpr ((decltype(kc)::value * NQ) / RPW == ks) copy_row(gcp, cyo, kc);
-                });
-            }
-#pragma unroll
-            for (int ob = 0; ob < 4; ++ob)
-                acc[ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(yv[ks & 1], xr[ob][ks], acc[ob], 0, 0, 0);
-            if constexpr (((L::LPOS >> ks) & 1u) != 0 && ks + 1 < NQ) {
-                // waves with a prefix end at this step store a snapshot (a wave-uniform branch)
-                const int J = w * NQ + ks;
-                if ((L::INT_MASK >> J) & 1u) put(4 + __builtin_popcount(L::INT_MASK & ((1u << J) - 1u)));
-            }
-            if constexpr (WE)  // E_b units: prefixes NP - NA - 1 .. 0
-                static_for<0, NP - NA>([&](auto uc) {
-                    if constexpr ((decltype(uc)::value * NQ) / (NP - NA) == ks)
-                        unit(std::integral_constant<int, NP - NA - 1 - decltype(uc)::value>{}, masked, mk, eto);
-                });
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        put(w);
+        static constexpr int tab_b(int u) { return chunk_b(2 * u) - 1; }
     };
 
     // transposed inner-tile operands of the update, two steps ahead; the first two are
@@ -898,16 +871,84 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         load_b(uyo, std::integral_constant<int, 0>{});
         if constexpr (NQ > 1) load_b(uyo, std::integral_constant<int, 1>{});
     };
+    // phase A: recompute of the tile in ring slot rbuf (partial S^T over this wave's quarter,
+    // 16 inner x 64 outer, into the S slots) | E_b of block nb (tables in ebuf) | copies of
+    // block cnb into cbuf, each spread over the recompute steps
+    auto phase_a = [&](auto masked, auto with_e, int ryo, int nb, int eyo, int cnb, int cyo) {
+        constexpr bool WE = decltype(with_e)::value;
+        uint64_t mk[4];
+        if constexpr (decltype(masked)::value) block_masks(nb, mk);
+        f32x4 acc[4];
+#pragma unroll
+        for (int ob = 0; ob < 4; ++ob) acc[ob] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const _Float16 *yrow = &Ys[0][0] + ryo + l16 * YP + dq0 + 8 * g4;
+        auto put = [&](int slot) {
+#pragma unroll
+            for (int ob = 0; ob < 4; ++ob) *(f32x4 *)&Sl[slot][(16 * ob + l16) * SLOTP + 4 * g4] = acc[ob];
+        };
+        if constexpr (WE) {
+            if constexpr (UPD)
+                static_for<0, NA>([&](auto ic) {
+                    constexpr int p = NP - 1 - decltype(ic)::value;
+                    *(f16x4 *)&At[p][lane * APITCH + 4 * w] = hv[decltype(ic)::value];
+                });
+        }
+        UTab tb[NUB > 0 ? NUB : 1];
+        f32x4 spv[NUB > 0 ? NUB : 1], ev[NUB > 0 ? NUB : 1];
+        if constexpr (WE)
+            static_for<0, NUB>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
+                if constexpr (Sched::tab_a(u) < 0) tb[u] = utab(std::integral_constant<int, NUB - 1 - u>{}, eyo);
+            });
+        f16x8 yv[2];
+        yv[0] = *(const f16x8 *)yrow;
+        static_for<0, NQ>([&](auto kc) {
+            constexpr int ks = decltype(kc)::value;
+            if constexpr (ks + 1 < NQ) yv[(ks + 1) & 1] = *(const f16x8 *)(yrow + 32 * (ks + 1));
+            if constexpr (WE) {
+                if constexpr (ks == 0) copy_tables(cnb, cyo);
+                static_for<0, RPW>([&](auto kc) {
+                    if constexpr ((decltype(kc)::value * NQ) / RPW == ks) copy_row(gcp, cyo, kc);
+                });
+            }
+#pragma unroll
+            for (int ob = 0; ob < 4; ++ob)
+                acc[ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(yv[ks & 1], xr[ob][ks], acc[ob], 0, 0, 0);
+            if constexpr (((L::LPOS >> ks) & 1u) != 0 && ks + 1 < NQ) {
+                // waves with a prefix end at this step store a snapshot (a wave-uniform branch)
+                const int J = w * NQ + ks;
+                if ((L::INT_MASK >> J) & 1u) put(4 + __builtin_popcount(L::INT_MASK & ((1u << J) - 1u)));
+            }
+            if constexpr (WE)  // E_b units: prefixes NUB - 1 .. 0
+                static_for<0, NUB>([&](auto uc) {
+                    constexpr int u = decltype(uc)::value;
+                    constexpr std::integral_constant<int, NUB - 1 - u> pc{};
+                    if constexpr (Sched::chunk_a(2 * u) == ks) uchunk_a(pc, masked, mk, tb[u], spv[u], ev[u]);
+                    if constexpr (Sched::chunk_a(2 * u + 1) == ks) uchunk_b(pc, masked, mk, tb[u], spv[u], ev[u]);
+                    if constexpr (Sched::tab_a(u) == ks) tb[u] = utab(pc, eyo);
+                });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        put(w);
+    };
+
     // phase B: dX[:, quarter] += A_band . Y[:, quarter] for the tile in ring slot ubuf | E_a of
     // block nb1 (tables in ebuf1).  The band operand is read only at the
     // steps where some wave's band changes (the same code for every wave, no branches).
     // (No branches in here: the gradient accumulators must not meet at a join.  E_a always
     // runs with masks; a block past the end has every cell masked.)
-    auto phase_b = [&](auto with_u, int uyo, const uint64_t(&mk1)[4], int eto1) {
+    auto phase_b = [&](auto with_u, int uyo, const uint64_t(&mk1)[4], int eyo1) {
         constexpr bool WE = NA > 0;
         constexpr bool WU = decltype(with_u)::value && UPD;
         constexpr std::true_type masked{};
         f16x8 af[2];
+        UTab tb[NA > 0 ? NA : 1];
+        f32x4 spv[NA > 0 ? NA : 1], ev[NA > 0 ? NA : 1];
+        if constexpr (WE)
+            static_for<0, NA>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
+                if constexpr (Sched::tab_b(u) < 0) tb[u] = utab(std::integral_constant<int, NP - 1 - u>{}, eyo1);
+            });
         static_for<0, NQ>([&](auto jc) {
             constexpr int jb = decltype(jc)::value;
             if constexpr (WU) {
@@ -924,26 +965,29 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             }
             if constexpr (WE)  // E_a units: prefixes NP - 1 .. NP - NA
                 static_for<0, NA>([&](auto uc) {
-                    if constexpr ((decltype(uc)::value * NQ) / NA == jb)
-                        unit(std::integral_constant<int, NP - 1 - decltype(uc)::value>{}, masked, mk1, eto1);
+                    constexpr int u = decltype(uc)::value;
+                    constexpr std::integral_constant<int, NP - 1 - u> pc{};
+                    if constexpr (Sched::chunk_b(2 * u) == jb) uchunk_a(pc, masked, mk1, tb[u], spv[u], ev[u]);
+                    if constexpr (Sched::chunk_b(2 * u + 1) == jb) uchunk_b(pc, masked, mk1, tb[u], spv[u], ev[u]);
+                    if constexpr (Sched::tab_b(u) == jb) tb[u] = utab(pc, eyo1);
                 });
             __builtin_amdgcn_sched_barrier(0);
         });
     };
-    // ring slots (FP16 elements) and table slots (floats) of blocks nb, nb + 1, nb + 2
-    int yo0 = 0, yo1 = BI * YP, yo2 = 2 * BI * YP;
-    int to0 = 0, to1 = 256, to2 = 512;
-    uint64_t mk_cur[4], mk_nxt[4];  // lane masks of blocks nb and nb + 1
-    block_masks(nb_begin, mk_cur);
+
+    // ring slots (FP16 elements) of blocks nb, nb + 1, nb + 2
+    int yo0 = 0, yo1 = RSL, yo2 = 2 * RSL;
+    uint64_t mk1[4];  // lane masks of block nb + 1
     if (nb_begin < nb_end) {
-        issue_block(nb_begin, yo0, to0);
-        issue_block(nb_begin + 1, yo1, to1);  // past the split's end: rows of the next split or the zero blocks
+        issue_block(nb_begin, yo0);
+        issue_block(nb_begin + 1, yo1);  // past the split's end: rows of the next split or the zero blocks
         wait_vm_n<NCW + 1>();
         lds_barrier();  // block 0 visible
-        phase_a(std::false_type{}, std::false_type{}, yo0, mk_cur, 0, 0, 0, 0);  // recompute of block 0 alone
+        phase_a(std::false_type{}, std::false_type{}, yo0, 0, 0, 0, 0);  // recompute of block 0 alone
         lds_barrier();  // slots of block 0 visible
         read_slots();
-        phase_b(std::false_type{}, 0, mk_cur, to0);  // E_a of block 0 alone
+        block_masks(nb_begin, mk1);
+        phase_b(std::false_type{}, 0, mk1, yo0);  // E_a of block 0 alone
     }
 
     for (int nb = nb_begin; nb < nb_end; ++nb) {
@@ -952,20 +996,17 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         // phase A: recompute of nb + 1 (past the end: a block of zeros or of the next split) | E_b(nb) |
         // copies of nb + 2
         if (needmask(nb))
-            phase_a(std::true_type{}, std::true_type{}, yo1, mk_cur, to0, nb + 2, yo2, to2);
+            phase_a(std::true_type{}, std::true_type{}, yo1, nb, yo0, nb + 2, yo2);
         else
-            phase_a(std::false_type{}, std::true_type{}, yo1, mk_cur, to0, nb + 2, yo2, to2);
+            phase_a(std::false_type{}, std::true_type{}, yo1, nb, yo0, nb + 2, yo2);
         gcp += (int64_t)BI * D;
-        block_masks(nb + 1, mk_nxt);
+        block_masks(nb + 1, mk1);
         if constexpr (UPD) u_pre(yo0);
         lds_barrier();  // band operands of nb and slots of nb + 1 visible
         read_slots();
-        phase_b(std::true_type{}, yo0, mk_nxt, to1);  // update of nb | E_a(nb + 1)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) mk_cur[t] = mk_nxt[t];
-        const int y = yo0, tt = to0;
+        phase_b(std::true_type{}, yo0, mk1, yo1);  // update of nb | E_a(nb + 1)
+        const int y = yo0;
         yo0 = yo1, yo1 = yo2, yo2 = y;
-        to0 = to1, to1 = to2, to2 = tt;
     }
 
     // ---------------- write the raw gradient block (scale divided out) and the radial sums
