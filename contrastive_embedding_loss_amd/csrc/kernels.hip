@@ -84,6 +84,8 @@ __device__ __forceinline__ float reduce_scatter32(float (&v)[32], int lane) {
 }
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// barrier that waits for this wave's LDS accesses only (not for its outstanding global loads)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Direct global -> LDS copies issued from inline assembly: the compiler does not
 // see them, so it adds no waits of its own before LDS accesses; the caller waits
@@ -182,7 +184,8 @@ __global__ __launch_bounds__(256) void k_half_copy(const u16 *__restrict__ x, co
 // ----------------------------------------------------------------------------
 // k_fwd: softmax forward.  One 128 x 128 tile of (query i, key j) per
 // workgroup, 4 waves of 64 x 64 (2 x 2 MFMA 32x32x16 blocks each), operands
-// staged through LDS in 64-wide slices of d.  At every prefix boundary the
+// copied global -> LDS directly in 64-wide slices of d, one slice ahead (two
+// workgroups per CU; one barrier per slice).  At every prefix boundary the
 // FP32 accumulators are read in place ("snapshotted") and each cell's
 // e = 2^(S a_i ik_j + c) is added to a row partial and a column partial; the
 // positive cell is left out of both (the statistics kernel adds it back from
@@ -190,7 +193,6 @@ __global__ __launch_bounds__(256) void k_half_copy(const u16 *__restrict__ x, co
 // ----------------------------------------------------------------------------
 constexpr int FB = 128;
 constexpr int FK = 64;
-constexpr int FPITCH = FK + 8;  // bf16 per LDS row (144 bytes): conflict-free 16-byte reads
 
 template <bool MASKED>
 __device__ __forceinline__ void fwd_snapshot(const f32x16 (&acc)[2][2], int p, int wi, int wj, int lane, int tid,
@@ -252,12 +254,17 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
                                                 const float *__restrict__ rowA, const float *__restrict__ colI,
                                                 float cshift, float *__restrict__ rowpart,
                                                 float *__restrict__ colpart) {
-    __shared__ __attribute__((aligned(16))) u16 Xs[FB * FPITCH];
-    __shared__ __attribute__((aligned(16))) u16 Ys[FB * FPITCH];
+    // Operand slices (128 rows x 64 bf16, 128 bytes per row) in a ring of two, copied
+    // global -> LDS directly one slice ahead.  Rows are unpadded; the 16-byte chunk c of
+    // row r sits at position c ^ ((r >> 1) & 7), so the MFMA operand reads (16 rows,
+    // one chunk each per 16 lanes) meet 64 different banks.
+    constexpr int SLB = FB * FK * 2;  // bytes per operand slice
+    __shared__ __attribute__((aligned(16))) u16 Ring[2][2][FB * FK];  // [slot][q | k]
     __shared__ float fA[kMaxP][FB];
     __shared__ float fI[kMaxP][FB];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wi = wave >> 1, wj = wave & 1;
     int64_t it, jt;
     {
@@ -285,25 +292,35 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
     }
     const bool masked = (i0 + FB > R) || (j0 + FB > N) || ((j0 < i0 + off + FB) && (i0 + off < j0 + FB));
 
-    uint4 xr[4], yr[4];
-    auto gload = [&](int d0) {
+    // copies: this wave moves pieces 4 wave .. 4 wave + 3 (8 rows x 128 bytes each) of both
+    // operands; lane l of piece pc fills row 8 pc + (l >> 3), position l & 7 (rows past the
+    // end repeat the last row: finite values in cells that are masked)
+    uint32_t vq[4], vk[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int row = 8 * (4 * wave + c) + (lane >> 3);
+        const uint32_t ch = (uint32_t)((lane & 7) ^ ((row >> 1) & 7));
+        const int64_t rq = i0 + row < R ? row : R - 1 - i0, rk = j0 + row < N ? row : N - 1 - j0;
+        vq[c] = (uint32_t)rq * (uint32_t)D * 2u + 16u * ch;
+        vk[c] = (uint32_t)rk * (uint32_t)D * 2u + 16u * ch;
+    }
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)&Ring[0][0][0];
+    const u16 *qt = q + i0 * D, *kt = k + j0 * D;  // tile row bases (wave-uniform)
+    auto issue = [&](int st) {
+        const int slot = st & 1;
+        const u16 *qs = qt + st * FK, *ks_ = kt + st * FK;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const int e = tid + 256 * c, row = e >> 3, ch = e & 7;
-            const int d = d0 + ch * 8;
-            const int64_t gi = i0 + row, gj = j0 + row;
-            xr[c] = (gi < R && d < Dsw) ? *(const uint4 *)(q + gi * D + d) : make_uint4(0, 0, 0, 0);
-            yr[c] = (gj < N && d < Dsw) ? *(const uint4 *)(k + gj * D + d) : make_uint4(0, 0, 0, 0);
+            const uint32_t m = ring_lds + (uint32_t)(slot * 2 * SLB + 1024 * (4 * wave + c));
+            dma_row1(qs, vq[c], m);
+            dma_row1(ks_, vk[c], m + SLB);
         }
     };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int e = tid + 256 * c, row = e >> 3, ch = e & 7;
-            *(uint4 *)&Xs[row * FPITCH + ch * 8] = xr[c];
-            *(uint4 *)&Ys[row * FPITCH + ch * 8] = yr[c];
-        }
-    };
+
+    // operand reads: rows wi 64 + b 32 + (lane & 31) (and wj for k); chunk 2 ks + (lane >> 5)
+    const int rl = lane & 31, sw = (rl >> 1) & 7;
+    const uint32_t rdq = (uint32_t)((wi * 64 + rl) * 128 + 16 * ((lane >> 5) ^ (sw & 1)));
+    const uint32_t rdk = (uint32_t)((wj * 64 + rl) * 128 + 16 * ((lane >> 5) ^ (sw & 1))) + SLB;
 
     f32x16 acc[2][2];
 #pragma unroll
@@ -315,21 +332,29 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
 
     const int nst = (Dsw + FK - 1) / FK;
     int pnext = 0;
-    gload(0);
-    lstore();
-    __syncthreads();
+    issue(0);
     for (int st = 0; st < nst; ++st) {
-        if (st + 1 < nst) gload((st + 1) * FK);
+        wait_vm();      // this wave's copies of slice st landed
+        lds_barrier();  // every wave's copies visible; every wave done with slice st - 1's slot
+        if (st + 1 < nst) issue(st + 1);
+        const char *sb = (const char *)&Ring[st & 1][0][0];
+        bf16x8 avn[2], bvn[2];
+        auto lread = [&](int ks, bf16x8(&av)[2], bf16x8(&bv)[2]) {
+            const uint32_t o = 16u * (uint32_t)((2 * ks) ^ (sw & 6));
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                av[b] = *(const bf16x8 *)(sb + rdq + o + b * 32 * 128);
+                bv[b] = *(const bf16x8 *)(sb + rdk + o + b * 32 * 128);
+            }
+        };
+        // operands of the next 16-wide step are read before the MFMAs of this one
+        lread(0, avn, bvn);
 #pragma unroll
         for (int ks = 0; ks < FK / 16; ++ks) {
             const int dk = st * FK + ks * 16;
+            bf16x8 av[2] = {avn[0], avn[1]}, bv[2] = {bvn[0], bvn[1]};
+            if (ks + 1 < FK / 16) lread(ks + 1, avn, bvn);
             if (dk < Dsw) {
-                bf16x8 av[2], bv[2];
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    av[b] = *(const bf16x8 *)&Xs[(wi * 64 + b * 32 + (lane & 31)) * FPITCH + ks * 16 + 8 * (lane >> 5)];
-                    bv[b] = *(const bf16x8 *)&Ys[(wj * 64 + b * 32 + (lane & 31)) * FPITCH + ks * 16 + 8 * (lane >> 5)];
-                }
 #pragma unroll
                 for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -345,11 +370,6 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
                     ++pnext;
                 }
             }
-        }
-        __syncthreads();
-        if (st + 1 < nst) {
-            lstore();
-            __syncthreads();
         }
     }
 }
@@ -588,7 +608,6 @@ struct Ladder {
     }
 };
 
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int N>
 __device__ __forceinline__ void wait_vm_n() {
