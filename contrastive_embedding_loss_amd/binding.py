@@ -18,6 +18,7 @@ SIGLIP = 1
 INFONCE_ROWS = 2
 ACCUMULATE = 1
 PROFILE = 2
+ONE_SPLIT = 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libuform_contrastive.so")
@@ -126,13 +127,14 @@ def _check(status: int) -> None:
 def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: float, kind: int, weights=None,
             row_offset: int = 0, want_dq: bool = True, want_dk: bool = True, extras: bool = False,
             dq: torch.Tensor | None = None, dk: torch.Tensor | None = None, accumulate: bool = False,
-            workspace: torch.Tensor | None = None, profile: bool = False):
+            workspace: torch.Tensor | None = None, profile: bool = False, one_split: bool = False):
     """Loss and gradients of the Matryoshka contrastive loss on q's device.
 
     q [R, D] and k [N, D] are contiguous bfloat16 device tensors.  Returns
     ``(loss, dq, dk)`` (float32 tensors; dq/dk None when not wanted), plus a
     dict of ``prefix_losses``, ``row_lse``, ``col_lse`` and ``pos_logit`` when
-    ``extras``.  Everything is enqueued on torch's current stream.
+    ``extras``.  Everything is enqueued on torch's current stream.  ``one_split`` runs each backward pass as
+    one inner split (a diagnostic: the in-place finish that large problems take).
     """
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
         raise TypeError("q and k must be bfloat16")
@@ -176,7 +178,7 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
     if workspace is not None:
         opt.workspace = workspace.data_ptr()
         opt.workspace_bytes = workspace.numel() * workspace.element_size()
-    opt.flags = (ACCUMULATE if accumulate else 0) | (PROFILE if profile else 0)
+    opt.flags = (ACCUMULATE if accumulate else 0) | (PROFILE if profile else 0) | (ONE_SPLIT if one_split else 0)
     stream = torch.cuda.current_stream(dev).cuda_stream
     status = library().uform_contrastive_fwd_bwd_ex(
         _ptr(q), _ptr(k), R, N, D, pw, P, float(scale), float(bias), int(kind), _ptr(loss), _ptr(dq), _ptr(dk),

@@ -83,6 +83,13 @@ struct BwdArgs {
     float *Cpart;  // [nsplit][P][NO]
     float *lossparts;
     int64_t loss_slot0;
+    // one inner split only: the gradient rows are finished in place (the finalize terms
+    // below) and written to fin_out instead of part / Cpart
+    float *fin_out;
+    const u16 *finX, *finY;                         // BF16 outer / inner rows
+    const float *diagA, *posdot, *invx, *gam;        // as in FinArgs
+    int64_t R, pos_shift;
+    int accumulate;
 };
 
 struct FinArgs {

@@ -70,7 +70,7 @@ uint32_t ladder_mask(const int32_t *pw, int32_t n) {
 }
 
 Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, int kind, int64_t off, bool want_dq,
-               bool want_dk) {
+               bool want_dk, bool one_split = false) {
     Plan p{};
     p.R = R;
     p.N = N;
@@ -86,6 +86,11 @@ Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, in
     p.nJt = cdiv(N, kFwdTile);
     choose_split(R, N, p.nsplit_row, p.bps_row);
     choose_split(N, R, p.nsplit_col, p.bps_col);
+    if (one_split) {
+        p.nsplit_row = p.nsplit_col = 1;
+        p.bps_row = cdiv(N, kBwdInner);
+        p.bps_col = cdiv(R, kBwdInner);
+    }
     // loss slots: softmax = row stats blocks + column stats blocks;
     // sigmoid = positive-cell blocks + row-pass workgroups
     if (softmax) {
@@ -131,8 +136,9 @@ Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, in
     // forward partials: one per wave column (row partials) / wave row (column partials) of a tile
     p.o_rowpart = take(softmax ? sizeof(float) * 2 * p.nJt * P * R : 0);
     p.o_colpart = take(softmax ? sizeof(float) * 2 * p.nIt * P * N : 0);
-    const size_t part_row = (want_dq || !softmax) ? sizeof(float) * p.nsplit_row * R * D : 0;
-    const size_t part_col = want_dk ? sizeof(float) * p.nsplit_col * N * D : 0;
+    // gradient partials only with inner splits (one split: the backward finishes the rows in place)
+    const size_t part_row = (want_dq && p.nsplit_row > 1) ? sizeof(float) * p.nsplit_row * R * D : 0;
+    const size_t part_col = (want_dk && p.nsplit_col > 1) ? sizeof(float) * p.nsplit_col * N * D : 0;
     p.o_part = take(part_row > part_col ? part_row : part_col);
     const size_t c_row = sizeof(float) * p.nsplit_row * P * R, c_col = sizeof(float) * p.nsplit_col * P * N;
     p.o_Cpart = take(c_row > c_col ? c_row : c_col);
@@ -277,7 +283,8 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     const u16 *q = (const u16 *)q_, *k = (const u16 *)k_;
     const int64_t off = opt ? opt->row_offset : 0;
     const bool softmax = kind != kSiglip;
-    Plan pl = make_plan(R, N, D, prefixes, P, kind, off, dq != nullptr, dk != nullptr);
+    Plan pl = make_plan(R, N, D, prefixes, P, kind, off, dq != nullptr, dk != nullptr,
+                        opt && (opt->flags & UFORM_CONTRASTIVE_ONE_SPLIT));
 
     void *ws = nullptr;
     if (opt && opt->workspace) {
@@ -430,8 +437,21 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
         ba.lossparts = lossparts;
         ba.loss_slot0 = pl.slots_a;
         const int64_t nsplit = rowpass ? pl.nsplit_row : pl.nsplit_col;
+        const bool fuse = out && nsplit == 1;  // one split: the backward finishes the rows itself
+        if (fuse) {
+            ba.fin_out = out;
+            ba.finX = rowpass ? q : k;
+            ba.finY = rowpass ? k : q;
+            ba.diagA = sa.diagA;
+            ba.posdot = posdot;
+            ba.invx = rowpass ? invq : invk;
+            ba.gam = rowpass ? gamq : gamk;
+            ba.R = R;
+            ba.pos_shift = rowpass ? 0 : -off;
+            ba.accumulate = (opt && (opt->flags & UFORM_CONTRASTIVE_ACCUMULATE)) ? 1 : 0;
+        }
         LAUNCH_NAMED("k_bwd", launch_bwd(ba, pl.mask, !softmax, nsplit, s));
-        if (out) {
+        if (out && !fuse) {
             FinArgs fa{};
             fa.X = rowpass ? q : k;
             fa.Y = rowpass ? k : q;

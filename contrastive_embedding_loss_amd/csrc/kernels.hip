@@ -621,6 +621,95 @@ __device__ __forceinline__ f16x4 ds_read_tr(const _Float16 *p) {
     return __builtin_bit_cast(f16x4, v);
 }
 
+// The finalize terms applied in place when a pass has one inner split: the radial sums C^p
+// of the 64 rows (four waves' parts, fixed order), the positive cell's exact FP32 term and
+// the normalisation Jacobian's radial part, then the finished gradient rows (zeros beyond
+// the widest prefix).  The same arithmetic as k_finalize with nsplit = 1.
+template <int NP, int NQ, uint32_t MASK>
+__device__ __forceinline__ void bwd_finish(const BwdArgs &a, const f32x16 (&dacc)[2][NQ], const float (&Cacc)[NP],
+                                        float csc, float *red, const float *inv_sc, int o0, int w, int lane,
+                                        int tid) {
+    constexpr int DW = 32 * (32 - __builtin_clz(MASK));
+    const int NO = (int)a.NO, D = a.D;
+    const int l32 = lane & 31, h32 = lane >> 5;
+    lds_barrier();
+    float *fin = red + 4 * NP * BO;  // [2][NP][BO]: running DG and RD per band
+#pragma unroll
+    for (int p = 0; p < NP; ++p) red[(w * NP + p) * BO + lane] = Cacc[p];
+    lds_barrier();
+    if (w == 0) {
+        const int o = o0 + lane;
+        float dg = 0.f, rd = 0.f;
+        if (o < NO) {
+            const int64_t ipos = o + a.pos_shift;
+            const bool has_pos = ipos >= 0 && ipos < a.R;
+            const float g = a.gam[o];
+#pragma unroll
+            for (int p = NP - 1; p >= 0; --p) {
+                const float c = (((red[(0 * NP + p) * BO + lane] + red[(1 * NP + p) * BO + lane]) +
+                                  red[(2 * NP + p) * BO + lane]) + red[(3 * NP + p) * BO + lane]) * csc;
+                const float dA = has_pos ? a.diagA[p * a.R + ipos] : 0.f;
+                const float dS = has_pos ? a.posdot[p * a.R + ipos] : 0.f;
+                const float ix = a.invx[p * a.NO + o];
+                dg += dA;
+                rd += ix * ix * fmaf(dA, dS, c * g);
+                fin[p * BO + lane] = dg;
+                fin[(NP + p) * BO + lane] = rd;
+            }
+        }
+    }
+    lds_barrier();
+    // per (block of 32 columns, 32 rows): the 16 rows' x and positive-row y first, then the rows
+    const u16 *__restrict__ fx = a.finX;
+    const u16 *__restrict__ fy = a.finY;
+    float *__restrict__ out = a.fin_out;
+    const bool accumulate = a.accumulate != 0;
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob) {
+        float sc[16];
+        int64_t xoff[16], yoff[16];
+        bool ok[16], pos[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int orow = ob * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+            const int o = o0 + orow;
+            ok[r] = o < NO;
+            const int64_t ipos = o + a.pos_shift;
+            pos[r] = ok[r] && ipos >= 0 && ipos < a.R;
+            sc[r] = ok[r] ? inv_sc[orow] * a.gam[o] : 0.f;
+            xoff[r] = (int64_t)(ok[r] ? o : 0) * D;
+            yoff[r] = pos[r] ? (int64_t)(o + a.diag_shift) * D : 0;
+        }
+#pragma unroll
+        for (int jb = 0; jb < NQ; ++jb) {
+            const int d = w * (DW / 4) + 32 * jb + l32;
+            const int band = __builtin_popcount(MASK & ((1u << (w * NQ + jb)) - 1u));
+            float xv[16], yv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                xv[r] = __uint_as_float((unsigned int)fx[xoff[r] + d] << 16);
+                yv[r] = pos[r] ? __uint_as_float((unsigned int)fy[yoff[r] + d] << 16) : 0.f;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int orow = ob * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+                const float v = fmaf(fin[band * BO + orow], yv[r],
+                                     fmaf(-fin[(NP + band) * BO + orow], xv[r], dacc[ob][jb][r] * sc[r]));
+                if (ok[r]) {
+                    float *p = out + xoff[r] + d;
+                    *p = accumulate ? *p + v : v;
+                }
+            }
+        }
+    }
+    if (DW < D && !a.accumulate) {
+        for (int e = tid; e < BO * (D - DW); e += 256) {
+            const int orow = e / (D - DW), d = DW + e % (D - DW);
+            if (o0 + orow < NO) a.fin_out[(int64_t)(o0 + orow) * D + d] = 0.f;
+        }
+    }
+}
+
 template <uint32_t MASK, bool SIG, bool UPD>
 __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     using L = Ladder<MASK>;
@@ -1031,19 +1120,23 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     // ---------------- write the raw gradient block (scale divided out) and the radial sums
     const int64_t split = blockIdx.y;
     if constexpr (UPD) {
-        float *dst = a.part + split * a.NO * D;
+        if (a.fin_out) {
+            bwd_finish<NP, NQ, MASK>(a, dacc, Cacc, csc, &Sl[0][0], inv_sc, o0, w, lane, tid);
+        } else {
+            float *dst = a.part + split * a.NO * D;
 #pragma unroll
-        for (int ob = 0; ob < 2; ++ob)
+            for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int orow = ob * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-                const float s = inv_sc[orow];
-                if (o0 + orow < NO) {
-                    float *rowp = dst + (int64_t)(o0 + orow) * D + dq0 + l32;
+                for (int r = 0; r < 16; ++r) {
+                    const int orow = ob * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+                    const float s = inv_sc[orow];
+                    if (o0 + orow < NO) {
+                        float *rowp = dst + (int64_t)(o0 + orow) * D + dq0 + l32;
 #pragma unroll
-                    for (int jb = 0; jb < NQ; ++jb) rowp[32 * jb] = dacc[ob][jb][r] * s;
+                        for (int jb = 0; jb < NQ; ++jb) rowp[32 * jb] = dacc[ob][jb][r] * s;
+                    }
                 }
-            }
+        }
     }
     // radial sums and sigmoid loss: add the four waves' inner rows (slots are free now)
     lds_barrier();
@@ -1058,7 +1151,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         }
     }
     lds_barrier();
-    if (w == 0 && ovalid) {
+    if (w == 0 && ovalid && !(UPD && a.fin_out)) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const float c = ((red[(0 * NP + p) * BO + lane] + red[(1 * NP + p) * BO + lane]) +

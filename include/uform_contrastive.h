@@ -112,13 +112,17 @@ typedef struct {
     float *pos_logit_out;        /* device [n_prefixes][R]: l^p_{i, off+i}; nullable            */
     void *workspace;             /* device, 256-byte aligned; NULL = library workspace          */
     size_t workspace_bytes;      /* >= uform_contrastive_workspace_bytes(...) when given        */
-    uint32_t flags;              /* bit 0: add into dq/dk instead of overwriting them           */
+    uint32_t flags;              /* UFORM_CONTRASTIVE_* bits below (accumulate, diagnostics)    */
 } uform_contrastive_options_t;
 
 #define UFORM_CONTRASTIVE_ACCUMULATE 1u
 /* Diagnostics: bracket each kernel launch of the call with a pair of events
  * on the stream (read them with uform_contrastive_profile). */
 #define UFORM_CONTRASTIVE_PROFILE 2u
+/* Diagnostics: run each backward pass as one inner split (no split partials; the
+ * backward kernel applies the finalize terms itself, as it does whenever the
+ * problem is large enough for one split to fill the GPU). */
+#define UFORM_CONTRASTIVE_ONE_SPLIT 4u
 
 /* As uform_contrastive_fwd_bwd, with the options above (options may be NULL). */
 uform_status_t uform_contrastive_fwd_bwd_ex(const void *q, const void *k, int64_t R, int64_t N, int64_t D,

@@ -26,12 +26,12 @@ def to_dev(bits):
     return torch.from_numpy(bf16_bits_to_f32(bits)).to("cuda").to(torch.bfloat16)
 
 
-def run_both(qb, kb, prefixes, scale, bias, kind, weights=None, off=0, label=""):
-    print(f"[case] {label} R={qb.shape[0]} N={kb.shape[0]} D={qb.shape[1]} kind={kind} prefixes={prefixes}",
-          flush=True)
+def run_both(qb, kb, prefixes, scale, bias, kind, weights=None, off=0, label="", one_split=False):
+    print(f"[case] {label} R={qb.shape[0]} N={kb.shape[0]} D={qb.shape[1]} kind={kind} prefixes={prefixes} "
+          f"one_split={one_split}", flush=True)
     q, k = to_dev(qb), to_dev(kb)
     loss, dq, dk, ex = binding.fwd_bwd(q, k, prefixes, scale, bias, kind, weights=weights, row_offset=off,
-                                       extras=True)
+                                       extras=True, one_split=one_split)
     torch.cuda.synchronize()
     ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), prefixes, scale, bias, kind,
                               weights=weights, row_offset=off)
@@ -95,6 +95,45 @@ def test_other_ladders(D, prefixes, kind):
     qb, kb = make_inputs(R, N, D, noise=0.4, seed=31 + D)
     got, ref = run_both(qb, kb, prefixes, 12.0, -2.0 if kind == SIGLIP else 0.0, kind, label="ladder")
     check(got, ref, kind)
+
+
+# One inner split per backward pass: the backward kernel applies the finalize terms in place
+# (the path every pass takes once the outer rows alone fill the GPU, e.g. 32768 x 32768).
+@pytest.mark.parametrize("case", ["infonce", "siglip", "rows", "siglip-tail", "infonce-tail"])
+def test_one_split_finish(case):
+    if case == "infonce":
+        qb, kb = make_inputs(300, 300, 1024, noise=0.5, seed=71)
+        args = (LADDER, 1 / 0.07, 0.0, INFONCE)
+        kw = dict(weights=(1, 1, 1, 1, 2))
+    elif case == "siglip":
+        qb, kb = make_inputs(200, 200, 1024, noise=0.5, seed=72)
+        args, kw = (LADDER, 10.0, -10.0, SIGLIP), {}
+    elif case == "rows":
+        qb, kb = make_inputs(96, 352, 1024, recipe="clustered", noise=0.2, seed=73, centroids=16, row_offset=128)
+        args, kw = (LADDER, 1 / 0.07, 0.0, INFONCE_ROWS), dict(off=128)
+    elif case == "siglip-tail":
+        qb, kb = make_inputs(160, 160, 192, noise=0.4, seed=74)
+        args, kw = ((64, 128), 12.0, -2.0, SIGLIP), {}
+    else:
+        qb, kb = make_inputs(160, 160, 320, noise=0.4, seed=75)
+        args, kw = ((64, 128, 256), 12.0, 0.0, INFONCE), {}
+    got, ref = run_both(qb, kb, *args, label="one-split-" + case, one_split=True, **kw)
+    check(got, ref, args[3])
+
+
+def test_one_split_accumulate_matches_split_path():
+    qb, kb = make_inputs(192, 192, 320, noise=0.5, seed=76)
+    q, k = to_dev(qb), to_dev(kb)
+    pf = (64, 128, 256)
+    a = binding.fwd_bwd(q, k, pf, 14.0, 0.0, INFONCE)
+    dq0 = torch.full_like(a[1], 0.5)
+    dk0 = torch.full_like(a[2], -0.25)
+    _, dq1, dk1 = binding.fwd_bwd(q, k, pf, 14.0, 0.0, INFONCE, dq=dq0.clone(), dk=dk0.clone(), accumulate=True,
+                                  one_split=True)
+    scale = max(a[1].abs().max().item(), a[2].abs().max().item())
+    assert (dq1 - (a[1] + 0.5)).abs().max().item() <= 1e-4 * scale + 1e-6
+    assert (dk1 - (a[2] - 0.25)).abs().max().item() <= 1e-4 * scale + 1e-6
+    assert (dq1[:, 256:] == 0.5).all() and (dk1[:, 256:] == -0.25).all()
 
 
 def test_single_pair_infonce_is_zero():
