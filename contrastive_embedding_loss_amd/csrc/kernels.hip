@@ -102,6 +102,20 @@ __device__ __forceinline__ void dma_row2(const void *base, uint32_t voff, uint32
                  "s"(base), "s"(m0v)
                  : "memory");
 }
+// the same with M0 = ma + mb (two scalar operands, one scalar add)
+__device__ __forceinline__ void dma_row1_add(const void *base, uint32_t voff, uint32_t ma, uint32_t mb) {
+    asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(ma), "s"(mb)
+                 : "memory");
+}
+__device__ __forceinline__ void dma_row2_add(const void *base, uint32_t voff, uint32_t ma, uint32_t mb) {
+    asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1\n\tglobal_load_lds_dwordx4 %0, %1 offset:1024" ::"v"(
+                     voff),
+                 "s"(base), "s"(ma), "s"(mb)
+                 : "memory");
+}
+__device__ __forceinline__ void dma4_add(const void *g, uint32_t ma, uint32_t mb) {
+    asm volatile("s_add_u32 m0, %1, %2\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(ma), "s"(mb) : "memory");
+}
 __device__ __forceinline__ void dma4_m0(const void *g, uint32_t m0v) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0v) : "memory");
 }
@@ -778,16 +792,21 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     uint32_t cvo[RPW];  // this lane's byte offset in each of its rows, from the block start
 #pragma unroll
     for (int k = 0; k < RPW; ++k) cvo[k] = (uint32_t)(4 * w + k) * (uint32_t)D * 2u + 16u * (uint32_t)lane;
+    // ring slots are addressed by byte offsets from the first slot; LDS addresses of this
+    // wave's rows and table entries within a slot (wave-uniform)
     const uint32_t ys_lds = (uint32_t)(uintptr_t)&Ys[0][0];
-    auto copy_row = [&](const _Float16 *gblk, int ybo, auto kc) {  // row 4 w + k of the block at gblk into slot ybo
+    uint32_t rowb[RPW];
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) rowb[k] = __builtin_amdgcn_readfirstlane(ys_lds + 2u * (uint32_t)((4 * w + k) * YP));
+    const uint32_t tabb = __builtin_amdgcn_readfirstlane(ys_lds + 2u * (uint32_t)(BI * YP) + 4u * (uint32_t)(64 * w));
+    auto copy_row = [&](const _Float16 *gblk, uint32_t ybb, auto kc) {  // row 4 w + k of the block at gblk into slot ybb
         constexpr int k = decltype(kc)::value;
-        const uint32_t m0v = ys_lds + 2u * (uint32_t)(ybo + (4 * w + k) * YP);
         if constexpr (IPR == 2)
-            dma_row2(gblk, cvo[k], m0v);
+            dma_row2_add(gblk, cvo[k], ybb, rowb[k]);
         else if constexpr (FULLP)
-            dma_row1(gblk, cvo[k], m0v);
+            dma_row1_add(gblk, cvo[k], ybb, rowb[k]);
         else if (lane < DW / 8)
-            dma_row1(gblk, cvo[k], m0v);
+            dma_row1_add(gblk, cvo[k], ybb, rowb[k]);
     };
     // table entry [which][p][r] of this lane (lanes past the end copy a harmless float)
     const int te = 64 * w + lane;
@@ -795,13 +814,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     const int tr = te % BI;
     const float *tbase = tact ? ((te / (NP * BI)) == 0 ? a.iI : a.iKap) + (int64_t)((te / BI) % NP) * NI + tr : a.iI;
     const int tlim = tact ? NI - 1 - tr : 0;  // rows past the end read the last row
-    auto copy_tables = [&](int nb, int ybo) {
-        dma4_m0(tbase + min(nb * BI, tlim), ys_lds + 2u * (uint32_t)(ybo + BI * YP) + 4u * (uint32_t)(64 * w));
-    };
+    auto copy_tables = [&](int nb, uint32_t ybb) { dma4_add(tbase + min(nb * BI, tlim), ybb, tabb); };
     const _Float16 *gcp = a.Y16 + (int64_t)nb_begin * BI * D;  // the next block to copy
-    auto issue_block = [&](int nb, int ybo) {
-        static_for<0, RPW>([&](auto kc) { copy_row(gcp, ybo, kc); });
-        copy_tables(nb, ybo);
+    auto issue_block = [&](int nb, uint32_t ybb) {
+        static_for<0, RPW>([&](auto kc) { copy_row(gcp, ybb, kc); });
+        copy_tables(nb, ybb);
         gcp += (int64_t)BI * D;
     };
 
@@ -854,8 +871,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     // blocks whose cells need masks: from nb_sp on (ragged or past the split's end; every
     // block if the outer rows are ragged), and those holding positives of these outer rows
     const int nb_sp = o0 + BO > NO ? 0 : min(NI / BI, nb_end);
-    const int c_hi = o0 + dsh + BO, c_lo = o0 + dsh - BI;
-    auto needmask = [&](int nb) { return nb >= nb_sp || (nb * BI < c_hi && nb * BI > c_lo); };
+    const int c_lo = o0 + dsh - BI;  // blocks with c_lo < n0 < c_lo + BO + BI hold positives
+    auto needmask = [&](int nb) { return nb >= nb_sp || (uint32_t)(nb * BI - c_lo - 1) < (uint32_t)(BO + BI - 1); };
     // lane masks of block nb's cells for inner rows 4 w + t (wave-uniform 64-bit masks)
     const uint64_t ovm = __builtin_amdgcn_ballot_w64(ovalid);
     auto block_masks = [&](int nb, uint64_t(&mk)[4]) {
@@ -872,16 +889,15 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     // Epilogue unit of prefix p for the block in ring slot eyo (its tables follow the tile), in
     // three parts that the phases spread over their MFMA steps: the table reads (utab), the
     // logits and exponentials (uchunk_a), the coefficients, radial sums and band operands (uchunk_b).
-    const float *tabs0 = (const float *)&Ys[0][BI * YP];
+    const char *tabs0 = (const char *)&Ys[0][BI * YP] + 16 * w;  // this wave's four inner rows
     struct UTab {
         f32x4 iy, kp;
     };
-    auto utab = [&](auto pc, int eyo) {
+    auto utab = [&](auto pc, uint32_t eyb) {
         constexpr int p = decltype(pc)::value;
-        const int eto = eyo / 2;  // the slot's tables, in floats from the first slot's
         UTab tb;
-        tb.iy = *(const f32x4 *)&tabs0[eto + p * BI + 4 * w];
-        if constexpr (!SIG) tb.kp = *(const f32x4 *)&tabs0[eto + (NP + p) * BI + 4 * w];
+        tb.iy = *(const f32x4 *)(tabs0 + eyb + 4 * p * BI);
+        if constexpr (!SIG) tb.kp = *(const f32x4 *)(tabs0 + eyb + 4 * (NP + p) * BI);
         return tb;
     };
     // S^p (quarters below wave_of(p), lowest first, shared by the prefixes, plus the snapshot) and
@@ -940,9 +956,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         }
         Cacc[p] = fmaf(av[0], Sp[0], fmaf(av[1], Sp[1], fmaf(av[2], Sp[2], fmaf(av[3], Sp[3], Cacc[p]))));
         if constexpr (UPD) {
-            f16x4 v;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = (_Float16)run[t];
+            // two values per conversion (round to nearest even), instead of a fused multiply-add per value
+            uint32_t h01, h23;
+            asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(h01) : "v"(run[0]), "v"(run[1]));
+            asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(h23) : "v"(run[2]), "v"(run[3]));
+            const f16x4 v = __builtin_bit_cast(f16x4, (uint64_t)h01 | ((uint64_t)h23 << 32));
             if constexpr (p >= NP - NA)
                 hv[NP - 1 - p] = v;  // E_a: held until phase A
             else
@@ -968,28 +986,28 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     // per-lane part of the transposed reads (loop invariant); ring slot and step are immediates
     const _Float16 *ytr = &Ys[0][0] + (8 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * YP + 16 * ((lane >> 4) & 1) +
                           4 * (lane & 3) + 32 * w * NQ;
-    auto load_b = [&](int uyo, auto jc) {
+    auto load_b = [&](uint32_t uyb, auto jc) {
         constexpr int jb = decltype(jc)::value;
-        const _Float16 *ysrc = ytr + uyo + 32 * jb;
+        const _Float16 *ysrc = (const _Float16 *)((const char *)ytr + uyb) + 32 * jb;
         const f16x4 lo = ds_read_tr(ysrc);
         const f16x4 hi = ds_read_tr(ysrc + 4 * YP);
         bf[jb % 3] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    auto u_pre = [&](int uyo) {
-        load_b(uyo, std::integral_constant<int, 0>{});
-        if constexpr (NQ > 1) load_b(uyo, std::integral_constant<int, 1>{});
+    auto u_pre = [&](uint32_t uyb) {
+        load_b(uyb, std::integral_constant<int, 0>{});
+        if constexpr (NQ > 1) load_b(uyb, std::integral_constant<int, 1>{});
     };
     // phase A: recompute of the tile in ring slot rbuf (partial S^T over this wave's quarter,
     // 16 inner x 64 outer, into the S slots) | E_b of block nb (tables in ebuf) | copies of
     // block cnb into cbuf, each spread over the recompute steps
-    auto phase_a = [&](auto masked, auto with_e, int ryo, int nb, int eyo, int cnb, int cyo) {
+    auto phase_a = [&](auto masked, auto with_e, uint32_t ryo, int nb, uint32_t eyo, int cnb, uint32_t cyo) {
         constexpr bool WE = decltype(with_e)::value;
         uint64_t mk[4];
         if constexpr (decltype(masked)::value) block_masks(nb, mk);
         f32x4 acc[4];
 #pragma unroll
         for (int ob = 0; ob < 4; ++ob) acc[ob] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const _Float16 *yrow = &Ys[0][0] + ryo + l16 * YP + dq0 + 8 * g4;
+        const _Float16 *yrow = (const _Float16 *)((const char *)&Ys[0][0] + ryo) + l16 * YP + dq0 + 8 * g4;
         auto put = [&](int slot) {
 #pragma unroll
             for (int ob = 0; ob < 4; ++ob) *(f32x4 *)&Sl[slot][(16 * ob + l16) * SLOTP + 4 * g4] = acc[ob];
@@ -1045,7 +1063,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     // steps where some wave's band changes (the same code for every wave, no branches).
     // (No branches in here: the gradient accumulators must not meet at a join.  E_a always
     // runs with masks; a block past the end has every cell masked.)
-    auto phase_b = [&](auto with_u, int uyo, const uint64_t(&mk1)[4], int eyo1) {
+    auto phase_b = [&](auto with_u, uint32_t uyo, const uint64_t(&mk1)[4], uint32_t eyo1) {
         constexpr bool WE = NA > 0;
         constexpr bool WU = decltype(with_u)::value && UPD;
         constexpr std::true_type masked{};
@@ -1083,8 +1101,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         });
     };
 
-    // ring slots (FP16 elements) of blocks nb, nb + 1, nb + 2
-    int yo0 = 0, yo1 = RSL, yo2 = 2 * RSL;
+    // ring slots (byte offsets) of blocks nb, nb + 1, nb + 2
+    uint32_t yo0 = 0, yo1 = 2 * RSL, yo2 = 4 * RSL;  // bytes
     uint64_t mk1[4];  // lane masks of block nb + 1
     if (nb_begin < nb_end) {
         issue_block(nb_begin, yo0);
@@ -1113,7 +1131,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         lds_barrier();  // band operands of nb and slots of nb + 1 visible
         read_slots();
         phase_b(std::true_type{}, yo0, mk1, yo1);  // update of nb | E_a(nb + 1)
-        const int y = yo0;
+        const uint32_t y = yo0;
         yo0 = yo1, yo1 = yo2, yo2 = y;
     }
 
