@@ -886,9 +886,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             for (int t = 0; t < 4; ++t) mk[t] = __builtin_amdgcn_ballot_w64(ovalid && nw + t < lim && nw + t != o + dsh);
         }
     };
-    // Epilogue unit of prefix p for the block in ring slot eyo (its tables follow the tile), in
-    // three parts that the phases spread over their MFMA steps: the table reads (utab), the
-    // logits and exponentials (uchunk_a), the coefficients, radial sums and band operands (uchunk_b).
+    // Epilogue unit of prefix p for the block in ring slot eyo (its tables follow the tile): the
+    // table reads (utab) and four parts that the phases spread over their MFMA steps, one or two
+    // per step: (0) S^p and S^p A_o, (1) the logits and exponentials, (2) the coefficients,
+    // (3) the running band operand, the radial sums and the FP16 band operand.
     const char *tabs0 = (const char *)&Ys[0][BI * YP] + 16 * w;  // this wave's four inner rows
     struct UTab {
         f32x4 iy, kp;
@@ -900,84 +901,94 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         if constexpr (!SIG) tb.kp = *(const f32x4 *)(tabs0 + eyb + 4 * (NP + p) * BI);
         return tb;
     };
-    // S^p (quarters below wave_of(p), lowest first, shared by the prefixes, plus the snapshot) and
-    // e = 2^(S A_o iy + C_o) (softmax) or the unmasked coefficient sigma(l) beta_o iy (sigmoid)
-    auto uchunk_a = [&](auto pc, auto masked, const uint64_t(&mk)[4], const UTab &tb, f32x4 &Sp, f32x4 &e) {
+    struct UState {
+        f32x4 Sp, e;
+        float av[4];
+    };
+    auto upart = [&](auto pc, auto kc, auto masked, const uint64_t(&mk)[4], const UTab &tb, UState &st) {
         constexpr int p = decltype(pc)::value;
+        constexpr int k = decltype(kc)::value;
         constexpr bool MK = decltype(masked)::value;
-        if constexpr (L::wave_of(p) == 0) {
-            Sp = sv[L::snap_slot(p)];
+        if constexpr (k == 0) {
+            // S^p: quarters below wave_of(p), lowest first (shared by the prefixes), plus the snapshot
+            if constexpr (L::wave_of(p) == 0) {
+                st.Sp = sv[L::snap_slot(p)];
+            } else {
+                st.Sp = sv[0];
+                static_for<1, L::wave_of(p)>([&](auto qc) { st.Sp += sv[decltype(qc)::value]; });
+                st.Sp += sv[L::snap_slot(p)];
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) st.e[t] = st.Sp[t] * Ao[p];
+        } else if constexpr (k == 1) {
+            if constexpr (!SIG) {
+                // e = 2^(S A_o iy + C_o)
+                float x[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) x[t] = fmaf(st.e[t], tb.iy[t], Co[p]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) st.e[t] = __builtin_amdgcn_exp2f(x[t]);
+            } else {
+                // the unmasked coefficient sigma(l) beta_o iy
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float uu = fmaf(st.e[t], tb.iy[t], a.b2);
+                    const float tt = __builtin_amdgcn_exp2f(-fabsf(uu));
+                    const float wq = 1.f + tt;
+                    const float rr = __builtin_amdgcn_rcpf(wq);
+                    const float sg = uu >= 0.f ? rr : tt * rr;
+                    st.e[t] = sg * Co[p] * tb.iy[t];  // Co holds beta_o for the sigmoid form
+                    if (a.want_loss) {
+                        // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
+                        const float corr = (tt - (wq - 1.f)) * rr * kLog2e;
+                        const float lt = fmaxf(uu, 0.f) + __builtin_amdgcn_logf(wq) + corr;
+                        Lacc[p] += (!MK || __builtin_amdgcn_inverse_ballot_w64(mk[t])) ? lt : 0.f;
+                    }
+                }
+            }
+        } else if constexpr (k == 2) {
+            // a^p = e (Rho_o iy + Kap) (softmax) or e (sigmoid), masked
+#pragma unroll
+            for (int t = 0; t < 4; ++t) st.av[t] = SIG ? st.e[t] : st.e[t] * fmaf(Ro[p], tb.iy[t], tb.kp[t]);
+            if constexpr (MK)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) st.av[t] = __builtin_amdgcn_inverse_ballot_w64(mk[t]) ? st.av[t] : 0.f;
         } else {
-            Sp = sv[0];
-            static_for<1, L::wave_of(p)>([&](auto qc) { Sp += sv[decltype(qc)::value]; });
-            Sp += sv[L::snap_slot(p)];
-        }
-        if constexpr (!SIG) {
-            float x[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) x[t] = Sp[t] * Ao[p];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) x[t] = fmaf(x[t], tb.iy[t], Co[p]);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) e[t] = __builtin_amdgcn_exp2f(x[t]);
-        } else {
+            // band operand suffix sums, radial sums, FP16 band operand
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const float uu = fmaf(Sp[t] * Ao[p], tb.iy[t], a.b2);
-                const float tt = __builtin_amdgcn_exp2f(-fabsf(uu));
-                const float wq = 1.f + tt;
-                const float rr = __builtin_amdgcn_rcpf(wq);
-                const float sg = uu >= 0.f ? rr : tt * rr;
-                e[t] = sg * Co[p] * tb.iy[t];  // Co holds beta_o for the sigmoid form
-                if (a.want_loss) {
-                    // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
-                    const float corr = (tt - (wq - 1.f)) * rr * kLog2e;
-                    const float lt = fmaxf(uu, 0.f) + __builtin_amdgcn_logf(wq) + corr;
-                    Lacc[p] += (!MK || __builtin_amdgcn_inverse_ballot_w64(mk[t])) ? lt : 0.f;
-                }
+                if constexpr (p == NP - 1)
+                    run[t] = st.av[t];
+                else
+                    run[t] += st.av[t];
+            }
+            Cacc[p] = fmaf(st.av[0], st.Sp[0],
+                           fmaf(st.av[1], st.Sp[1], fmaf(st.av[2], st.Sp[2], fmaf(st.av[3], st.Sp[3], Cacc[p]))));
+            if constexpr (UPD) {
+                // two values per conversion (round to nearest even), instead of a fused multiply-add per value
+                uint32_t h01, h23;
+                asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(h01) : "v"(run[0]), "v"(run[1]));
+                asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(h23) : "v"(run[2]), "v"(run[3]));
+                const f16x4 v = __builtin_bit_cast(f16x4, (uint64_t)h01 | ((uint64_t)h23 << 32));
+                if constexpr (p >= NP - NA)
+                    hv[NP - 1 - p] = v;  // E_a: held until phase A
+                else
+                    *(f16x4 *)&At[p][lane * APITCH + 4 * w] = v;
             }
         }
     };
-    // a^p = e (Rho_o iy + Kap) (softmax) or e (sigmoid), masked; radial sums; band operand suffix sums
-    auto uchunk_b = [&](auto pc, auto masked, const uint64_t(&mk)[4], const UTab &tb, const f32x4 &Sp,
-                        const f32x4 &e) {
-        constexpr int p = decltype(pc)::value;
-        constexpr bool MK = decltype(masked)::value;
-        float av[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) av[t] = SIG ? e[t] : e[t] * fmaf(Ro[p], tb.iy[t], tb.kp[t]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if constexpr (MK) av[t] = __builtin_amdgcn_inverse_ballot_w64(mk[t]) ? av[t] : 0.f;
-            if constexpr (p == NP - 1)
-                run[t] = av[t];
-            else
-                run[t] += av[t];
-        }
-        Cacc[p] = fmaf(av[0], Sp[0], fmaf(av[1], Sp[1], fmaf(av[2], Sp[2], fmaf(av[3], Sp[3], Cacc[p]))));
-        if constexpr (UPD) {
-            // two values per conversion (round to nearest even), instead of a fused multiply-add per value
-            uint32_t h01, h23;
-            asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(h01) : "v"(run[0]), "v"(run[1]));
-            asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(h23) : "v"(run[2]), "v"(run[3]));
-            const f16x4 v = __builtin_bit_cast(f16x4, (uint64_t)h01 | ((uint64_t)h23 << 32));
-            if constexpr (p >= NP - NA)
-                hv[NP - 1 - p] = v;  // E_a: held until phase A
-            else
-                *(f16x4 *)&At[p][lane * APITCH + 4 * w] = v;
-        }
-    };
-    // Schedules (compile time): unit u's two chunks and its table reads, by MFMA step.
-    // Phase A runs E_b (units u = 0 .. NUB - 1 are prefixes NUB - 1 - u), phase B runs E_a
-    // (units u = 0 .. NA - 1 are prefixes NP - 1 - u); a table step of -1 is before the first step.
+    // Schedules (compile time): the step of part k of unit u and of its table reads.  Phase A
+    // runs E_b (units u = 0 .. NUB - 1 are prefixes NUB - 1 - u), phase B runs E_a (units
+    // u = 0 .. NA - 1 are prefixes NP - 1 - u) from its second step on (the S slots are read
+    // just before it); a table step of -1 is before the first step.
     constexpr int NUB = NP - NA;
     struct Sched {
-        static constexpr int chunk_a(int k) { return NUB > 0 ? (k * NQ) / (2 * NUB) : 0; }
-        static constexpr int tab_a(int u) { return chunk_a(2 * u) - 1; }
-        static constexpr int chunk_b(int k) {
-            return NA > 0 ? ((k * NQ) / (2 * NA) + 1 < NQ ? (k * NQ) / (2 * NA) + 1 : NQ - 1) : 0;
+        static constexpr int part_a(int u, int k) { return NUB > 0 ? ((4 * u + k) * NQ) / (4 * NUB) : 0; }
+        static constexpr int tab_a(int u) { return part_a(u, 0) - 1; }
+        static constexpr int part_b(int u, int k) {
+            return NA > 0 ? (((4 * u + k) * (NQ - 1)) / (4 * NA) + 1 < NQ ? ((4 * u + k) * (NQ - 1)) / (4 * NA) + 1 : NQ - 1) : 0;
         }
-        static constexpr int tab_b(int u) { return chunk_b(2 * u) - 1; }
+        static constexpr int tab_b(int u) { return part_b(u, 0) - 1; }
     };
 
     // transposed inner-tile operands of the update, two steps ahead; the first two are
@@ -1020,7 +1031,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
                 });
         }
         UTab tb[NUB > 0 ? NUB : 1];
-        f32x4 spv[NUB > 0 ? NUB : 1], ev[NUB > 0 ? NUB : 1];
+        UState us[NUB > 0 ? NUB : 1];
         if constexpr (WE)
             static_for<0, NUB>([&](auto uc) {
                 constexpr int u = decltype(uc)::value;
@@ -1049,8 +1060,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
                 static_for<0, NUB>([&](auto uc) {
                     constexpr int u = decltype(uc)::value;
                     constexpr std::integral_constant<int, NUB - 1 - u> pc{};
-                    if constexpr (Sched::chunk_a(2 * u) == ks) uchunk_a(pc, masked, mk, tb[u], spv[u], ev[u]);
-                    if constexpr (Sched::chunk_a(2 * u + 1) == ks) uchunk_b(pc, masked, mk, tb[u], spv[u], ev[u]);
+                    static_for<0, 4>([&](auto kc) {
+                        if constexpr (Sched::part_a(u, decltype(kc)::value) == ks) upart(pc, kc, masked, mk, tb[u], us[u]);
+                    });
                     if constexpr (Sched::tab_a(u) == ks) tb[u] = utab(pc, eyo);
                 });
             __builtin_amdgcn_sched_barrier(0);
@@ -1069,7 +1081,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         constexpr std::true_type masked{};
         f16x8 af[2];
         UTab tb[NA > 0 ? NA : 1];
-        f32x4 spv[NA > 0 ? NA : 1], ev[NA > 0 ? NA : 1];
+        UState us[NA > 0 ? NA : 1];
         if constexpr (WE)
             static_for<0, NA>([&](auto uc) {
                 constexpr int u = decltype(uc)::value;
@@ -1093,8 +1105,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
                 static_for<0, NA>([&](auto uc) {
                     constexpr int u = decltype(uc)::value;
                     constexpr std::integral_constant<int, NP - 1 - u> pc{};
-                    if constexpr (Sched::chunk_b(2 * u) == jb) uchunk_a(pc, masked, mk1, tb[u], spv[u], ev[u]);
-                    if constexpr (Sched::chunk_b(2 * u + 1) == jb) uchunk_b(pc, masked, mk1, tb[u], spv[u], ev[u]);
+                    static_for<0, 4>([&](auto kc) {
+                        if constexpr (Sched::part_b(u, decltype(kc)::value) == jb) upart(pc, kc, masked, mk1, tb[u], us[u]);
+                    });
                     if constexpr (Sched::tab_b(u) == jb) tb[u] = utab(pc, eyo1);
                 });
             __builtin_amdgcn_sched_barrier(0);
