@@ -84,6 +84,10 @@ __device__ __forceinline__ float reduce_scatter32(float (&v)[32], int lane) {
 }
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 // barrier that waits for this wave's LDS accesses only (not for its outstanding global loads)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
@@ -263,6 +267,15 @@ __device__ __forceinline__ void fwd_snapshot(const f32x16 (&acc)[2][2], int p, i
     }
 }
 
+// Slices (64 wide) covered by the prefixes of ladder MASK (bit ds: a prefix ends at 32 (ds + 1)),
+// for ladders whose prefixes all end on a slice boundary; 0 otherwise.
+constexpr int fwd_ladder_slices(uint32_t mask) {
+    if (mask == 0u || (mask & 0x55555555u) != 0u) return 0;
+    return (32 - __builtin_clz(mask)) / 2;
+}
+constexpr uint32_t fwd_ladder(uint32_t mask) { return fwd_ladder_slices(mask) > 0 ? mask : 0u; }
+
+template <uint32_t MASK>
 __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const u16 *__restrict__ k, int64_t R,
                                                 int64_t N, int D, Prefixes pf, int64_t off,
                                                 const float *__restrict__ rowA, const float *__restrict__ colI,
@@ -344,6 +357,93 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
+    if constexpr (MASK != 0u) {
+        // Prefix ladder known at compile time: no branch inside a slice.  Per slice st (ring slot
+        // st & 1): the operands of step ks + 1 are read before the MFMAs of step ks; after the
+        // reads of the slice's last step, one barrier publishes slice st + 1 (and frees slot
+        // st & 1 for the copies of slice st + 2), so the last step's MFMAs run with the first
+        // operands of slice st + 1 already on their way.  Snapshots follow the slices where a
+        // prefix ends.
+        constexpr int NSL = fwd_ladder_slices(MASK);
+        static_assert(NSL >= 1, "every prefix must end on a 64-wide slice boundary");
+        constexpr int NPm = __builtin_popcount(MASK);
+        const char *ring0 = (const char *)&Ring[0][0][0];
+        auto lread = [&](int st, int ks, bf16x8(&av)[2], bf16x8(&bv)[2]) {
+            const char *sb = ring0 + (st & 1) * 2 * SLB;
+            const uint32_t o = 16u * (uint32_t)((2 * ks) ^ (sw & 6));
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                av[b] = *(const bf16x8 *)(sb + rdq + o + b * 32 * 128);
+                bv[b] = *(const bf16x8 *)(sb + rdk + o + b * 32 * 128);
+            }
+        };
+        auto mfma4 = [&](const bf16x8(&av)[2], const bf16x8(&bv)[2]) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
+        };
+        issue(0);
+        if (NSL > 1) issue(1);
+        if (NSL > 1)
+            wait_vm_n<8>();  // slice 0 landed (slice 1's eight copies may still be in flight)
+        else
+            wait_vm();
+        lds_barrier();
+        bf16x8 av0[2], bv0[2], av1[2], bv1[2];
+        lread(0, 0, av0, bv0);
+        int st = 0;
+        auto slice = [&](auto lastc) {
+            constexpr bool LAST = decltype(lastc)::value;  // the ladder's final slice
+            // steps 0..2: read the next step, then this step's MFMAs (operands alternate av0/av1)
+            lread(st, 1, av1, bv1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma4(av0, bv0);
+            __builtin_amdgcn_sched_barrier(0);
+            lread(st, 2, av0, bv0);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma4(av1, bv1);
+            __builtin_amdgcn_sched_barrier(0);
+            lread(st, 3, av1, bv1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma4(av0, bv0);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!LAST) {
+                wait_vm();      // this wave's copies of slice st + 1 landed
+                lds_barrier();  // every wave's copies visible; every wave's reads of slot st & 1 done
+                if (st + 2 < NSL) issue(st + 2);
+                lread(st + 1, 0, av0, bv0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mfma4(av1, bv1);
+            __builtin_amdgcn_sched_barrier(0);
+            ++st;
+        };
+        static_for<0, NPm>([&](auto pc) {
+            constexpr int p = decltype(pc)::value;
+            // slices up to the end of prefix p: bit positions of MASK in units of 64
+            constexpr int endsl = [] {
+                int c = -1;
+                for (int ds = 0; ds < 32; ++ds)
+                    if (MASK & (1u << ds))
+                        if (++c == p) return (ds + 1) / 2;
+                return 0;
+            }();
+            if constexpr (p + 1 < NPm) {
+                for (; st < endsl;) slice(std::false_type{});
+            } else {
+                for (; st < endsl - 1;) slice(std::false_type{});
+                slice(std::true_type{});
+            }
+            if (masked)
+                fwd_snapshot<true>(acc, p, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, it, jt, rowpart,
+                                   colpart);
+            else
+                fwd_snapshot<false>(acc, p, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, it, jt, rowpart,
+                                    colpart);
+        });
+    } else {
     const int nst = (Dsw + FK - 1) / FK;
     int pnext = 0;
     issue(0);
@@ -385,6 +485,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
                 }
             }
         }
+    }
     }
 }
 
@@ -623,10 +724,6 @@ struct Ladder {
 };
 
 
-template <int N>
-__device__ __forceinline__ void wait_vm_n() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 
@@ -1314,12 +1411,34 @@ hipError_t launch_half_copy(const u16 *x, const float *sig, int64_t rows, int D,
     return hipGetLastError();
 }
 
+// Prefix ladders with a compiled backward (bit ds set: a prefix ends at 32 (ds + 1)).
+#define UFORM_LADDERS(X)                                                        \
+    X(0x8000808Au) /* 64, 128, 256, 512, 1024 */                                \
+    X(0x0000808Au) /* 64, 128, 256, 512 */                                      \
+    X(0x0000008Au) /* 64, 128, 256 */                                           \
+    X(0x0000000Au) /* 64, 128 */                                                \
+    X(0x80000000u) /* 1024 */                                                   \
+    X(0x00008000u) /* 512 */                                                    \
+    X(0x00000080u) /* 256 */                                                    \
+    X(0x00000008u) /* 128 */
+
 hipError_t launch_fwd(const u16 *q, const u16 *k, int64_t R, int64_t N, int D, const Prefixes &pf, int64_t off,
                       const float *rowA, const float *colI, float cshift, float *rowpart, float *colpart,
                       hipStream_t s) {
     const int64_t nIt = (R + FB - 1) / FB, nJt = (N + FB - 1) / FB;
-    hipLaunchKernelGGL(k_fwd, dim3((unsigned)(nIt * nJt)), dim3(256), 0, s, q, k, R, N, D, pf, off, rowA, colI,
-                       cshift, rowpart, colpart);
+    uint32_t mask = 0;
+    for (int p = 0; p < pf.n; ++p) mask |= 1u << (pf.w[p] / 32 - 1);
+    const dim3 grid((unsigned)(nIt * nJt));
+#define UFORM_CASE(m)                                                                                          \
+    if (fwd_ladder(m) != 0u && mask == (m)) {                                                                  \
+        hipLaunchKernelGGL(k_fwd<fwd_ladder(m)>, grid, dim3(256), 0, s, q, k, R, N, D, pf, off, rowA, colI, cshift, \
+                           rowpart, colpart);                                                                  \
+        return hipGetLastError();                                                                              \
+    }
+    UFORM_LADDERS(UFORM_CASE)
+#undef UFORM_CASE
+    hipLaunchKernelGGL(k_fwd<0u>, grid, dim3(256), 0, s, q, k, R, N, D, pf, off, rowA, colI, cshift, rowpart,
+                       colpart);
     return hipGetLastError();
 }
 
@@ -1348,17 +1467,6 @@ static hipError_t launch_bwd_mask(const BwdArgs &a, bool sig, dim3 grid, hipStre
         hipLaunchKernelGGL((k_bwd<MASK, true, false>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
-
-// Prefix ladders with a compiled backward (bit ds set: a prefix ends at 32 (ds + 1)).
-#define UFORM_LADDERS(X)                                                        \
-    X(0x8000808Au) /* 64, 128, 256, 512, 1024 */                                \
-    X(0x0000808Au) /* 64, 128, 256, 512 */                                      \
-    X(0x0000008Au) /* 64, 128, 256 */                                           \
-    X(0x0000000Au) /* 64, 128 */                                                \
-    X(0x80000000u) /* 1024 */                                                   \
-    X(0x00008000u) /* 512 */                                                    \
-    X(0x00000080u) /* 256 */                                                    \
-    X(0x00000008u) /* 128 */
 
 bool bwd_mask_supported(uint32_t mask) {
 #define UFORM_CASE(m) if (mask == (m)) return true;

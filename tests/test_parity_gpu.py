@@ -193,3 +193,21 @@ def test_loss_only_calls():
         full = binding.fwd_bwd(q, k, LADDER, s, b, kind)
         only = binding.fwd_bwd(q, k, LADDER, s, b, kind, want_dq=False, want_dk=False)
         assert torch.equal(full[0], only[0])
+
+
+@pytest.mark.parametrize("kind", [INFONCE, INFONCE_ROWS])
+def test_forward_any_prefixes_loss_only(kind):
+    # prefixes ending on odd multiples of 32 take the forward that reads the prefix list at run
+    # time (the compiled-ladder forward covers lists ending on multiples of 64); no gradients
+    R, N, D, pf = (150, 150, 384, (32, 96, 160, 352)) if kind == INFONCE else (70, 230, 256, (96, 224))
+    qb, kb = make_inputs(R, N, D, noise=1.5, seed=81 + D)
+    print(f"[case] generic-forward kind={kind} R={R} N={N} D={D} prefixes={pf}", flush=True)
+    q, k = to_dev(qb), to_dev(kb)
+    loss, _, _, ex = binding.fwd_bwd(q, k, pf, 13.0, 0.0, kind, want_dq=False, want_dk=False, extras=True)
+    torch.cuda.synchronize()
+    ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), pf, 13.0, 0.0, kind, grads=False)
+    assert abs(loss.item() - ref["loss"]) <= 1e-3 * abs(ref["loss"])
+    np.testing.assert_allclose(ex["prefix_losses"].cpu().numpy(), ref["prefix_losses"], rtol=1e-3)
+    assert np.abs(ex["row_lse"].cpu().numpy() - ref["row_lse"]).max() <= 1e-3
+    assert np.abs(ex["pos_logit"].cpu().numpy() - ref["pos_logit"]).max() <= 1e-3
+    assert np.abs(ex["col_lse"].cpu().numpy() - ref["col_lse"]).max() <= 1e-3
