@@ -219,7 +219,7 @@ __device__ __forceinline__ void fwd_snapshot(const f32x16 (&acc)[2][2], int p, i
                                              int64_t it, int64_t jt,
                                              float *__restrict__ rowpart, float *__restrict__ colpart) {
     float rs[32];
-    float cs[2] = {0.f, 0.f};
+    float cs[2];
     float Ij[2];
     int64_t gj[2];
 #pragma unroll
@@ -234,19 +234,18 @@ __device__ __forceinline__ void fwd_snapshot(const f32x16 (&acc)[2][2], int p, i
         for (int r = 0; r < 16; ++r) {
             const int il = wi * 64 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             const float Ai = fA[p][il];
-            float rsum = 0.f;
+            float e[2];
 #pragma unroll
             for (int bj = 0; bj < 2; ++bj) {
-                float e = __builtin_amdgcn_exp2f(fmaf(acc[bi][bj][r] * Ai, Ij[bj], cshift));
+                e[bj] = __builtin_amdgcn_exp2f(fmaf(acc[bi][bj][r] * Ai, Ij[bj], cshift));
                 if (MASKED) {
                     const int64_t gi = i0 + il;
                     const bool ok = (gi < R) & (gj[bj] < N) & (gj[bj] != gi + off);
-                    e = ok ? e : 0.f;
+                    e[bj] = ok ? e[bj] : 0.f;
                 }
-                rsum += e;
-                cs[bj] += e;
+                cs[bj] = (bi == 0 && r == 0) ? e[bj] : cs[bj] + e[bj];  // no addition of a zero start
             }
-            rs[bi * 16 + r] = rsum;
+            rs[bi * 16 + r] = e[0] + e[1];
         }
     }
     // row sums: lane (lane & 31) of each half ends up with row index v = lane & 31
@@ -358,23 +357,47 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
     if constexpr (MASK != 0u) {
-        // Prefix ladder known at compile time: no branch inside a slice.  Per slice st (ring slot
-        // st & 1): the operands of step ks + 1 are read before the MFMAs of step ks; after the
-        // reads of the slice's last step, one barrier publishes slice st + 1 (and frees slot
-        // st & 1 for the copies of slice st + 2), so the last step's MFMAs run with the first
-        // operands of slice st + 1 already on their way.  Snapshots follow the slices where a
-        // prefix ends.
-        constexpr int NSL = fwd_ladder_slices(MASK);
-        static_assert(NSL >= 1, "every prefix must end on a 64-wide slice boundary");
+        // Prefix ladder known at compile time: no branch inside a slice.  The ring holds four
+        // 32-wide slices (rows of 64 bytes; the 16-byte chunk c of row r at position
+        // c ^ ((r >> 2) & 3), so the operand reads of 16 rows meet 64 different banks).  Per slice
+        // st (slot st & 3): the operands of step 1 are read before the MFMAs of step 0; then one
+        // barrier publishes slice st + 1 and frees slot st & 3 for the copies of slice st + 4
+        // (three slices ahead), and the first operands of slice st + 1 are read before the MFMAs
+        // of step 1.  Snapshots follow the slices where a prefix ends.
+        constexpr int FK2 = 32;
+        constexpr int SLB2 = FB * FK2 * 2;  // bytes per operand slice
+        constexpr int NSL = 2 * fwd_ladder_slices(MASK);
+        static_assert(NSL >= 2, "every prefix must end on a 64-wide boundary");
         constexpr int NPm = __builtin_popcount(MASK);
+        // copies: this wave moves pieces 2 wave, 2 wave + 1 (16 rows x 64 bytes each) of both operands
+        uint32_t cq[2], ck[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int row = 16 * (2 * wave + c) + (lane >> 2);
+            const uint32_t ch = (uint32_t)((lane & 3) ^ ((row >> 2) & 3));
+            const int64_t rq = i0 + row < R ? row : R - 1 - i0, rk = j0 + row < N ? row : N - 1 - j0;
+            cq[c] = (uint32_t)rq * (uint32_t)D * 2u + 16u * ch;
+            ck[c] = (uint32_t)rk * (uint32_t)D * 2u + 16u * ch;
+        }
+        auto issue2 = [&](int st) {
+            const uint32_t m = ring_lds + (uint32_t)((st & 3) * 2 * SLB2 + 2048 * wave);
+            const u16 *qs = qt + st * FK2, *ks_ = kt + st * FK2;
+            dma_row1(qs, cq[0], m);
+            dma_row1(qs, cq[1], m + 1024);
+            dma_row1(ks_, ck[0], m + SLB2);
+            dma_row1(ks_, ck[1], m + SLB2 + 1024);
+        };
+        const int sw4 = (rl >> 2) & 3, h = lane >> 5;
+        const uint32_t rq0 = (uint32_t)((wi * 64 + rl) * 64), rk0 = (uint32_t)((wj * 64 + rl) * 64) + SLB2;
+        const uint32_t po0 = 16u * (uint32_t)(h ^ sw4), po1 = 16u * (uint32_t)((2 + h) ^ sw4);
         const char *ring0 = (const char *)&Ring[0][0][0];
-        auto lread = [&](int st, int ks, bf16x8(&av)[2], bf16x8(&bv)[2]) {
-            const char *sb = ring0 + (st & 1) * 2 * SLB;
-            const uint32_t o = 16u * (uint32_t)((2 * ks) ^ (sw & 6));
+        auto lread = [&](int st, auto ksc, bf16x8(&av)[2], bf16x8(&bv)[2]) {
+            const char *sb = ring0 + (st & 3) * 2 * SLB2;
+            const uint32_t o = decltype(ksc)::value == 0 ? po0 : po1;
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-                av[b] = *(const bf16x8 *)(sb + rdq + o + b * 32 * 128);
-                bv[b] = *(const bf16x8 *)(sb + rdk + o + b * 32 * 128);
+                av[b] = *(const bf16x8 *)(sb + rq0 + o + b * 32 * 64);
+                bv[b] = *(const bf16x8 *)(sb + rk0 + o + b * 32 * 64);
             }
         };
         auto mfma4 = [&](const bf16x8(&av)[2], const bf16x8(&bv)[2]) {
@@ -384,36 +407,37 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
                 for (int b = 0; b < 2; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
         };
-        issue(0);
-        if (NSL > 1) issue(1);
-        if (NSL > 1)
-            wait_vm_n<8>();  // slice 0 landed (slice 1's eight copies may still be in flight)
+        constexpr std::integral_constant<int, 0> K0{};
+        constexpr std::integral_constant<int, 1> K1{};
+        issue2(0);
+        issue2(1);
+        issue2(2);
+        if (NSL > 3) issue2(3);
+        if (NSL > 3)
+            wait_vm_n<12>();  // slice 0 landed (slices 1..3 may still be in flight)
         else
-            wait_vm();
+            wait_vm_n<8>();
         lds_barrier();
         bf16x8 av0[2], bv0[2], av1[2], bv1[2];
-        lread(0, 0, av0, bv0);
+        lread(0, K0, av0, bv0);
         int st = 0;
         auto slice = [&](auto lastc) {
             constexpr bool LAST = decltype(lastc)::value;  // the ladder's final slice
-            // steps 0..2: read the next step, then this step's MFMAs (operands alternate av0/av1)
-            lread(st, 1, av1, bv1);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma4(av0, bv0);
-            __builtin_amdgcn_sched_barrier(0);
-            lread(st, 2, av0, bv0);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma4(av1, bv1);
-            __builtin_amdgcn_sched_barrier(0);
-            lread(st, 3, av1, bv1);
+            lread(st, K1, av1, bv1);
             __builtin_amdgcn_sched_barrier(0);
             mfma4(av0, bv0);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (!LAST) {
-                wait_vm();      // this wave's copies of slice st + 1 landed
-                lds_barrier();  // every wave's copies visible; every wave's reads of slot st & 1 done
-                if (st + 2 < NSL) issue(st + 2);
-                lread(st + 1, 0, av0, bv0);
+                // this wave's copies of slice st + 1 landed (those of st + 2 and st + 3 may be in flight)
+                if (st + 3 < NSL)
+                    wait_vm_n<8>();
+                else if (st + 2 < NSL)
+                    wait_vm_n<4>();
+                else
+                    wait_vm();
+                lds_barrier();  // every wave's copies visible; every wave's reads of slot st & 3 done
+                if (st + 4 < NSL) issue2(st + 4);
+                lread(st + 1, K0, av0, bv0);
             }
             __builtin_amdgcn_sched_barrier(0);
             mfma4(av1, bv1);
@@ -422,12 +446,12 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
         };
         static_for<0, NPm>([&](auto pc) {
             constexpr int p = decltype(pc)::value;
-            // slices up to the end of prefix p: bit positions of MASK in units of 64
+            // 32-wide slices up to the end of prefix p
             constexpr int endsl = [] {
                 int c = -1;
                 for (int ds = 0; ds < 32; ++ds)
                     if (MASK & (1u << ds))
-                        if (++c == p) return (ds + 1) / 2;
+                        if (++c == p) return ds + 1;
                 return 0;
             }();
             if constexpr (p + 1 < NPm) {
