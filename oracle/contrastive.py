@@ -107,7 +107,11 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
     Returns a dict with ``loss`` (float), ``prefix_losses`` [P], ``row_lse``
     [P, R] (log-sum-exp of each row's logits; InfoNCE kinds), ``pos_logit``
     [P, R], ``col_lse`` [P, N] (log-sum-exp over the R rows of each column's
-    logits; InfoNCE kinds) and, when ``grads``, ``dq`` [R, D] and ``dk`` [N, D].
+    logits; InfoNCE kinds) and, when ``grads``, ``dq`` [R, D], ``dk`` [N, D],
+    ``dscale`` = dL/ds = sum_p (w_p/W) sum_ij g^p_ij cos^p_ij and ``dbias`` =
+    dL/db = sum_p (w_p/W) sum_ij g^p_ij, with g^p = dL^p/dl^p the residual
+    (the learned temperature and bias of the sigmoid form: "Scaling-Up
+    Contrastive Learning over NVLink Multicast", section "One Set or Two").
     """
     q = np.ascontiguousarray(q, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
@@ -144,6 +148,8 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
     pos_logit = np.zeros((P, R))
     dq = np.zeros((R, D)) if grads else None
     dk = np.zeros((N, D)) if grads else None
+    dscale = 0.0
+    dbias = 0.0
 
     with _blas_single_thread(), ThreadPoolExecutor(max_workers=threads) as pool:
         for p, width in enumerate(prefixes):
@@ -205,17 +211,21 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
                 p_col = np.exp(logits - col_lse[p][cols][None, :])
                 return (p_row - E + p_col - E) / (2.0 * N)
 
-            # ---- dq: u_i = sum_j g_ij * s * kh_j, then through the normalisation of q_i
+            # ---- dq: u_i = sum_j g_ij * s * kh_j, then through the normalisation of q_i;
+            # with it the block's sums of g * cos (dL^p/ds) and of g (dL^p/db)
             def grad_rows(rb):
                 r0, r1 = rb
-                logits = s * (qh[r0:r1] @ kh.T) + b
+                cos = qh[r0:r1] @ kh.T
+                logits = s * cos + b
                 g = residual(logits, all_rows[r0:r1], all_cols)
                 u = s * (g @ kh)
                 radial = np.sum(u * qh[r0:r1], axis=1)
-                return (u - radial[:, None] * qh[r0:r1]) / qnorm[r0:r1, None]
+                return (u - radial[:, None] * qh[r0:r1]) / qnorm[r0:r1, None], np.sum(g * cos), np.sum(g)
 
-            for (r0, r1), part in zip(row_blocks, pool.map(grad_rows, row_blocks)):
+            for (r0, r1), (part, gc, gs) in zip(row_blocks, pool.map(grad_rows, row_blocks)):
                 dq[r0:r1, :width] += (w[p] / W) * part
+                dscale += (w[p] / W) * gc
+                dbias += (w[p] / W) * gs
 
             # ---- dk: v_j = sum_i g_ij * s * qh_i, then through the normalisation of k_j
             def grad_cols(cb):
@@ -240,6 +250,8 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
     if grads:
         result["dq"] = dq
         result["dk"] = dk
+        result["dscale"] = float(dscale)
+        result["dbias"] = float(dbias)
     return result
 
 

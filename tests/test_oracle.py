@@ -136,11 +136,15 @@ def test_matches_torch_library_loss_and_autograd(rng, kind, R, N, off, prefixes,
     out = contrastive_fwd_bwd(q, k, prefixes, s, b, kind, weights=weights, row_offset=off)
     qt = torch.tensor(q, requires_grad=True)
     kt = torch.tensor(k, requires_grad=True)
-    lt = _torch_loss(qt, kt, prefixes, s, b, kind, weights, off)
+    st = torch.tensor(s, dtype=torch.float64, requires_grad=True)
+    bt = torch.tensor(b, dtype=torch.float64, requires_grad=True)
+    lt = _torch_loss(qt, kt, prefixes, st, bt, kind, weights, off)
     lt.backward()
     assert out["loss"] == pytest.approx(lt.item(), rel=1e-12)
     np.testing.assert_allclose(out["dq"], qt.grad.numpy(), rtol=1e-9, atol=1e-13)
     np.testing.assert_allclose(out["dk"], kt.grad.numpy(), rtol=1e-9, atol=1e-13)
+    assert out["dscale"] == pytest.approx(st.grad.item(), rel=1e-9, abs=1e-14)
+    assert out["dbias"] == pytest.approx(bt.grad.item(), rel=1e-9, abs=1e-14)
     if kind == INFONCE_ROWS:
         for p, width in enumerate(prefixes):
             logits = s * F.normalize(qt[:, :width], dim=1) @ F.normalize(kt[:, :width], dim=1).T + b
@@ -176,6 +180,17 @@ def test_gradients_match_central_differences(rng, kind, R, N, off):
         fd = (loss(xp, k) - loss(xm, k)) / (2 * h) if which == 0 else (loss(q, xp) - loss(q, xm)) / (2 * h)
         an = out["dq"][i, d] if which == 0 else out["dk"][i, d]
         assert an == pytest.approx(fd, rel=1e-6, abs=1e-9), (which, i, d)
+
+    # the temperature and the bias
+    def loss_sb(ss, bb):
+        return contrastive_fwd_bwd(q, k, prefixes, ss, bb, kind, weights=weights, row_offset=off,
+                                   grads=False)["loss"]
+
+    h = 1e-5
+    fd_s = (loss_sb(s + h, b) - loss_sb(s - h, b)) / (2 * h)
+    fd_b = (loss_sb(s, b + h) - loss_sb(s, b - h)) / (2 * h)
+    assert out["dscale"] == pytest.approx(fd_s, rel=1e-6, abs=1e-9)
+    assert out["dbias"] == pytest.approx(fd_b, rel=1e-6, abs=1e-9)
 
 
 # ----------------------------------------------------------------------------- invariants
@@ -241,6 +256,10 @@ def test_bias_invariance_infonce(rng):
     c = contrastive_fwd_bwd(q, k, [32, 64], 14.0, 3.5, INFONCE)
     assert c["loss"] == pytest.approx(a["loss"], rel=1e-12)
     np.testing.assert_allclose(c["dq"], a["dq"], rtol=1e-9, atol=1e-15)
+    # a softmax does not see a shift common to its logits: dL/db vanishes for both softmax kinds
+    assert abs(c["dbias"]) <= 1e-15
+    r = contrastive_fwd_bwd(q[:5], k, [32, 64], 14.0, 3.5, INFONCE_ROWS, row_offset=2)
+    assert abs(r["dbias"]) <= 1e-15
 
 
 @pytest.mark.parametrize("kind", [INFONCE, INFONCE_ROWS, SIGLIP])
