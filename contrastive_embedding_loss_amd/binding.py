@@ -44,6 +44,8 @@ class Options(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("flags", ctypes.c_uint32),
+        ("dscale_out", ctypes.c_void_p),
+        ("dbias_out", ctypes.c_void_p),
     ]
 
 
@@ -133,7 +135,8 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
     q [R, D] and k [N, D] are contiguous bfloat16 device tensors.  Returns
     ``(loss, dq, dk)`` (float32 tensors; dq/dk None when not wanted), plus a
     dict of ``prefix_losses``, ``row_lse``, ``col_lse`` and ``pos_logit`` when
-    ``extras``.  Everything is enqueued on torch's current stream.  ``one_split`` runs each backward pass as
+    ``extras`` (and ``dscale``, ``dbias``: dL/dscale and dL/dbias, when a
+    gradient is wanted).  Everything is enqueued on torch's current stream.  ``one_split`` runs each backward pass as
     one inner split (a diagnostic: the in-place finish that large problems take).
     """
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
@@ -175,6 +178,11 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
         if softmax:
             opt.row_lse_out = ex["row_lse"].data_ptr()
             opt.col_lse_out = ex["col_lse"].data_ptr()
+        if dq is not None or dk is not None:
+            ex["dscale"] = torch.empty(1, **f32)
+            ex["dbias"] = torch.empty(1, **f32)
+            opt.dscale_out = ex["dscale"].data_ptr()
+            opt.dbias_out = ex["dbias"].data_ptr()
     if workspace is not None:
         opt.workspace = workspace.data_ptr()
         opt.workspace_bytes = workspace.numel() * workspace.element_size()

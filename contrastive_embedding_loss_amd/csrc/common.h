@@ -58,6 +58,7 @@ struct StatsArgs {
     float *kC, *kRho, *kKap;  // key-side tables
     float *diagA;             // [P][R]: exact coefficient of the positive cell
     float *lossparts;         // [slot][P]
+    float *biasparts;         // sigmoid form: [slot][P], minus the positives' sigma(-l); nullable
     int64_t slot0;
 };
 
@@ -83,6 +84,8 @@ struct BwdArgs {
     float *Cpart;  // [nsplit][P][NO]
     float *lossparts;
     int64_t loss_slot0;
+    float *biasparts;  // sigmoid form, the pass with want_loss: [slot][P] sums of sigma(l) over the masked cells
+    float *tsum;       // nullable: [NO] per outer row, sum over p of its radial coefficient (dL/dscale)
     // one inner split only: the gradient rows are finished in place (the finalize terms
     // below) and written to fin_out instead of part / Cpart
     float *fin_out;
@@ -101,6 +104,7 @@ struct FinArgs {
     int64_t nsplit, diag_shift, pos_shift;
     int accumulate;
     float *out;
+    float *tsum;  // nullable: [NO] per row, sum over p of its radial coefficient (dL/dscale)
 };
 
 struct LossArgs {
@@ -110,6 +114,11 @@ struct LossArgs {
     double norm;
     float wnorm[kMaxP];
     float *loss_out, *prefix_losses_out;
+    const float *tsum;        // [ntsum] per-row radial sums of one backward pass (dL/dscale), or nullptr
+    int64_t ntsum;
+    float inv_scale;
+    const float *biasparts;   // sigmoid form: [nslots][P] (dL/dbias), or nullptr (softmax: dL/dbias = 0)
+    float *dscale_out, *dbias_out;
 };
 
 // launchers (kernels.hip)

@@ -46,7 +46,7 @@ struct Plan {
     size_t o_invq, o_invk, o_qA, o_kA, o_posdot, o_qH, o_kH;
     size_t o_qIYR, o_kIYR, o_sigq, o_sigk, o_gamq, o_gamk;
     size_t o_qC, o_qRho, o_qKap, o_kC, o_kRho, o_kKap, o_negfrac, o_kNegfrac, o_diagA, o_gmax;
-    size_t o_rowpart, o_colpart, o_part, o_Cpart, o_loss;
+    size_t o_rowpart, o_colpart, o_part, o_Cpart, o_loss, o_tsum, o_bias;
     size_t total;
 };
 
@@ -143,6 +143,9 @@ Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, in
     const size_t c_row = sizeof(float) * p.nsplit_row * P * R, c_col = sizeof(float) * p.nsplit_col * P * N;
     p.o_Cpart = take(c_row > c_col ? c_row : c_col);
     p.o_loss = take(sizeof(float) * p.nslots * P);
+    // per-row radial sums of one gradient pass (dL/dscale); sigmoid bias partials (dL/dbias)
+    p.o_tsum = take((want_dq || want_dk) ? sizeof(float) * (R > N ? R : N) : 0);
+    p.o_bias = take((want_dq || want_dk) && !softmax ? sizeof(float) * p.nslots * P : 0);
     p.total = off_b;
     return p;
 }
@@ -184,6 +187,12 @@ uform_status_t validate(const void *q, const void *k, int64_t R, int64_t N, int6
     }
     if (opt && opt->workspace && !aligned(opt->workspace, 256))
         return fail(uform_status_invalid_argument_k, "workspace must be 256-byte aligned");
+    if (opt && (opt->dscale_out || opt->dbias_out)) {
+        if (!dq && !dk)
+            return fail(uform_status_invalid_argument_k, "dscale_out and dbias_out come from a gradient pass: give dq or dk");
+        if ((opt->dscale_out && !aligned(opt->dscale_out, 4)) || (opt->dbias_out && !aligned(opt->dbias_out, 4)))
+            return fail(uform_status_invalid_argument_k, "dscale_out and dbias_out must be 4-byte aligned");
+    }
     if (D % 64 != 0 || D > kMaxD) return fail(uform_status_unsupported_k, "D must be a multiple of 64 and at most 1024");
     if (kind != kSiglip && std::fabs(scale) > UFORM_CONTRASTIVE_MAX_SOFTMAX_SCALE)
         return fail(uform_status_unsupported_k, "softmax kinds support |scale| <= 40");
@@ -380,6 +389,10 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     sa.kKap = F(pl.o_kKap);
     sa.diagA = F(pl.o_diagA);
     sa.lossparts = lossparts;
+    float *const dscale_out = opt ? opt->dscale_out : nullptr, *const dbias_out = opt ? opt->dbias_out : nullptr;
+    float *const biasparts = (!softmax && dbias_out) ? F(pl.o_bias) : nullptr;
+    float *const tsum = dscale_out ? F(pl.o_tsum) : nullptr;
+    sa.biasparts = biasparts;
 
     if (softmax) {
         LAUNCH_NAMED("k_fwd", launch_fwd(q, k, R, N, Di, pf, off, qA, invk, cshift, F(pl.o_rowpart),
@@ -436,6 +449,10 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
         ba.Cpart = F(pl.o_Cpart);
         ba.lossparts = lossparts;
         ba.loss_slot0 = pl.slots_a;
+        ba.biasparts = biasparts;
+        // the radial sums of the first gradient pass give dL/dscale
+        float *const ts = (out && (rowpass || !dq)) ? tsum : nullptr;
+        ba.tsum = ts;
         const int64_t nsplit = rowpass ? pl.nsplit_row : pl.nsplit_col;
         const bool fuse = out && nsplit == 1;  // one split: the backward finishes the rows itself
         if (fuse) {
@@ -470,6 +487,7 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
             fa.pos_shift = rowpass ? 0 : -off;
             fa.accumulate = (opt && (opt->flags & UFORM_CONTRASTIVE_ACCUMULATE)) ? 1 : 0;
             fa.out = out;
+            fa.tsum = ts;
             LAUNCH_NAMED("k_finalize", launch_finalize(fa, s));
         }
         return uform_status_success_k;
@@ -491,6 +509,12 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     for (int i = 0; i < kMaxP; ++i) la.wnorm[i] = wnorm[i];
     la.loss_out = loss_out;
     la.prefix_losses_out = opt ? opt->prefix_losses_out : nullptr;
+    la.tsum = tsum;
+    la.ntsum = dq ? R : N;
+    la.inv_scale = 1.0f / scale;
+    la.biasparts = biasparts;
+    la.dscale_out = dscale_out;
+    la.dbias_out = dbias_out;
     LAUNCH_NAMED("k_loss", launch_loss(la, s));
     return uform_status_success_k;
 }

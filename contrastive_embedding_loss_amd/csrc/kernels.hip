@@ -639,7 +639,7 @@ __global__ __launch_bounds__(256) void k_siglip_tabs(StatsArgs a) {
     const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int P = a.pf.n;
     for (int p = 0; p < P; ++p) {
-        float lpos = 0.f;
+        float lpos = 0.f, sig_neg = 0.f;
         if (r < a.R) {
             const int64_t i = r;
             const float iq = a.invq[p * a.R + i], ik = a.invk[p * a.N + i + a.off];
@@ -648,7 +648,7 @@ __global__ __launch_bounds__(256) void k_siglip_tabs(StatsArgs a) {
             // softplus(-l) and sigmoid(-l), both overflow-free
             const float t = expf(-fabsf(l));
             lpos = fmaxf(-l, 0.f) + log1pf(t);
-            const float sig_neg = (l >= 0.f) ? t / (1.f + t) : 1.f / (1.f + t);
+            sig_neg = (l >= 0.f) ? t / (1.f + t) : 1.f / (1.f + t);
             a.qC[p * a.R + i] = a.sgn * a.wnorm[p] * iq / a.invq[(P - 1) * a.R + i];
             a.diagA[p * a.R + i] = -a.wnorm[p] * a.scale * sig_neg * a.inv_den * iq * ik;
             if (a.pos_logit_out) a.pos_logit_out[p * a.R + i] = l;
@@ -658,6 +658,8 @@ __global__ __launch_bounds__(256) void k_siglip_tabs(StatsArgs a) {
             a.kC[p * a.N + j] = a.sgn * a.wnorm[p] * ik / a.invk[(P - 1) * a.N + j];
         }
         block_sum_write(lpos, red, &a.lossparts[((int64_t)a.slot0 + blockIdx.x) * P + p]);
+        // the positive cell's residual is sigma(l) - 1 = -sigma(-l)
+        if (a.biasparts) block_sum_write(-sig_neg, red, &a.biasparts[((int64_t)a.slot0 + blockIdx.x) * P + p]);
     }
 }
 
@@ -774,7 +776,7 @@ __device__ __forceinline__ void bwd_finish(const BwdArgs &a, const f32x16 (&dacc
     lds_barrier();
     if (w == 0) {
         const int o = o0 + lane;
-        float dg = 0.f, rd = 0.f;
+        float dg = 0.f, rd = 0.f, ts = 0.f;
         if (o < NO) {
             const int64_t ipos = o + a.pos_shift;
             const bool has_pos = ipos >= 0 && ipos < a.R;
@@ -786,11 +788,14 @@ __device__ __forceinline__ void bwd_finish(const BwdArgs &a, const f32x16 (&dacc
                 const float dA = has_pos ? a.diagA[p * a.R + ipos] : 0.f;
                 const float dS = has_pos ? a.posdot[p * a.R + ipos] : 0.f;
                 const float ix = a.invx[p * a.NO + o];
+                const float T = fmaf(dA, dS, c * g);  // (w_p / W) s sum_j g_oj cos_oj
                 dg += dA;
-                rd += ix * ix * fmaf(dA, dS, c * g);
+                rd += ix * ix * T;
+                ts += T;
                 fin[p * BO + lane] = dg;
                 fin[(NP + p) * BO + lane] = rd;
             }
+            if (a.tsum) a.tsum[o] = ts;
         }
     }
     lds_barrier();
@@ -968,9 +973,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         for (int j = 0; j < NQ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) dacc[ob][j][r] = 0.f;
-    float Cacc[NP], Lacc[NP];
+    float Cacc[NP], Lacc[NP], Bacc[NP];  // radial sums; sigmoid form: loss and sum of sigma(l)
 #pragma unroll
-    for (int p = 0; p < NP; ++p) Cacc[p] = Lacc[p] = 0.f;
+    for (int p = 0; p < NP; ++p) Cacc[p] = Lacc[p] = Bacc[p] = 0.f;
 
     // ---- Two-phase software pipeline.  Epilogue E of a block = one unit per prefix
     // (lane = outer row, inner rows 4 w .. 4 w + 3, four independent chains), widest
@@ -1063,7 +1068,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
                         // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
                         const float corr = (tt - (wq - 1.f)) * rr * kLog2e;
                         const float lt = fmaxf(uu, 0.f) + __builtin_amdgcn_logf(wq) + corr;
-                        Lacc[p] += (!MK || __builtin_amdgcn_inverse_ballot_w64(mk[t])) ? lt : 0.f;
+                        const bool in = !MK || __builtin_amdgcn_inverse_ballot_w64(mk[t]);
+                        Lacc[p] += in ? lt : 0.f;
+                        Bacc[p] += in ? (uu >= 0.f ? rr : tt * rr) : 0.f;  // sigma(l), without the scaling
                     }
                 }
             }
@@ -1292,14 +1299,18 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     }
     // radial sums and sigmoid loss: add the four waves' inner rows (slots are free now)
     lds_barrier();
-    float *red = &Sl[0][0];  // [4][NP][BO] then [4][NP]
+    float *red = &Sl[0][0];  // [4][NP][BO], then [4][NP] twice
 #pragma unroll
     for (int p = 0; p < NP; ++p) red[(w * NP + p) * BO + lane] = Cacc[p];
     if (SIG && a.want_loss) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const float v = wave_sum(Lacc[p]);
-            if (lane == 0) red[4 * NP * BO + w * NP + p] = v;
+            const float u = wave_sum(Bacc[p]);
+            if (lane == 0) {
+                red[4 * NP * BO + w * NP + p] = v;
+                red[4 * NP * BO + 4 * NP + w * NP + p] = u;
+            }
         }
     }
     lds_barrier();
@@ -1314,7 +1325,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     if (SIG && a.want_loss && tid < NP) {
         const float *lr = red + 4 * NP * BO;
         const float v = ((lr[0 * NP + tid] + lr[1 * NP + tid]) + lr[2 * NP + tid]) + lr[3 * NP + tid];
-        a.lossparts[((int64_t)a.loss_slot0 + split * gridDim.x + blockIdx.x) * NP + tid] = v * kLn2;
+        const int64_t slot = (int64_t)a.loss_slot0 + split * gridDim.x + blockIdx.x;
+        a.lossparts[slot * NP + tid] = v * kLn2;
+        if (a.biasparts) {
+            const float *br = lr + 4 * NP;
+            a.biasparts[slot * NP + tid] = ((br[0 * NP + tid] + br[1 * NP + tid]) + br[2 * NP + tid]) + br[3 * NP + tid];
+        }
     }
 }
 
@@ -1354,7 +1370,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs a) {
     const bool has_pos = ipos >= 0 && ipos < a.R;
     const int64_t ypos = o + a.diag_shift;  // positive's row in Y
     if (threadIdx.x == 0) {
-        float dg = 0.f, rd = 0.f;
+        float dg = 0.f, rd = 0.f, ts = 0.f;
         for (int p = P - 1; p >= 0; --p) {
             float C = 0.f;
             for (int s = 0; s < a.nsplit; ++s) C += a.Cpart[((int64_t)s * P + p) * a.NO + o];
@@ -1364,11 +1380,15 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs a) {
                 dS = a.posdot[p * a.R + ipos];
             }
             const float ix = a.invx[p * a.NO + o];
+            // radial coefficient of prefix p: (w_p / W) s sum_j g_oj cos_oj, the positive cell included
+            const float T = fmaf(dA, dS, C * a.gam[o]);
             dg += dA;
-            rd += ix * ix * fmaf(dA, dS, C * a.gam[o]);
+            rd += ix * ix * T;
+            ts += T;
             DG[p] = dg;
             RD[p] = rd;
         }
+        if (a.tsum) a.tsum[o] = ts;
     }
     __syncthreads();
     const int D = a.D;
@@ -1415,6 +1435,39 @@ __global__ __launch_bounds__(256) void k_loss(LossArgs a) {
             if (a.prefix_losses_out) a.prefix_losses_out[p] = (float)lp[p];
         }
         *a.loss_out = (float)tot;
+    }
+    // dL/dscale = (1/s) sum over the rows of one backward pass of sum_p (w_p / W) s sum_j g cos
+    if (a.dscale_out) {
+        double v = 0.0;
+        for (int64_t o = threadIdx.x; o < a.ntsum; o += 256) v += (double)a.tsum[o];
+        __syncthreads();
+        red[threadIdx.x] = v;
+        __syncthreads();
+        for (int h = 128; h >= 1; h >>= 1) {
+            if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) *a.dscale_out = (float)(red[0] * (double)a.inv_scale);
+        __syncthreads();
+    }
+    // dL/dbias = sum_p (w_p / W) sum_ij g_ij: zero for a softmax (a common shift of a row's or a
+    // column's logits cancels); for the sigmoid form (sum of sigma(l) - number of positives) / N
+    if (a.dbias_out) {
+        double tot = 0.0;
+        for (int p = 0; p < P && a.biasparts; ++p) {
+            double v = 0.0;
+            for (int64_t s = threadIdx.x; s < a.nslots; s += 256) v += (double)a.biasparts[s * P + p];
+            __syncthreads();
+            red[threadIdx.x] = v;
+            __syncthreads();
+            for (int h = 128; h >= 1; h >>= 1) {
+                if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+                __syncthreads();
+            }
+            tot += (double)a.wnorm[p] * red[0] * a.norm;
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) *a.dbias_out = (float)tot;
     }
 }
 

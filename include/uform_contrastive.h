@@ -113,6 +113,16 @@ typedef struct {
     void *workspace;             /* device, 256-byte aligned; NULL = library workspace          */
     size_t workspace_bytes;      /* >= uform_contrastive_workspace_bytes(...) when given        */
     uint32_t flags;              /* UFORM_CONTRASTIVE_* bits below (accumulate, diagnostics)    */
+    /* Gradients of the loss with respect to the logit scale s and bias b (the
+     * learned temperature and bias of "Scaling-Up Contrastive Learning over
+     * NVLink Multicast", section "One Set or Two"): dL/ds = sum_p (w_p/W)
+     * sum_ij g^p_ij cos^p_ij and dL/db = sum_p (w_p/W) sum_ij g^p_ij, g^p =
+     * dL^p/dl^p.  dL/db is 0 for the softmax kinds (a common shift of a
+     * softmax's logits cancels).  Device, 1 float each, overwritten (also with
+     * UFORM_CONTRASTIVE_ACCUMULATE); they come from a gradient pass, so a call
+     * that sets either must give dq or dk (else invalid-argument).  Nullable. */
+    float *dscale_out;
+    float *dbias_out;
 } uform_contrastive_options_t;
 
 #define UFORM_CONTRASTIVE_ACCUMULATE 1u

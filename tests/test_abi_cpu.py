@@ -93,6 +93,16 @@ def test_option_checks():
     opt.prefix_weights = None
     opt.workspace = 0x1000010
     assert _call(opt=opt) == 1
+    opt.workspace = None
+    # dL/dscale and dL/dbias come from a gradient pass and need an aligned float
+    opt.dscale_out = 0x60000
+    assert _call(dq=0, dk=0, opt=opt) == 1
+    assert "dq or dk" in binding.last_error()
+    opt.dscale_out = 0x60002
+    assert _call(opt=opt) == 1
+    opt.dscale_out = None
+    opt.dbias_out = 0x60000
+    assert _call(dq=0, dk=0, kind=1, opt=opt) == 1
 
 
 def test_workspace_bytes():

@@ -211,3 +211,27 @@ def test_forward_any_prefixes_loss_only(kind):
     assert np.abs(ex["row_lse"].cpu().numpy() - ref["row_lse"]).max() <= 1e-3
     assert np.abs(ex["pos_logit"].cpu().numpy() - ref["pos_logit"]).max() <= 1e-3
     assert np.abs(ex["col_lse"].cpu().numpy() - ref["col_lse"]).max() <= 1e-3
+
+
+# dL/dscale and dL/dbias: from the first gradient pass (dq, else dk), with the split-partial
+# finalize and with the in-place finish; dL/db is exactly zero for the softmax kinds
+@pytest.mark.parametrize("kind,one_split,want_dq", [
+    (INFONCE, False, True), (INFONCE, True, True), (SIGLIP, False, True), (SIGLIP, True, False),
+    (INFONCE_ROWS, False, True), (INFONCE_ROWS, True, False)])
+def test_scale_and_bias_gradients(kind, one_split, want_dq):
+    R, N, off = (200, 200, 0) if kind != INFONCE_ROWS else (96, 352, 128)
+    qb, kb = make_inputs(R, N, 1024, noise=0.8, seed=91 + kind, row_offset=off)
+    s, b = (10.0, -6.0) if kind == SIGLIP else (14.0, 0.0)
+    print(f"[case] scale-bias kind={kind} one_split={one_split} want_dq={want_dq}", flush=True)
+    q, k = to_dev(qb), to_dev(kb)
+    _, _, _, ex = binding.fwd_bwd(q, k, LADDER, s, b, kind, weights=(1, 1, 1, 1, 2), row_offset=off,
+                                  want_dq=want_dq, extras=True, one_split=one_split)
+    torch.cuda.synchronize()
+    ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), LADDER, s, b, kind,
+                              weights=(1, 1, 1, 1, 2), row_offset=off)
+    got_s, got_b = ex["dscale"].item(), ex["dbias"].item()
+    assert got_s == pytest.approx(ref["dscale"], rel=1e-3, abs=1e-6), (got_s, ref["dscale"])
+    if kind == SIGLIP:
+        assert got_b == pytest.approx(ref["dbias"], rel=1e-3, abs=1e-6), (got_b, ref["dbias"])
+    else:
+        assert got_b == 0.0 and abs(ref["dbias"]) < 1e-12
