@@ -43,7 +43,8 @@ import numpy as np
 INFONCE = 0
 SIGLIP = 1
 INFONCE_ROWS = 2
-KIND_NAMES = {INFONCE: "infonce", SIGLIP: "siglip", INFONCE_ROWS: "infonce_rows"}
+ONESET_SIGLIP = 3
+KIND_NAMES = {INFONCE: "infonce", SIGLIP: "siglip", INFONCE_ROWS: "infonce_rows", ONESET_SIGLIP: "oneset_siglip"}
 
 
 # --------------------------------------------------------------------------
@@ -84,8 +85,15 @@ def sigmoid(x: np.ndarray) -> np.ndarray:
 # the loss
 # --------------------------------------------------------------------------
 
-def _positive_mask(rows: np.ndarray, cols: np.ndarray, row_offset: int) -> np.ndarray:
-    """E[a, b] = 1 where column cols[b] is the positive of row rows[a]."""
+def _positive_mask(rows: np.ndarray, cols: np.ndarray, row_offset: int, oneset: bool = False) -> np.ndarray:
+    """E[a, b] = 1 where column cols[b] is the positive of row rows[a]: key row_offset + row for
+    the two-set kinds; for the one-set form, the other row of the row's pair, (row_offset + row) xor 1."""
+    g = rows[:, None] + row_offset
+    return (cols[None, :] == (g ^ 1 if oneset else g)).astype(np.float64)
+
+
+def _self_mask(rows: np.ndarray, cols: np.ndarray, row_offset: int) -> np.ndarray:
+    """1 where column cols[b] is row rows[a] itself (one-set form: the cell is not scored)."""
     return (cols[None, :] == (rows[:, None] + row_offset)).astype(np.float64)
 
 
@@ -102,7 +110,16 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
     widths P_1 < ... < P_P <= D, ``weights`` their weights (default all 1).
     ``kind`` is INFONCE (symmetric CLIP, needs R == N and row_offset == 0),
     INFONCE_ROWS (row cross-entropy of the R local rows against all N keys,
-    plus the column partial log-sum-exp over the local rows), or SIGLIP.
+    plus the column partial log-sum-exp over the local rows), SIGLIP, or
+    ONESET_SIGLIP: one set scored against itself ("Scaling-Up Contrastive
+    Learning over NVLink Multicast", section "One Set or Two": an image and its
+    caption are two rows of the set marked as a positive pair; mirrored cells
+    carry the same labels, and the owner of a row differentiates both).  Then
+    ``k`` is the whole set [N, D] (N even; rows 2m and 2m + 1 are a pair), ``q``
+    its rows row_offset .. row_offset + R - 1, the loss is this share's part
+    (1/N) sum over local rows i and every j other than i itself of
+    softplus(-z_ij l_ij), and ``dq`` is the gradient of the whole set's loss
+    with respect to those rows (both mirrored cells), with no ``dk``.
 
     Returns a dict with ``loss`` (float), ``prefix_losses`` [P], ``row_lse``
     [P, R] (log-sum-exp of each row's logits; InfoNCE kinds), ``pos_logit``
@@ -129,6 +146,9 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
         raise ValueError("need 1 <= R <= N and row_offset + R <= N")
     if kind == INFONCE and (R != N or row_offset != 0):
         raise ValueError("symmetric InfoNCE needs R == N and row_offset == 0")
+    oneset = kind == ONESET_SIGLIP
+    if oneset and (N % 2 != 0 or not np.array_equal(q, k[row_offset:row_offset + R])):
+        raise ValueError("the one-set form needs an even set k and q = k[row_offset:row_offset + R]")
     w = np.ones(P) if weights is None else np.asarray(weights, dtype=np.float64)
     W = float(np.sum(w))
     s = float(scale)
@@ -147,7 +167,7 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
     col_lse = np.zeros((P, N))
     pos_logit = np.zeros((P, R))
     dq = np.zeros((R, D)) if grads else None
-    dk = np.zeros((N, D)) if grads else None
+    dk = np.zeros((N, D)) if grads and not oneset else None
     dscale = 0.0
     dbias = 0.0
 
@@ -163,7 +183,13 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
                 rows = all_rows[r0:r1]
                 pos = logits[rows - r0, pos_col[r0:r1]]
                 out = {"pos": pos}
-                if kind == SIGLIP:
+                if oneset:
+                    pos = logits[rows - r0, pos_col[r0:r1] ^ 1]
+                    out["pos"] = pos
+                    z = 2.0 * _positive_mask(rows, all_cols, row_offset, True) - 1.0
+                    keep = 1.0 - _self_mask(rows, all_cols, row_offset)
+                    out["siglip_rows"] = np.sum(keep * softplus(-z * logits), axis=1)
+                elif kind == SIGLIP:
                     z = 2.0 * _positive_mask(rows, all_cols, row_offset) - 1.0
                     out["siglip_rows"] = np.sum(softplus(-z * logits), axis=1)
                 else:
@@ -176,7 +202,7 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
             parts = list(pool.map(forward_rows, row_blocks))
             for (r0, r1), part in zip(row_blocks, parts):
                 pos_logit[p, r0:r1] = part["pos"]
-            if kind == SIGLIP:
+            if kind in (SIGLIP, ONESET_SIGLIP):
                 siglip_rows = np.concatenate([part["siglip_rows"] for part in parts])
                 prefix_losses[p] = np.sum(siglip_rows) / N
             else:
@@ -202,6 +228,9 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
 
             # ---- residuals g_ij = dL^p / dl_ij on a slice of the grid
             def residual(logits, rows, cols):
+                if oneset:
+                    E = _positive_mask(rows, cols, row_offset, True)
+                    return (sigmoid(logits) - E) * (1.0 - _self_mask(rows, cols, row_offset)) / N
                 E = _positive_mask(rows, cols, row_offset)
                 if kind == SIGLIP:
                     return (sigmoid(logits) - E) / N
@@ -222,10 +251,14 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
                 radial = np.sum(u * qh[r0:r1], axis=1)
                 return (u - radial[:, None] * qh[r0:r1]) / qnorm[r0:r1, None], np.sum(g * cos), np.sum(g)
 
+            # one set: cell (j, i) has the residual and the derivative of cell (i, j)
+            mirror = 2.0 if oneset else 1.0
             for (r0, r1), (part, gc, gs) in zip(row_blocks, pool.map(grad_rows, row_blocks)):
-                dq[r0:r1, :width] += (w[p] / W) * part
+                dq[r0:r1, :width] += mirror * (w[p] / W) * part
                 dscale += (w[p] / W) * gc
                 dbias += (w[p] / W) * gs
+            if oneset:
+                continue
 
             # ---- dk: v_j = sum_i g_ij * s * qh_i, then through the normalisation of k_j
             def grad_cols(cb):
@@ -244,7 +277,7 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
         "prefix_losses": prefix_losses,
         "pos_logit": pos_logit,
     }
-    if kind != SIGLIP:
+    if kind in (INFONCE, INFONCE_ROWS):
         result["row_lse"] = row_lse
         result["col_lse"] = col_lse
     if grads:

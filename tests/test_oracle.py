@@ -17,7 +17,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import INFONCE, INFONCE_ROWS, SIGLIP, contrastive_fwd_bwd
+from oracle import INFONCE, INFONCE_ROWS, ONESET_SIGLIP, SIGLIP, contrastive_fwd_bwd
 
 torch = pytest.importorskip("torch")
 F = torch.nn.functional
@@ -295,3 +295,72 @@ def test_blocking_does_not_change_results(rng):
     assert c["loss"] == pytest.approx(a["loss"], rel=1e-14)
     np.testing.assert_allclose(c["dq"], a["dq"], rtol=1e-12, atol=1e-16)
     np.testing.assert_allclose(c["dk"], a["dk"], rtol=1e-12, atol=1e-16)
+
+
+# ----------------------------------------------------------------------------- one-set sigmoid form
+
+def _oneset(x, prefixes, s, b, R=None, off=0, weights=None, grads=True):
+    R = x.shape[0] if R is None else R
+    return contrastive_fwd_bwd(x[off:off + R], x, prefixes, s, b, ONESET_SIGLIP, weights=weights, row_offset=off,
+                               grads=grads)
+
+
+def test_oneset_identical_rows_closed_form():
+    # every cosine is 1, so every scored cell has l = s + b: one positive and N - 2 negatives per row
+    N, D, s, b = 10, 64, 6.0, -2.0
+    x = np.tile(np.linspace(-1.0, 1.0, D), (N, 1))
+    out = _oneset(x, [32, 64], s, b, grads=False)
+    want = (N * _softplus(-(s + b)) + N * (N - 2) * _softplus(s + b)) / N
+    assert out["loss"] == pytest.approx(want, rel=1e-12)
+
+
+def test_oneset_matches_torch_autograd_of_the_whole_set():
+    rng = np.random.default_rng(5)
+    N, D, prefixes, weights, s, b = 10, 48, [16, 48], [1, 2], 7.0, -3.0
+    x = rng.standard_normal((N, D))
+    x[1::2] = x[0::2] + 0.6 * rng.standard_normal((N // 2, D))
+    out = _oneset(x, prefixes, s, b, weights=weights)
+    xt = torch.tensor(x, requires_grad=True)
+    st = torch.tensor(s, dtype=torch.float64, requires_grad=True)
+    bt = torch.tensor(b, dtype=torch.float64, requires_grad=True)
+    z = -torch.ones(N, N, dtype=torch.float64)
+    z[torch.arange(N), torch.arange(N) ^ 1] = 1.0
+    keep = 1.0 - torch.eye(N, dtype=torch.float64)
+    total = 0.0
+    for p, width in enumerate(prefixes):
+        xh = F.normalize(xt[:, :width], dim=1)
+        logits = st * xh @ xh.T + bt
+        total = total + weights[p] * (-(keep * F.logsigmoid(z * logits)).sum() / N)
+    total = total / sum(weights)
+    total.backward()
+    assert out["loss"] == pytest.approx(total.item(), rel=1e-12)
+    np.testing.assert_allclose(out["dq"], xt.grad.numpy(), rtol=1e-9, atol=1e-13)
+    assert out["dscale"] == pytest.approx(st.grad.item(), rel=1e-9)
+    assert out["dbias"] == pytest.approx(bt.grad.item(), rel=1e-9)
+    assert out["dk"] is None
+
+
+def test_oneset_central_differences_of_the_set():
+    rng = np.random.default_rng(6)
+    N, D, prefixes, s, b = 8, 64, [32, 64], 5.0, -1.5
+    x = rng.standard_normal((N, D))
+    out = _oneset(x, prefixes, s, b)
+    for i in range(N):
+        for d in rng.choice(D, 6, replace=False):
+            h = 1e-6
+            xp, xm = x.copy(), x.copy()
+            xp[i, d] += h
+            xm[i, d] -= h
+            fd = (_oneset(xp, prefixes, s, b, grads=False)["loss"] - _oneset(xm, prefixes, s, b, grads=False)["loss"]) / (2 * h)
+            assert out["dq"][i, d] == pytest.approx(fd, rel=1e-6, abs=1e-9)
+
+
+def test_oneset_shards_rebuild_the_set():
+    rng = np.random.default_rng(7)
+    N, D, prefixes, s, b = 12, 64, [32, 64], 9.0, -4.0
+    x = rng.standard_normal((N, D))
+    full = _oneset(x, prefixes, s, b)
+    parts = [_oneset(x, prefixes, s, b, R=4, off=o) for o in (0, 4, 8)]
+    assert sum(p["loss"] for p in parts) == pytest.approx(full["loss"], rel=1e-12)
+    np.testing.assert_allclose(np.concatenate([p["dq"] for p in parts]), full["dq"], rtol=1e-10, atol=1e-14)
+    assert sum(p["dscale"] for p in parts) == pytest.approx(full["dscale"], rel=1e-10)
