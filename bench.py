@@ -66,7 +66,8 @@ def main():
     import torch
 
     from contrastive_embedding_loss_amd import binding
-    from contrastive_embedding_loss_amd.inputs import WORKLOADS, bf16_bits_to_f32, make_inputs, workload_inputs
+    from contrastive_embedding_loss_amd.inputs import (ONESET_SIGLIP, WORKLOADS, bf16_bits_to_f32, make_inputs,
+                                                       workload_inputs)
 
     dev = torch.device("cuda:0")
     if args.copy_calibration:
@@ -82,19 +83,23 @@ def main():
     w = WORKLOADS[args.workload]
     t0 = time.time()
     qb, kb = workload_inputs(w)
-    q = torch.from_numpy(bf16_bits_to_f32(qb)).to(dev).to(torch.bfloat16)
+    oneset = w.kind == ONESET_SIGLIP
     k = torch.from_numpy(bf16_bits_to_f32(kb)).to(dev).to(torch.bfloat16)
+    if oneset:  # the one-set form scores the set's own rows: q is a view of k
+        q = k[w.row_offset:w.row_offset + w.R]
+    else:
+        q = torch.from_numpy(bf16_bits_to_f32(qb)).to(dev).to(torch.bfloat16)
     print(f"[bench] inputs {w.name} R={w.R} N={w.N} D={w.D} ready in {time.time() - t0:.1f}s", file=sys.stderr,
           flush=True)
     R, N, D, P = w.R, w.N, w.D, len(w.prefixes)
     f32 = dict(dtype=torch.float32, device=dev)
     loss = torch.empty(1, **f32)
     dq = torch.empty(R, D, **f32)
-    dk = torch.empty(N, D, **f32)
+    dk = None if oneset else torch.empty(N, D, **f32)
 
     def step(profile=False):
         return binding.fwd_bwd(q, k, w.prefixes, w.scale, w.bias, w.kind, weights=w.weights,
-                               row_offset=w.row_offset, dq=dq, dk=dk, profile=profile)
+                               row_offset=w.row_offset, dq=dq, dk=dk, want_dk=not oneset, profile=profile)
 
     for _ in range(args.warmup):
         step()
@@ -112,7 +117,9 @@ def main():
     kern = binding.profile()
     ms_per_step = 1e3 * elapsed / args.steps
 
-    flops = 8.0 * R * N * D
+    # two-set kinds: forward 2RND + one logit recompute 2RND + dQ 2RND + dK 2RND; the one-set form
+    # has the share's logits 2RND and dX 2RND, in one backward pass
+    flops = (4.0 if oneset else 8.0) * R * N * D
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     pair_scores = float(R) * N * P / (ms_per_step * 1e-3)
     kern_per_step = {n: t / args.steps for n, t in kern.items()}
@@ -124,9 +131,9 @@ def main():
     # Algorithmic MFMA work credited to one launch: 3 R N D = its gradient contraction 2 R N D
     # plus half of the single logit recompute 2 R N D that the step's count includes (each
     # launch actually executes a full recompute, 4 R N D in all; the extra is not credited).
-    launches = 2
+    launches = 1 if oneset else 2
     bwd_ms = kern_per_step.get("k_bwd", float("nan")) / launches
-    bwd_tflops = 3.0 * R * N * D / (bwd_ms * 1e-3) / 1e12
+    bwd_tflops = (4.0 if oneset else 3.0) * R * N * D / (bwd_ms * 1e-3) / 1e12
     roofline = {"kernel": "k_bwd", "bound": "mfma", "achieved": round(bwd_tflops, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(w.name), "avg_launch_ms": round(bwd_ms, 4),
@@ -138,6 +145,8 @@ def main():
 
         n_s = min(args.cpu_sample, R)
         qs, ks = make_inputs(n_s, n_s, D, w.recipe, w.noise, w.seed, w.extra.get("centroids", 256))
+        if oneset:
+            qs = ks  # the one-set sample scores its whole set
         cores = len(os.sched_getaffinity(0))
         print(f"[bench] oracle sample {n_s}x{n_s} on {cores} cores", file=sys.stderr, flush=True)
         kind = w.kind
@@ -145,10 +154,11 @@ def main():
         contrastive_fwd_bwd(bf16_bits_to_f64(qs), bf16_bits_to_f64(ks), w.prefixes, w.scale, w.bias, kind,
                             weights=w.weights, threads=cores)
         tc = time.perf_counter() - t1
-        cpu = {"value": round(8.0 * n_s * n_s * D / tc / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+        fl = 4.0 if oneset else 8.0
+        cpu = {"value": round(fl * n_s * n_s * D / tc / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
                "kind": "oracle",
                "sample": f"FP64 oracle fwd+bwd on a {n_s}x{n_s} batch of the same recipe and prefixes "
-                         f"({tc:.1f} s), rate = 8*R*N*D/t"}
+                         f"({tc:.1f} s), rate = {fl:.0f}*R*N*D/t"}
 
     out = {
         "metric": "fwd+bwd TFLOP/s & pair-scores/s at N=32768, 5 prefixes; % BF16 MFMA peak",
@@ -164,7 +174,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "R": R, "N": N, "D": D, "prefixes": list(w.prefixes),
-                   "kind": ["infonce", "siglip", "infonce_rows"][w.kind], "scale": w.scale, "bias": w.bias,
+                   "kind": ["infonce", "siglip", "infonce_rows", "oneset_siglip"][w.kind], "scale": w.scale,
+                   "bias": w.bias,
                    "weights": list(w.weights) if w.weights else None, "recipe": w.recipe},
         "pair_scores_per_s": pair_scores,
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),

@@ -16,6 +16,7 @@ import torch  # imported before the library so both share one HIP runtime
 INFONCE = 0
 SIGLIP = 1
 INFONCE_ROWS = 2
+ONESET_SIGLIP = 3  # one set scored against itself: q = k[row_offset:row_offset + R], no dk
 ACCUMULATE = 1
 PROFILE = 2
 ONE_SPLIT = 4
@@ -153,6 +154,8 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
     loss = torch.empty(1, **f32)
     if want_dq and dq is None:
         dq = torch.zeros(R, D, **f32) if accumulate else torch.empty(R, D, **f32)
+    if kind == ONESET_SIGLIP:
+        want_dk = False  # the one-set form's only gradient is dq
     if want_dk and dk is None:
         dk = torch.zeros(N, D, **f32) if accumulate else torch.empty(N, D, **f32)
     if not want_dq:
@@ -168,7 +171,7 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
         opt.prefix_weights = ctypes.cast(wbuf, ctypes.POINTER(ctypes.c_float))
     ex = None
     if extras:
-        softmax = kind != SIGLIP
+        softmax = kind not in (SIGLIP, ONESET_SIGLIP)
         ex = {"prefix_losses": torch.empty(P, **f32), "pos_logit": torch.empty(P, R, **f32)}
         if softmax:
             ex["row_lse"] = torch.empty(P, R, **f32)

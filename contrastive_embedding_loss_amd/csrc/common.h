@@ -21,6 +21,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kInfonce = 0;
 constexpr int kSiglip = 1;
 constexpr int kRows = 2;
+constexpr int kOneset = 3;  // one-set sigmoid form: computed as the sigmoid kind with pxor = 1, mirror = 2
 
 __host__ __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -35,6 +36,7 @@ struct Prefixes {
 struct PrepArgs {
     const u16 *q, *k;
     int64_t R, N, off;
+    int pxor;  // positive of local row i: key (off + i) ^ pxor (1: the one-set form's pairs)
     int D;
     Prefixes pf;
     float a_scale, gam_scale;
@@ -44,6 +46,8 @@ struct PrepArgs {
 // Statistics / coefficient-table kernels.  "q" tables are [P][R], "k" tables [P][N].
 struct StatsArgs {
     int64_t R, N, off, nJt, nIt;
+    int pxor;      // as in PrepArgs
+    float mirror;  // 2 for the one-set form (a row's gradient through both mirrored cells), else 1
     Prefixes pf;
     int kind;
     float scale, bias, cshift, lse_offset, inv_den, sgn;
@@ -77,7 +81,8 @@ struct BwdArgs {
     const float *gterm;           // [P] device global term per prefix, or nullptr to use gterm_val
     float gterm_val[kMaxP];
     float wnorm[kMaxP];
-    int64_t diag_shift;           // positive of outer o is inner o + diag_shift
+    int64_t diag_shift;           // positive of outer o is inner (o + diag_shift) ^ pxor
+    int pxor;                     // 1: one-set form, where inner o + diag_shift is o itself and is not scored
     int64_t blocks_per_split;
     int do_update, want_loss;
     float *part;   // [nsplit][NO][D]
@@ -102,6 +107,7 @@ struct FinArgs {
     Prefixes pf;
     const float *part, *Cpart, *diagA, *posdot, *invx, *gam;
     int64_t nsplit, diag_shift, pos_shift;
+    int pxor;  // positive's row in Y: (o + diag_shift) ^ pxor
     int accumulate;
     float *out;
     float *tsum;  // nullable: [NO] per row, sum over p of its radial coefficient (dL/dscale)

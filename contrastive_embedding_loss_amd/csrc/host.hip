@@ -164,9 +164,16 @@ uform_status_t validate(const void *q, const void *k, int64_t R, int64_t N, int6
         return fail(uform_status_invalid_argument_k, "dq and dk must be 16-byte aligned");
     if (R < 1 || N < 1 || D < 1) return fail(uform_status_invalid_argument_k, "R, N and D must be positive");
     if (R > N) return fail(uform_status_invalid_argument_k, "R must not exceed N");
-    if (kind != kInfonce && kind != kSiglip && kind != kRows) return fail(uform_status_invalid_argument_k, "unknown kind");
+    if (kind != kInfonce && kind != kSiglip && kind != kRows && kind != kOneset)
+        return fail(uform_status_invalid_argument_k, "unknown kind");
     const int64_t off = opt ? opt->row_offset : 0;
     if (off < 0 || off + R > N) return fail(uform_status_invalid_argument_k, "need 0 <= row_offset and row_offset + R <= N");
+    if (kind == kOneset) {
+        if (N % 2 != 0) return fail(uform_status_invalid_argument_k, "the one-set form needs an even set (rows 2m, 2m + 1 pair up)");
+        if ((const char *)q != (const char *)k + off * D * 2)
+            return fail(uform_status_invalid_argument_k, "the one-set form needs q = k + row_offset * D (its rows of the set)");
+        if (dk) return fail(uform_status_invalid_argument_k, "the one-set form has one gradient, dq (pass dk = NULL)");
+    }
     if (kind == kInfonce && (R != N || off != 0))
         return fail(uform_status_invalid_argument_k, "symmetric InfoNCE needs R == N and row_offset == 0");
     if (!prefixes) return fail(uform_status_invalid_argument_k, "prefixes must be a host array");
@@ -194,9 +201,10 @@ uform_status_t validate(const void *q, const void *k, int64_t R, int64_t N, int6
             return fail(uform_status_invalid_argument_k, "dscale_out and dbias_out must be 4-byte aligned");
     }
     if (D % 64 != 0 || D > kMaxD) return fail(uform_status_unsupported_k, "D must be a multiple of 64 and at most 1024");
-    if (kind != kSiglip && std::fabs(scale) > UFORM_CONTRASTIVE_MAX_SOFTMAX_SCALE)
+    const bool sigmoid_kind = kind == kSiglip || kind == kOneset;
+    if (!sigmoid_kind && std::fabs(scale) > UFORM_CONTRASTIVE_MAX_SOFTMAX_SCALE)
         return fail(uform_status_unsupported_k, "softmax kinds support |scale| <= 40");
-    if ((dq || dk || kind == kSiglip) && !bwd_mask_supported(ladder_mask(prefixes, n_prefixes)))
+    if ((dq || dk || sigmoid_kind) && !bwd_mask_supported(ladder_mask(prefixes, n_prefixes)))
         return fail(uform_status_unsupported_k, "this prefix ladder has no compiled backward kernel");
     if (N > (int64_t)1 << 31) return fail(uform_status_unsupported_k, "N must be below 2^31");
     return uform_status_success_k;
@@ -287,9 +295,15 @@ struct ProfScope {
 #define LAUNCH(expr) LAUNCH_NAMED(#expr, expr)
 
 uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t D, const int32_t *prefixes,
-                   int32_t P, float scale, float bias, int32_t kind, float *loss_out, float *dq, float *dk,
+                   int32_t P, float scale, float bias, int32_t kind_in, float *loss_out, float *dq, float *dk,
                    hipStream_t s, const uform_contrastive_options_t *opt) {
     const u16 *q = (const u16 *)q_, *k = (const u16 *)k_;
+    // the one-set form runs as the sigmoid kind whose positive of row g is g ^ 1, whose cell (g, g)
+    // is not scored, and whose row gradients count both mirrored cells
+    const bool oneset = kind_in == kOneset;
+    const int32_t kind = oneset ? kSiglip : kind_in;
+    const int pxor = oneset ? 1 : 0;
+    const float mirror = oneset ? 2.0f : 1.0f;
     const int64_t off = opt ? opt->row_offset : 0;
     const bool softmax = kind != kSiglip;
     Plan pl = make_plan(R, N, D, prefixes, P, kind, off, dq != nullptr, dk != nullptr,
@@ -335,7 +349,8 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     pa.D = Di;
     pa.pf = pf;
     pa.a_scale = scale * kLog2e;
-    pa.gam_scale = (float)(abs_s / den);
+    pa.gam_scale = (float)(mirror * abs_s / den);
+    pa.pxor = pxor;
     pa.invq = invq;
     pa.invk = invk;
     pa.qA = qA;
@@ -357,6 +372,8 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     sa.R = R;
     sa.N = N;
     sa.off = off;
+    sa.pxor = pxor;
+    sa.mirror = mirror;
     sa.nJt = 2 * pl.nJt;  // partials per row: two per column tile
     sa.nIt = 2 * pl.nIt;
     sa.pf = pf;
@@ -442,6 +459,7 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
             ba.gterm = gmax + 2 * P;
         }
         ba.diag_shift = rowpass ? off : -off;
+        ba.pxor = pxor;
         ba.blocks_per_split = rowpass ? pl.bps_row : pl.bps_col;
         ba.do_update = out != nullptr;
         ba.want_loss = (!softmax && rowpass) ? 1 : 0;
@@ -484,6 +502,7 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
             fa.gam = rowpass ? gamq : gamk;
             fa.nsplit = nsplit;
             fa.diag_shift = ba.diag_shift;
+            fa.pxor = pxor;
             fa.pos_shift = rowpass ? 0 : -off;
             fa.accumulate = (opt && (opt->flags & UFORM_CONTRASTIVE_ACCUMULATE)) ? 1 : 0;
             fa.out = out;
@@ -511,7 +530,7 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     la.prefix_losses_out = opt ? opt->prefix_losses_out : nullptr;
     la.tsum = tsum;
     la.ntsum = dq ? R : N;
-    la.inv_scale = 1.0f / scale;
+    la.inv_scale = 1.0f / (mirror * scale);  // the radial sums count both mirrored cells; dL/ds counts each once
     la.biasparts = biasparts;
     la.dscale_out = dscale_out;
     la.dbias_out = dbias_out;
@@ -580,9 +599,10 @@ uform_status_t uform_contrastive_fwd_bwd(const void *q, const void *k, int64_t R
 size_t uform_contrastive_workspace_bytes(int64_t R, int64_t N, int64_t D, int32_t n_prefixes, int32_t kind) {
     if (R < 1 || N < 1 || R > N || D < 64 || D % 64 != 0 || D > kMaxD || n_prefixes < 1 || n_prefixes > kMaxP)
         return 0;
-    if (kind != kInfonce && kind != kSiglip && kind != kRows) return 0;
+    if (kind != kInfonce && kind != kSiglip && kind != kRows && kind != kOneset) return 0;
     int32_t pw[kMaxP];
     for (int32_t i = 0; i < n_prefixes; ++i) pw[i] = (int32_t)(D - 32 * (n_prefixes - 1 - i));  // any ladder ending at D
+    if (kind == kOneset) return make_plan(R, N, D, pw, n_prefixes, kSiglip, 0, true, false).total;
     return make_plan(R, N, D, pw, n_prefixes, kind, 0, true, true).total;
 }
 
@@ -591,14 +611,15 @@ uform_status_t uform_contrastive_supported(int64_t D, const int32_t *prefixes, i
     g_last_error.clear();
     if (!prefixes || n_prefixes < 1 || n_prefixes > kMaxP)
         return fail(uform_status_invalid_argument_k, "prefixes must be a host array of 1..8 widths");
-    if (kind != kInfonce && kind != kSiglip && kind != kRows) return fail(uform_status_invalid_argument_k, "unknown kind");
+    if (kind != kInfonce && kind != kSiglip && kind != kRows && kind != kOneset)
+        return fail(uform_status_invalid_argument_k, "unknown kind");
     for (int32_t i = 0; i < n_prefixes; ++i) {
         if (prefixes[i] < 32 || prefixes[i] % 32 != 0 || (i > 0 && prefixes[i] <= prefixes[i - 1]))
             return fail(uform_status_invalid_argument_k, "prefix widths must be increasing multiples of 32");
     }
     if (D < 1 || prefixes[n_prefixes - 1] > D) return fail(uform_status_invalid_argument_k, "the widest prefix exceeds D");
     if (D % 64 != 0 || D > kMaxD) return fail(uform_status_unsupported_k, "D must be a multiple of 64 and at most 1024");
-    if ((with_gradients || kind == kSiglip) && !bwd_mask_supported(ladder_mask(prefixes, n_prefixes)))
+    if ((with_gradients || kind == kSiglip || kind == kOneset) && !bwd_mask_supported(ladder_mask(prefixes, n_prefixes)))
         return fail(uform_status_unsupported_k, "this prefix ladder has no compiled backward kernel");
     return uform_status_success_k;
 }

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
     const bool isq = row < a.R;
     const int D = a.D;
     const u16 *x = isq ? a.q + row * D : a.k + (row - a.R) * D;
-    const u16 *y = isq ? a.k + (row + a.off) * D : x;
+    const u16 *y = isq ? a.k + ((row + a.off) ^ a.pxor) * D : x;
     const int P = a.pf.n;
     float ss_run = 0.f, dot_run = 0.f;
     float inv[kMaxP];
@@ -568,7 +568,7 @@ __global__ __launch_bounds__(256) void k_rowstats(StatsArgs a) {
         const float negsum = fold_partials(a.rowpart, a.nJt, P, p, a.R, i, i < a.R, fold);
         if (lead && i < a.R) {
             const float neg = negsum;
-            const float iq = a.invq[p * a.R + i], ik = a.invk[p * a.N + i + a.off];
+            const float iq = a.invq[p * a.R + i], ik = a.invk[p * a.N + ((i + a.off) ^ a.pxor)];
             const float S = a.posdot[p * a.R + i];
             const float A = a.qA[p * a.R + i];
             const float x = fmaf(S * A, ik, a.cshift);
@@ -642,7 +642,7 @@ __global__ __launch_bounds__(256) void k_siglip_tabs(StatsArgs a) {
         float lpos = 0.f, sig_neg = 0.f;
         if (r < a.R) {
             const int64_t i = r;
-            const float iq = a.invq[p * a.R + i], ik = a.invk[p * a.N + i + a.off];
+            const float iq = a.invq[p * a.R + i], ik = a.invk[p * a.N + ((i + a.off) ^ a.pxor)];
             const float S = a.posdot[p * a.R + i];
             const float l = a.scale * S * iq * ik + a.bias;
             // softplus(-l) and sigmoid(-l), both overflow-free
@@ -650,7 +650,7 @@ __global__ __launch_bounds__(256) void k_siglip_tabs(StatsArgs a) {
             lpos = fmaxf(-l, 0.f) + log1pf(t);
             sig_neg = (l >= 0.f) ? t / (1.f + t) : 1.f / (1.f + t);
             a.qC[p * a.R + i] = a.sgn * a.wnorm[p] * iq / a.invq[(P - 1) * a.R + i];
-            a.diagA[p * a.R + i] = -a.wnorm[p] * a.scale * sig_neg * a.inv_den * iq * ik;
+            a.diagA[p * a.R + i] = -a.mirror * a.wnorm[p] * a.scale * sig_neg * a.inv_den * iq * ik;
             if (a.pos_logit_out) a.pos_logit_out[p * a.R + i] = l;
         } else if (r < a.R + a.N) {
             const int64_t j = r - a.R;
@@ -818,7 +818,7 @@ __device__ __forceinline__ void bwd_finish(const BwdArgs &a, const f32x16 (&dacc
             pos[r] = ok[r] && ipos >= 0 && ipos < a.R;
             sc[r] = ok[r] ? inv_sc[orow] * a.gam[o] : 0.f;
             xoff[r] = (int64_t)(ok[r] ? o : 0) * D;
-            yoff[r] = pos[r] ? (int64_t)(o + a.diag_shift) * D : 0;
+            yoff[r] = pos[r] ? (int64_t)((o + a.diag_shift) ^ a.pxor) * D : 0;
         }
 #pragma unroll
         for (int jb = 0; jb < NQ; ++jb) {
@@ -850,7 +850,9 @@ __device__ __forceinline__ void bwd_finish(const BwdArgs &a, const f32x16 (&dacc
     }
 }
 
-template <uint32_t MASK, bool SIG, bool UPD>
+// SIG: sigmoid form; UPD: the gradient contraction runs; LOSS: the pass also sums the sigmoid
+// form's loss (and sigma(l) for dL/dbias), a compile-time choice so the epilogue has no branch
+template <uint32_t MASK, bool SIG, bool UPD, bool LOSS>
 __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     using L = Ladder<MASK>;
     constexpr int NP = L::NP;
@@ -997,8 +999,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     // blocks whose cells need masks: from nb_sp on (ragged or past the split's end; every
     // block if the outer rows are ragged), and those holding positives of these outer rows
     const int nb_sp = o0 + BO > NO ? 0 : min(NI / BI, nb_end);
-    const int c_lo = o0 + dsh - BI;  // blocks with c_lo < n0 < c_lo + BO + BI hold positives
-    auto needmask = [&](int nb) { return nb >= nb_sp || (uint32_t)(nb * BI - c_lo - 1) < (uint32_t)(BO + BI - 1); };
+    // blocks with c_lo < n0 < c_lo + BO + BI hold positives (one-set form: and the cells of a row
+    // with itself; a pair's two rows are adjacent, so the range grows by one row on either side)
+    const int pxr = a.pxor;
+    const int c_lo = o0 + dsh - BI - pxr;
+    const uint32_t c_len = (uint32_t)(BO + BI - 1 + 2 * pxr);
+    auto needmask = [&](int nb) { return nb >= nb_sp || (uint32_t)(nb * BI - c_lo - 1) < c_len; };
     // lane masks of block nb's cells for inner rows 4 w + t (wave-uniform 64-bit masks)
     const uint64_t ovm = __builtin_amdgcn_ballot_w64(ovalid);
     auto block_masks = [&](int nb, uint64_t(&mk)[4]) {
@@ -1009,7 +1015,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             const int nw = nb * BI + 4 * w;
             const int lim = min(NI, nb_end * BI);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) mk[t] = __builtin_amdgcn_ballot_w64(ovalid && nw + t < lim && nw + t != o + dsh);
+            for (int t = 0; t < 4; ++t)
+                mk[t] = __builtin_amdgcn_ballot_w64(ovalid && nw + t < lim && nw + t != ((o + dsh) ^ pxr) &&
+                                                    (pxr == 0 || nw + t != o + dsh));
         }
     };
     // Epilogue unit of prefix p for the block in ring slot eyo (its tables follow the tile): the
@@ -1064,7 +1072,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
                     const float rr = __builtin_amdgcn_rcpf(wq);
                     const float sg = uu >= 0.f ? rr : tt * rr;
                     st.e[t] = sg * Co[p] * tb.iy[t];  // Co holds beta_o for the sigmoid form
-                    if (a.want_loss) {
+                    if constexpr (LOSS) {
                         // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
                         const float corr = (tt - (wq - 1.f)) * rr * kLog2e;
                         const float lt = fmaxf(uu, 0.f) + __builtin_amdgcn_logf(wq) + corr;
@@ -1302,7 +1310,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     float *red = &Sl[0][0];  // [4][NP][BO], then [4][NP] twice
 #pragma unroll
     for (int p = 0; p < NP; ++p) red[(w * NP + p) * BO + lane] = Cacc[p];
-    if (SIG && a.want_loss) {
+    if constexpr (SIG && LOSS) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const float v = wave_sum(Lacc[p]);
@@ -1322,7 +1330,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             a.Cpart[(split * NP + p) * a.NO + o] = c * csc;
         }
     }
-    if (SIG && a.want_loss && tid < NP) {
+    if (SIG && LOSS && tid < NP) {
         const float *lr = red + 4 * NP * BO;
         const float v = ((lr[0 * NP + tid] + lr[1 * NP + tid]) + lr[2 * NP + tid]) + lr[3 * NP + tid];
         const int64_t slot = (int64_t)a.loss_slot0 + split * gridDim.x + blockIdx.x;
@@ -1368,7 +1376,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs a) {
     const int P = a.pf.n;
     const int64_t ipos = o + a.pos_shift;  // index of the positive's query row in diagA/posdot
     const bool has_pos = ipos >= 0 && ipos < a.R;
-    const int64_t ypos = o + a.diag_shift;  // positive's row in Y
+    const int64_t ypos = (o + a.diag_shift) ^ a.pxor;  // positive's row in Y
     if (threadIdx.x == 0) {
         float dg = 0.f, rd = 0.f, ts = 0.f;
         for (int p = P - 1; p >= 0; --p) {
@@ -1537,11 +1545,13 @@ hipError_t launch_siglip_tabs(const StatsArgs &a, hipStream_t s) {
 template <uint32_t MASK>
 static hipError_t launch_bwd_mask(const BwdArgs &a, bool sig, dim3 grid, hipStream_t s) {
     if (!sig)
-        hipLaunchKernelGGL((k_bwd<MASK, false, true>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_bwd<MASK, false, true, false>), grid, dim3(256), 0, s, a);
+    else if (a.do_update && a.want_loss)
+        hipLaunchKernelGGL((k_bwd<MASK, true, true, true>), grid, dim3(256), 0, s, a);
     else if (a.do_update)
-        hipLaunchKernelGGL((k_bwd<MASK, true, true>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_bwd<MASK, true, true, false>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((k_bwd<MASK, true, false>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_bwd<MASK, true, false, true>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@ import numpy as np
 INFONCE = 0
 SIGLIP = 1
 INFONCE_ROWS = 2
+ONESET_SIGLIP = 3
 
 DEFAULT_PREFIXES = (64, 128, 256, 512, 1024)
 
@@ -48,7 +49,7 @@ class Workload:
     scale: float = float(np.float32(1.0 / 0.07))
     bias: float = 0.0
     row_offset: int = 0
-    recipe: str = "gauss"          # gauss | clustered | student_t
+    recipe: str = "gauss"          # gauss | clustered | student_t | pairs
     noise: float = 0.3
     seed: int = 0
     extra: dict = field(default_factory=dict)
@@ -65,6 +66,9 @@ WORKLOADS = {
     "infonce_32768": Workload("infonce_32768", INFONCE, 32768, 32768, weights=(1, 1, 1, 1, 2),
                               scale=float(np.float32(1.0 / 0.05)), recipe="student_t",
                               noise=0.4, seed=4),
+    # the one-set sigmoid form at one GPU's share of an eight-GPU set: 16384 rows of 131072
+    "oneset_16384x131072": Workload("oneset_16384x131072", ONESET_SIGLIP, 16384, 131072, scale=10.0,
+                                    bias=-10.0, recipe="pairs", noise=0.5, seed=5),
 }
 
 
@@ -78,6 +82,8 @@ def draw_f64(R: int, N: int, D: int, recipe: str = "gauss", noise: float = 0.3, 
     clustered:  centroids C ~ N(0,1) [centroids, D]; assignment a(j) ~ U{0..C-1}
                 for every key j; k_j = C_{a(j)} + noise * N(0,1); then
                 q_i = C_{a(off+i)} + noise * N(0,1) with independent noise.
+    pairs:      one set (the one-set form): x_{2m} ~ N(0,1) for the N/2 pairs, then
+                x_{2m+1} = x_{2m} + noise * N(0,1); k = x, q = x[off:off+R].
     """
     rng = np.random.default_rng(seed)
     if recipe in ("gauss", "student_t"):
@@ -95,6 +101,13 @@ def draw_f64(R: int, N: int, D: int, recipe: str = "gauss", noise: float = 0.3, 
         k = C[assign] + noise * rng.standard_normal((N, D))
         q = C[assign[row_offset:row_offset + R]] + noise * rng.standard_normal((R, D))
         return q, k
+    if recipe == "pairs":
+        if N % 2:
+            raise ValueError("the pairs recipe needs an even N")
+        x = np.empty((N, D))
+        x[0::2] = rng.standard_normal((N // 2, D))
+        x[1::2] = x[0::2] + noise * rng.standard_normal((N // 2, D))
+        return x[row_offset:row_offset + R].copy(), x
     raise ValueError(f"unknown recipe {recipe!r}")
 
 

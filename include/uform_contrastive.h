@@ -61,7 +61,20 @@ typedef enum {
     uform_contrastive_infonce_k = 0,      /* symmetric CLIP 1/2 (row CE + column CE) */
     uform_contrastive_siglip_k = 1,       /* pairwise sigmoid, z = +1 at (i, off + i) */
     uform_contrastive_infonce_rows_k = 2, /* row CE of the R local rows + column PLSE */
+    uform_contrastive_oneset_siglip_k = 3, /* one set scored against itself, sigmoid form (below) */
 } uform_contrastive_kind_t;
+
+/* The one-set sigmoid form ("Scaling-Up Contrastive Learning over NVLink
+ * Multicast", section "One Set or Two": one set scored against itself, an
+ * image and its caption two rows of the set marked as a positive pair,
+ * mirrored cells with the same labels, the owner of a row differentiating
+ * both).  k is the whole set [N][D] (N even; rows 2m and 2m + 1 are a pair),
+ * q = k + row_offset * D its rows row_offset .. row_offset + R - 1 (checked).
+ * loss_out is this share's part, (1/N) sum over its rows g and every j != g
+ * of softplus(-z_gj l_gj), z = +1 at j = g xor 1; a cell of a row with
+ * itself is not scored.  dq is the gradient of the whole set's loss with
+ * respect to the share's rows (both mirrored cells); dk must be NULL.  One
+ * backward pass, over the share's rows. */
 
 typedef enum {
     uform_status_success_k = 0,
@@ -88,7 +101,8 @@ typedef enum {
  *              strictly increasing multiples of 32, last <= D;
  *              1 <= n_prefixes <= 8.
  *  scale, bias finite; softmax kinds need |scale| <= 40 (else unsupported).
- *  kind        a uform_contrastive_kind_t; INFONCE needs R == N.
+ *  kind        a uform_contrastive_kind_t; INFONCE needs R == N; the one-set
+ *              form needs q inside k and dk = NULL (see above).
  *  loss_out    device, 1 float: the weighted loss (written asynchronously).
  *  dq, dk      device FP32 [R][D] and [N][D], 16-byte aligned, overwritten;
  *              NULL skips that gradient.

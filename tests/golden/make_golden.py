@@ -10,7 +10,8 @@ same arrays the GPU receives) and this script stores, in
 * ``dq_rows`` / ``dk_rows``: 16 seeded row indices (first and last row
   included) with those rows of dq / dk (float32), and ``dq_absmax`` /
   ``dk_absmax``: max |dq|, max |dk| over the whole tensors (the scale of the
-  gradient tolerance);
+  gradient tolerance); the one-set form has no dk;
+* ``dscale`` and ``dbias``: dL/dscale and dL/dbias (float64);
 * ``tab_idx``: 256 seeded row/column indices with ``pos_logit`` (and for the
   softmax kinds ``row_lse`` / ``col_lse``) at those indices, all prefixes.
 
@@ -29,10 +30,10 @@ import numpy as np
 ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 sys.path.insert(0, ROOT)
 
-from contrastive_embedding_loss_amd.inputs import SIGLIP, WORKLOADS, workload_inputs  # noqa: E402
+from contrastive_embedding_loss_amd.inputs import ONESET_SIGLIP, SIGLIP, WORKLOADS, workload_inputs  # noqa: E402
 from oracle import bf16_bits_to_f64, contrastive_fwd_bwd  # noqa: E402
 
-LARGE = ("siglip_16384", "rows_4096x65536", "infonce_32768")
+LARGE = ("siglip_16384", "rows_4096x65536", "infonce_32768", "oneset_16384x131072")
 
 
 def sample_indices(n: int, count: int, seed: int) -> np.ndarray:
@@ -53,15 +54,18 @@ def make(name: str) -> str:
         "loss": np.float64(ref["loss"]),
         "prefix_losses": np.asarray(ref["prefix_losses"], dtype=np.float64),
         "dq_absmax": np.float64(np.abs(ref["dq"]).max()),
-        "dk_absmax": np.float64(np.abs(ref["dk"]).max()),
+        "dscale": np.float64(ref["dscale"]),
+        "dbias": np.float64(ref["dbias"]),
     }
     out["dq_rows"] = sample_indices(w.R, 16, 1000 + w.seed)
-    out["dk_rows"] = sample_indices(w.N, 16, 2000 + w.seed)
     out["dq"] = ref["dq"][out["dq_rows"]].astype(np.float32)
-    out["dk"] = ref["dk"][out["dk_rows"]].astype(np.float32)
+    if w.kind != ONESET_SIGLIP:
+        out["dk_absmax"] = np.float64(np.abs(ref["dk"]).max())
+        out["dk_rows"] = sample_indices(w.N, 16, 2000 + w.seed)
+        out["dk"] = ref["dk"][out["dk_rows"]].astype(np.float32)
     out["tab_idx"] = sample_indices(w.R, 256, 3000 + w.seed)
     out["pos_logit"] = ref["pos_logit"][:, out["tab_idx"]].astype(np.float64)
-    if w.kind != SIGLIP:
+    if w.kind not in (SIGLIP, ONESET_SIGLIP):
         out["row_lse"] = ref["row_lse"][:, out["tab_idx"]].astype(np.float64)
         out["col_idx"] = sample_indices(w.N, 256, 4000 + w.seed)
         out["col_lse"] = ref["col_lse"][:, out["col_idx"]].astype(np.float64)

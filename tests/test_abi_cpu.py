@@ -55,6 +55,9 @@ INVALID = [
     dict(prefixes=[64, 48, 1024]), dict(prefixes=[100, 1024]), dict(prefixes=[64, 2048]),
     dict(prefixes=PREFIXES, n_prefixes=0), dict(prefixes=[32 * (i + 1) for i in range(9)]),
     dict(scale=float("inf")), dict(scale=float("nan")), dict(bias=float("nan")), dict(scale=0.0),
+    # one-set form: q must be k's rows, the set even, and no dk
+    dict(kind=3, dk=0), dict(kind=3, q=0x20000, dk=0, N=255, R=255, D=1024),
+    dict(kind=3, q=0x20000 + 2048 * 3, dk=0, R=64, N=256),
 ]
 
 

@@ -235,3 +235,39 @@ def test_scale_and_bias_gradients(kind, one_split, want_dq):
         assert got_b == pytest.approx(ref["dbias"], rel=1e-3, abs=1e-6), (got_b, ref["dbias"])
     else:
         assert got_b == 0.0 and abs(ref["dbias"]) < 1e-12
+
+
+# The one-set sigmoid form: q is a view of the set k; one backward pass gives dq = dX of the share
+@pytest.mark.parametrize("N,R,off,D,prefixes,one_split", [
+    (256, 256, 0, 1024, LADDER, False), (352, 96, 128, 1024, LADDER, False), (300, 64, 33, 1024, LADDER, True),
+    (320, 320, 0, 320, (64, 128, 256), True), (192, 80, 7, 192, (64, 128), False)])
+def test_oneset_siglip(N, R, off, D, prefixes, one_split):
+    from contrastive_embedding_loss_amd.inputs import ONESET_SIGLIP
+    from oracle import ONESET_SIGLIP as ORACLE_ONESET
+    qb, kb = make_inputs(R, N, D, recipe="pairs", noise=0.6, seed=101 + R, row_offset=off)
+    print(f"[case] oneset N={N} R={R} off={off} D={D} prefixes={prefixes} one_split={one_split}", flush=True)
+    k = to_dev(kb)
+    q = k[off:off + R]
+    loss, dq, dk, ex = binding.fwd_bwd(q, k, prefixes, 10.0, -6.0, ONESET_SIGLIP, row_offset=off, extras=True,
+                                       one_split=one_split)
+    torch.cuda.synchronize()
+    assert dk is None
+    ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), prefixes, 10.0, -6.0, ORACLE_ONESET,
+                              row_offset=off)
+    assert abs(loss.item() - ref["loss"]) <= 1e-3 * abs(ref["loss"]), (loss.item(), ref["loss"])
+    g = dq.cpu().numpy()
+    assert np.abs(g - ref["dq"]).max() <= 2e-3 * np.abs(ref["dq"]).max()
+    np.testing.assert_allclose(ex["prefix_losses"].cpu().numpy(), ref["prefix_losses"], rtol=1e-3)
+    assert np.abs(ex["pos_logit"].cpu().numpy() - ref["pos_logit"]).max() <= 1e-3
+    assert ex["dscale"].item() == pytest.approx(ref["dscale"], rel=1e-3, abs=1e-6)
+    assert ex["dbias"].item() == pytest.approx(ref["dbias"], rel=1e-3, abs=1e-6)
+
+
+def test_oneset_loss_only_matches_full_call():
+    from contrastive_embedding_loss_amd.inputs import ONESET_SIGLIP
+    qb, kb = make_inputs(128, 256, 1024, recipe="pairs", noise=0.6, seed=111, row_offset=64)
+    k = to_dev(kb)
+    q = k[64:192]
+    full = binding.fwd_bwd(q, k, LADDER, 10.0, -6.0, ONESET_SIGLIP, row_offset=64)
+    only = binding.fwd_bwd(q, k, LADDER, 10.0, -6.0, ONESET_SIGLIP, row_offset=64, want_dq=False)
+    assert torch.equal(full[0], only[0])

@@ -1,11 +1,11 @@
 """GPU parity at the full workload sizes, in the launch configuration the bench times.
 
 ``infonce_4096`` is compared with a live oracle run element by element.  The
-three large workloads are compared with the oracle's stored values
+four large workloads are compared with the oracle's stored values
 (``tests/golden/<workload>.npz``, written by ``tests/golden/make_golden.py``
 from ``oracle/`` alone): the loss and every prefix loss (rel <= 1e-3), 16
 sampled rows of dq and dk against 2e-3 x max|grad| of the whole oracle
-tensor, and 256 sampled row/column log-sum-exps and positive logits
+tensor, dL/dscale and dL/dbias (rel <= 1e-3), and 256 sampled row/column log-sum-exps and positive logits
 (max-abs <= 1e-3).  Properties that hold at any size are checked on the whole
 GPU output: finiteness, zeros beyond the widest prefix, and the Euler
 identity x . dx = 0 of the scale-invariant loss, per row (within 1e-2 of
@@ -20,7 +20,8 @@ import pytest
 torch = pytest.importorskip("torch")
 
 from contrastive_embedding_loss_amd import binding  # noqa: E402
-from contrastive_embedding_loss_amd.inputs import SIGLIP, WORKLOADS, bf16_bits_to_f32, workload_inputs  # noqa: E402
+from contrastive_embedding_loss_amd.inputs import (  # noqa: E402
+    ONESET_SIGLIP, SIGLIP, WORKLOADS, bf16_bits_to_f32, workload_inputs)
 from oracle import bf16_bits_to_f64, contrastive_fwd_bwd  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -30,8 +31,11 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 def run_gpu(w):
     print(f"[case] {w.name} R={w.R} N={w.N} D={w.D} kind={w.kind}", flush=True)
     qb, kb = workload_inputs(w)
-    q = torch.from_numpy(bf16_bits_to_f32(qb)).to("cuda").to(torch.bfloat16)
     k = torch.from_numpy(bf16_bits_to_f32(kb)).to("cuda").to(torch.bfloat16)
+    if w.kind == ONESET_SIGLIP:  # the share's rows are a view of the set
+        q = k[w.row_offset:w.row_offset + w.R]
+    else:
+        q = torch.from_numpy(bf16_bits_to_f32(qb)).to("cuda").to(torch.bfloat16)
     loss, dq, dk, ex = binding.fwd_bwd(q, k, w.prefixes, w.scale, w.bias, w.kind, weights=w.weights,
                                        row_offset=w.row_offset, extras=True)
     torch.cuda.synchronize()
@@ -41,6 +45,8 @@ def run_gpu(w):
 def check_properties(w, q, k, dq, dk):
     Dw = w.prefixes[-1]
     for x, g in ((q, dq), (k, dk)):
+        if g is None:
+            continue
         assert torch.isfinite(g).all()
         if Dw < w.D:
             assert (g[:, Dw:] == 0).all()
@@ -67,7 +73,7 @@ def test_infonce_4096_full_oracle():
     check_properties(w, q, k, dq, dk)
 
 
-@pytest.mark.parametrize("name", ["siglip_16384", "rows_4096x65536", "infonce_32768"])
+@pytest.mark.parametrize("name", ["siglip_16384", "rows_4096x65536", "infonce_32768", "oneset_16384x131072"])
 def test_large_workload_against_stored_oracle(name):
     path = os.path.join(GOLDEN, f"{name}.npz")
     g = np.load(path)
@@ -76,15 +82,20 @@ def test_large_workload_against_stored_oracle(name):
     assert abs(loss - float(g["loss"])) <= 1e-3 * abs(float(g["loss"])), (loss, float(g["loss"]))
     np.testing.assert_allclose(ex["prefix_losses"].cpu().numpy(), g["prefix_losses"], rtol=1e-3)
     for name_g, t in (("dq", dq), ("dk", dk)):
+        if t is None:
+            continue
         rows = torch.from_numpy(g[f"{name_g}_rows"]).to("cuda")
         got = t.index_select(0, rows).cpu().numpy()
         e = np.abs(got - g[name_g]).max()
         assert e <= 2e-3 * float(g[f"{name_g}_absmax"]), (name_g, e, float(g[f"{name_g}_absmax"]))
         # the whole tensor's scale agrees too
         assert abs(t.abs().max().item() - float(g[f"{name_g}_absmax"])) <= 2e-3 * float(g[f"{name_g}_absmax"])
+    if "dscale" in g:
+        assert ex["dscale"].item() == pytest.approx(float(g["dscale"]), rel=1e-3, abs=1e-6)
+        assert ex["dbias"].item() == pytest.approx(float(g["dbias"]), rel=1e-3, abs=1e-6)
     idx = g["tab_idx"]
     assert np.abs(ex["pos_logit"].cpu().numpy()[:, idx] - g["pos_logit"]).max() <= 1e-3
-    if w.kind != SIGLIP:
+    if w.kind not in (SIGLIP, ONESET_SIGLIP):
         assert np.abs(ex["row_lse"].cpu().numpy()[:, idx] - g["row_lse"]).max() <= 1e-3
         assert np.abs(ex["col_lse"].cpu().numpy()[:, g["col_idx"]] - g["col_lse"]).max() <= 1e-3
     check_properties(w, q, k, dq, dk)
