@@ -271,3 +271,21 @@ def test_oneset_loss_only_matches_full_call():
     full = binding.fwd_bwd(q, k, LADDER, 10.0, -6.0, ONESET_SIGLIP, row_offset=64)
     only = binding.fwd_bwd(q, k, LADDER, 10.0, -6.0, ONESET_SIGLIP, row_offset=64, want_dq=False)
     assert torch.equal(full[0], only[0])
+
+
+@pytest.mark.parametrize("N,R,off", [(2, 2, 0), (2, 1, 1), (64, 1, 37)])
+def test_oneset_edge_shares(N, R, off):
+    # a set of one pair; a single row whose partner lies outside the share
+    from contrastive_embedding_loss_amd.inputs import ONESET_SIGLIP
+    from oracle import ONESET_SIGLIP as ORACLE_ONESET
+    qb, kb = make_inputs(R, N, 1024, recipe="pairs", noise=0.6, seed=121 + N + off, row_offset=off)
+    print(f"[case] oneset-edge N={N} R={R} off={off}", flush=True)
+    k = to_dev(kb)
+    loss, dq, _, ex = binding.fwd_bwd(k[off:off + R], k, LADDER, 10.0, -6.0, ONESET_SIGLIP, row_offset=off,
+                                      extras=True)
+    torch.cuda.synchronize()
+    ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), LADDER, 10.0, -6.0, ORACLE_ONESET,
+                              row_offset=off)
+    assert abs(loss.item() - ref["loss"]) <= 1e-3 * abs(ref["loss"]) + 1e-7, (loss.item(), ref["loss"])
+    assert np.abs(dq.cpu().numpy() - ref["dq"]).max() <= 2e-3 * np.abs(ref["dq"]).max() + 1e-12
+    assert ex["dscale"].item() == pytest.approx(ref["dscale"], rel=1e-3, abs=1e-7)
