@@ -41,6 +41,7 @@ struct PrepArgs {
     Prefixes pf;
     float a_scale, gam_scale;
     float *invq, *invk, *qA, *kA, *qIYR, *kIYR, *posdot, *sigq, *sigk, *gamq, *gamk;
+    float *gmax;  // [4][P], zeroed here for k_maxes
 };
 
 // Statistics / coefficient-table kernels.  "q" tables are [P][R], "k" tables [P][N].

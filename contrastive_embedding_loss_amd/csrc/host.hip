@@ -362,6 +362,7 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     pa.sigk = sigk;
     pa.gamq = gamq;
     pa.gamk = gamk;
+    pa.gmax = F(pl.o_gmax);
     LAUNCH_NAMED("k_prep", launch_prep(pa, s));
     if (dq || dk || !softmax) {
         LAUNCH_NAMED("k_half_copy", launch_half_copy(q, sigq, R, Di, qH, s));

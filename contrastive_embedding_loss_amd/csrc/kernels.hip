@@ -131,6 +131,7 @@ __device__ __forceinline__ void dma4_m0(const void *g, uint32_t m0v) {
 // with their positive key.  One wave per row.
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
+    if (blockIdx.x == 0 && threadIdx.x < 4 * a.pf.n) a.gmax[threadIdx.x] = 0.f;  // k_maxes' start
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + wave;
     if (row >= a.R + a.N) return;
@@ -1347,22 +1348,28 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
 // a fixed tree, so the result does not depend on scheduling).
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_maxes(const float *t0, const float *t1, const float *t2, const float *t3,
-                                               int64_t n0, int64_t n1, int64_t n2, int64_t n3, int P,
+                                               int64_t n0, int64_t n1, int64_t n2, int64_t n3, int P, int chunks,
                                                float *gmax) {
+    // block (t, p, c) takes chunk c of table t, prefix p; gmax starts at 0 (k_prep) and takes
+    // each chunk's maximum by an integer maximum of the bit patterns (the values are >= 0, so
+    // the order of the bits is the order of the values, and the result does not depend on
+    // the order of the blocks)
     __shared__ float red[256];
-    const int t = blockIdx.x / P, p = blockIdx.x % P;
+    const int c = blockIdx.x % chunks, tp = blockIdx.x / chunks;
+    const int t = tp / P, p = tp % P;
     const float *src = t == 0 ? t0 : t == 1 ? t1 : t == 2 ? t2 : t3;
     const int64_t n = t == 0 ? n0 : t == 1 ? n1 : t == 2 ? n2 : n3;
+    const int64_t per = (n + chunks - 1) / chunks, b = c * per, e = b + per < n ? b + per : n;
     float m = 0.f;
     if (src)
-        for (int64_t i = threadIdx.x; i < n; i += 256) m = fmaxf(m, src[p * n + i]);
+        for (int64_t i = b + threadIdx.x; i < e; i += 256) m = fmaxf(m, src[p * n + i]);
     red[threadIdx.x] = m;
     __syncthreads();
     for (int h = 128; h >= 1; h >>= 1) {
         if ((int)threadIdx.x < h) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + h]);
         __syncthreads();
     }
-    if (threadIdx.x == 0) gmax[t * P + p] = red[0];
+    if (threadIdx.x == 0) atomicMax((int *)&gmax[t * P + p], __float_as_int(red[0]));
 }
 
 // ----------------------------------------------------------------------------
@@ -1573,7 +1580,12 @@ hipError_t launch_bwd(const BwdArgs &a, uint32_t mask, bool sig, int64_t nsplit,
 
 hipError_t launch_maxes(const float *t0, const float *t1, const float *t2, const float *t3, int64_t n0, int64_t n1,
                         int64_t n2, int64_t n3, int P, float *gmax, hipStream_t s) {
-    hipLaunchKernelGGL(k_maxes, dim3((unsigned)(4 * P)), dim3(256), 0, s, t0, t1, t2, t3, n0, n1, n2, n3, P, gmax);
+    int64_t nmax = n0 > n1 ? n0 : n1;
+    nmax = nmax > n2 ? nmax : n2;
+    nmax = nmax > n3 ? nmax : n3;
+    const int chunks = (int)(nmax / 4096 < 1 ? 1 : (nmax / 4096 > 64 ? 64 : nmax / 4096));
+    hipLaunchKernelGGL(k_maxes, dim3((unsigned)(4 * P * chunks)), dim3(256), 0, s, t0, t1, t2, t3, n0, n1, n2, n3, P,
+                       chunks, gmax);
     return hipGetLastError();
 }
 
