@@ -1379,16 +1379,28 @@ __global__ __launch_bounds__(256) void k_maxes(const float *t0, const float *t1,
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_finalize(FinArgs a) {
     __shared__ float DG[kMaxP], RD[kMaxP];
+    __shared__ float Cs[kMaxP];
     const int64_t o = blockIdx.x;
     const int P = a.pf.n;
     const int64_t ipos = o + a.pos_shift;  // index of the positive's query row in diagA/posdot
     const bool has_pos = ipos >= 0 && ipos < a.R;
     const int64_t ypos = (o + a.diag_shift) ^ a.pxor;  // positive's row in Y
+    // radial sums over the splits: wave p adds prefix p's partials (a fixed order per lane,
+    // then a fixed tree across the lanes)
+    {
+        const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
+        for (int p = wv; p < P; p += 4) {
+            float c = 0.f;
+            for (int64_t s = ln; s < a.nsplit; s += 64) c += a.Cpart[(s * P + p) * a.NO + o];
+            c = wave_sum(c);
+            if (ln == 0) Cs[p] = c;
+        }
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
         float dg = 0.f, rd = 0.f, ts = 0.f;
         for (int p = P - 1; p >= 0; --p) {
-            float C = 0.f;
-            for (int s = 0; s < a.nsplit; ++s) C += a.Cpart[((int64_t)s * P + p) * a.NO + o];
+            const float C = Cs[p];
             float dA = 0.f, dS = 0.f;
             if (has_pos) {
                 dA = a.diagA[p * a.R + ipos];
