@@ -56,7 +56,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 void choose_split(int64_t NO, int64_t NI, int64_t &nsplit, int64_t &bps) {
     const int64_t wgs = cdiv(NO, kBwdOuter);
     const int64_t nblocks = cdiv(NI, kBwdInner);
-    int64_t want = cdiv(512, wgs);
+    int64_t want = cdiv(256, wgs);  // one round of workgroups: one per CU (a workgroup fills its CU)
     if (want < 1) want = 1;
     if (want > nblocks) want = nblocks;
     bps = cdiv(nblocks, want);
