@@ -852,8 +852,9 @@ __device__ __forceinline__ void bwd_finish(const BwdArgs &a, const f32x16 (&dacc
 }
 
 // SIG: sigmoid form; UPD: the gradient contraction runs; LOSS: the pass also sums the sigmoid
-// form's loss (and sigma(l) for dL/dbias), a compile-time choice so the epilogue has no branch
-template <uint32_t MASK, bool SIG, bool UPD, bool LOSS>
+// form's loss; BIAS: and sigma(l) for dL/dbias.  Compile-time choices, so the epilogue has no
+// branch and carries only the sums a call asks for.
+template <uint32_t MASK, bool SIG, bool UPD, bool LOSS, bool BIAS>
 __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     using L = Ladder<MASK>;
     constexpr int NP = L::NP;
@@ -1079,7 +1080,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
                         const float lt = fmaxf(uu, 0.f) + __builtin_amdgcn_logf(wq) + corr;
                         const bool in = !MK || __builtin_amdgcn_inverse_ballot_w64(mk[t]);
                         Lacc[p] += in ? lt : 0.f;
-                        Bacc[p] += in ? (uu >= 0.f ? rr : tt * rr) : 0.f;  // sigma(l), without the scaling
+                        if constexpr (BIAS) Bacc[p] += in ? (uu >= 0.f ? rr : tt * rr) : 0.f;  // sigma(l), unscaled
                     }
                 }
             }
@@ -1336,7 +1337,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
         const float v = ((lr[0 * NP + tid] + lr[1 * NP + tid]) + lr[2 * NP + tid]) + lr[3 * NP + tid];
         const int64_t slot = (int64_t)a.loss_slot0 + split * gridDim.x + blockIdx.x;
         a.lossparts[slot * NP + tid] = v * kLn2;
-        if (a.biasparts) {
+        if constexpr (BIAS) {
             const float *br = lr + 4 * NP;
             a.biasparts[slot * NP + tid] = ((br[0 * NP + tid] + br[1 * NP + tid]) + br[2 * NP + tid]) + br[3 * NP + tid];
         }
@@ -1563,14 +1564,19 @@ hipError_t launch_siglip_tabs(const StatsArgs &a, hipStream_t s) {
 
 template <uint32_t MASK>
 static hipError_t launch_bwd_mask(const BwdArgs &a, bool sig, dim3 grid, hipStream_t s) {
+    const bool bias = a.biasparts != nullptr;
     if (!sig)
-        hipLaunchKernelGGL((k_bwd<MASK, false, true, false>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_bwd<MASK, false, true, false, false>), grid, dim3(256), 0, s, a);
+    else if (a.do_update && a.want_loss && bias)
+        hipLaunchKernelGGL((k_bwd<MASK, true, true, true, true>), grid, dim3(256), 0, s, a);
     else if (a.do_update && a.want_loss)
-        hipLaunchKernelGGL((k_bwd<MASK, true, true, true>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_bwd<MASK, true, true, true, false>), grid, dim3(256), 0, s, a);
     else if (a.do_update)
-        hipLaunchKernelGGL((k_bwd<MASK, true, true, false>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_bwd<MASK, true, true, false, false>), grid, dim3(256), 0, s, a);
+    else if (bias)
+        hipLaunchKernelGGL((k_bwd<MASK, true, false, true, true>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((k_bwd<MASK, true, false, true>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_bwd<MASK, true, false, true, false>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
