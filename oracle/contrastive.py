@@ -92,6 +92,40 @@ def _positive_mask(rows: np.ndarray, cols: np.ndarray, row_offset: int, oneset: 
     return (cols[None, :] == (g ^ 1 if oneset else g)).astype(np.float64)
 
 
+def _listed_mask(rows: np.ndarray, cols: np.ndarray, positives) -> np.ndarray:
+    """1 where (rows[a], cols[b]) is one of the listed extra positive pairs (CSR: row_ptr, col);
+    rows and cols are contiguous index ranges."""
+    E = np.zeros((len(rows), len(cols)))
+    if positives is None:
+        return E
+    row_ptr, pcol = positives
+    r0, r1, c0 = int(rows[0]), int(rows[-1]) + 1, int(cols[0])
+    owner = np.repeat(np.arange(r0, r1), np.diff(row_ptr[r0:r1 + 1]))  # the row of each listed entry
+    col = pcol[row_ptr[r0]:row_ptr[r1]]
+    inside = (col >= c0) & (col < c0 + len(cols))
+    E[owner[inside] - r0, col[inside] - c0] = 1.0
+    return E
+
+
+def check_positives(positives, R: int, N: int, row_offset: int, oneset: bool):
+    """Validate an extra-positive list and return it as (row_ptr int64 [R + 1], col int64 [nnz]).
+
+    Row i's extra positives are col[row_ptr[i]:row_ptr[i + 1]]: strictly increasing key (set)
+    indices in [0, N), none of them the row's own positive (row_offset + i, or its pair partner
+    (row_offset + i) xor 1 in the one-set form) and, in the one-set form, not the row itself."""
+    row_ptr = np.asarray(positives[0], dtype=np.int64)
+    col = np.asarray(positives[1], dtype=np.int64)
+    if row_ptr.shape != (R + 1,) or row_ptr[0] != 0 or np.any(np.diff(row_ptr) < 0) or row_ptr[-1] != len(col):
+        raise ValueError("row_ptr must have R + 1 non-decreasing entries from 0 to len(col)")
+    for i in range(R):
+        c = col[row_ptr[i]:row_ptr[i + 1]]
+        g = row_offset + i
+        own = g ^ 1 if oneset else g
+        if np.any(c < 0) or np.any(c >= N) or np.any(np.diff(c) <= 0) or np.any(c == own) or (oneset and np.any(c == g)):
+            raise ValueError(f"row {i}: extra positives must be increasing, in [0, N), and not the row's own pair")
+    return row_ptr, col
+
+
 def _self_mask(rows: np.ndarray, cols: np.ndarray, row_offset: int) -> np.ndarray:
     """1 where column cols[b] is row rows[a] itself (one-set form: the cell is not scored)."""
     return (cols[None, :] == (rows[:, None] + row_offset)).astype(np.float64)
@@ -102,7 +136,7 @@ def _default_block(n: int) -> int:
 
 
 def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_offset=0,
-                        grads=True, threads=None, block=None):
+                        grads=True, threads=None, block=None, positives=None):
     """Loss, per-prefix losses, statistics and gradients of the Matryoshka loss.
 
     q: [R, D] queries, k: [N, D] keys (any real values; the tests pass
@@ -120,6 +154,13 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
     (1/N) sum over local rows i and every j other than i itself of
     softplus(-z_ij l_ij), and ``dq`` is the gradient of the whole set's loss
     with respect to those rows (both mirrored cells), with no ``dk``.
+
+    ``positives`` (sigmoid kinds only) = (row_ptr, col) lists extra positive
+    pairs in CSR form: each entry of the batch may carry several positives
+    ("Scaling-Up Contrastive Learning over NVLink Multicast", the training-stack
+    paragraph on loader-side properties), and a listed cell gets the label
+    z = +1 like the row's own positive.  In the one-set form the caller lists
+    both (i, j) and (j, i) so that mirrored cells keep equal labels.
 
     Returns a dict with ``loss`` (float), ``prefix_losses`` [P], ``row_lse``
     [P, R] (log-sum-exp of each row's logits; InfoNCE kinds), ``pos_logit``
@@ -149,6 +190,10 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
     oneset = kind == ONESET_SIGLIP
     if oneset and (N % 2 != 0 or not np.array_equal(q, k[row_offset:row_offset + R])):
         raise ValueError("the one-set form needs an even set k and q = k[row_offset:row_offset + R]")
+    if positives is not None:
+        if kind not in (SIGLIP, ONESET_SIGLIP):
+            raise ValueError("extra positives are defined for the sigmoid kinds")
+        positives = check_positives(positives, R, N, row_offset, oneset)
     w = np.ones(P) if weights is None else np.asarray(weights, dtype=np.float64)
     W = float(np.sum(w))
     s = float(scale)
@@ -186,11 +231,13 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
                 if oneset:
                     pos = logits[rows - r0, pos_col[r0:r1] ^ 1]
                     out["pos"] = pos
-                    z = 2.0 * _positive_mask(rows, all_cols, row_offset, True) - 1.0
+                    z = 2.0 * (_positive_mask(rows, all_cols, row_offset, True)
+                               + _listed_mask(rows, all_cols, positives)) - 1.0
                     keep = 1.0 - _self_mask(rows, all_cols, row_offset)
                     out["siglip_rows"] = np.sum(keep * softplus(-z * logits), axis=1)
                 elif kind == SIGLIP:
-                    z = 2.0 * _positive_mask(rows, all_cols, row_offset) - 1.0
+                    z = 2.0 * (_positive_mask(rows, all_cols, row_offset)
+                               + _listed_mask(rows, all_cols, positives)) - 1.0
                     out["siglip_rows"] = np.sum(softplus(-z * logits), axis=1)
                 else:
                     out["row_lse"] = logsumexp(logits, axis=1)
@@ -229,10 +276,11 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
             # ---- residuals g_ij = dL^p / dl_ij on a slice of the grid
             def residual(logits, rows, cols):
                 if oneset:
-                    E = _positive_mask(rows, cols, row_offset, True)
+                    E = _positive_mask(rows, cols, row_offset, True) + _listed_mask(rows, cols, positives)
                     return (sigmoid(logits) - E) * (1.0 - _self_mask(rows, cols, row_offset)) / N
                 E = _positive_mask(rows, cols, row_offset)
                 if kind == SIGLIP:
+                    E = E + _listed_mask(rows, cols, positives)
                     return (sigmoid(logits) - E) / N
                 p_row = np.exp(logits - row_lse[p][rows][:, None])
                 if kind == INFONCE_ROWS:

@@ -364,3 +364,111 @@ def test_oneset_shards_rebuild_the_set():
     assert sum(p["loss"] for p in parts) == pytest.approx(full["loss"], rel=1e-12)
     np.testing.assert_allclose(np.concatenate([p["dq"] for p in parts]), full["dq"], rtol=1e-10, atol=1e-14)
     assert sum(p["dscale"] for p in parts) == pytest.approx(full["dscale"], rel=1e-10)
+
+
+# ----------------------------------------------------------------------------- several positives per entry
+
+def _csr(pairs, R):
+    """CSR lists (row_ptr, col) of a set of (row, column) pairs."""
+    rows = [sorted(c for r, c in pairs if r == i) for i in range(R)]
+    row_ptr = np.cumsum([0] + [len(c) for c in rows])
+    return row_ptr, np.array([c for cs in rows for c in cs], dtype=np.int64)
+
+
+def test_extra_positives_identical_rows_closed_form():
+    # every cosine is 1: row i has 1 + m_i cells at l = s + b labelled +1 and N - 1 - m_i labelled -1
+    R, N, off, s, b = 4, 9, 2, 5.0, -3.0
+    x = np.tile(np.linspace(-1.0, 2.0, 64), (N, 1))
+    pairs = {(0, 0), (0, 5), (0, 8), (2, 1), (3, 0)}
+    out = contrastive_fwd_bwd(x[:R], x, [32, 64], s, b, SIGLIP, row_offset=off, positives=_csr(pairs, R))
+    m = [sum(1 for r, _ in pairs if r == i) for i in range(R)]
+    want = sum((1 + mi) * _softplus(-(s + b)) + (N - 1 - mi) * _softplus(s + b) for mi in m) / N
+    assert out["loss"] == pytest.approx(want, rel=1e-12)
+    want_db = sum((1 + mi) * (_sigmoid(s + b) - 1.0) + (N - 1 - mi) * _sigmoid(s + b) for mi in m) / N
+    assert out["dbias"] == pytest.approx(want_db, rel=1e-12)
+
+
+@pytest.mark.parametrize("R,N,off", [(5, 5, 0), (4, 9, 3)])
+def test_extra_positives_match_torch_autograd(rng, R, N, off):
+    D, prefixes, weights, s, b = 96, [32, 96], [2, 1], 6.0, -2.5
+    q = rng.standard_normal((R, D))
+    k = rng.standard_normal((N, D))
+    pairs = {(i, j) for i in range(R) for j in range(N) if j != off + i and rng.random() < 0.3}
+    out = contrastive_fwd_bwd(q, k, prefixes, s, b, SIGLIP, weights=weights, row_offset=off,
+                              positives=_csr(pairs, R))
+    qt = torch.tensor(q, requires_grad=True)
+    kt = torch.tensor(k, requires_grad=True)
+    st = torch.tensor(s, dtype=torch.float64, requires_grad=True)
+    bt = torch.tensor(b, dtype=torch.float64, requires_grad=True)
+    z = -torch.ones(R, N, dtype=torch.float64)
+    for i in range(R):
+        z[i, off + i] = 1.0
+    for i, j in pairs:
+        z[i, j] = 1.0
+    total = 0.0
+    for p, width in enumerate(prefixes):
+        logits = st * F.normalize(qt[:, :width], dim=1) @ F.normalize(kt[:, :width], dim=1).T + bt
+        total = total + weights[p] * (-F.logsigmoid(z * logits).sum() / N)
+    total = total / sum(weights)
+    total.backward()
+    assert out["loss"] == pytest.approx(total.item(), rel=1e-12)
+    np.testing.assert_allclose(out["dq"], qt.grad.numpy(), rtol=1e-9, atol=1e-13)
+    np.testing.assert_allclose(out["dk"], kt.grad.numpy(), rtol=1e-9, atol=1e-13)
+    assert out["dscale"] == pytest.approx(st.grad.item(), rel=1e-9)
+    assert out["dbias"] == pytest.approx(bt.grad.item(), rel=1e-9)
+
+
+def test_oneset_extra_positives_match_torch_autograd_of_the_whole_set():
+    rng = np.random.default_rng(11)
+    N, D, prefixes, s, b = 10, 64, [32, 64], 7.0, -3.0
+    x = rng.standard_normal((N, D))
+    pairs = set()
+    for i in range(N):
+        for j in range(i + 1, N):
+            if j != i ^ 1 and rng.random() < 0.3:
+                pairs |= {(i, j), (j, i)}
+    out = contrastive_fwd_bwd(x, x, prefixes, s, b, ONESET_SIGLIP, positives=_csr(pairs, N))
+    xt = torch.tensor(x, requires_grad=True)
+    z = -torch.ones(N, N, dtype=torch.float64)
+    z[torch.arange(N), torch.arange(N) ^ 1] = 1.0
+    for i, j in pairs:
+        z[i, j] = 1.0
+    keep = 1.0 - torch.eye(N, dtype=torch.float64)
+    total = 0.0
+    for width in prefixes:
+        xh = F.normalize(xt[:, :width], dim=1)
+        total = total + (-(keep * F.logsigmoid(z * (s * xh @ xh.T + b))).sum() / N)
+    total = total / len(prefixes)
+    total.backward()
+    assert out["loss"] == pytest.approx(total.item(), rel=1e-12)
+    np.testing.assert_allclose(out["dq"], xt.grad.numpy(), rtol=1e-9, atol=1e-13)
+    # a share of the set carries the rows' own lists; the shares rebuild the set
+    rp, col = _csr(pairs, N)
+    parts = []
+    for o in (0, 4, 8):
+        R = min(4, N - o)
+        prp = rp[o:o + R + 1] - rp[o]
+        parts.append(contrastive_fwd_bwd(x[o:o + R], x, prefixes, s, b, ONESET_SIGLIP, row_offset=o,
+                                         positives=(prp, col[rp[o]:rp[o + R]])))
+    assert sum(p["loss"] for p in parts) == pytest.approx(out["loss"], rel=1e-12)
+    np.testing.assert_allclose(np.concatenate([p["dq"] for p in parts]), out["dq"], rtol=1e-10, atol=1e-14)
+
+
+@pytest.mark.parametrize("kind,row_ptr,col,off", [
+    (SIGLIP, [0, 1, 1], [1], 1),          # row 0's own positive (column 1)
+    (SIGLIP, [0, 2, 2], [3, 3], 0),       # repeated column
+    (SIGLIP, [0, 2, 2], [4, 2], 0),       # not increasing
+    (SIGLIP, [0, 1, 1], [6], 0),          # past N
+    (SIGLIP, [0, 1, 1], [-1], 0),         # negative
+    (SIGLIP, [0, 1], [2], 0),             # row_ptr too short
+    (SIGLIP, [0, 2, 1], [2, 3], 0),       # row_ptr decreasing
+    (ONESET_SIGLIP, [0, 1, 1], [1], 0),   # row 0's pair partner
+    (ONESET_SIGLIP, [0, 1, 1], [0], 0),   # the row itself
+    (INFONCE_ROWS, [0, 1, 1], [3], 0),    # softmax kinds take no list
+])
+def test_extra_positive_lists_are_checked(rng, kind, row_ptr, col, off):
+    x = rng.standard_normal((6, 32))
+    q = x[off:off + 2]
+    with pytest.raises(ValueError):
+        contrastive_fwd_bwd(q, x, [32], 4.0, -1.0, kind, row_offset=off, grads=False,
+                            positives=(np.array(row_ptr), np.array(col)))
