@@ -47,6 +47,8 @@ class Options(ctypes.Structure):
         ("flags", ctypes.c_uint32),
         ("dscale_out", ctypes.c_void_p),
         ("dbias_out", ctypes.c_void_p),
+        ("pos_row_ptr", ctypes.POINTER(ctypes.c_int64)),
+        ("pos_col", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -71,6 +73,9 @@ def library() -> ctypes.CDLL:
     lib.uform_contrastive_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                       ctypes.c_int32, ctypes.c_int32]
     lib.uform_contrastive_workspace_bytes.restype = ctypes.c_size_t
+    lib.uform_contrastive_workspace_bytes_ex.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
+    lib.uform_contrastive_workspace_bytes_ex.restype = ctypes.c_size_t
     lib.uform_contrastive_supported.argtypes = [ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.c_int32]
     lib.uform_contrastive_supported.restype = ctypes.c_int
@@ -101,8 +106,10 @@ def supported(D: int, prefixes, kind: int, with_gradients: bool = True) -> int:
     return int(library().uform_contrastive_supported(D, pw, len(prefixes), kind, int(with_gradients)))
 
 
-def workspace_bytes(R: int, N: int, D: int, n_prefixes: int, kind: int) -> int:
-    return int(library().uform_contrastive_workspace_bytes(R, N, D, n_prefixes, kind))
+def workspace_bytes(R: int, N: int, D: int, n_prefixes: int, kind: int, n_positives: int | None = None) -> int:
+    if n_positives is None:
+        return int(library().uform_contrastive_workspace_bytes(R, N, D, n_prefixes, kind))
+    return int(library().uform_contrastive_workspace_bytes_ex(R, N, D, n_prefixes, kind, int(n_positives)))
 
 
 def profile() -> dict:
@@ -130,7 +137,8 @@ def _check(status: int) -> None:
 def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: float, kind: int, weights=None,
             row_offset: int = 0, want_dq: bool = True, want_dk: bool = True, extras: bool = False,
             dq: torch.Tensor | None = None, dk: torch.Tensor | None = None, accumulate: bool = False,
-            workspace: torch.Tensor | None = None, profile: bool = False, one_split: bool = False):
+            workspace: torch.Tensor | None = None, profile: bool = False, one_split: bool = False,
+            positives=None):
     """Loss and gradients of the Matryoshka contrastive loss on q's device.
 
     q [R, D] and k [N, D] are contiguous bfloat16 device tensors.  Returns
@@ -139,6 +147,8 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
     ``extras`` (and ``dscale``, ``dbias``: dL/dscale and dL/dbias, when a
     gradient is wanted).  Everything is enqueued on torch's current stream.  ``one_split`` runs each backward pass as
     one inner split (a diagnostic: the in-place finish that large problems take).
+    ``positives`` = (row_ptr, col), host integer arrays in CSR form, lists extra
+    positive cells of the sigmoid kinds (row i: columns col[row_ptr[i]:row_ptr[i + 1]]).
     """
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
         raise TypeError("q and k must be bfloat16")
@@ -186,6 +196,18 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
             ex["dbias"] = torch.empty(1, **f32)
             opt.dscale_out = ex["dscale"].data_ptr()
             opt.dbias_out = ex["dbias"].data_ptr()
+    pos_keep = None
+    if positives is not None:
+        import numpy as np
+        rp = np.ascontiguousarray(np.asarray(positives[0]), dtype=np.int64)
+        pc = np.ascontiguousarray(np.asarray(positives[1]), dtype=np.int32)
+        if rp.shape != (R + 1,):
+            raise ValueError("positives: row_ptr must have R + 1 entries")
+        if rp[-1] > pc.size:
+            raise ValueError("positives: col is shorter than row_ptr[R]")
+        pos_keep = (rp, pc)
+        opt.pos_row_ptr = rp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        opt.pos_col = pc.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     if workspace is not None:
         opt.workspace = workspace.data_ptr()
         opt.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -195,7 +217,7 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
         _ptr(q), _ptr(k), R, N, D, pw, P, float(scale), float(bias), int(kind), _ptr(loss), _ptr(dq), _ptr(dk),
         ctypes.c_void_p(stream), ctypes.byref(opt))
     _check(status)
-    del wbuf
+    del wbuf, pos_keep
     if extras:
         return loss, dq, dk, ex
     return loss, dq, dk

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libuform_contrastive.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["kernels.hip", "host.hip"]
+SOURCES = ["kernels.hip", "positives.hip", "host.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

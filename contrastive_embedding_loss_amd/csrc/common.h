@@ -144,6 +144,33 @@ hipError_t launch_maxes(const float *t0, const float *t1, const float *t2, const
 hipError_t launch_finalize(const FinArgs &a, hipStream_t s);
 hipError_t launch_loss(const LossArgs &a, hipStream_t s);
 
+// Extra positives of the sigmoid form (positives.hip).  A listed cell scored as a negative by
+// the main passes differs from its positive form by -l in the loss and by -1 in the residual.
+struct PosArgs {
+    const u16 *x, *y;          // outer rows [NO][D] and inner rows [NI][D], BF16
+    const float *invx, *invy;  // [P][NO], [P][NI]: 1 / |row[:w_p]|
+    int64_t NO, NI;
+    int D;
+    Prefixes pf;
+    const int32_t *ptr, *idx;  // outer row o's listed inner rows: idx[ptr[o] .. ptr[o + 1])
+    float t, b;                // logit scale and bias
+    float gc[kMaxP];           // -mirror (w_p / W) t / den: the gradient factor of one listed cell
+    float *out;                // [NO][D] FP32 gradient the corrections are added to, or nullptr
+    float *parts;              // [blocks][2][P]: the block's sums of -l^p and cos^p, or nullptr
+};
+struct PosFoldArgs {
+    const float *parts;  // [nblk][2][P]
+    int64_t nblk;
+    Prefixes pf;
+    double norm;         // 1 / den
+    float wnorm[kMaxP];
+    int64_t npos;        // listed cells
+    float *loss_out, *prefix_losses_out, *dscale_out, *dbias_out;  // updated in place (nullable but loss_out)
+};
+constexpr int kPosBlocks = 1024;  // most workgroups of one extra-positive pass
+hipError_t launch_pos(const PosArgs &a, hipStream_t s, int64_t *blocks_out);
+hipError_t launch_pos_fold(const PosFoldArgs &a, hipStream_t s);
+
 constexpr int kFwdTile = 128;   // forward tile (rows and columns)
 constexpr int kBwdOuter = 64;   // outer rows per backward workgroup
 constexpr int kBwdInner = 16;   // inner rows per backward block

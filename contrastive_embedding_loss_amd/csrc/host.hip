@@ -47,6 +47,9 @@ struct Plan {
     size_t o_qIYR, o_kIYR, o_sigq, o_sigk, o_gamq, o_gamk;
     size_t o_qC, o_qRho, o_qKap, o_kC, o_kRho, o_kKap, o_negfrac, o_kNegfrac, o_diagA, o_gmax;
     size_t o_rowpart, o_colpart, o_part, o_Cpart, o_loss, o_tsum, o_bias;
+    int64_t npos;                      // listed extra positives
+    bool pos_cols;                     // the column lists are needed (two-set sigmoid with dk)
+    size_t o_plist, o_pparts;           // extra positives: row then column lists, partial sums
     size_t total;
 };
 
@@ -70,7 +73,7 @@ uint32_t ladder_mask(const int32_t *pw, int32_t n) {
 }
 
 Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, int kind, int64_t off, bool want_dq,
-               bool want_dk, bool one_split = false) {
+               bool want_dk, bool one_split = false, int64_t npos = -1) {
     Plan p{};
     p.R = R;
     p.N = N;
@@ -146,6 +149,13 @@ Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, in
     // per-row radial sums of one gradient pass (dL/dscale); sigmoid bias partials (dL/dbias)
     p.o_tsum = take((want_dq || want_dk) ? sizeof(float) * (R > N ? R : N) : 0);
     p.o_bias = take((want_dq || want_dk) && !softmax ? sizeof(float) * p.nslots * P : 0);
+    // extra positives (npos >= 0: a list is given), int32 in one region (one copy): the row lists
+    // [R + 1 | npos], then, for dk of the two-set form, the column lists [N + 1 | npos]; then
+    // the pass's partial sums
+    p.npos = npos;
+    p.pos_cols = npos >= 0 && want_dk;
+    p.o_plist = take(npos >= 0 ? sizeof(int32_t) * ((R + 1 + npos) + (p.pos_cols ? N + 1 + npos : 0)) : 0);
+    p.o_pparts = take(npos >= 0 ? sizeof(float) * kPosBlocks * 2 * P : 0);
     p.total = off_b;
     return p;
 }
@@ -200,6 +210,28 @@ uform_status_t validate(const void *q, const void *k, int64_t R, int64_t N, int6
         if ((opt->dscale_out && !aligned(opt->dscale_out, 4)) || (opt->dbias_out && !aligned(opt->dbias_out, 4)))
             return fail(uform_status_invalid_argument_k, "dscale_out and dbias_out must be 4-byte aligned");
     }
+    if (opt && opt->pos_row_ptr) {
+        if (kind != kSiglip && kind != kOneset)
+            return fail(uform_status_invalid_argument_k, "extra positives are defined for the sigmoid kinds");
+        const int64_t *rp = opt->pos_row_ptr;
+        if (rp[0] != 0) return fail(uform_status_invalid_argument_k, "pos_row_ptr[0] must be 0");
+        for (int64_t i = 0; i < R; ++i)
+            if (rp[i + 1] < rp[i]) return fail(uform_status_invalid_argument_k, "pos_row_ptr must not decrease");
+        if (rp[R] > 0 && !opt->pos_col)
+            return fail(uform_status_invalid_argument_k, "pos_col must be a host array when positives are listed");
+        if (rp[R] >= ((int64_t)1 << 31) - 1)
+            return fail(uform_status_unsupported_k, "at most 2^31 - 2 extra positives per call");
+        for (int64_t i = 0; i < R; ++i) {
+            const int64_t g = off + i, own = kind == kOneset ? (g ^ 1) : g;
+            for (int64_t e = rp[i]; e < rp[i + 1]; ++e) {
+                const int64_t j = opt->pos_col[e];
+                if (j < 0 || j >= N || (e > rp[i] && j <= opt->pos_col[e - 1]) || j == own || (kind == kOneset && j == g))
+                    return fail(uform_status_invalid_argument_k,
+                                "row " + std::to_string(i) + ": extra positives must be increasing columns in [0, N), "
+                                "none of them the row's own positive (nor, in the one-set form, the row itself)");
+            }
+        }
+    }
     if (D % 64 != 0 || D > kMaxD) return fail(uform_status_unsupported_k, "D must be a multiple of 64 and at most 1024");
     const bool sigmoid_kind = kind == kSiglip || kind == kOneset;
     if (!sigmoid_kind && std::fabs(scale) > UFORM_CONTRASTIVE_MAX_SOFTMAX_SCALE)
@@ -218,6 +250,49 @@ struct Cached {
 };
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Cached> g_cache;
+
+// Pinned host staging of the extra-positive lists, one per device and stream.  The copy out of
+// it is enqueued on the stream; an event after the copy guards the buffer's next refill.
+struct Staging {
+    int32_t *host = nullptr;
+    size_t count = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+};
+std::map<std::pair<int, hipStream_t>, Staging> g_staging;
+
+// Fill the pinned staging buffer of (device, stream) through fill(buf) and enqueue its copy to dst.
+template <class Fill>
+uform_status_t stage_and_copy(hipStream_t s, int32_t *dst, size_t count, Fill fill) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(uform_status_device_error_k, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lock(g_mu);
+    Staging &st = g_staging[{dev, s}];
+    if (!st.ev && hipEventCreateWithFlags(&st.ev, hipEventDisableTiming) != hipSuccess) {
+        st.ev = nullptr;
+        return fail(uform_status_device_error_k, "hipEventCreate failed");
+    }
+    if (st.pending && hipEventSynchronize(st.ev) != hipSuccess)  // the previous copy out of the buffer is done
+        return fail(uform_status_device_error_k, "waiting for the previous list copy failed");
+    st.pending = false;
+    if (st.count < count) {
+        if (st.host) (void)hipHostFree(st.host);
+        st.host = nullptr;
+        st.count = 0;
+        if (hipHostMalloc((void **)&st.host, sizeof(int32_t) * count, hipHostMallocDefault) != hipSuccess || !st.host) {
+            (void)hipGetLastError();
+            st.host = nullptr;
+            return fail(uform_status_out_of_memory_k, "pinned staging allocation failed");
+        }
+        st.count = count;
+    }
+    fill(st.host);
+    if (hipMemcpyAsync(dst, st.host, sizeof(int32_t) * count, hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipEventRecord(st.ev, s) != hipSuccess)
+        return fail(uform_status_device_error_k, "enqueueing the list copy failed");
+    st.pending = true;
+    return uform_status_success_k;
+}
 
 uform_status_t get_workspace(hipStream_t s, size_t need, void **out) {
     int dev = 0;
@@ -306,8 +381,9 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     const float mirror = oneset ? 2.0f : 1.0f;
     const int64_t off = opt ? opt->row_offset : 0;
     const bool softmax = kind != kSiglip;
+    const int64_t npos = (opt && opt->pos_row_ptr) ? opt->pos_row_ptr[R] : -1;
     Plan pl = make_plan(R, N, D, prefixes, P, kind, off, dq != nullptr, dk != nullptr,
-                        opt && (opt->flags & UFORM_CONTRASTIVE_ONE_SPLIT));
+                        opt && (opt->flags & UFORM_CONTRASTIVE_ONE_SPLIT), npos);
 
     void *ws = nullptr;
     if (opt && opt->workspace) {
@@ -319,6 +395,30 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     }
     char *base = (char *)ws;
     auto F = [&](size_t o) { return (float *)(base + o); };
+    int32_t *const plist = npos >= 0 ? (int32_t *)(base + pl.o_plist) : nullptr;
+    int32_t *const clist = pl.pos_cols ? plist + (R + 1 + npos) : nullptr;  // right after the row lists
+    if (npos >= 0) {
+        // row lists as given; column lists (rows ascending per column) by a counting pass
+        const int64_t *rp = opt->pos_row_ptr;
+        const int32_t *pc = opt->pos_col;
+        const size_t nrow = (size_t)(R + 1 + npos), ncol = pl.pos_cols ? (size_t)(N + 1 + npos) : 0;
+        uform_status_t st = stage_and_copy(s, plist, nrow + ncol, [&](int32_t *h) {
+            for (int64_t i = 0; i <= R; ++i) h[i] = (int32_t)rp[i];
+            for (int64_t e = 0; e < npos; ++e) h[R + 1 + e] = pc[e];
+            if (!pl.pos_cols) return;
+            int32_t *cp = h + nrow, *cr = cp + N + 1;
+            for (int64_t j = 0; j <= N; ++j) cp[j] = 0;
+            for (int64_t e = 0; e < npos; ++e) ++cp[pc[e] + 1];
+            for (int64_t j = 0; j < N; ++j) cp[j + 1] += cp[j];
+            std::vector<int32_t> fill((size_t)N, 0);
+            for (int64_t i = 0; i < R; ++i)
+                for (int64_t e = rp[i]; e < rp[i + 1]; ++e) {
+                    const int32_t j = pc[e];
+                    cr[cp[j] + fill[j]++] = (int32_t)i;
+                }
+        });
+        if (st != uform_status_success_k) return st;
+    }
 
     Prefixes pf{};
     pf.n = P;
@@ -520,6 +620,41 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
         uform_status_t st = pass(false, dk);
         if (st != uform_status_success_k) return st;
     }
+    int64_t pos_blocks = 0;
+    if (npos >= 0) {
+        // listed cells: loss and row gradients over the row lists, column gradients over the column lists
+        PosArgs pa2{};
+        pa2.D = Di;
+        pa2.pf = pf;
+        pa2.t = scale;
+        pa2.b = bias;
+        pa2.x = q;
+        pa2.y = k;
+        pa2.invx = invq;
+        pa2.invy = invk;
+        pa2.NO = R;
+        pa2.NI = N;
+        pa2.ptr = plist;
+        pa2.idx = plist + R + 1;
+        for (int i = 0; i < P; ++i) pa2.gc[i] = (float)(-(double)mirror * wnorm[i] * scale / den);
+        pa2.out = dq;
+        pa2.parts = F(pl.o_pparts);
+        LAUNCH_NAMED("k_pos", launch_pos(pa2, s, &pos_blocks));
+        if (dk) {
+            pa2.x = k;
+            pa2.y = q;
+            pa2.invx = invk;
+            pa2.invy = invq;
+            pa2.NO = N;
+            pa2.NI = R;
+            pa2.ptr = clist;
+            pa2.idx = clist + N + 1;
+            for (int i = 0; i < P; ++i) pa2.gc[i] = (float)(-(double)wnorm[i] * scale / den);
+            pa2.out = dk;
+            pa2.parts = nullptr;
+            LAUNCH_NAMED("k_pos", launch_pos(pa2, s, nullptr));
+        }
+    }
 
     LossArgs la{};
     la.pf = pf;
@@ -536,6 +671,20 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     la.dscale_out = dscale_out;
     la.dbias_out = dbias_out;
     LAUNCH_NAMED("k_loss", launch_loss(la, s));
+    if (npos >= 0) {
+        PosFoldArgs fa{};
+        fa.parts = F(pl.o_pparts);
+        fa.nblk = pos_blocks;
+        fa.pf = pf;
+        fa.norm = 1.0 / den;
+        for (int i = 0; i < kMaxP; ++i) fa.wnorm[i] = wnorm[i];
+        fa.npos = npos;
+        fa.loss_out = loss_out;
+        fa.prefix_losses_out = la.prefix_losses_out;
+        fa.dscale_out = dscale_out;
+        fa.dbias_out = dbias_out;
+        LAUNCH_NAMED("k_pos_fold", launch_pos_fold(fa, s));
+    }
     return uform_status_success_k;
 }
 
@@ -598,13 +747,20 @@ uform_status_t uform_contrastive_fwd_bwd(const void *q, const void *k, int64_t R
 }
 
 size_t uform_contrastive_workspace_bytes(int64_t R, int64_t N, int64_t D, int32_t n_prefixes, int32_t kind) {
+    return uform_contrastive_workspace_bytes_ex(R, N, D, n_prefixes, kind, -1);
+}
+
+size_t uform_contrastive_workspace_bytes_ex(int64_t R, int64_t N, int64_t D, int32_t n_prefixes, int32_t kind,
+                                            int64_t n_positives) {
+    if (n_positives >= 0 && kind != kSiglip && kind != kOneset) return 0;
     if (R < 1 || N < 1 || R > N || D < 64 || D % 64 != 0 || D > kMaxD || n_prefixes < 1 || n_prefixes > kMaxP)
         return 0;
     if (kind != kInfonce && kind != kSiglip && kind != kRows && kind != kOneset) return 0;
     int32_t pw[kMaxP];
     for (int32_t i = 0; i < n_prefixes; ++i) pw[i] = (int32_t)(D - 32 * (n_prefixes - 1 - i));  // any ladder ending at D
-    if (kind == kOneset) return make_plan(R, N, D, pw, n_prefixes, kSiglip, 0, true, false).total;
-    return make_plan(R, N, D, pw, n_prefixes, kind, 0, true, true).total;
+    const int64_t npos = n_positives < 0 ? -1 : n_positives;
+    if (kind == kOneset) return make_plan(R, N, D, pw, n_prefixes, kSiglip, 0, true, false, false, npos).total;
+    return make_plan(R, N, D, pw, n_prefixes, kind, 0, true, true, false, npos).total;
 }
 
 uform_status_t uform_contrastive_supported(int64_t D, const int32_t *prefixes, int32_t n_prefixes, int32_t kind,
@@ -647,6 +803,14 @@ void uform_contrastive_release(void) {
         }
     }
     g_cache.clear();
+    for (auto &kv : g_staging) {
+        if (kv.second.ev) {
+            (void)hipEventSynchronize(kv.second.ev);
+            (void)hipEventDestroy(kv.second.ev);
+        }
+        if (kv.second.host) (void)hipHostFree(kv.second.host);
+    }
+    g_staging.clear();
 }
 
 }  // extern "C"

@@ -1,0 +1,170 @@
+// Several positives per entry for the sigmoid form.
+//
+// An entry of the batch may carry several positives besides its own pair
+// ("Scaling-Up Contrastive Learning over NVLink Multicast", the training-stack
+// paragraph on loader-side properties); each listed cell takes the label z = +1.
+// The main passes score every listed cell as a negative.  With l = t cos + b,
+// softplus(-l) - softplus(l) = -l and (sigma(l) - 1) - sigma(l) = -1, so the
+// listed cells change the loss by -l^p, the residual by -1/den, and the row
+// gradient by the derivative of -l^p through the prefix normalisation:
+//
+//   dx_o[:w_p] += c_p (y_i[:w_p] |x_o^p|^-1 |y_i^p|^-1 - cos^p x_o[:w_p] |x_o^p|^-2)
+//
+// with c_p = -mirror (w_p / W) t / den.  One wave owns one outer row and walks
+// its list in order, so every sum has a fixed order and no atomics are needed.
+// The lists are sparse (a few cells per row against the N of the dense pass):
+// the pass is a gather of listed rows, bound by HBM and latency, not by MFMA.
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace uform {
+namespace {
+
+__device__ __forceinline__ float wsum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+// 16 BF16 values (32 bytes, 16-byte aligned) widened to FP32.
+__device__ __forceinline__ void load16(const u16 *p, float v[16]) {
+    const uint4 a = *(const uint4 *)p, b = *(const uint4 *)(p + 8);
+    const unsigned int w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        v[2 * c] = __uint_as_float(w[c] << 16);
+        v[2 * c + 1] = __uint_as_float(w[c] & 0xffff0000u);
+    }
+}
+
+// Lane l holds elements 16 l .. 16 l + 15 of a row (D <= 1024); waves walk the outer rows
+// blockIdx.x * 4 + wave, stepping by the grid.
+__global__ __launch_bounds__(256) void k_pos(PosArgs a) {
+    __shared__ float red[4][2 * kMaxP];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int P = a.pf.n, D = a.D;
+    const int d0 = 16 * lane;
+    const bool act = d0 < D;
+    int pl = P;  // the narrowest prefix that covers this lane's elements (P: none)
+    for (int p = P - 1; p >= 0; --p)
+        if (d0 < a.pf.w[p]) pl = p;
+    float ls[kMaxP], cs[kMaxP];  // sums of -l^p and cos^p over this wave's cells (wave-uniform)
+#pragma unroll
+    for (int p = 0; p < kMaxP; ++p) ls[p] = cs[p] = 0.f;
+
+    for (int64_t o = (int64_t)blockIdx.x * 4 + wave; o < a.NO; o += (int64_t)gridDim.x * 4) {
+        const int e0 = a.ptr[o], e1 = a.ptr[o + 1];
+        if (e0 >= e1) continue;
+        float xv[16];
+        if (act)
+            load16(a.x + o * D + d0, xv);
+        else
+            for (int c = 0; c < 16; ++c) xv[c] = 0.f;
+        float ix[kMaxP];
+        for (int p = 0; p < P; ++p) ix[p] = a.invx[p * a.NO + o];
+        float acc[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) acc[c] = 0.f;
+        float xc = 0.f;  // sum over cells and covering prefixes of c_p cos^p |x^p|^-2
+        for (int e = e0; e < e1; ++e) {
+            const int64_t i = a.idx[e];
+            float yv[16];
+            if (act)
+                load16(a.y + i * D + d0, yv);
+            else
+                for (int c = 0; c < 16; ++c) yv[c] = 0.f;
+            float part = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) part = fmaf(xv[c], yv[c], part);
+            float yc = 0.f;  // sum over covering prefixes of c_p |x^p|^-1 |y^p|^-1
+            for (int p = 0; p < P; ++p) {
+                const float dot = wsum(d0 < a.pf.w[p] ? part : 0.f);
+                const float iy = a.invy[p * a.NI + i];
+                const float cosv = dot * ix[p] * iy;
+                ls[p] -= fmaf(a.t, cosv, a.b);
+                cs[p] += cosv;
+                if (p >= pl) {
+                    yc = fmaf(a.gc[p], ix[p] * iy, yc);
+                    xc = fmaf(a.gc[p], cosv * ix[p] * ix[p], xc);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 16; ++c) acc[c] = fmaf(yc, yv[c], acc[c]);
+        }
+        if (a.out && act && pl < P) {
+            float4 *dst = (float4 *)(a.out + o * D + d0);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float4 v = dst[c];
+                v.x += acc[4 * c] - xc * xv[4 * c];
+                v.y += acc[4 * c + 1] - xc * xv[4 * c + 1];
+                v.z += acc[4 * c + 2] - xc * xv[4 * c + 2];
+                v.w += acc[4 * c + 3] - xc * xv[4 * c + 3];
+                dst[c] = v;
+            }
+        }
+    }
+    if (!a.parts) return;
+    if (lane == 0)
+        for (int p = 0; p < P; ++p) {
+            red[wave][p] = ls[p];
+            red[wave][kMaxP + p] = cs[p];
+        }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < 2 * P) {
+        const int slot = t < P ? t : kMaxP + (t - P);
+        const float v = (red[0][slot] + red[1][slot]) + (red[2][slot] + red[3][slot]);
+        a.parts[(int64_t)blockIdx.x * 2 * P + t] = v;  // [block][0: -l | 1: cos][p]
+    }
+}
+
+// One workgroup: fixed-order sums of the blocks' partials, folded into the outputs of the
+// dense passes (loss, L^p, dL/dscale, dL/dbias).
+__global__ __launch_bounds__(256) void k_pos_fold(PosFoldArgs a) {
+    __shared__ double red[256];
+    __shared__ double sums[2 * kMaxP];
+    const int P = a.pf.n;
+    for (int t = 0; t < 2 * P; ++t) {
+        double v = 0.0;
+        for (int64_t b = threadIdx.x; b < a.nblk; b += 256) v += (double)a.parts[b * 2 * P + t];
+        red[threadIdx.x] = v;
+        __syncthreads();
+        for (int h = 128; h >= 1; h >>= 1) {
+            if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) sums[t] = red[0];
+        __syncthreads();
+    }
+    if (threadIdx.x != 0) return;
+    double dloss = 0.0, dscale = 0.0;
+    for (int p = 0; p < P; ++p) {
+        const double dl = sums[p] * a.norm;  // change of L^p
+        if (a.prefix_losses_out) a.prefix_losses_out[p] = (float)((double)a.prefix_losses_out[p] + dl);
+        dloss += (double)a.wnorm[p] * dl;
+        dscale -= (double)a.wnorm[p] * sums[P + p] * a.norm;
+    }
+    *a.loss_out = (float)((double)*a.loss_out + dloss);
+    if (a.dscale_out) *a.dscale_out = (float)((double)*a.dscale_out + dscale);
+    if (a.dbias_out) *a.dbias_out = (float)((double)*a.dbias_out - (double)a.npos * a.norm);
+}
+
+}  // namespace
+
+hipError_t launch_pos(const PosArgs &a, hipStream_t s, int64_t *blocks_out) {
+    int64_t blocks = (a.NO + 3) / 4;
+    if (blocks > kPosBlocks) blocks = kPosBlocks;
+    if (blocks_out) *blocks_out = blocks;
+    hipLaunchKernelGGL(k_pos, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_pos_fold(const PosFoldArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_pos_fold, dim3(1), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace uform

@@ -121,3 +121,72 @@ def make_inputs(R: int, N: int, D: int, recipe: str = "gauss", noise: float = 0.
 def workload_inputs(w: Workload):
     return make_inputs(w.R, w.N, w.D, w.recipe, w.noise, w.seed,
                        w.extra.get("centroids", 256), w.row_offset)
+
+
+def make_band_inputs(R: int, D: int, extra_pos: int = 2, hard_neg: int = 2, noise: float = 0.3,
+                     hard_noise: float = 1.0, seed: int = 0):
+    """Entries with several positives and explicit hard negatives, gathered as extra key rows.
+
+    Each entry may carry several positives and explicit hard negatives that the
+    loss gathers as extra columns ("Scaling-Up Contrastive Learning over NVLink
+    Multicast", the training-stack paragraph on loader-side properties).  Draws,
+    in order: q ~ N(0,1) [R, D]; own keys k_i = q_i + noise * N(0,1); per entry
+    i (in order) a count m_i ~ U{0..2 extra_pos}; then for each entry in order
+    its m_i extra positives q_i + noise * N(0,1) and its hard_neg hard negatives
+    q_i + hard_noise * N(0,1), appended after the R own keys.  Returns the BF16
+    bits of q [R, D] and k [N, D] and the CSR lists (row_ptr int64 [R + 1],
+    col int32) of each entry's extra positive columns.
+    """
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((R, D))
+    rows = [q + noise * rng.standard_normal((R, D))]
+    m = rng.integers(0, 2 * extra_pos + 1, size=R)
+    row_ptr = np.zeros(R + 1, dtype=np.int64)
+    cols = []
+    n = R
+    for i in range(R):
+        if m[i]:
+            rows.append(q[i] + noise * rng.standard_normal((int(m[i]), D)))
+            cols.extend(range(n, n + int(m[i])))
+            n += int(m[i])
+        if hard_neg:
+            rows.append(q[i] + hard_noise * rng.standard_normal((hard_neg, D)))
+            n += hard_neg
+        row_ptr[i + 1] = len(cols)
+    k = np.concatenate(rows)
+    to_bits = lambda x: f32_to_bf16_bits(x.astype(np.float32))  # noqa: E731
+    return to_bits(q), to_bits(k), row_ptr, np.asarray(cols, dtype=np.int32)
+
+
+def random_positive_lists(R: int, N: int, row_offset: int, mean: float, seed: int, oneset: bool = False,
+                          dense_row: int | None = None):
+    """Seeded random extra-positive lists (CSR) over R local rows of N keys.
+
+    Each cell (i, j) other than the row's own positive (row_offset + i; in the
+    one-set form its partner (row_offset + i) xor 1 and the row itself) is
+    listed with probability mean / N; row ``dense_row`` (if given) lists every
+    allowed column.  The one-set form draws over the whole set and keeps
+    (i, j) and (j, i) together, then returns the rows of the share.
+    """
+    rng = np.random.default_rng(seed)
+    Rs, off = (N, 0) if oneset else (R, row_offset)
+    pick = rng.random((Rs, N)) < mean / N
+    if oneset:
+        pick = np.triu(pick, 1)
+        pick = pick | pick.T
+    g = np.arange(Rs) + off
+    own = g ^ 1 if oneset else g
+    pick[np.arange(Rs), own] = False
+    if oneset:
+        pick[np.arange(Rs), g] = False
+    if oneset:
+        pick = pick[row_offset:row_offset + R]
+        g, own = g[row_offset:row_offset + R], own[row_offset:row_offset + R]
+    if dense_row is not None:
+        pick[dense_row] = True
+        pick[dense_row, own[dense_row]] = False
+        if oneset:
+            pick[dense_row, g[dense_row]] = False
+    counts = pick.sum(axis=1)
+    row_ptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return row_ptr, np.nonzero(pick)[1].astype(np.int32)

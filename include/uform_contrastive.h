@@ -137,6 +137,30 @@ typedef struct {
      * that sets either must give dq or dk (else invalid-argument).  Nullable. */
     float *dscale_out;
     float *dbias_out;
+    /* Several positives per entry, sigmoid kinds only ("Scaling-Up
+     * Contrastive Learning over NVLink Multicast", the training-stack
+     * paragraph on loader-side properties: an entry may carry several
+     * positives and explicit hard negatives).  HOST CSR lists, read during the
+     * call only: local row i's extra positives are the key (set) indices
+     * pos_col[pos_row_ptr[i] .. pos_row_ptr[i + 1] - 1], and every listed cell
+     * gets the label z = +1 like the row's own positive (loss, dq, dk,
+     * dL/dscale, dL/dbias and L^p all follow).  pos_row_ptr has R + 1 entries
+     * with pos_row_ptr[0] = 0, never decreasing, and pos_row_ptr[R] <= 2^31 - 3;
+     * a row's columns are strictly increasing, in [0, N), and none of them is
+     * the row's own positive (row_offset + i; in the one-set form its pair
+     * partner (row_offset + i) xor 1 and the row itself).  A list that breaks
+     * this, or a list with a softmax kind, is invalid-argument.  In the
+     * one-set form list both (i, j) and (j, i) so that mirrored cells keep
+     * equal labels.  Explicit hard negatives need no list: append them to k
+     * as extra key rows (N > R), which every row scores as negatives.  The
+     * lists reach the device through a pinned staging buffer per stream and a
+     * copy enqueued on the stream; the call waits (on the host) only for the
+     * previous call's list copy on that stream.  Such a call cannot be captured
+     * into a graph.  A caller-given workspace must hold
+     * uform_contrastive_workspace_bytes_ex(..., pos_row_ptr[R]) bytes.
+     * pos_row_ptr = NULL: no extra positives. */
+    const int64_t *pos_row_ptr;
+    const int32_t *pos_col;
 } uform_contrastive_options_t;
 
 #define UFORM_CONTRASTIVE_ACCUMULATE 1u
@@ -157,6 +181,11 @@ uform_status_t uform_contrastive_fwd_bwd_ex(const void *q, const void *k, int64_
 /* Device workspace a call of this shape needs, in bytes (gradients included);
  * 0 for arguments the call would reject. */
 size_t uform_contrastive_workspace_bytes(int64_t R, int64_t N, int64_t D, int32_t n_prefixes, int32_t kind);
+
+/* As above, for a call that lists n_positives extra positives (pos_row_ptr[R];
+ * sigmoid kinds only, else 0); n_positives < 0 means no list. */
+size_t uform_contrastive_workspace_bytes_ex(int64_t R, int64_t N, int64_t D, int32_t n_prefixes, int32_t kind,
+                                            int64_t n_positives);
 
 /* Whether a call with this width, prefix ladder and kind can run, without
  * touching any device: success, invalid-argument or unsupported (the reason

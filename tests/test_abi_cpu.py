@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from contrastive_embedding_loss_amd import binding
@@ -23,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     lib = binding.library()
     for n in names:
         assert hasattr(lib, n), n
@@ -133,3 +134,49 @@ def test_other_ladders_need_the_forward_only(prefixes):
     assert binding.supported(1024, prefixes, 0) == 2
     assert binding.supported(1024, prefixes, 1, with_gradients=False) == 2  # SigLIP's loss needs the backward
     assert binding.supported(1024, prefixes, 0, with_gradients=False) == 0
+
+
+@pytest.mark.parametrize("kind,R,N,off,row_ptr,col", [
+    (1, 2, 8, 0, [1, 1, 1], []),            # row_ptr[0] != 0
+    (1, 2, 8, 0, [0, 2, 1], [3, 4]),        # decreasing row_ptr
+    (1, 2, 8, 0, [0, 1, 1], [0]),           # row 0's own positive
+    (1, 2, 8, 3, [0, 0, 1], [4]),           # row 1's own positive (offset 3)
+    (1, 2, 8, 0, [0, 2, 2], [5, 5]),        # repeated column
+    (1, 2, 8, 0, [0, 2, 2], [6, 2]),        # decreasing columns
+    (1, 2, 8, 0, [0, 1, 1], [8]),           # past N
+    (1, 2, 8, 0, [0, 1, 1], [-2]),          # negative
+    (0, 8, 8, 0, [0] * 8 + [1], [3]),       # softmax kinds take no list
+    (2, 2, 8, 0, [0, 1, 1], [3]),
+    (3, 2, 8, 0, [0, 1, 1], [1]),           # one-set: row 0's pair partner
+    (3, 2, 8, 0, [0, 0, 1], [1]),           # one-set: row 1 itself
+])
+def test_positive_list_checks(kind, R, N, off, row_ptr, col):
+    rp = np.asarray(row_ptr, dtype=np.int64)
+    pc = np.asarray(col if col else [0], dtype=np.int32)
+    opt = binding.Options()
+    opt.row_offset = off
+    opt.pos_row_ptr = rp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    opt.pos_col = pc.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    k = 0x20000
+    q = k + 2 * off * 1024 if kind == 3 else 0x10000
+    dk = 0 if kind == 3 else 0x50000
+    assert _call(q=q, k=k, R=R, N=N, kind=kind, dk=dk, opt=opt) == 1, binding.last_error()
+    msg = binding.last_error()
+    assert ("sigmoid" in msg) if kind in (0, 2) else ("pos_row_ptr" in msg or "row " in msg), msg
+
+
+def test_positive_list_needs_col_array():
+    rp = np.asarray([0, 1, 1], dtype=np.int64)
+    opt = binding.Options()
+    opt.pos_row_ptr = rp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    assert _call(R=2, N=8, kind=1, opt=opt) == 1
+    assert "pos_col" in binding.last_error()
+
+
+def test_workspace_bytes_with_positives():
+    base = binding.workspace_bytes(256, 1024, 1024, 5, 1)
+    with_list = binding.workspace_bytes(256, 1024, 1024, 5, 1, 5000)
+    assert with_list >= base + 4 * (257 + 1025 + 2 * 5000)
+    assert binding.workspace_bytes(256, 1024, 1024, 5, 1, -1) == base
+    assert binding.workspace_bytes(256, 256, 1024, 5, 0, 10) == 0  # softmax kinds take no list
+    assert binding.workspace_bytes(256, 1024, 1024, 5, 3, 5000) > binding.workspace_bytes(256, 1024, 1024, 5, 3)

@@ -289,3 +289,87 @@ def test_oneset_edge_shares(N, R, off):
     assert abs(loss.item() - ref["loss"]) <= 1e-3 * abs(ref["loss"]) + 1e-7, (loss.item(), ref["loss"])
     assert np.abs(dq.cpu().numpy() - ref["dq"]).max() <= 2e-3 * np.abs(ref["dq"]).max() + 1e-12
     assert ex["dscale"].item() == pytest.approx(ref["dscale"], rel=1e-3, abs=1e-7)
+
+
+# ----------------------------------------------------------------------------- several positives per entry
+
+def _pos_case(qb, kb, prefixes, s, b, kind, off, positives, want_dq=True, want_dk=True, label=""):
+    from oracle import ONESET_SIGLIP as ORACLE_ONESET
+    from contrastive_embedding_loss_amd.inputs import ONESET_SIGLIP
+    R, N = qb.shape[0], kb.shape[0]
+    print(f"[case] positives {label} R={R} N={N} D={qb.shape[1]} kind={kind} off={off} "
+          f"listed={int(positives[0][-1])} dq={want_dq} dk={want_dk}", flush=True)
+    k = to_dev(kb)
+    q = k[off:off + R] if kind == ONESET_SIGLIP else to_dev(qb)
+    loss, dq, dk, ex = binding.fwd_bwd(q, k, prefixes, s, b, kind, row_offset=off, extras=True,
+                                       want_dq=want_dq, want_dk=want_dk, positives=positives)
+    torch.cuda.synchronize()
+    okind = ORACLE_ONESET if kind == ONESET_SIGLIP else kind
+    ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), prefixes, s, b, okind, row_offset=off,
+                              positives=positives)
+    assert abs(loss.item() - ref["loss"]) <= 1e-3 * abs(ref["loss"]), (loss.item(), ref["loss"])
+    np.testing.assert_allclose(ex["prefix_losses"].cpu().numpy(), ref["prefix_losses"], rtol=1e-3)
+    for name, g in (("dq", dq), ("dk", dk)):
+        if g is None:
+            continue
+        e = np.abs(g.cpu().numpy() - ref[name]).max()
+        assert e <= 2e-3 * np.abs(ref[name]).max(), (name, e)
+    if "dscale" in ex:
+        assert ex["dscale"].item() == pytest.approx(ref["dscale"], rel=1e-3, abs=1e-6)
+        assert ex["dbias"].item() == pytest.approx(ref["dbias"], rel=1e-3, abs=1e-6)
+    return loss, dq, dk
+
+
+@pytest.mark.parametrize("R,extra_pos,hard_neg,D,prefixes", [
+    (200, 2, 2, 1024, LADDER), (96, 3, 0, 1024, LADDER), (130, 1, 3, 192, (64, 128))])
+def test_band_entries_with_positives_and_hard_negatives(R, extra_pos, hard_neg, D, prefixes):
+    from contrastive_embedding_loss_amd.inputs import make_band_inputs
+    qb, kb, rp, col = make_band_inputs(R, D, extra_pos, hard_neg, noise=0.5, seed=131 + R)
+    _pos_case(qb, kb, prefixes, 10.0, -10.0, SIGLIP, 0, (rp, col), label="band")
+
+
+@pytest.mark.parametrize("R,N,off,mean,dense_row,want_dq,want_dk", [
+    (150, 400, 200, 5.0, 7, True, True), (150, 400, 200, 5.0, None, False, True),
+    (150, 400, 200, 5.0, None, True, False), (64, 64, 0, 60.0, 3, True, True)])
+def test_random_positive_lists_two_set(R, N, off, mean, dense_row, want_dq, want_dk):
+    from contrastive_embedding_loss_amd.inputs import random_positive_lists
+    qb, kb = make_inputs(R, N, 1024, noise=0.6, seed=141 + R, row_offset=off)
+    pos = random_positive_lists(R, N, off, mean, seed=142 + R, dense_row=dense_row)
+    _pos_case(qb, kb, LADDER, 8.0, -5.0, SIGLIP, off, pos, want_dq=want_dq, want_dk=want_dk, label="random")
+
+
+@pytest.mark.parametrize("N,R,off,dense_row", [(256, 96, 64, 5), (300, 300, 0, None)])
+def test_random_positive_lists_oneset(N, R, off, dense_row):
+    from contrastive_embedding_loss_amd.inputs import ONESET_SIGLIP, random_positive_lists
+    qb, kb = make_inputs(R, N, 1024, recipe="pairs", noise=0.6, seed=151 + R, row_offset=off)
+    pos = random_positive_lists(R, N, off, 4.0, seed=152 + R, oneset=True, dense_row=dense_row)
+    _pos_case(qb, kb, LADDER, 10.0, -6.0, ONESET_SIGLIP, off, pos, label="oneset")
+
+
+def test_positive_list_edge_cases():
+    from contrastive_embedding_loss_amd.inputs import random_positive_lists
+    qb, kb = make_inputs(100, 160, 1024, noise=0.6, seed=161, row_offset=30)
+    q, k = to_dev(qb), to_dev(kb)
+    print("[case] positives: empty list equals no list; loss-only equals the full call; own workspace", flush=True)
+    plain = binding.fwd_bwd(q, k, LADDER, 10.0, -10.0, SIGLIP, row_offset=30, extras=True)
+    empty = binding.fwd_bwd(q, k, LADDER, 10.0, -10.0, SIGLIP, row_offset=30, extras=True,
+                            positives=(np.zeros(101, dtype=np.int64), np.zeros(0, dtype=np.int32)))
+    for a, b in zip(plain[:3], empty[:3]):
+        assert torch.equal(a, b)
+    for name in ("prefix_losses", "dscale", "dbias"):
+        assert torch.equal(plain[3][name], empty[3][name]), name
+    pos = random_positive_lists(100, 160, 30, 6.0, seed=162)
+    full = binding.fwd_bwd(q, k, LADDER, 10.0, -10.0, SIGLIP, row_offset=30, positives=pos)
+    only = binding.fwd_bwd(q, k, LADDER, 10.0, -10.0, SIGLIP, row_offset=30, positives=pos, want_dq=False,
+                           want_dk=False)
+    assert torch.equal(full[0], only[0])
+    nbytes = binding.workspace_bytes(100, 160, 1024, len(LADDER), SIGLIP, int(pos[0][-1]))
+    assert nbytes > binding.workspace_bytes(100, 160, 1024, len(LADDER), SIGLIP)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    own = binding.fwd_bwd(q, k, LADDER, 10.0, -10.0, SIGLIP, row_offset=30, positives=pos, workspace=ws)
+    for a, b in zip(full, own):
+        assert torch.equal(a, b)
+    # a list one byte short of its workspace is refused before any launch
+    with pytest.raises(binding.UformError):
+        binding.fwd_bwd(q, k, LADDER, 10.0, -10.0, SIGLIP, row_offset=30, positives=pos, workspace=ws[:nbytes - 512])
+    torch.cuda.synchronize()
