@@ -67,7 +67,7 @@ def main():
 
     from contrastive_embedding_loss_amd import binding
     from contrastive_embedding_loss_amd.inputs import (ONESET_SIGLIP, WORKLOADS, bf16_bits_to_f32, make_inputs,
-                                                       workload_inputs)
+                                                       workload_inputs, workload_positives)
 
     dev = torch.device("cuda:0")
     if args.copy_calibration:
@@ -97,9 +97,12 @@ def main():
     dq = torch.empty(R, D, **f32)
     dk = None if oneset else torch.empty(N, D, **f32)
 
+    positives = workload_positives(w)  # entries with several positives: host CSR lists, staged each step
+
     def step(profile=False):
         return binding.fwd_bwd(q, k, w.prefixes, w.scale, w.bias, w.kind, weights=w.weights,
-                               row_offset=w.row_offset, dq=dq, dk=dk, want_dk=not oneset, profile=profile)
+                               row_offset=w.row_offset, dq=dq, dk=dk, want_dk=not oneset, profile=profile,
+                               positives=positives)
 
     for _ in range(args.warmup):
         step()
@@ -144,20 +147,29 @@ def main():
         from oracle import bf16_bits_to_f64, contrastive_fwd_bwd
 
         n_s = min(args.cpu_sample, R)
-        qs, ks = make_inputs(n_s, n_s, D, w.recipe, w.noise, w.seed, w.extra.get("centroids", 256))
+        pos_s = None
+        if w.recipe == "band":  # entries of the same recipe, about n_s keys in all
+            from contrastive_embedding_loss_amd.inputs import make_band_inputs
+            e = w.extra
+            qs, ks, rp_s, col_s = make_band_inputs(max(1, n_s * R // N), D, e["extra_pos"], e["hard_neg"], w.noise,
+                                                   e["hard_noise"], w.seed)
+            pos_s = (rp_s, col_s)
+        else:
+            qs, ks = make_inputs(n_s, n_s, D, w.recipe, w.noise, w.seed, w.extra.get("centroids", 256))
         if oneset:
             qs = ks  # the one-set sample scores its whole set
+        r_s, c_s = qs.shape[0], ks.shape[0]
         cores = len(os.sched_getaffinity(0))
-        print(f"[bench] oracle sample {n_s}x{n_s} on {cores} cores", file=sys.stderr, flush=True)
+        print(f"[bench] oracle sample {r_s}x{c_s} on {cores} cores", file=sys.stderr, flush=True)
         kind = w.kind
         t1 = time.perf_counter()
         contrastive_fwd_bwd(bf16_bits_to_f64(qs), bf16_bits_to_f64(ks), w.prefixes, w.scale, w.bias, kind,
-                            weights=w.weights, threads=cores)
+                            weights=w.weights, threads=cores, positives=pos_s)
         tc = time.perf_counter() - t1
         fl = 4.0 if oneset else 8.0
-        cpu = {"value": round(fl * n_s * n_s * D / tc / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+        cpu = {"value": round(fl * r_s * c_s * D / tc / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
                "kind": "oracle",
-               "sample": f"FP64 oracle fwd+bwd on a {n_s}x{n_s} batch of the same recipe and prefixes "
+               "sample": f"FP64 oracle fwd+bwd on a {r_s}x{c_s} batch of the same recipe and prefixes "
                          f"({tc:.1f} s), rate = {fl:.0f}*R*N*D/t"}
 
     out = {
@@ -176,7 +188,8 @@ def main():
         "config": {"workload": w.name, "R": R, "N": N, "D": D, "prefixes": list(w.prefixes),
                    "kind": ["infonce", "siglip", "infonce_rows", "oneset_siglip"][w.kind], "scale": w.scale,
                    "bias": w.bias,
-                   "weights": list(w.weights) if w.weights else None, "recipe": w.recipe},
+                   "weights": list(w.weights) if w.weights else None, "recipe": w.recipe,
+                   **({"extra_positives": int(positives[0][-1])} if positives is not None else {})},
         "pair_scores_per_s": pair_scores,
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernel_ms_per_step": {n: round(t, 4) for n, t in kern_per_step.items()},

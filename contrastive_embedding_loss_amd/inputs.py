@@ -119,8 +119,22 @@ def make_inputs(R: int, N: int, D: int, recipe: str = "gauss", noise: float = 0.
 
 
 def workload_inputs(w: Workload):
+    if w.recipe == "band":
+        return make_band_inputs(w.R, w.D, w.extra["extra_pos"], w.extra["hard_neg"], w.noise,
+                                w.extra["hard_noise"], w.seed)[:2]
     return make_inputs(w.R, w.N, w.D, w.recipe, w.noise, w.seed,
                        w.extra.get("centroids", 256), w.row_offset)
+
+
+def band_lists(R: int, extra_pos: int, hard_neg: int):
+    """Key layout of the band recipe: entry i carries m_i = i mod (2 extra_pos + 1) extra positives
+    and hard_neg hard negatives, appended in entry order after the R own keys.  Returns the CSR
+    lists (row_ptr int64 [R + 1], col int32) of the extra positive columns and the key count N."""
+    m = np.arange(R, dtype=np.int64) % (2 * extra_pos + 1)
+    first = R + np.concatenate([[0], np.cumsum(m + hard_neg)[:-1]])  # first appended key of each entry
+    row_ptr = np.concatenate([[0], np.cumsum(m)]).astype(np.int64)
+    col = (np.repeat(first - row_ptr[:-1], m) + np.arange(int(row_ptr[-1]))).astype(np.int32)
+    return row_ptr, col, int(R + m.sum() + R * hard_neg)
 
 
 def make_band_inputs(R: int, D: int, extra_pos: int = 2, hard_neg: int = 2, noise: float = 0.3,
@@ -129,33 +143,25 @@ def make_band_inputs(R: int, D: int, extra_pos: int = 2, hard_neg: int = 2, nois
 
     Each entry may carry several positives and explicit hard negatives that the
     loss gathers as extra columns ("Scaling-Up Contrastive Learning over NVLink
-    Multicast", the training-stack paragraph on loader-side properties).  Draws,
-    in order: q ~ N(0,1) [R, D]; own keys k_i = q_i + noise * N(0,1); per entry
-    i (in order) a count m_i ~ U{0..2 extra_pos}; then for each entry in order
-    its m_i extra positives q_i + noise * N(0,1) and its hard_neg hard negatives
-    q_i + hard_noise * N(0,1), appended after the R own keys.  Returns the BF16
-    bits of q [R, D] and k [N, D] and the CSR lists (row_ptr int64 [R + 1],
-    col int32) of each entry's extra positive columns.
+    Multicast", the training-stack paragraph on loader-side properties).  Layout
+    as in ``band_lists``.  Draws, in order: q ~ N(0,1) [R, D]; own keys
+    k_i = q_i + noise * N(0,1); then one N(0,1) matrix for all appended keys in
+    key order, each appended key being its entry's q_i plus noise (extra
+    positives) or hard_noise (hard negatives) times its row of that matrix.
+    Returns the BF16 bits of q [R, D] and k [N, D] and the CSR lists.
     """
+    row_ptr, col, N = band_lists(R, extra_pos, hard_neg)
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((R, D))
-    rows = [q + noise * rng.standard_normal((R, D))]
-    m = rng.integers(0, 2 * extra_pos + 1, size=R)
-    row_ptr = np.zeros(R + 1, dtype=np.int64)
-    cols = []
-    n = R
-    for i in range(R):
-        if m[i]:
-            rows.append(q[i] + noise * rng.standard_normal((int(m[i]), D)))
-            cols.extend(range(n, n + int(m[i])))
-            n += int(m[i])
-        if hard_neg:
-            rows.append(q[i] + hard_noise * rng.standard_normal((hard_neg, D)))
-            n += hard_neg
-        row_ptr[i + 1] = len(cols)
-    k = np.concatenate(rows)
+    own = q + noise * rng.standard_normal((R, D))
+    m = np.diff(row_ptr)
+    entry = np.repeat(np.arange(R), m + hard_neg)  # the entry of each appended key
+    # within an entry: its m_i positives first, then its hard negatives
+    rank = np.arange(N - R) - np.repeat(np.concatenate([[0], np.cumsum(m + hard_neg)[:-1]]), m + hard_neg)
+    amp = np.where(rank < m[entry], noise, hard_noise)
+    k = np.concatenate([own, q[entry] + amp[:, None] * rng.standard_normal((N - R, D))])
     to_bits = lambda x: f32_to_bf16_bits(x.astype(np.float32))  # noqa: E731
-    return to_bits(q), to_bits(k), row_ptr, np.asarray(cols, dtype=np.int32)
+    return to_bits(q), to_bits(k), row_ptr, col
 
 
 def random_positive_lists(R: int, N: int, row_offset: int, mean: float, seed: int, oneset: bool = False,
@@ -190,3 +196,18 @@ def random_positive_lists(R: int, N: int, row_offset: int, mean: float, seed: in
     counts = pick.sum(axis=1)
     row_ptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     return row_ptr, np.nonzero(pick)[1].astype(np.int32)
+
+
+# Two-set sigmoid batches whose entries carry several positives (0..4, two on average) and two
+# explicit hard negatives each, appended as extra key rows (16384 entries: N = 16384 * 5).
+WORKLOADS["siglip_band_16384"] = Workload(
+    "siglip_band_16384", SIGLIP, 16384, band_lists(16384, 2, 2)[2], scale=10.0, bias=-10.0, recipe="band",
+    noise=0.5, seed=6, extra={"extra_pos": 2, "hard_neg": 2, "hard_noise": 1.0})
+
+
+def workload_positives(w: Workload):
+    """The extra-positive lists of a workload (band recipe), else None."""
+    if w.recipe != "band":
+        return None
+    row_ptr, col, _ = band_lists(w.R, w.extra["extra_pos"], w.extra["hard_neg"])
+    return row_ptr, col

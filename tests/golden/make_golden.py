@@ -30,10 +30,11 @@ import numpy as np
 ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 sys.path.insert(0, ROOT)
 
-from contrastive_embedding_loss_amd.inputs import ONESET_SIGLIP, SIGLIP, WORKLOADS, workload_inputs  # noqa: E402
+from contrastive_embedding_loss_amd.inputs import (  # noqa: E402
+    ONESET_SIGLIP, SIGLIP, WORKLOADS, workload_inputs, workload_positives)
 from oracle import bf16_bits_to_f64, contrastive_fwd_bwd  # noqa: E402
 
-LARGE = ("siglip_16384", "rows_4096x65536", "infonce_32768", "oneset_16384x131072")
+LARGE = ("siglip_16384", "rows_4096x65536", "infonce_32768", "oneset_16384x131072", "siglip_band_16384")
 
 
 def sample_indices(n: int, count: int, seed: int) -> np.ndarray:
@@ -49,7 +50,7 @@ def make(name: str) -> str:
     qb, kb = workload_inputs(w)
     t0 = time.time()
     ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), w.prefixes, w.scale, w.bias, w.kind,
-                              weights=w.weights, row_offset=w.row_offset)
+                              weights=w.weights, row_offset=w.row_offset, positives=workload_positives(w))
     out = {
         "loss": np.float64(ref["loss"]),
         "prefix_losses": np.asarray(ref["prefix_losses"], dtype=np.float64),

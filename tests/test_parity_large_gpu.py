@@ -21,7 +21,7 @@ torch = pytest.importorskip("torch")
 
 from contrastive_embedding_loss_amd import binding  # noqa: E402
 from contrastive_embedding_loss_amd.inputs import (  # noqa: E402
-    ONESET_SIGLIP, SIGLIP, WORKLOADS, bf16_bits_to_f32, workload_inputs)
+    ONESET_SIGLIP, SIGLIP, WORKLOADS, bf16_bits_to_f32, workload_inputs, workload_positives)
 from oracle import bf16_bits_to_f64, contrastive_fwd_bwd  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -37,7 +37,7 @@ def run_gpu(w):
     else:
         q = torch.from_numpy(bf16_bits_to_f32(qb)).to("cuda").to(torch.bfloat16)
     loss, dq, dk, ex = binding.fwd_bwd(q, k, w.prefixes, w.scale, w.bias, w.kind, weights=w.weights,
-                                       row_offset=w.row_offset, extras=True)
+                                       row_offset=w.row_offset, extras=True, positives=workload_positives(w))
     torch.cuda.synchronize()
     return qb, kb, q, k, loss.item(), dq, dk, ex
 
@@ -73,7 +73,8 @@ def test_infonce_4096_full_oracle():
     check_properties(w, q, k, dq, dk)
 
 
-@pytest.mark.parametrize("name", ["siglip_16384", "rows_4096x65536", "infonce_32768", "oneset_16384x131072"])
+@pytest.mark.parametrize("name", ["siglip_16384", "rows_4096x65536", "infonce_32768", "oneset_16384x131072",
+                                  "siglip_band_16384"])
 def test_large_workload_against_stored_oracle(name):
     path = os.path.join(GOLDEN, f"{name}.npz")
     g = np.load(path)
