@@ -373,3 +373,36 @@ def test_positive_list_edge_cases():
     with pytest.raises(binding.UformError):
         binding.fwd_bwd(q, k, LADDER, 10.0, -10.0, SIGLIP, row_offset=30, positives=pos, workspace=ws[:nbytes - 512])
     torch.cuda.synchronize()
+
+
+def test_positive_lists_accumulate_and_two_streams():
+    # accumulate adds the listed cells' terms on top like the rest; the staging buffers of two streams
+    # (one per stream) do not mix lists of calls in flight on both
+    from contrastive_embedding_loss_amd.inputs import random_positive_lists
+    qb, kb = make_inputs(160, 260, 1024, noise=0.6, seed=171, row_offset=50)
+    q, k = to_dev(qb), to_dev(kb)
+    pa = random_positive_lists(160, 260, 50, 5.0, seed=172)
+    pb = random_positive_lists(160, 260, 50, 9.0, seed=173)
+    print("[case] positives: accumulate twice; two streams interleaved", flush=True)
+    l1, dq1, dk1 = binding.fwd_bwd(q, k, LADDER, 10.0, -8.0, SIGLIP, row_offset=50, positives=pa)
+    _, dq2, dk2 = binding.fwd_bwd(q, k, LADDER, 10.0, -8.0, SIGLIP, row_offset=50, positives=pa, accumulate=True,
+                                  dq=dq1.clone(), dk=dk1.clone())
+    torch.cuda.synchronize()
+    for a, b in ((dq2, dq1), (dk2, dk1)):
+        assert (a - 2 * b).abs().max().item() <= 1e-5 * b.abs().max().item()
+    ref = {}
+    for name, pos in (("a", pa), ("b", pb)):
+        ref[name] = binding.fwd_bwd(q, k, LADDER, 10.0, -8.0, SIGLIP, row_offset=50, positives=pos)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    got = {"a": [], "b": []}
+    for _ in range(3):
+        for name, pos, st in (("a", pa, s1), ("b", pb, s2)):
+            with torch.cuda.stream(st):
+                got[name].append(binding.fwd_bwd(q, k, LADDER, 10.0, -8.0, SIGLIP, row_offset=50, positives=pos))
+    torch.cuda.synchronize()
+    for name in ("a", "b"):
+        for out in got[name]:
+            for x, y in zip(out, ref[name]):
+                assert torch.equal(x, y), name
+    assert not torch.equal(ref["a"][0], ref["b"][0])
