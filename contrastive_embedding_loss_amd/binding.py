@@ -200,7 +200,10 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
     if positives is not None:
         import numpy as np
         rp = np.ascontiguousarray(np.asarray(positives[0]), dtype=np.int64)
-        pc = np.ascontiguousarray(np.asarray(positives[1]), dtype=np.int32)
+        pc_in = np.asarray(positives[1])
+        if pc_in.size and (pc_in.min() < -2**31 or pc_in.max() >= 2**31):
+            raise ValueError("positives: column indices must fit int32")
+        pc = np.ascontiguousarray(pc_in, dtype=np.int32)
         if rp.shape != (R + 1,):
             raise ValueError("positives: row_ptr must have R + 1 entries")
         if rp[-1] > pc.size:
