@@ -145,11 +145,12 @@ typedef struct {
      * pos_col[pos_row_ptr[i] .. pos_row_ptr[i + 1] - 1], and every listed cell
      * gets the label z = +1 like the row's own positive (loss, dq, dk,
      * dL/dscale, dL/dbias and L^p all follow).  pos_row_ptr has R + 1 entries
-     * with pos_row_ptr[0] = 0, never decreasing, and pos_row_ptr[R] <= 2^31 - 2;
-     * a row's columns are strictly increasing, in [0, N), and none of them is
-     * the row's own positive (row_offset + i; in the one-set form its pair
-     * partner (row_offset + i) xor 1 and the row itself).  A list that breaks
-     * this, or a list with a softmax kind, is invalid-argument.  In the
+     * with pos_row_ptr[0] = 0 and never decreasing; a row's columns are
+     * strictly increasing, in [0, N), and none of them is the row's own
+     * positive (row_offset + i; in the one-set form its pair partner
+     * (row_offset + i) xor 1 and the row itself).  A list that breaks this,
+     * or a list with a softmax kind, is invalid-argument; more than 2^31 - 2
+     * listed cells in one call is unsupported.  In the
      * one-set form list both (i, j) and (j, i) so that mirrored cells keep
      * equal labels.  Explicit hard negatives need no list: append them to k
      * as extra key rows (N > R), which every row scores as negatives.  The
