@@ -48,7 +48,7 @@ def measured_traffic(workload: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="infonce_32768")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -110,15 +110,20 @@ def main():
     binding.profile()  # clear
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    # timed region: K steps, each kernel bracketed by events on the launch stream
+    # timed region: K steps, each step and each kernel bracketed by events on the launch stream
+    stream = torch.cuda.current_stream(dev)
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for _ in range(args.steps):
+    for a_ev, b_ev in marks:
+        a_ev.record(stream)
         step(profile=True)
+        b_ev.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     kern = binding.profile()
     ms_per_step = 1e3 * elapsed / args.steps
+    step_ms = sorted(a_ev.elapsed_time(b_ev) for a_ev, b_ev in marks)
 
     # two-set kinds: forward 2RND + one logit recompute 2RND + dQ 2RND + dK 2RND; the one-set form
     # has the share's logits 2RND and dX 2RND, in one backward pass
@@ -141,6 +146,20 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(w.name), "avg_launch_ms": round(bwd_ms, 4),
                 "executed_tflops": round(4.0 * R * N * D / (bwd_ms * 1e-3) / 1e12, 1)}
+
+    # HBM-bound stages: algorithmic bytes (rows read once, tables and partials as laid out) per launch
+    n_jt, n_it = -(-N // 128), -(-R // 128)
+    stage_bytes = {
+        "k_prep": (R + N) * D * 2 + 4 * ((R + N) * (3 * P + 2) + R * P),
+        "k_rowstats": 4 * R * P * (2 * n_jt + 9),
+        "k_colstats": 4 * N * P * (2 * n_it + 9),
+    }
+    hbm_stages = {}
+    for name, nbytes in stage_bytes.items():
+        if name in kern_per_step:
+            t = kern_per_step[name]
+            hbm_stages[name] = {"ms": round(t, 4), "bytes": nbytes, "GB_per_s": round(nbytes / (t * 1e-3) / 1e9, 1),
+                                "frac_of_8TBps": round(nbytes / (t * 1e-3) / 8e12, 3)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -180,6 +199,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(step_ms[len(step_ms) // 2], 4),
+        "ms_per_step_min": round(step_ms[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -194,6 +215,7 @@ def main():
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernel_ms_per_step": {n: round(t, 4) for n, t in kern_per_step.items()},
         "roofline": roofline,
+        "hbm_stages": hbm_stages,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
