@@ -128,52 +128,114 @@ __device__ __forceinline__ void dma4_m0(const void *g, uint32_t m0v) {
 // k_prep: per-prefix inverse L2 norms of every row (and s log2(e) times
 // them), the exact power-of-two row scale sig ~ 1/|row| and the backward's
 // per-row operand scale gam; for query rows also the prefix dot products
-// with their positive key.  One wave per row.
+// with their positive key.  A workgroup takes 64 consecutive rows of the list
+// (query rows, then key rows), a wave 16 of them, one at a time with the next
+// row's loads in flight.  Lane l holds the 16-byte chunks l and l + 64 of a
+// row (D <= 1024); prefix ends are multiples of 32, so no chunk straddles
+// one, and the sum over a prefix is an inclusive scan over the chunks read at
+// the prefix's last chunk.  Results go through LDS so that the tables are
+// written with consecutive rows on consecutive lanes.
 // ----------------------------------------------------------------------------
+constexpr int kPrepRows = 64;
+
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ float wave_scan(float v, int lane) {
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+        const float u = __shfl_up(v, k);
+        v += lane >= k ? u : 0.f;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float sq8(const uint4 &a) {
+    const unsigned int w[4] = {a.x, a.y, a.z, a.w};
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s = fmaf(bf16_lo(w[c]), bf16_lo(w[c]), fmaf(bf16_hi(w[c]), bf16_hi(w[c]), s));
+    return s;
+}
+__device__ __forceinline__ float dot8(const uint4 &a, const uint4 &b) {
+    const unsigned int u[4] = {a.x, a.y, a.z, a.w}, v[4] = {b.x, b.y, b.z, b.w};
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s = fmaf(bf16_lo(u[c]), bf16_lo(v[c]), fmaf(bf16_hi(u[c]), bf16_hi(v[c]), s));
+    return s;
+}
+
 __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
+    __shared__ float res[kPrepRows][2 * kMaxP + 1];  // per row: inv[P] | posdot[P] | sig
     if (blockIdx.x == 0 && threadIdx.x < 4 * a.pf.n) a.gmax[threadIdx.x] = 0.f;  // k_maxes' start
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-    if (row >= a.R + a.N) return;
-    const bool isq = row < a.R;
-    const int D = a.D;
-    const u16 *x = isq ? a.q + row * D : a.k + (row - a.R) * D;
-    const u16 *y = isq ? a.k + ((row + a.off) ^ a.pxor) * D : x;
-    const int P = a.pf.n;
-    float ss_run = 0.f, dot_run = 0.f;
-    float inv[kMaxP];
-    int start = 0;
-    for (int p = 0; p < P; ++p) {
-        const int end = a.pf.w[p];
-        float ss = 0.f, dt = 0.f;
-        for (int d = start + 2 * lane; d < end; d += 128) {
-            const unsigned int xv = *(const unsigned int *)(x + d);
-            const float x0 = bf16_lo(xv), x1 = bf16_hi(xv);
-            ss = fmaf(x0, x0, fmaf(x1, x1, ss));
-            if (isq) {
-                const unsigned int yv = *(const unsigned int *)(y + d);
-                dt = fmaf(x0, bf16_lo(yv), fmaf(x1, bf16_hi(yv), dt));
-            }
+    const int64_t rows = a.R + a.N, g0 = (int64_t)blockIdx.x * kPrepRows;
+    const int D = a.D, P = a.pf.n, nch = D / 8;
+    // this lane's prefix (lane < P): its chunk count
+    int m = 1;
+#pragma unroll
+    for (int p = 0; p < kMaxP; ++p)
+        if (p < P && lane == p) m = a.pf.w[p] / 8;
+    const bool c0 = lane < nch, c1 = lane + 64 < nch;
+    uint4 bx[2][2], by[2][2];
+    auto fetch = [&](int j, int s) {
+        const int64_t g = g0 + 16 * wave + j;
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        bx[s][0] = bx[s][1] = by[s][0] = by[s][1] = z;
+        if (g >= rows) return;
+        const bool isq = g < a.R;
+        const u16 *x = isq ? a.q + g * D : a.k + (g - a.R) * D;
+        if (c0) bx[s][0] = *(const uint4 *)(x + 8 * lane);
+        if (c1) bx[s][1] = *(const uint4 *)(x + 8 * (lane + 64));
+        if (isq) {
+            const u16 *y = a.k + ((g + a.off) ^ a.pxor) * D;
+            if (c0) by[s][0] = *(const uint4 *)(y + 8 * lane);
+            if (c1) by[s][1] = *(const uint4 *)(y + 8 * (lane + 64));
         }
-        ss_run += wave_sum(ss);
-        dot_run += wave_sum(dt);
-        inv[p] = 1.0f / sqrtf(fmaxf(ss_run, 1.17549435e-38f));
-        if (lane == 0 && isq) a.posdot[p * a.R + row] = dot_run;
-        start = end;
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        if (j + 1 < 16) fetch(j + 1, (j + 1) & 1);
+        const int64_t g = g0 + 16 * wave + j;
+        if (g >= rows) continue;  // wave-uniform
+        const int s = j & 1;
+        const float S0 = wave_scan(sq8(bx[s][0]), lane), S1 = wave_scan(sq8(bx[s][1]), lane);
+        const float T0 = wave_scan(dot8(bx[s][0], by[s][0]), lane), T1 = wave_scan(dot8(bx[s][1], by[s][1]), lane);
+        // lane p < P: sums over prefix p's chunks (the first 64 chunks' total at lane 63).  Every
+        // lane takes part in every shuffle (a lane outside the exec mask supplies no value).
+        const int s1 = max(m - 65, 0);
+        const float a0 = __shfl(S0, min(m, 64) - 1), a1 = __shfl(S1, s1);
+        const float b0 = __shfl(T0, min(m, 64) - 1), b1 = __shfl(T1, s1);
+        const float ss = a0 + (m > 64 ? a1 : 0.f), dt = b0 + (m > 64 ? b1 : 0.f);
+        const int r = 16 * wave + j;
+        if (lane < P) {
+            res[r][lane] = 1.0f / sqrtf(fmaxf(ss, 1.17549435e-38f));
+            res[r][kMaxP + lane] = dt;
+        }
+        if (lane == P - 1) {
+            const float norm = sqrtf(ss);
+            res[r][2 * kMaxP] = norm > 0.f ? ldexpf(1.0f, -ilogbf(norm)) : 1.0f;
+        }
     }
-    if (lane != 0) return;
-    const float norm = sqrtf(ss_run);
-    const float sig = norm > 0.f ? ldexpf(1.0f, -ilogbf(norm)) : 1.0f;
-    const int64_t r = isq ? row : row - a.R;
-    const int64_t nr = isq ? a.R : a.N;
-    float *invt = isq ? a.invq : a.invk, *At = isq ? a.qA : a.kA, *It = isq ? a.qIYR : a.kIYR;
-    for (int p = 0; p < P; ++p) {
-        invt[p * nr + r] = inv[p];
-        At[p * nr + r] = a.a_scale * inv[p];
-        It[p * nr + r] = inv[p] / sig;
+    __syncthreads();
+    // tables [p][row]: consecutive rows on consecutive lanes (two runs where the block holds both kinds)
+    for (int e = threadIdx.x; e < kPrepRows * (P + 1); e += 256) {
+        const int p = e / kPrepRows, r = e % kPrepRows;
+        const int64_t g = g0 + r;
+        if (g >= rows) continue;
+        const bool isq = g < a.R;
+        const int64_t i = isq ? g : g - a.R, nr = isq ? a.R : a.N;
+        const float sig = res[r][2 * kMaxP];
+        if (p < P) {
+            const float inv = res[r][p];
+            (isq ? a.invq : a.invk)[p * nr + i] = inv;
+            (isq ? a.qA : a.kA)[p * nr + i] = a.a_scale * inv;
+            (isq ? a.qIYR : a.kIYR)[p * nr + i] = inv / sig;
+            if (isq) a.posdot[p * a.R + i] = res[r][kMaxP + p];
+        } else {
+            (isq ? a.sigq : a.sigk)[i] = sig;
+            (isq ? a.gamq : a.gamk)[i] = a.gam_scale * res[r][P - 1];
+        }
     }
-    (isq ? a.sigq : a.sigk)[r] = sig;
-    (isq ? a.gamq : a.gamk)[r] = a.gam_scale * inv[P - 1];
 }
 
 // ----------------------------------------------------------------------------
@@ -1504,7 +1566,7 @@ __global__ __launch_bounds__(256) void k_loss(LossArgs a) {
 // ----------------------------------------------------------------------------
 hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
     const int64_t rows = a.R + a.N;
-    hipLaunchKernelGGL(k_prep, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_prep, dim3((unsigned)((rows + kPrepRows - 1) / kPrepRows)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
