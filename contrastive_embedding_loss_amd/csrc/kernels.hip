@@ -128,15 +128,15 @@ __device__ __forceinline__ void dma4_m0(const void *g, uint32_t m0v) {
 // k_prep: per-prefix inverse L2 norms of every row (and s log2(e) times
 // them), the exact power-of-two row scale sig ~ 1/|row| and the backward's
 // per-row operand scale gam; for query rows also the prefix dot products
-// with their positive key.  A workgroup takes 64 consecutive rows of the list
-// (query rows, then key rows), a wave 16 of them, one at a time with the next
-// row's loads in flight.  Lane l holds the 16-byte chunks l and l + 64 of a
+// with their positive key.  A workgroup takes 4 RPW consecutive rows of the
+// list (query rows, then key rows), a wave RPW of them (16, 4 or 1: enough
+// workgroups to fill the GPU), one at a time with the next row's loads in flight.  Lane l holds the 16-byte chunks l and l + 64 of a
 // row (D <= 1024); prefix ends are multiples of 32, so no chunk straddles
 // one, and the sum over a prefix is an inclusive scan over the chunks read at
 // the prefix's last chunk.  Results go through LDS so that the tables are
 // written with consecutive rows on consecutive lanes.
 // ----------------------------------------------------------------------------
-constexpr int kPrepRows = 64;
+constexpr int kPrepRows = 64;  // most rows per workgroup
 
 // inclusive prefix sum over the 64 lanes
 __device__ __forceinline__ float wave_scan(float v, int lane) {
@@ -163,11 +163,13 @@ __device__ __forceinline__ float dot8(const uint4 &a, const uint4 &b) {
     return s;
 }
 
+template <int RPW>
 __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
-    __shared__ float res[kPrepRows][2 * kMaxP + 1];  // per row: inv[P] | posdot[P] | sig
+    constexpr int RB = 4 * RPW;  // rows per workgroup
+    __shared__ float res[RB][2 * kMaxP + 1];  // per row: inv[P] | posdot[P] | sig
     if (blockIdx.x == 0 && threadIdx.x < 4 * a.pf.n) a.gmax[threadIdx.x] = 0.f;  // k_maxes' start
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t rows = a.R + a.N, g0 = (int64_t)blockIdx.x * kPrepRows;
+    const int64_t rows = a.R + a.N, g0 = (int64_t)blockIdx.x * RB;
     const int D = a.D, P = a.pf.n, nch = D / 8;
     // this lane's prefix (lane < P): its chunk count
     int m = 1;
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
     const bool c0 = lane < nch, c1 = lane + 64 < nch;
     uint4 bx[2][2], by[2][2];
     auto fetch = [&](int j, int s) {
-        const int64_t g = g0 + 16 * wave + j;
+        const int64_t g = g0 + RPW * wave + j;
         const uint4 z = make_uint4(0, 0, 0, 0);
         bx[s][0] = bx[s][1] = by[s][0] = by[s][1] = z;
         if (g >= rows) return;
@@ -193,9 +195,9 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
     };
     fetch(0, 0);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        if (j + 1 < 16) fetch(j + 1, (j + 1) & 1);
-        const int64_t g = g0 + 16 * wave + j;
+    for (int j = 0; j < RPW; ++j) {
+        if (j + 1 < RPW) fetch(j + 1, (j + 1) & 1);
+        const int64_t g = g0 + RPW * wave + j;
         if (g >= rows) continue;  // wave-uniform
         const int s = j & 1;
         const float S0 = wave_scan(sq8(bx[s][0]), lane), S1 = wave_scan(sq8(bx[s][1]), lane);
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
         const float a0 = __shfl(S0, min(m, 64) - 1), a1 = __shfl(S1, s1);
         const float b0 = __shfl(T0, min(m, 64) - 1), b1 = __shfl(T1, s1);
         const float ss = a0 + (m > 64 ? a1 : 0.f), dt = b0 + (m > 64 ? b1 : 0.f);
-        const int r = 16 * wave + j;
+        const int r = RPW * wave + j;
         if (lane < P) {
             res[r][lane] = 1.0f / sqrtf(fmaxf(ss, 1.17549435e-38f));
             res[r][kMaxP + lane] = dt;
@@ -218,8 +220,8 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
     }
     __syncthreads();
     // tables [p][row]: consecutive rows on consecutive lanes (two runs where the block holds both kinds)
-    for (int e = threadIdx.x; e < kPrepRows * (P + 1); e += 256) {
-        const int p = e / kPrepRows, r = e % kPrepRows;
+    for (int e = threadIdx.x; e < RB * (P + 1); e += 256) {
+        const int p = e / RB, r = e % RB;
         const int64_t g = g0 + r;
         if (g >= rows) continue;
         const bool isq = g < a.R;
@@ -596,33 +598,45 @@ __device__ __forceinline__ void block_sum_write(float v, float *red /*[4]*/, flo
     __syncthreads();
 }
 
-// Sum of the per-tile partials of row (or column) r, prefix p: the 4 waves of a
-// block each take every 4th tile (kStatRows consecutive rows per wave, so the
-// loads coalesce), then the four sums are added in a fixed order.
+// Sum of the per-tile partials of row (or column) r, prefix p: the W waves of a block (4, 8 or
+// 16, by the number of partials) each take every W-th tile (kStatRows consecutive rows per
+// wave, so the loads coalesce), then the waves' sums are added in a fixed order.
+constexpr int kStatWaves = 16;  // most waves per block
+inline int stat_waves(int64_t ntiles) { return ntiles >= 128 ? 16 : ntiles >= 64 ? 8 : 4; }
 __device__ __forceinline__ float fold_partials(const float *part, int64_t ntiles, int P, int p, int64_t len,
                                                int64_t r, bool ok, float (*fold)[kStatRows]) {
     const int g = threadIdx.x / kStatRows, rl = threadIdx.x % kStatRows;
     float v = 0.f;
     if (ok) {
         // four independent running sums (loads in flight), added in a fixed order
+        const int W = (int)(blockDim.x / 64);
         float u[4] = {0.f, 0.f, 0.f, 0.f};
         int64_t t = g;
-        for (; t + 12 < ntiles; t += 16)
+        for (; t + 3 * W < ntiles; t += 4 * W)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) u[k] += part[((t + 4 * k) * P + p) * len + r];
-        for (; t < ntiles; t += 4) u[0] += part[(t * P + p) * len + r];
+            for (int k = 0; k < 4; ++k) u[k] += part[((t + W * k) * P + p) * len + r];
+        for (; t < ntiles; t += W) u[0] += part[(t * P + p) * len + r];
         v = (u[0] + u[1]) + (u[2] + u[3]);
     }
     fold[g][rl] = v;
     __syncthreads();
-    const float s = (fold[0][rl] + fold[1][rl]) + (fold[2][rl] + fold[3][rl]);
+    float s = 0.f;
+    for (int h = 0; h < (int)(blockDim.x / 64); h += 4)
+        s += (fold[h][rl] + fold[h + 1][rl]) + (fold[h + 2][rl] + fold[h + 3][rl]);
     __syncthreads();
     return s;
 }
 
-__global__ __launch_bounds__(256) void k_rowstats(StatsArgs a) {
-    __shared__ float red[4];
-    __shared__ float fold[4][kStatRows];
+// The loss partial of a statistics block: only wave 0 (the block's rows) holds terms.
+__device__ __forceinline__ void lead_sum_write(float v, float *dst) {
+    if (threadIdx.x < 64) {
+        v = wave_sum(v);
+        if (threadIdx.x == 0) *dst = v;
+    }
+}
+
+__global__ __launch_bounds__(64 * kStatWaves) void k_rowstats(StatsArgs a) {
+    __shared__ float fold[kStatWaves][kStatRows];
     const int64_t i = (int64_t)blockIdx.x * kStatRows + threadIdx.x % kStatRows;
     const bool lead = threadIdx.x < kStatRows;
     const int P = a.pf.n;
@@ -649,13 +663,12 @@ __global__ __launch_bounds__(256) void k_rowstats(StatsArgs a) {
             a.qKap[p * a.R + i] = a.sgn * invZ * a.qIYR[p * a.R + i];
             if (a.kind == kRows) a.diagA[p * a.R + i] = -a.wnorm[p] * a.scale * (neg * invZ) * a.inv_den * iq * ik;
         }
-        block_sum_write(ce, red, &a.lossparts[((int64_t)a.slot0 + blockIdx.x) * P + p]);
+        lead_sum_write(ce, &a.lossparts[((int64_t)a.slot0 + blockIdx.x) * P + p]);
     }
 }
 
-__global__ __launch_bounds__(256) void k_colstats(StatsArgs a) {
-    __shared__ float red[4];
-    __shared__ float fold[4][kStatRows];
+__global__ __launch_bounds__(64 * kStatWaves) void k_colstats(StatsArgs a) {
+    __shared__ float fold[kStatWaves][kStatRows];
     const int64_t j = (int64_t)blockIdx.x * kStatRows + threadIdx.x % kStatRows;
     const bool lead = threadIdx.x < kStatRows;
     const int P = a.pf.n;
@@ -691,7 +704,7 @@ __global__ __launch_bounds__(256) void k_colstats(StatsArgs a) {
                 a.kNegfrac[p * a.N + j] = 0.f;
             }
         }
-        block_sum_write(ce, red, &a.lossparts[((int64_t)a.slot0 + blockIdx.x) * P + p]);
+        lead_sum_write(ce, &a.lossparts[((int64_t)a.slot0 + blockIdx.x) * P + p]);
     }
 }
 
@@ -1566,7 +1579,13 @@ __global__ __launch_bounds__(256) void k_loss(LossArgs a) {
 // ----------------------------------------------------------------------------
 hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
     const int64_t rows = a.R + a.N;
-    hipLaunchKernelGGL(k_prep, dim3((unsigned)((rows + kPrepRows - 1) / kPrepRows)), dim3(256), 0, s, a);
+    // 16 rows per wave where that still gives 1024 workgroups, else 4, else 1
+    if (rows >= 1024 * kPrepRows)
+        hipLaunchKernelGGL(k_prep<16>, dim3((unsigned)((rows + 63) / 64)), dim3(256), 0, s, a);
+    else if (rows >= 1024 * 16)
+        hipLaunchKernelGGL(k_prep<4>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_prep<1>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1610,12 +1629,14 @@ hipError_t launch_fwd(const u16 *q, const u16 *k, int64_t R, int64_t N, int D, c
 }
 
 hipError_t launch_rowstats(const StatsArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_rowstats, dim3((unsigned)((a.R + kStatRows - 1) / kStatRows)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_rowstats, dim3((unsigned)((a.R + kStatRows - 1) / kStatRows)), dim3(64 * stat_waves(a.nJt)), 0,
+                       s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_colstats(const StatsArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_colstats, dim3((unsigned)((a.N + kStatRows - 1) / kStatRows)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_colstats, dim3((unsigned)((a.N + kStatRows - 1) / kStatRows)), dim3(64 * stat_waves(a.nIt)), 0,
+                       s, a);
     return hipGetLastError();
 }
 
