@@ -406,3 +406,28 @@ def test_positive_lists_accumulate_and_two_streams():
             for x, y in zip(out, ref[name]):
                 assert torch.equal(x, y), name
     assert not torch.equal(ref["a"][0], ref["b"][0])
+
+
+@pytest.mark.parametrize("D,prefixes,one_split", [
+    (1024, (1024,), False), (256, (64, 128, 256), True), (512, (64, 128, 256, 512), False), (1024, LADDER, True)])
+def test_positive_lists_other_ladders_and_finish(D, prefixes, one_split):
+    # the listed cells' pass adds onto dq/dk after either finish (in place, or the split partials' fold)
+    from contrastive_embedding_loss_amd.inputs import random_positive_lists
+    R, N, off = 120, 330, 90
+    qb, kb = make_inputs(R, N, D, noise=0.7, seed=181 + D + len(prefixes), row_offset=off)
+    pos = random_positive_lists(R, N, off, 6.0, seed=182 + D, dense_row=11)
+    print(f"[case] positives ladder={prefixes} D={D} one_split={one_split}", flush=True)
+    q, k = to_dev(qb), to_dev(kb)
+    loss, dq, dk, ex = binding.fwd_bwd(q, k, prefixes, 9.0, -7.0, SIGLIP, row_offset=off, extras=True,
+                                       one_split=one_split, positives=pos)
+    torch.cuda.synchronize()
+    ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), prefixes, 9.0, -7.0, SIGLIP,
+                              row_offset=off, positives=pos)
+    assert abs(loss.item() - ref["loss"]) <= 1e-3 * abs(ref["loss"]), (loss.item(), ref["loss"])
+    for name, g in (("dq", dq), ("dk", dk)):
+        e = np.abs(g.cpu().numpy() - ref[name]).max()
+        assert e <= 2e-3 * np.abs(ref[name]).max(), (name, e)
+    if prefixes[-1] < D:
+        assert (dq[:, prefixes[-1]:] == 0).all() and (dk[:, prefixes[-1]:] == 0).all()
+    assert ex["dscale"].item() == pytest.approx(ref["dscale"], rel=1e-3, abs=1e-6)
+    assert ex["dbias"].item() == pytest.approx(ref["dbias"], rel=1e-3, abs=1e-6)
