@@ -1139,6 +1139,15 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
                 for (int t = 0; t < 4; ++t) x[t] = fmaf(st.e[t], tb.iy[t], Co[p]);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) st.e[t] = __builtin_amdgcn_exp2f(x[t]);
+            } else if constexpr (!LOSS) {
+                // the unmasked coefficient sigma(l) beta_o iy; sigma = 1 / (1 + 2^-u) directly (2^-u = inf
+                // gives 0), with no loss term to share 2^-|u| with
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float uu = fmaf(st.e[t], tb.iy[t], a.b2);
+                    const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-uu));
+                    st.e[t] = sg * Co[p] * tb.iy[t];  // Co holds beta_o for the sigmoid form
+                }
             } else {
                 // the unmasked coefficient sigma(l) beta_o iy
 #pragma unroll
