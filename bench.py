@@ -59,7 +59,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the loss's multi-GPU "
-              "sharding is a design, not part of this build)", file=sys.stderr)
+              "sharding is a design only; the library runs on one GPU)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

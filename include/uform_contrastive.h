@@ -79,12 +79,12 @@ typedef enum {
 typedef enum {
     uform_status_success_k = 0,
     uform_status_invalid_argument_k = 1, /* a null or misaligned pointer, a bad size or prefix list */
-    uform_status_unsupported_k = 2,      /* valid request outside this build's limits */
+    uform_status_unsupported_k = 2,      /* valid request outside the library's limits */
     uform_status_out_of_memory_k = 3,    /* workspace allocation failed */
     uform_status_device_error_k = 4,     /* a HIP call or a kernel launch failed */
 } uform_status_t;
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define UFORM_CONTRASTIVE_MAX_PREFIXES 8
 #define UFORM_CONTRASTIVE_MAX_DIM 1024
 /* Softmax kinds use one fixed log-sum-exp shift per call, exact while

@@ -21,7 +21,7 @@ Sources (cited by page title and section):
   training-stack paragraphs (BF16 storage, FP32 accumulation, FP32
   log-sum-exps and partial-gradient slabs).
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
 
 * two-set loss: queries q (R rows) against keys k (N rows); the positive of
   local row i is column ``row_offset + i``;
