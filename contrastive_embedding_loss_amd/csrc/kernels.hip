@@ -1065,12 +1065,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     //   phase B(t): update of t         | E_a(t + 1)                   -> barrier
     // E_a's band operands are held in registers until phase A writes them, because
     // the update of t reads the band operand buffer during phase B.
-    // prefixes NP - NA .. NP - 1 belong to E_a.  On ladders of five or more prefixes (measured): the
-    // softmax form runs every unit beside the recompute and the update alone; the sigmoid form puts
-    // three units beside the update in its pass with the loss and one in the pass without (an even
-    // split makes its live values outgrow the register file, and the outer-row operands are then
-    // reloaded from scratch inside the loop).  Smaller ladders split evenly.
-    constexpr int NA = NP >= 5 ? (SIG ? (LOSS ? 3 : 1) : 0) : NP / 2;
+    // prefixes NP - NA .. NP - 1 belong to E_a.  Measured: on ladders of four or more prefixes the
+    // softmax form runs every unit beside the recompute and the update alone; on ladders of five or
+    // more the sigmoid form puts three units beside the update in its pass with the loss and one in
+    // the pass without (an even split makes its live values outgrow the register file, and the
+    // outer-row operands are then reloaded from scratch inside the loop).  Otherwise an even split.
+    constexpr int NA = SIG ? (NP >= 5 ? (LOSS ? 3 : 1) : NP / 2) : (NP >= 4 ? 0 : NP / 2);
     f32x4 sv[NSLOT];
     auto read_slots = [&]() {
 #pragma unroll
