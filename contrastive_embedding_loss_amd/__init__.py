@@ -10,11 +10,14 @@ fails loudly if it is missing.
 INFONCE = 0
 SIGLIP = 1
 INFONCE_ROWS = 2
+ONESET_SIGLIP = 3
+
+_BINDING_NAMES = ("fwd_bwd", "workspace_bytes", "supported", "status_name", "last_error", "profile", "release",
+                  "library", "UformError")
 
 
 def __getattr__(name):
-    if name in ("fwd_bwd", "fwd_bwd_ex", "workspace_bytes", "status_name", "release", "library",
-                "UformError"):
+    if name in _BINDING_NAMES:
         from . import binding
         return getattr(binding, name)
     raise AttributeError(name)

@@ -129,6 +129,19 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check_grad_buffer(name, t, shape, dev) -> None:
+    """A caller-given gradient buffer must be exactly what the kernels write: contiguous
+    float32 of the given shape on q's device (anything else would be written past its end)."""
+    if t is None:
+        return
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if t.device != dev or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on q's device")
+
+
 def _check(status: int) -> None:
     if status != 0:
         raise UformError(status, last_error())
@@ -154,11 +167,19 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
         raise TypeError("q and k must be bfloat16")
     if not (q.is_cuda and k.is_cuda):
         raise TypeError("q and k must be device tensors")
+    if q.dim() != 2 or k.dim() != 2 or q.shape[1] != k.shape[1]:
+        raise ValueError("q and k must be [R, D] and [N, D]")
+    if q.device != k.device:
+        raise ValueError("q and k must be on one device")
     q = q.contiguous()
     k = k.contiguous()
     R, D = q.shape
     N = k.shape[0]
     dev = q.device
+    _check_grad_buffer("dq", dq, (R, D), dev)
+    _check_grad_buffer("dk", dk, (N, D), dev)
+    if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on q's device")
     P = len(prefixes)
     f32 = dict(dtype=torch.float32, device=dev)
     loss = torch.empty(1, **f32)

@@ -326,11 +326,16 @@ struct ProfRec {
     const char *name;
     hipEvent_t a, b;
 };
-std::mutex g_prof_mu;
+std::mutex g_prof_mu;  // guards g_prof_live and g_prof_pool; a profiled call holds it throughout
 std::vector<ProfRec> g_prof_live;
 std::vector<hipEvent_t> g_prof_pool;
-bool g_prof_on = false;
-hipStream_t g_prof_stream = nullptr;
+
+// Per-call profiling state, passed down by value: a call without the flag never touches the
+// shared records, so it needs no lock.
+struct ProfCtx {
+    bool on = false;
+    hipStream_t stream = nullptr;
+};
 
 hipEvent_t prof_event() {
     if (!g_prof_pool.empty()) {
@@ -345,24 +350,24 @@ hipEvent_t prof_event() {
 
 struct ProfScope {
     ProfRec rec{};
-    bool on;
-    ProfScope(const char *name) : on(g_prof_on) {
-        if (!on) return;
+    ProfCtx ctx;
+    ProfScope(const ProfCtx &c, const char *name) : ctx(c) {
+        if (!ctx.on) return;
         rec.name = name;
         rec.a = prof_event();
         rec.b = prof_event();
-        if (rec.a) (void)hipEventRecord(rec.a, g_prof_stream);
+        if (rec.a) (void)hipEventRecord(rec.a, ctx.stream);
     }
     ~ProfScope() {
-        if (!on) return;
-        if (rec.b) (void)hipEventRecord(rec.b, g_prof_stream);
+        if (!ctx.on) return;
+        if (rec.b) (void)hipEventRecord(rec.b, ctx.stream);
         if (rec.a && rec.b) g_prof_live.push_back(rec);
     }
 };
 
 #define LAUNCH_NAMED(name, expr)                                                                     \
     do {                                                                                             \
-        ProfScope prof_(name);                                                                       \
+        ProfScope prof_(prof, name);                                                                 \
         hipError_t e_ = (expr);                                                                      \
         if (e_ != hipSuccess) return fail(uform_status_device_error_k, std::string("launch failed: ") + \
                                                                           hipGetErrorString(e_));      \
@@ -371,7 +376,7 @@ struct ProfScope {
 
 uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t D, const int32_t *prefixes,
                    int32_t P, float scale, float bias, int32_t kind_in, float *loss_out, float *dq, float *dk,
-                   hipStream_t s, const uform_contrastive_options_t *opt) {
+                   hipStream_t s, const uform_contrastive_options_t *opt, const ProfCtx &prof) {
     const u16 *q = (const u16 *)q_, *k = (const u16 *)k_;
     // the one-set form runs as the sigmoid kind whose positive of row g is g ^ 1, whose cell (g, g)
     // is not scored, and whose row gradients count both mirrored cells
@@ -698,16 +703,12 @@ uform_status_t uform_contrastive_fwd_bwd_ex(const void *q, const void *k, int64_
                                             const uform_contrastive_options_t *options) {
     uform_status_t st = validate(q, k, R, N, D, prefixes, n_prefixes, scale, bias, kind, loss_out, dq, dk, options);
     if (st != uform_status_success_k) return st;
-    const bool prof = options && (options->flags & UFORM_CONTRASTIVE_PROFILE);
+    ProfCtx prof;
+    prof.on = options && (options->flags & UFORM_CONTRASTIVE_PROFILE);
+    prof.stream = stream;
     std::unique_lock<std::mutex> lock(g_prof_mu, std::defer_lock);
-    if (prof) {
-        lock.lock();
-        g_prof_on = true;
-        g_prof_stream = stream;
-    }
-    st = run(q, k, R, N, D, prefixes, n_prefixes, scale, bias, kind, loss_out, dq, dk, stream, options);
-    g_prof_on = false;
-    return st;
+    if (prof.on) lock.lock();
+    return run(q, k, R, N, D, prefixes, n_prefixes, scale, bias, kind, loss_out, dq, dk, stream, options, prof);
 }
 
 int32_t uform_contrastive_profile(const char **names, float *ms, int32_t cap) {

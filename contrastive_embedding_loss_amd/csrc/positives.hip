@@ -1,8 +1,9 @@
 // Several positives per entry for the sigmoid form.
 //
 // An entry of the batch may carry several positives besides its own pair
-// ("Scaling-Up Contrastive Learning over NVLink Multicast", the training-stack
-// paragraph on loader-side properties); each listed cell takes the label z = +1.
+// (UForm README, "Multimodal Perception from 64 to 1024 Dimensions", the
+// training-stack paragraph on loader-side properties); each listed cell takes
+// the label z = +1.
 // The main passes score every listed cell as a negative.  With l = t cos + b,
 // softplus(-l) - softplus(l) = -l and (sigma(l) - 1) - sigma(l) = -1, so the
 // listed cells change the loss by -l^p, the residual by -1/den, and the row

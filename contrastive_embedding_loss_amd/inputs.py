@@ -142,8 +142,9 @@ def make_band_inputs(R: int, D: int, extra_pos: int = 2, hard_neg: int = 2, nois
     """Entries with several positives and explicit hard negatives, gathered as extra key rows.
 
     Each entry may carry several positives and explicit hard negatives that the
-    loss gathers as extra columns ("Scaling-Up Contrastive Learning over NVLink
-    Multicast", the training-stack paragraph on loader-side properties).  Layout
+    loss gathers as extra columns (UForm README, "Multimodal Perception from 64
+    to 1024 Dimensions", the training-stack paragraph on loader-side
+    properties).  Layout
     as in ``band_lists``.  Draws, in order: q ~ N(0,1) [R, D]; own keys
     k_i = q_i + noise * N(0,1); then one N(0,1) matrix for all appended keys in
     key order, each appended key being its entry's q_i plus noise (extra

@@ -116,7 +116,11 @@ uform_status_t uform_contrastive_fwd_bwd(const void *q, const void *k, int64_t R
 
 typedef struct {
     const float *prefix_weights; /* host [n_prefixes], finite and > 0; NULL = all 1            */
-    int64_t row_offset;          /* key index of local row 0's positive; 0 <= off, off + R <= N */
+    /* Key index of local row 0's positive; 0 <= off, off + R <= N.  A GPU that owns rows
+     * off .. off + R - 1 of a batch scores them against every key with their global offset
+     * ("Scaling-Up Contrastive Learning over NVLink Multicast", section "Across the Box:
+     * Pointers, Not Gathers": each score call carries the local and the peer row offsets). */
+    int64_t row_offset;
     float *prefix_losses_out;    /* device [n_prefixes]: unweighted L^p; nullable               */
     float *col_lse_out;          /* device [n_prefixes][N]: LSE over the R rows of column j
                                     (INFONCE: full column LSE; INFONCE_ROWS: the PLSE);
@@ -124,8 +128,14 @@ typedef struct {
     float *row_lse_out;          /* device [n_prefixes][R]: LSE over the N keys of row i;
                                     softmax kinds only; nullable                                */
     float *pos_logit_out;        /* device [n_prefixes][R]: l^p_{i, off+i}; nullable            */
-    void *workspace;             /* device, 256-byte aligned; NULL = library workspace          */
-    size_t workspace_bytes;      /* >= uform_contrastive_workspace_bytes(...) when given        */
+    /* Caller-lent device memory for every intermediate of the call ("UForm for Swift", section
+     * "Arenas": results land in memory the caller passes, rewound by each call, so a steady
+     * loop allocates nothing once it reaches its high-water mark).  256-byte aligned, at least
+     * uform_contrastive_workspace_bytes(...) bytes (_ex with a positive list); its contents are
+     * scratch, overwritten by the call; it serves one call at a time (calls that share it must
+     * be ordered on one stream).  NULL = the library's cached workspace of (device, stream). */
+    void *workspace;
+    size_t workspace_bytes;
     uint32_t flags;              /* UFORM_CONTRASTIVE_* bits below (accumulate, diagnostics)    */
     /* Gradients of the loss with respect to the logit scale s and bias b (the
      * learned temperature and bias of "Scaling-Up Contrastive Learning over
@@ -137,10 +147,10 @@ typedef struct {
      * that sets either must give dq or dk (else invalid-argument).  Nullable. */
     float *dscale_out;
     float *dbias_out;
-    /* Several positives per entry, sigmoid kinds only ("Scaling-Up
-     * Contrastive Learning over NVLink Multicast", the training-stack
+    /* Several positives per entry, sigmoid kinds only (UForm README,
+     * "Multimodal Perception from 64 to 1024 Dimensions", the training-stack
      * paragraph on loader-side properties: an entry may carry several
-     * positives and explicit hard negatives).  HOST CSR lists, read during the
+     * positives and explicit hard negatives, gathered as extra columns).  HOST CSR lists, read during the
      * call only: local row i's extra positives are the key (set) indices
      * pos_col[pos_row_ptr[i] .. pos_row_ptr[i + 1] - 1], and every listed cell
      * gets the label z = +1 like the row's own positive (loss, dq, dk,
@@ -180,17 +190,24 @@ uform_status_t uform_contrastive_fwd_bwd_ex(const void *q, const void *k, int64_
                                             hipStream_t stream, const uform_contrastive_options_t *options);
 
 /* Device workspace a call of this shape needs, in bytes (gradients included);
- * 0 for arguments the call would reject. */
+ * 0 for arguments the call would reject.  The size of the caller-lent memory
+ * of the options' workspace ("UForm for Swift", section "Arenas": the caller
+ * sizes the memory a call lands in, and a loop that reuses it allocates once). */
 size_t uform_contrastive_workspace_bytes(int64_t R, int64_t N, int64_t D, int32_t n_prefixes, int32_t kind);
 
 /* As above, for a call that lists n_positives extra positives (pos_row_ptr[R];
- * sigmoid kinds only, else 0); n_positives < 0 means no list. */
+ * sigmoid kinds only, else 0); n_positives < 0 means no list ("UForm for Swift",
+ * section "Arenas", as above; the lists of the UForm README's loader-side
+ * paragraph take n_positives int32 entries of it). */
 size_t uform_contrastive_workspace_bytes_ex(int64_t R, int64_t N, int64_t D, int32_t n_prefixes, int32_t kind,
                                             int64_t n_positives);
 
 /* Whether a call with this width, prefix ladder and kind can run, without
  * touching any device: success, invalid-argument or unsupported (the reason
- * is in uform_contrastive_last_error()).  The backward is compiled for the
+ * is in uform_contrastive_last_error()).  The ladders are the nested prefixes
+ * of the UForm README's Matryoshka paragraph ({64, 128, 256, 512, 1024} and
+ * the shorter ladders of the narrower tiers); the statuses those of "UForm
+ * for Swift", section "Errors".  The backward is compiled for the
  * ladders {64,128,256,512,1024}, {64,128,256,512}, {64,128,256}, {64,128}
  * and the single widths {128}, {256}, {512}, {1024}; a softmax call without
  * gradients accepts any valid ladder. */
@@ -198,19 +215,28 @@ uform_status_t uform_contrastive_supported(int64_t D, const int32_t *prefixes, i
                                           int32_t with_gradients);
 
 /* "success", "invalid-argument", "unsupported", "out-of-memory", "device-error";
- * "unknown" otherwise.  Static strings. */
+ * "unknown" otherwise.  Static strings ("UForm for Swift", section "Errors":
+ * statuses uform_status_*_k whose names read like "invalid-argument"). */
 const char *uform_status_name(uform_status_t status);
 
-/* Human-readable reason of this thread's last non-success status ("" if none). */
+/* Human-readable reason of this thread's last non-success status ("" if none)
+ * ("UForm for Swift", section "Errors": a failed verb reports its status and
+ * the reason beside it). */
 const char *uform_contrastive_last_error(void);
 
 /* Diagnostics for calls made with UFORM_CONTRASTIVE_PROFILE: waits for their
  * events and writes up to cap (kernel name, summed milliseconds) pairs, one
  * per kernel, covering every profiled call since the previous read (which it
- * clears).  Returns the number of distinct kernels.  Names are static. */
+ * clears).  Returns the number of distinct kernels.  Names are static.  (The
+ * per-stage times behind a loss-step time such as "Scaling-Up Contrastive
+ * Learning over NVLink Multicast", section "Bird's Eye View & the Results",
+ * reports; section "On the Chip" attributes the step to its kernels.) */
 int32_t uform_contrastive_profile(const char **names, float *ms, int32_t cap);
 
-/* Frees the library's cached workspaces (waits for their streams first). */
+/* Frees the library's cached workspaces and pinned list staging (waits for
+ * their streams first).  The cached workspace is the library's own arena of
+ * "UForm for Swift", section "Arenas" (allocated once at its high-water mark
+ * per device and stream); this returns it. */
 void uform_contrastive_release(void);
 
 #ifdef __cplusplus

@@ -157,8 +157,8 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
 
     ``positives`` (sigmoid kinds only) = (row_ptr, col) lists extra positive
     pairs in CSR form: each entry of the batch may carry several positives
-    ("Scaling-Up Contrastive Learning over NVLink Multicast", the training-stack
-    paragraph on loader-side properties), and a listed cell gets the label
+    (UForm README, "Multimodal Perception from 64 to 1024 Dimensions", the
+    training-stack paragraph on loader-side properties), and a listed cell gets the label
     z = +1 like the row's own positive.  In the one-set form the caller lists
     both (i, j) and (j, i) so that mirrored cells keep equal labels.
 

@@ -30,6 +30,41 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(lib, n), n
 
 
+PAGE_TITLES = ("Scaling-Up Contrastive Learning over NVLink Multicast", "UForm for Swift", "UForm README")
+
+
+def _comment_before(text, pos):
+    """The block comment that ends closest before ``pos`` (the declaration's own comment)."""
+    end = text.rfind("*/", 0, pos)
+    start = text.rfind("/*", 0, end)
+    return _flat(text[start:end])
+
+
+def _flat(c):
+    """Comment text on one line: the leading '*' of continuation lines dropped."""
+    return re.sub(r"\s+", " ", re.sub(r"\n\s*\*(?!/)", " ", c))
+
+
+def test_every_declaration_cites_the_pages():
+    # each exported function and the options that carry a separate idea (offset, caller
+    # memory, extra positives) name the page and section that define them
+    text = open(HEADER).read()
+    missing = []
+    for name in declared_functions():
+        pos = re.search(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*" + name + r"\s*\(", text, re.M).start()
+        comment = _comment_before(text, pos)
+        if name == "uform_contrastive_fwd_bwd":  # described by the file's opening comment
+            comment = _flat(text[:text.index("#ifndef")])
+        if name == "uform_contrastive_fwd_bwd_ex":  # its options carry their own citations
+            continue
+        if not any(t in comment for t in PAGE_TITLES):
+            missing.append(name)
+    for field in ("row_offset;", "void *workspace;", "const int64_t *pos_row_ptr;", "float *dscale_out;"):
+        if not any(t in _comment_before(text, text.index(field)) for t in PAGE_TITLES):
+            missing.append(field)
+    assert not missing, missing
+
+
 def test_status_names():
     assert [binding.status_name(s) for s in range(5)] == [
         "success", "invalid-argument", "unsupported", "out-of-memory", "device-error"]
@@ -180,3 +215,29 @@ def test_workspace_bytes_with_positives():
     assert binding.workspace_bytes(256, 1024, 1024, 5, 1, -1) == base
     assert binding.workspace_bytes(256, 256, 1024, 5, 0, 10) == 0  # softmax kinds take no list
     assert binding.workspace_bytes(256, 1024, 1024, 5, 3, 5000) > binding.workspace_bytes(256, 1024, 1024, 5, 3)
+
+
+def test_binding_refuses_gradient_buffers_the_kernels_would_overrun():
+    import torch
+    dev = torch.device("cpu")
+    ok = torch.empty(4, 8, dtype=torch.float32)
+    binding._check_grad_buffer("dq", ok, (4, 8), dev)
+    binding._check_grad_buffer("dq", None, (4, 8), dev)
+    with pytest.raises(TypeError):
+        binding._check_grad_buffer("dq", ok.to(torch.bfloat16), (4, 8), dev)
+    with pytest.raises(ValueError):
+        binding._check_grad_buffer("dq", ok, (4, 16), dev)
+    with pytest.raises(ValueError):
+        binding._check_grad_buffer("dk", torch.empty(8, 4, dtype=torch.float32).t(), (4, 8), dev)
+    with pytest.raises(ValueError):
+        binding._check_grad_buffer("dk", ok, (4, 8), torch.device("cuda", 0))
+
+
+def test_package_exports():
+    import contrastive_embedding_loss_amd as pkg
+    assert (pkg.INFONCE, pkg.SIGLIP, pkg.INFONCE_ROWS, pkg.ONESET_SIGLIP) == (0, 1, 2, 3)
+    assert pkg.ONESET_SIGLIP == binding.ONESET_SIGLIP
+    for name in pkg._BINDING_NAMES:
+        assert getattr(pkg, name) is getattr(binding, name), name
+    with pytest.raises(AttributeError):
+        pkg.fwd_bwd_ex
