@@ -52,7 +52,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="infonce_32768")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=24576, help="rows of the oracle's timed sample")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="time the oracle on a sample of this many rows of the same recipe instead of the "
+                         "workload's own arrays (0: the workload's own arrays)")
+    ap.add_argument("--no-gemm-ceiling", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (a known-size kernel "
                          "against which the HBM byte counters are scaled) and exit")
@@ -161,35 +164,67 @@ def main():
             hbm_stages[name] = {"ms": round(t, 4), "bytes": nbytes, "GB_per_s": round(nbytes / (t * 1e-3) / 1e9, 1),
                                 "frac_of_8TBps": round(nbytes / (t * 1e-3) / 8e12, 3)}
 
+    # ceiling of a plain library GEMM of the forward's contraction shape on this chip, timed in this
+    # run: hipBLASLt through torch.matmul, BF16 in and out, R x D times D x N
+    gemm = None
+    if not args.no_gemm_ceiling:
+        qg = q.contiguous()
+        kt = k.t().contiguous()  # D x N, contiguous: a plain GEMM
+        c = torch.matmul(qg, kt)
+        for _ in range(2):
+            torch.matmul(qg, kt, out=c)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        torch.cuda.synchronize()
+        for a_ev, b_ev in ev:
+            a_ev.record(stream)
+            torch.matmul(qg, kt, out=c)
+            b_ev.record(stream)
+        torch.cuda.synchronize()
+        g_ms = sorted(a_ev.elapsed_time(b_ev) for a_ev, b_ev in ev)[len(ev) // 2]
+        g_tf = 2.0 * R * N * D / (g_ms * 1e-3) / 1e12
+        gemm = {"lib": "hipBLASLt (torch.matmul, bf16 in/out)", "shape": [R, D, N], "ms": round(g_ms, 4),
+                "tflops": round(g_tf, 1), "pct_bf16_peak": round(100.0 * g_tf / PEAK_BF16_TFLOPS, 2)}
+        del c, kt, qg
+        torch.cuda.empty_cache()
+        print(f"[bench] GEMM ceiling {R}x{D}x{N}: {g_ms:.3f} ms = {g_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import bf16_bits_to_f64, contrastive_fwd_bwd
 
-        n_s = min(args.cpu_sample, R)
-        pos_s = None
-        if w.recipe == "band":  # entries of the same recipe, about n_s keys in all
-            from contrastive_embedding_loss_amd.inputs import make_band_inputs
-            e = w.extra
-            qs, ks, rp_s, col_s = make_band_inputs(max(1, n_s * R // N), D, e["extra_pos"], e["hard_neg"], w.noise,
-                                                   e["hard_noise"], w.seed)
-            pos_s = (rp_s, col_s)
-        else:
-            qs, ks = make_inputs(n_s, n_s, D, w.recipe, w.noise, w.seed, w.extra.get("centroids", 256))
-        if oneset:
-            qs = ks  # the one-set sample scores its whole set
-        r_s, c_s = qs.shape[0], ks.shape[0]
         cores = len(os.sched_getaffinity(0))
-        print(f"[bench] oracle sample {r_s}x{c_s} on {cores} cores", file=sys.stderr, flush=True)
         kind = w.kind
+        if args.cpu_sample:  # a sample of the same recipe (to bound the oracle's time)
+            n_s = min(args.cpu_sample, R)
+            pos_s = None
+            if w.recipe == "band":  # entries of the same recipe, about n_s keys in all
+                from contrastive_embedding_loss_amd.inputs import make_band_inputs
+                e = w.extra
+                qs, ks, rp_s, col_s = make_band_inputs(max(1, n_s * R // N), D, e["extra_pos"], e["hard_neg"],
+                                                       w.noise, e["hard_noise"], w.seed)
+                pos_s = (rp_s, col_s)
+            else:
+                qs, ks = make_inputs(n_s, n_s, D, w.recipe, w.noise, w.seed, w.extra.get("centroids", 256))
+            if oneset:
+                qs = ks  # the one-set sample scores its whole set
+            off_s = 0
+            what = "a sample of the same recipe and prefixes"
+        else:  # the workload's own BF16 arrays, the very inputs the GPU steps ran on
+            qs, ks, pos_s, off_s = qb, kb, positives, w.row_offset
+            what = f"the {w.name} workload's own BF16 inputs (the arrays the timed GPU steps used)"
+        r_s, c_s = qs.shape[0], ks.shape[0]
+        print(f"[bench] oracle on {r_s}x{c_s} ({'sample' if args.cpu_sample else 'the workload itself'}) "
+              f"on {cores} cores", file=sys.stderr, flush=True)
         t1 = time.perf_counter()
         contrastive_fwd_bwd(bf16_bits_to_f64(qs), bf16_bits_to_f64(ks), w.prefixes, w.scale, w.bias, kind,
-                            weights=w.weights, threads=cores, positives=pos_s)
+                            weights=w.weights, row_offset=off_s, threads=cores, positives=pos_s)
         tc = time.perf_counter() - t1
         fl = 4.0 if oneset else 8.0
         cpu = {"value": round(fl * r_s * c_s * D / tc / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
                "kind": "oracle",
-               "sample": f"FP64 oracle fwd+bwd on a {r_s}x{c_s} batch of the same recipe and prefixes "
-                         f"({tc:.1f} s), rate = {fl:.0f}*R*N*D/t"}
+               "sample": f"FP64 oracle fwd+bwd on {what}: {r_s}x{c_s}, D={D}, {P} prefixes, "
+                         f"{tc:.1f} s; rate = {fl:.0f}*R*N*D/t"}
+        print(f"[bench] oracle {tc:.1f} s", file=sys.stderr, flush=True)
 
     out = {
         "metric": "fwd+bwd TFLOP/s & pair-scores/s at N=32768, 5 prefixes; % BF16 MFMA peak",
@@ -213,6 +248,8 @@ def main():
                    **({"extra_positives": int(positives[0][-1])} if positives is not None else {})},
         "pair_scores_per_s": pair_scores,
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "pct_of_gemm_ceiling": round(100.0 * tflops / gemm["tflops"], 2) if gemm else None,
+        "gemm_ceiling": gemm,
         "kernel_ms_per_step": {n: round(t, 4) for n, t in kern_per_step.items()},
         "roofline": roofline,
         "hbm_stages": hbm_stages,

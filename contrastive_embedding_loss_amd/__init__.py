@@ -11,6 +11,7 @@ INFONCE = 0
 SIGLIP = 1
 INFONCE_ROWS = 2
 ONESET_SIGLIP = 3
+ONESET_SIGLIP_EDGES = 4
 
 _BINDING_NAMES = ("fwd_bwd", "workspace_bytes", "supported", "status_name", "last_error", "profile", "release",
                   "library", "UformError")

@@ -17,6 +17,7 @@ INFONCE = 0
 SIGLIP = 1
 INFONCE_ROWS = 2
 ONESET_SIGLIP = 3  # one set scored against itself: q = k[row_offset:row_offset + R], no dk
+ONESET_SIGLIP_EDGES = 4  # the same, every positive listed as a relation (``positives``), no implicit pairs
 ACCUMULATE = 1
 PROFILE = 2
 ONE_SPLIT = 4
@@ -185,8 +186,8 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
     loss = torch.empty(1, **f32)
     if want_dq and dq is None:
         dq = torch.zeros(R, D, **f32) if accumulate else torch.empty(R, D, **f32)
-    if kind == ONESET_SIGLIP:
-        want_dk = False  # the one-set form's only gradient is dq
+    if kind in (ONESET_SIGLIP, ONESET_SIGLIP_EDGES):
+        want_dk = False  # the one-set forms' only gradient is dq
     if want_dk and dk is None:
         dk = torch.zeros(N, D, **f32) if accumulate else torch.empty(N, D, **f32)
     if not want_dq:
@@ -202,13 +203,15 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
         opt.prefix_weights = ctypes.cast(wbuf, ctypes.POINTER(ctypes.c_float))
     ex = None
     if extras:
-        softmax = kind not in (SIGLIP, ONESET_SIGLIP)
-        ex = {"prefix_losses": torch.empty(P, **f32), "pos_logit": torch.empty(P, R, **f32)}
+        softmax = kind not in (SIGLIP, ONESET_SIGLIP, ONESET_SIGLIP_EDGES)
+        ex = {"prefix_losses": torch.empty(P, **f32)}
+        opt.prefix_losses_out = ex["prefix_losses"].data_ptr()
+        if kind != ONESET_SIGLIP_EDGES:  # every other kind has one positive per row
+            ex["pos_logit"] = torch.empty(P, R, **f32)
+            opt.pos_logit_out = ex["pos_logit"].data_ptr()
         if softmax:
             ex["row_lse"] = torch.empty(P, R, **f32)
             ex["col_lse"] = torch.empty(P, N, **f32)
-        opt.prefix_losses_out = ex["prefix_losses"].data_ptr()
-        opt.pos_logit_out = ex["pos_logit"].data_ptr()
         if softmax:
             opt.row_lse_out = ex["row_lse"].data_ptr()
             opt.col_lse_out = ex["col_lse"].data_ptr()

@@ -22,6 +22,7 @@ constexpr int kInfonce = 0;
 constexpr int kSiglip = 1;
 constexpr int kRows = 2;
 constexpr int kOneset = 3;  // one-set sigmoid form: computed as the sigmoid kind with pxor = 1, mirror = 2
+constexpr int kOnesetEdges = 4;  // one-set form with listed relations only: pxor = 0, mirror = 2, no implicit positive
 
 __host__ __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -48,6 +49,7 @@ struct PrepArgs {
 struct StatsArgs {
     int64_t R, N, off, nJt, nIt;
     int pxor;      // as in PrepArgs
+    int nopos;     // 1: no implicit positive (one-set form with listed relations): no positive-cell terms
     float mirror;  // 2 for the one-set form (a row's gradient through both mirrored cells), else 1
     Prefixes pf;
     int kind;
@@ -66,6 +68,18 @@ struct StatsArgs {
     float *biasparts;         // sigmoid form: [slot][P], minus the positives' sigma(-l); nullable
     int64_t slot0;
 };
+
+// Listed cells (extra positives) of one (outer block of 64 rows, inner block of 16 rows) pair of a
+// backward pass: bit o of m[r] marks the cell of outer row 64 ob + o and inner row 16 nb + r.  A
+// pass's entries are sorted by outer block, then by nb (one entry per pair); the backward leaves
+// these cells out of its band operands and sums, and the extra-positive pass gives them their whole
+// loss and residual in FP32.
+struct ListEnt {
+    int32_t nb, pad;
+    uint64_t m[16];
+};
+constexpr int kListEntWords = (int)(sizeof(ListEnt) / 4);
+static_assert(sizeof(ListEnt) == 136, "ListEnt layout");
 
 struct BwdArgs {
     const _Float16 *X16;  // outer rows scaled by their sig, FP16 [NO][D]
@@ -95,6 +109,9 @@ struct BwdArgs {
     // one inner split only: the gradient rows are finished in place (the finalize terms
     // below) and written to fin_out instead of part / Cpart
     float *fin_out;
+    // listed cells: entries lent[lptr[ob] .. lptr[ob + 1]) of outer block ob (lptr nullable)
+    const int32_t *lptr;
+    const ListEnt *lent;
     const u16 *finX, *finY;                         // BF16 outer / inner rows
     const float *diagA, *posdot, *invx, *gam;        // as in FinArgs
     int64_t R, pos_shift;
@@ -144,8 +161,9 @@ hipError_t launch_maxes(const float *t0, const float *t1, const float *t2, const
 hipError_t launch_finalize(const FinArgs &a, hipStream_t s);
 hipError_t launch_loss(const LossArgs &a, hipStream_t s);
 
-// Extra positives of the sigmoid form (positives.hip).  A listed cell scored as a negative by
-// the main passes differs from its positive form by -l in the loss and by -1 in the residual.
+// Extra positives of the sigmoid form (positives.hip).  The backward passes leave every listed
+// cell out (ListEnt masks); this pass gives each its positive-label loss softplus(-l) and its
+// residual (sigma(l) - 1) / den = -sigma(-l) / den, all in FP32.
 struct PosArgs {
     const u16 *x, *y;          // outer rows [NO][D] and inner rows [NI][D], BF16
     const float *invx, *invy;  // [P][NO], [P][NI]: 1 / |row[:w_p]|
@@ -154,17 +172,17 @@ struct PosArgs {
     Prefixes pf;
     const int32_t *ptr, *idx;  // outer row o's listed inner rows: idx[ptr[o] .. ptr[o + 1])
     float t, b;                // logit scale and bias
-    float gc[kMaxP];           // -mirror (w_p / W) t / den: the gradient factor of one listed cell
-    float *out;                // [NO][D] FP32 gradient the corrections are added to, or nullptr
-    float *parts;              // [blocks][2][P]: the block's sums of -l^p and cos^p, or nullptr
+    float gc[kMaxP];           // mirror (w_p / W) t / den: with -sigma(-l^p), the gradient factor of a listed cell
+    float *out;                // [NO][D] FP32 gradient the listed cells' terms are added to, or nullptr
+    float *parts;              // [blocks][3][P]: the block's sums of softplus(-l^p), sigma(-l^p) cos^p and
+                               // sigma(-l^p), or nullptr
 };
 struct PosFoldArgs {
-    const float *parts;  // [nblk][2][P]
+    const float *parts;  // [nblk][3][P]
     int64_t nblk;
     Prefixes pf;
     double norm;         // 1 / den
     float wnorm[kMaxP];
-    int64_t npos;        // listed cells
     float *loss_out, *prefix_losses_out, *dscale_out, *dbias_out;  // updated in place (nullable but loss_out)
 };
 constexpr int kPosBlocks = 1024;  // most workgroups of one extra-positive pass

@@ -7,6 +7,7 @@
 // C verb per operation, statuses spelled like "invalid-argument"); the loss
 // follows "Scaling-Up Contrastive Learning over NVLink Multicast", section
 // "One Set or Two".
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -49,11 +50,53 @@ struct Plan {
     size_t o_rowpart, o_colpart, o_part, o_Cpart, o_loss, o_tsum, o_bias;
     int64_t npos;                      // listed extra positives
     bool pos_cols;                     // the column lists are needed (two-set sigmoid with dk)
-    size_t o_plist, o_pparts;           // extra positives: row then column lists, partial sums
+    size_t o_plist, o_pparts;           // extra positives: lists and mask tables (ListWords), partial sums
     size_t total;
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Word offsets (int32) of the extra-positive region of the workspace, at most npos cells:
+// row lists [R + 1 | npos]; column lists [N + 1 | npos] (for dk); then per backward pass the
+// outer blocks' entry ranges [blocks + 1] and at most npos ListEnt entries (8-byte aligned).
+struct ListWords {
+    size_t rows, cols, lptr_r, ent_r, lptr_c, ent_c, total;
+    ListWords(int64_t R, int64_t N, int64_t npos, bool pos_cols) {
+        const size_t n = npos > 0 ? (size_t)npos : 0;
+        auto even = [](size_t w) { return (w + 1) & ~(size_t)1; };
+        rows = 0;
+        cols = rows + (size_t)R + 1 + n;
+        lptr_r = cols + (pos_cols ? (size_t)N + 1 + n : 0);
+        ent_r = even(lptr_r + (size_t)((R + kBwdOuter - 1) / kBwdOuter) + 1);
+        lptr_c = ent_r + n * kListEntWords;
+        ent_c = even(lptr_c + (pos_cols ? (size_t)((N + kBwdOuter - 1) / kBwdOuter) + 1 : 0));
+        total = ent_c + (pos_cols ? n * kListEntWords : 0);
+    }
+};
+
+// Mask tables of one backward pass from its outer rows' CSR lists (ptr [NO + 1], idx): per block
+// of kBwdOuter outer rows, one ListEnt per inner block that holds listed cells, sorted by nb.
+void build_list_ents(int64_t NO, const int32_t *ptr, const int32_t *idx, int32_t *lptr, std::vector<ListEnt> &ents) {
+    const int64_t nob = (NO + kBwdOuter - 1) / kBwdOuter;
+    std::vector<std::pair<int32_t, int32_t>> cells;  // (inner block, row in block * 64 + outer lane)
+    lptr[0] = 0;
+    for (int64_t ob = 0; ob < nob; ++ob) {
+        cells.clear();
+        const int64_t o1 = std::min(NO, (ob + 1) * kBwdOuter);
+        for (int64_t o = ob * kBwdOuter; o < o1; ++o)
+            for (int32_t e = ptr[o]; e < ptr[o + 1]; ++e)
+                cells.emplace_back(idx[e] / kBwdInner, (idx[e] % kBwdInner) * 64 + (int32_t)(o - ob * kBwdOuter));
+        std::sort(cells.begin(), cells.end());
+        for (size_t c = 0; c < cells.size(); ++c) {
+            if (c == 0 || cells[c].first != cells[c - 1].first) {
+                ents.push_back(ListEnt{});
+                ents.back().nb = cells[c].first;
+            }
+            ents.back().m[cells[c].second / 64] |= 1ull << (cells[c].second % 64);
+        }
+        lptr[ob + 1] = (int32_t)ents.size();
+    }
+}
 
 // Inner splits so that a pass launches enough workgroups for 256 CUs.
 void choose_split(int64_t NO, int64_t NI, int64_t &nsplit, int64_t &bps) {
@@ -154,8 +197,8 @@ Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, in
     // the pass's partial sums
     p.npos = npos;
     p.pos_cols = npos >= 0 && want_dk;
-    p.o_plist = take(npos >= 0 ? sizeof(int32_t) * ((R + 1 + npos) + (p.pos_cols ? N + 1 + npos : 0)) : 0);
-    p.o_pparts = take(npos >= 0 ? sizeof(float) * kPosBlocks * 2 * P : 0);
+    p.o_plist = take(npos >= 0 ? sizeof(int32_t) * ListWords(R, N, npos, p.pos_cols).total : 0);
+    p.o_pparts = take(npos >= 0 ? sizeof(float) * kPosBlocks * 3 * P : 0);
     p.total = off_b;
     return p;
 }
@@ -174,16 +217,19 @@ uform_status_t validate(const void *q, const void *k, int64_t R, int64_t N, int6
         return fail(uform_status_invalid_argument_k, "dq and dk must be 16-byte aligned");
     if (R < 1 || N < 1 || D < 1) return fail(uform_status_invalid_argument_k, "R, N and D must be positive");
     if (R > N) return fail(uform_status_invalid_argument_k, "R must not exceed N");
-    if (kind != kInfonce && kind != kSiglip && kind != kRows && kind != kOneset)
-        return fail(uform_status_invalid_argument_k, "unknown kind");
+    if (kind < kInfonce || kind > kOnesetEdges) return fail(uform_status_invalid_argument_k, "unknown kind");
     const int64_t off = opt ? opt->row_offset : 0;
     if (off < 0 || off + R > N) return fail(uform_status_invalid_argument_k, "need 0 <= row_offset and row_offset + R <= N");
-    if (kind == kOneset) {
-        if (N % 2 != 0) return fail(uform_status_invalid_argument_k, "the one-set form needs an even set (rows 2m, 2m + 1 pair up)");
+    const bool oneset = kind == kOneset || kind == kOnesetEdges;
+    if (kind == kOneset && N % 2 != 0)
+        return fail(uform_status_invalid_argument_k, "the one-set form with pairs needs an even set (rows 2m, 2m + 1 pair up)");
+    if (oneset) {
         if ((const char *)q != (const char *)k + off * D * 2)
-            return fail(uform_status_invalid_argument_k, "the one-set form needs q = k + row_offset * D (its rows of the set)");
-        if (dk) return fail(uform_status_invalid_argument_k, "the one-set form has one gradient, dq (pass dk = NULL)");
+            return fail(uform_status_invalid_argument_k, "the one-set forms need q = k + row_offset * D (its rows of the set)");
+        if (dk) return fail(uform_status_invalid_argument_k, "the one-set forms have one gradient, dq (pass dk = NULL)");
     }
+    if (kind == kOnesetEdges && opt && opt->pos_logit_out)
+        return fail(uform_status_invalid_argument_k, "the one-set form with listed relations has no single positive logit");
     if (kind == kInfonce && (R != N || off != 0))
         return fail(uform_status_invalid_argument_k, "symmetric InfoNCE needs R == N and row_offset == 0");
     if (!prefixes) return fail(uform_status_invalid_argument_k, "prefixes must be a host array");
@@ -211,8 +257,8 @@ uform_status_t validate(const void *q, const void *k, int64_t R, int64_t N, int6
             return fail(uform_status_invalid_argument_k, "dscale_out and dbias_out must be 4-byte aligned");
     }
     if (opt && opt->pos_row_ptr) {
-        if (kind != kSiglip && kind != kOneset)
-            return fail(uform_status_invalid_argument_k, "extra positives are defined for the sigmoid kinds");
+        if (kind != kSiglip && !oneset)
+            return fail(uform_status_invalid_argument_k, "listed positives are defined for the sigmoid kinds");
         const int64_t *rp = opt->pos_row_ptr;
         if (rp[0] != 0) return fail(uform_status_invalid_argument_k, "pos_row_ptr[0] must be 0");
         for (int64_t i = 0; i < R; ++i)
@@ -222,18 +268,30 @@ uform_status_t validate(const void *q, const void *k, int64_t R, int64_t N, int6
         if (rp[R] >= ((int64_t)1 << 31) - 1)
             return fail(uform_status_unsupported_k, "at most 2^31 - 2 extra positives per call");
         for (int64_t i = 0; i < R; ++i) {
-            const int64_t g = off + i, own = kind == kOneset ? (g ^ 1) : g;
+            const int64_t g = off + i, own = kind == kSiglip ? g : kind == kOneset ? (g ^ 1) : -1;
             for (int64_t e = rp[i]; e < rp[i + 1]; ++e) {
                 const int64_t j = opt->pos_col[e];
-                if (j < 0 || j >= N || (e > rp[i] && j <= opt->pos_col[e - 1]) || j == own || (kind == kOneset && j == g))
+                if (j < 0 || j >= N || (e > rp[i] && j <= opt->pos_col[e - 1]) || j == own || (oneset && j == g))
                     return fail(uform_status_invalid_argument_k,
-                                "row " + std::to_string(i) + ": extra positives must be increasing columns in [0, N), "
-                                "none of them the row's own positive (nor, in the one-set form, the row itself)");
+                                "row " + std::to_string(i) + ": listed positives must be increasing columns in [0, N), "
+                                "none of them the row's own positive (nor, in the one-set forms, the row itself)");
             }
+        }
+        if (oneset) {  // mirrored cells carry one label: a pair of two rows of the share is listed both ways
+            for (int64_t i = 0; i < R; ++i)
+                for (int64_t e = rp[i]; e < rp[i + 1]; ++e) {
+                    const int64_t j = opt->pos_col[e] - off;
+                    if (j < 0 || j >= R) continue;
+                    const int32_t *b = opt->pos_col + rp[j], *en = opt->pos_col + rp[j + 1];
+                    if (!std::binary_search(b, en, (int32_t)(off + i)))
+                        return fail(uform_status_invalid_argument_k,
+                                    "rows " + std::to_string(off + i) + " and " + std::to_string(off + j) +
+                                        ": a one-set pair must be listed both ways");
+                }
         }
     }
     if (D % 64 != 0 || D > kMaxD) return fail(uform_status_unsupported_k, "D must be a multiple of 64 and at most 1024");
-    const bool sigmoid_kind = kind == kSiglip || kind == kOneset;
+    const bool sigmoid_kind = kind == kSiglip || oneset;
     if (!sigmoid_kind && std::fabs(scale) > UFORM_CONTRASTIVE_MAX_SOFTMAX_SCALE)
         return fail(uform_status_unsupported_k, "softmax kinds support |scale| <= 40");
     if ((dq || dk || sigmoid_kind) && !bwd_mask_supported(ladder_mask(prefixes, n_prefixes)))
@@ -378,11 +436,14 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
                    int32_t P, float scale, float bias, int32_t kind_in, float *loss_out, float *dq, float *dk,
                    hipStream_t s, const uform_contrastive_options_t *opt, const ProfCtx &prof) {
     const u16 *q = (const u16 *)q_, *k = (const u16 *)k_;
-    // the one-set form runs as the sigmoid kind whose positive of row g is g ^ 1, whose cell (g, g)
-    // is not scored, and whose row gradients count both mirrored cells
-    const bool oneset = kind_in == kOneset;
+    // the one-set forms run as the sigmoid kind whose cell (g, g) is not scored and whose row
+    // gradients count both mirrored cells; with pairs the positive of row g is g ^ 1, with listed
+    // relations no cell is an implicit positive (pxor = 0 points the positive at the self cell,
+    // which the masks already leave out, and nopos gives it no terms)
+    const bool oneset = kind_in == kOneset || kind_in == kOnesetEdges;
+    const bool nopos = kind_in == kOnesetEdges;
     const int32_t kind = oneset ? kSiglip : kind_in;
-    const int pxor = oneset ? 1 : 0;
+    const int pxor = kind_in == kOneset ? 1 : 0;
     const float mirror = oneset ? 2.0f : 1.0f;
     const int64_t off = opt ? opt->row_offset : 0;
     const bool softmax = kind != kSiglip;
@@ -401,18 +462,21 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     char *base = (char *)ws;
     auto F = [&](size_t o) { return (float *)(base + o); };
     int32_t *const plist = npos >= 0 ? (int32_t *)(base + pl.o_plist) : nullptr;
-    int32_t *const clist = pl.pos_cols ? plist + (R + 1 + npos) : nullptr;  // right after the row lists
+    const ListWords lw(R, N, npos, pl.pos_cols);
+    int32_t *const clist = pl.pos_cols ? plist + lw.cols : nullptr;
     if (npos >= 0) {
-        // row lists as given; column lists (rows ascending per column) by a counting pass
+        // row lists as given; column lists (rows ascending per column) by a counting pass; the
+        // backward passes' mask tables of the listed cells
         const int64_t *rp = opt->pos_row_ptr;
         const int32_t *pc = opt->pos_col;
-        const size_t nrow = (size_t)(R + 1 + npos), ncol = pl.pos_cols ? (size_t)(N + 1 + npos) : 0;
-        uform_status_t st = stage_and_copy(s, plist, nrow + ncol, [&](int32_t *h) {
-            for (int64_t i = 0; i <= R; ++i) h[i] = (int32_t)rp[i];
-            for (int64_t e = 0; e < npos; ++e) h[R + 1 + e] = pc[e];
-            if (!pl.pos_cols) return;
-            int32_t *cp = h + nrow, *cr = cp + N + 1;
-            for (int64_t j = 0; j <= N; ++j) cp[j] = 0;
+        std::vector<int32_t> h(lw.total, 0);
+        for (int64_t i = 0; i <= R; ++i) h[lw.rows + i] = (int32_t)rp[i];
+        for (int64_t e = 0; e < npos; ++e) h[lw.rows + R + 1 + e] = pc[e];
+        std::vector<ListEnt> ents;
+        build_list_ents(R, h.data() + lw.rows, h.data() + lw.rows + R + 1, h.data() + lw.lptr_r, ents);
+        std::memcpy(h.data() + lw.ent_r, ents.data(), ents.size() * sizeof(ListEnt));
+        if (pl.pos_cols) {
+            int32_t *cp = h.data() + lw.cols, *cr = cp + N + 1;
             for (int64_t e = 0; e < npos; ++e) ++cp[pc[e] + 1];
             for (int64_t j = 0; j < N; ++j) cp[j + 1] += cp[j];
             std::vector<int32_t> fill((size_t)N, 0);
@@ -421,6 +485,12 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
                     const int32_t j = pc[e];
                     cr[cp[j] + fill[j]++] = (int32_t)i;
                 }
+            ents.clear();
+            build_list_ents(N, cp, cr, h.data() + lw.lptr_c, ents);
+            std::memcpy(h.data() + lw.ent_c, ents.data(), ents.size() * sizeof(ListEnt));
+        }
+        uform_status_t st = stage_and_copy(s, plist, h.size(), [&](int32_t *dst) {
+            std::memcpy(dst, h.data(), h.size() * sizeof(int32_t));
         });
         if (st != uform_status_success_k) return st;
     }
@@ -479,6 +549,7 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     sa.N = N;
     sa.off = off;
     sa.pxor = pxor;
+    sa.nopos = nopos ? 1 : 0;
     sa.mirror = mirror;
     sa.nJt = 2 * pl.nJt;  // partials per row: two per column tile
     sa.nIt = 2 * pl.nIt;
@@ -564,6 +635,10 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
             ba.oNeg = nullptr;
             ba.gterm = gmax + 2 * P;
         }
+        if (npos >= 0) {  // listed cells leave the dense pass (the extra-positive pass takes them)
+            ba.lptr = plist + (rowpass ? lw.lptr_r : lw.lptr_c);
+            ba.lent = (const ListEnt *)(plist + (rowpass ? lw.ent_r : lw.ent_c));
+        }
         ba.diag_shift = rowpass ? off : -off;
         ba.pxor = pxor;
         ba.blocks_per_split = rowpass ? pl.bps_row : pl.bps_col;
@@ -639,8 +714,8 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
         pa2.invy = invk;
         pa2.NO = R;
         pa2.NI = N;
-        pa2.ptr = plist;
-        pa2.idx = plist + R + 1;
+        pa2.ptr = plist + lw.rows;
+        pa2.idx = plist + lw.rows + R + 1;
         for (int i = 0; i < P; ++i) pa2.gc[i] = (float)(-(double)mirror * wnorm[i] * scale / den);
         pa2.out = dq;
         pa2.parts = F(pl.o_pparts);
@@ -683,7 +758,6 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
         fa.pf = pf;
         fa.norm = 1.0 / den;
         for (int i = 0; i < kMaxP; ++i) fa.wnorm[i] = wnorm[i];
-        fa.npos = npos;
         fa.loss_out = loss_out;
         fa.prefix_losses_out = la.prefix_losses_out;
         fa.dscale_out = dscale_out;
@@ -753,14 +827,15 @@ size_t uform_contrastive_workspace_bytes(int64_t R, int64_t N, int64_t D, int32_
 
 size_t uform_contrastive_workspace_bytes_ex(int64_t R, int64_t N, int64_t D, int32_t n_prefixes, int32_t kind,
                                             int64_t n_positives) {
-    if (n_positives >= 0 && kind != kSiglip && kind != kOneset) return 0;
+    if (n_positives >= 0 && kind != kSiglip && kind != kOneset && kind != kOnesetEdges) return 0;
     if (R < 1 || N < 1 || R > N || D < 64 || D % 64 != 0 || D > kMaxD || n_prefixes < 1 || n_prefixes > kMaxP)
         return 0;
-    if (kind != kInfonce && kind != kSiglip && kind != kRows && kind != kOneset) return 0;
+    if (kind < kInfonce || kind > kOnesetEdges) return 0;
     int32_t pw[kMaxP];
     for (int32_t i = 0; i < n_prefixes; ++i) pw[i] = (int32_t)(D - 32 * (n_prefixes - 1 - i));  // any ladder ending at D
     const int64_t npos = n_positives < 0 ? -1 : n_positives;
-    if (kind == kOneset) return make_plan(R, N, D, pw, n_prefixes, kSiglip, 0, true, false, false, npos).total;
+    if (kind == kOneset || kind == kOnesetEdges)
+        return make_plan(R, N, D, pw, n_prefixes, kSiglip, 0, true, false, false, npos).total;
     return make_plan(R, N, D, pw, n_prefixes, kind, 0, true, true, false, npos).total;
 }
 
@@ -769,15 +844,14 @@ uform_status_t uform_contrastive_supported(int64_t D, const int32_t *prefixes, i
     g_last_error.clear();
     if (!prefixes || n_prefixes < 1 || n_prefixes > kMaxP)
         return fail(uform_status_invalid_argument_k, "prefixes must be a host array of 1..8 widths");
-    if (kind != kInfonce && kind != kSiglip && kind != kRows && kind != kOneset)
-        return fail(uform_status_invalid_argument_k, "unknown kind");
+    if (kind < kInfonce || kind > kOnesetEdges) return fail(uform_status_invalid_argument_k, "unknown kind");
     for (int32_t i = 0; i < n_prefixes; ++i) {
         if (prefixes[i] < 32 || prefixes[i] % 32 != 0 || (i > 0 && prefixes[i] <= prefixes[i - 1]))
             return fail(uform_status_invalid_argument_k, "prefix widths must be increasing multiples of 32");
     }
     if (D < 1 || prefixes[n_prefixes - 1] > D) return fail(uform_status_invalid_argument_k, "the widest prefix exceeds D");
     if (D % 64 != 0 || D > kMaxD) return fail(uform_status_unsupported_k, "D must be a multiple of 64 and at most 1024");
-    if ((with_gradients || kind == kSiglip || kind == kOneset) && !bwd_mask_supported(ladder_mask(prefixes, n_prefixes)))
+    if ((with_gradients || kind == kSiglip || kind == kOneset || kind == kOnesetEdges) && !bwd_mask_supported(ladder_mask(prefixes, n_prefixes)))
         return fail(uform_status_unsupported_k, "this prefix ladder has no compiled backward kernel");
     return uform_status_success_k;
 }

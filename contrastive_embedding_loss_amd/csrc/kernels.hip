@@ -15,6 +15,7 @@
 // X = k, Y = q.  S^p = <x[:P_p], y[:P_p]>, logits in base-2 units
 // u = l * log2(e); softmax kinds use one fixed shift c = -|s| log2(e) so that
 // x = (l - b - |s|) log2(e) <= 0 and one exp per cell serves row and column sums.
+#include <climits>
 #include <type_traits>
 
 #include "common.h"
@@ -719,15 +720,19 @@ __global__ __launch_bounds__(256) void k_siglip_tabs(StatsArgs a) {
         if (r < a.R) {
             const int64_t i = r;
             const float iq = a.invq[p * a.R + i], ik = a.invk[p * a.N + ((i + a.off) ^ a.pxor)];
-            const float S = a.posdot[p * a.R + i];
-            const float l = a.scale * S * iq * ik + a.bias;
-            // softplus(-l) and sigmoid(-l), both overflow-free
-            const float t = expf(-fabsf(l));
-            lpos = fmaxf(-l, 0.f) + log1pf(t);
-            sig_neg = (l >= 0.f) ? t / (1.f + t) : 1.f / (1.f + t);
             a.qC[p * a.R + i] = a.sgn * a.wnorm[p] * iq / a.invq[(P - 1) * a.R + i];
-            a.diagA[p * a.R + i] = -a.mirror * a.wnorm[p] * a.scale * sig_neg * a.inv_den * iq * ik;
-            if (a.pos_logit_out) a.pos_logit_out[p * a.R + i] = l;
+            if (a.nopos) {  // no implicit positive: its loss, residual and coefficient are 0
+                a.diagA[p * a.R + i] = 0.f;
+            } else {
+                const float S = a.posdot[p * a.R + i];
+                const float l = a.scale * S * iq * ik + a.bias;
+                // softplus(-l) and sigmoid(-l), both overflow-free
+                const float t = expf(-fabsf(l));
+                lpos = fmaxf(-l, 0.f) + log1pf(t);
+                sig_neg = (l >= 0.f) ? t / (1.f + t) : 1.f / (1.f + t);
+                a.diagA[p * a.R + i] = -a.mirror * a.wnorm[p] * a.scale * sig_neg * a.inv_den * iq * ik;
+                if (a.pos_logit_out) a.pos_logit_out[p * a.R + i] = l;
+            }
         } else if (r < a.R + a.N) {
             const int64_t j = r - a.R;
             const float ik = a.invk[p * a.N + j];
@@ -927,9 +932,10 @@ __device__ __forceinline__ void bwd_finish(const BwdArgs &a, const f32x16 (&dacc
 }
 
 // SIG: sigmoid form; UPD: the gradient contraction runs; LOSS: the pass also sums the sigmoid
-// form's loss; BIAS: and sigma(l) for dL/dbias.  Compile-time choices, so the epilogue has no
-// branch and carries only the sums a call asks for.
-template <uint32_t MASK, bool SIG, bool UPD, bool LOSS, bool BIAS>
+// form's loss; BIAS: and sigma(l) for dL/dbias; LIST: listed cells (extra positives) are left
+// out of the pass.  Compile-time choices, so the epilogue has no branch and carries only the
+// sums a call asks for.
+template <uint32_t MASK, bool SIG, bool UPD, bool LOSS, bool BIAS, bool LIST>
 __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     using L = Ladder<MASK>;
     constexpr int NP = L::NP;
@@ -1086,7 +1092,25 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
     const int pxr = a.pxor;
     const int c_lo = o0 + dsh - BI - pxr;
     const uint32_t c_len = (uint32_t)(BO + BI - 1 + 2 * pxr);
-    auto needmask = [&](int nb) { return nb >= nb_sp || (uint32_t)(nb * BI - c_lo - 1) < c_len; };
+    // listed cells (extra positives): this outer block's entries, sorted by nb; lnb is the nb of
+    // entry lcur (INT_MAX past the last).  Blocks are visited in increasing order, so the cursor
+    // only moves forward, and it reads an entry only when it passes one.
+    // (LIST: a compile-time variant, so that calls without lists keep the plain block loop.)
+    int lcur = 0, lend = 0;
+    if constexpr (LIST) {
+        lcur = a.lptr[blockIdx.x];
+        lend = a.lptr[blockIdx.x + 1];
+    }
+    int lnb = LIST && lcur < lend ? a.lent[lcur].nb : INT_MAX;
+    auto listed = [&](int nb) {
+        if constexpr (!LIST) return false;
+        while (lnb < nb) {
+            ++lcur;
+            lnb = lcur < lend ? a.lent[lcur].nb : INT_MAX;
+        }
+        return lnb == nb;
+    };
+    auto needmask = [&](int nb) { return nb >= nb_sp || (uint32_t)(nb * BI - c_lo - 1) < c_len || listed(nb); };
     // lane masks of block nb's cells for inner rows 4 w + t (wave-uniform 64-bit masks)
     const uint64_t ovm = __builtin_amdgcn_ballot_w64(ovalid);
     auto block_masks = [&](int nb, uint64_t(&mk)[4]) {
@@ -1100,6 +1124,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
             for (int t = 0; t < 4; ++t)
                 mk[t] = __builtin_amdgcn_ballot_w64(ovalid && nw + t < lim && nw + t != ((o + dsh) ^ pxr) &&
                                                     (pxr == 0 || nw + t != o + dsh));
+            if (listed(nb)) {
+                const uint64_t *lm = a.lent[lcur].m + 4 * w;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) mk[t] &= ~lm[t];
+            }
         }
     };
     // Epilogue unit of prefix p for the block in ring slot eyo (its tables follow the tile): the
@@ -1659,22 +1688,29 @@ hipError_t launch_siglip_tabs(const StatsArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <uint32_t MASK, bool LIST>
+static hipError_t launch_bwd_sig(const BwdArgs &a, dim3 grid, hipStream_t s) {
+    const bool bias = a.biasparts != nullptr;
+    if (a.do_update && a.want_loss && bias)
+        hipLaunchKernelGGL((k_bwd<MASK, true, true, true, true, LIST>), grid, dim3(256), 0, s, a);
+    else if (a.do_update && a.want_loss)
+        hipLaunchKernelGGL((k_bwd<MASK, true, true, true, false, LIST>), grid, dim3(256), 0, s, a);
+    else if (a.do_update)
+        hipLaunchKernelGGL((k_bwd<MASK, true, true, false, false, LIST>), grid, dim3(256), 0, s, a);
+    else if (bias)
+        hipLaunchKernelGGL((k_bwd<MASK, true, false, true, true, LIST>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_bwd<MASK, true, false, true, false, LIST>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 template <uint32_t MASK>
 static hipError_t launch_bwd_mask(const BwdArgs &a, bool sig, dim3 grid, hipStream_t s) {
-    const bool bias = a.biasparts != nullptr;
-    if (!sig)
-        hipLaunchKernelGGL((k_bwd<MASK, false, true, false, false>), grid, dim3(256), 0, s, a);
-    else if (a.do_update && a.want_loss && bias)
-        hipLaunchKernelGGL((k_bwd<MASK, true, true, true, true>), grid, dim3(256), 0, s, a);
-    else if (a.do_update && a.want_loss)
-        hipLaunchKernelGGL((k_bwd<MASK, true, true, true, false>), grid, dim3(256), 0, s, a);
-    else if (a.do_update)
-        hipLaunchKernelGGL((k_bwd<MASK, true, true, false, false>), grid, dim3(256), 0, s, a);
-    else if (bias)
-        hipLaunchKernelGGL((k_bwd<MASK, true, false, true, true>), grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_bwd<MASK, true, false, true, false>), grid, dim3(256), 0, s, a);
-    return hipGetLastError();
+    if (!sig) {
+        hipLaunchKernelGGL((k_bwd<MASK, false, true, false, false, false>), grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    return a.lptr ? launch_bwd_sig<MASK, true>(a, grid, s) : launch_bwd_sig<MASK, false>(a, grid, s);
 }
 
 bool bwd_mask_supported(uint32_t mask) {

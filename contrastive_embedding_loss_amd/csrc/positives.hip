@@ -3,13 +3,16 @@
 // An entry of the batch may carry several positives besides its own pair
 // (UForm README, "Multimodal Perception from 64 to 1024 Dimensions", the
 // training-stack paragraph on loader-side properties); each listed cell takes
-// the label z = +1.
-// The main passes score every listed cell as a negative.  With l = t cos + b,
-// softplus(-l) - softplus(l) = -l and (sigma(l) - 1) - sigma(l) = -1, so the
-// listed cells change the loss by -l^p, the residual by -1/den, and the row
-// gradient by the derivative of -l^p through the prefix normalisation:
+// the label z = +1.  The dense backward passes leave every listed cell out of
+// their band operands and sums (as they do the row's own positive), so this
+// pass gives each listed cell, in FP32, its whole positive-label loss
+// softplus(-l^p) with l = t cos + b, and its whole residual
+// g^p = (sigma(l^p) - 1) / den = -sigma(-l^p) / den.  Summing sigma(l) in a 16-bit
+// band operand and subtracting 1 afterwards would lose a confident positive's
+// small residual to the operand's rounding.  The row gradient takes g^p
+// through the prefix normalisation:
 //
-//   dx_o[:w_p] += c_p (y_i[:w_p] |x_o^p|^-1 |y_i^p|^-1 - cos^p x_o[:w_p] |x_o^p|^-2)
+//   dx_o[:w_p] += c_p sigma(-l^p) (y_i[:w_p] |x_o^p|^-1 |y_i^p|^-1 - cos^p x_o[:w_p] |x_o^p|^-2)
 //
 // with c_p = -mirror (w_p / W) t / den.  One wave owns one outer row and walks
 // its list in order, so every sum has a fixed order and no atomics are needed.
@@ -43,7 +46,7 @@ __device__ __forceinline__ void load16(const u16 *p, float v[16]) {
 // Lane l holds elements 16 l .. 16 l + 15 of a row (D <= 1024); waves walk the outer rows
 // blockIdx.x * 4 + wave, stepping by the grid.
 __global__ __launch_bounds__(256) void k_pos(PosArgs a) {
-    __shared__ float red[4][2 * kMaxP];
+    __shared__ float red[4][3 * kMaxP];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int P = a.pf.n, D = a.D;
     const int d0 = 16 * lane;
@@ -51,9 +54,10 @@ __global__ __launch_bounds__(256) void k_pos(PosArgs a) {
     int pl = P;  // the narrowest prefix that covers this lane's elements (P: none)
     for (int p = P - 1; p >= 0; --p)
         if (d0 < a.pf.w[p]) pl = p;
-    float ls[kMaxP], cs[kMaxP];  // sums of -l^p and cos^p over this wave's cells (wave-uniform)
+    // sums over this wave's cells (wave-uniform): softplus(-l^p), sigma(-l^p) cos^p, sigma(-l^p)
+    float ls[kMaxP], cs[kMaxP], gs[kMaxP];
 #pragma unroll
-    for (int p = 0; p < kMaxP; ++p) ls[p] = cs[p] = 0.f;
+    for (int p = 0; p < kMaxP; ++p) ls[p] = cs[p] = gs[p] = 0.f;
 
     for (int64_t o = (int64_t)blockIdx.x * 4 + wave; o < a.NO; o += (int64_t)gridDim.x * 4) {
         const int e0 = a.ptr[o], e1 = a.ptr[o + 1];
@@ -79,16 +83,21 @@ __global__ __launch_bounds__(256) void k_pos(PosArgs a) {
             float part = 0.f;
 #pragma unroll
             for (int c = 0; c < 16; ++c) part = fmaf(xv[c], yv[c], part);
-            float yc = 0.f;  // sum over covering prefixes of c_p |x^p|^-1 |y^p|^-1
+            float yc = 0.f;  // sum over covering prefixes of c_p sigma(-l^p) |x^p|^-1 |y^p|^-1
             for (int p = 0; p < P; ++p) {
                 const float dot = wsum(d0 < a.pf.w[p] ? part : 0.f);
                 const float iy = a.invy[p * a.NI + i];
                 const float cosv = dot * ix[p] * iy;
-                ls[p] -= fmaf(a.t, cosv, a.b);
-                cs[p] += cosv;
+                const float l = fmaf(a.t, cosv, a.b);
+                // sigma(-l) = 1 / (1 + e^l) (e^l = inf gives 0); softplus(-l) = max(-l, 0) + log1p(e^-|l|)
+                const float sn = 1.0f / (1.0f + expf(l));
+                ls[p] += fmaxf(-l, 0.f) + log1pf(expf(-fabsf(l)));
+                cs[p] = fmaf(sn, cosv, cs[p]);
+                gs[p] += sn;
                 if (p >= pl) {
-                    yc = fmaf(a.gc[p], ix[p] * iy, yc);
-                    xc = fmaf(a.gc[p], cosv * ix[p] * ix[p], xc);
+                    const float c = a.gc[p] * sn;
+                    yc = fmaf(c, ix[p] * iy, yc);
+                    xc = fmaf(c, cosv * ix[p] * ix[p], xc);
                 }
             }
 #pragma unroll
@@ -112,25 +121,27 @@ __global__ __launch_bounds__(256) void k_pos(PosArgs a) {
         for (int p = 0; p < P; ++p) {
             red[wave][p] = ls[p];
             red[wave][kMaxP + p] = cs[p];
+            red[wave][2 * kMaxP + p] = gs[p];
         }
     __syncthreads();
     const int t = threadIdx.x;
-    if (t < 2 * P) {
-        const int slot = t < P ? t : kMaxP + (t - P);
+    if (t < 3 * P) {
+        const int slot = (t / P) * kMaxP + t % P;
         const float v = (red[0][slot] + red[1][slot]) + (red[2][slot] + red[3][slot]);
-        a.parts[(int64_t)blockIdx.x * 2 * P + t] = v;  // [block][0: -l | 1: cos][p]
+        a.parts[(int64_t)blockIdx.x * 3 * P + t] = v;  // [block][0: softplus(-l) | 1: sigma(-l) cos | 2: sigma(-l)][p]
     }
 }
 
 // One workgroup: fixed-order sums of the blocks' partials, folded into the outputs of the
-// dense passes (loss, L^p, dL/dscale, dL/dbias).
+// dense passes (loss, L^p, dL/dscale, dL/dbias).  Per listed cell and prefix the loss gains
+// softplus(-l^p) / den and the residual is -sigma(-l^p) / den, which dL/ds takes times cos^p.
 __global__ __launch_bounds__(256) void k_pos_fold(PosFoldArgs a) {
     __shared__ double red[256];
-    __shared__ double sums[2 * kMaxP];
+    __shared__ double sums[3 * kMaxP];
     const int P = a.pf.n;
-    for (int t = 0; t < 2 * P; ++t) {
+    for (int t = 0; t < 3 * P; ++t) {
         double v = 0.0;
-        for (int64_t b = threadIdx.x; b < a.nblk; b += 256) v += (double)a.parts[b * 2 * P + t];
+        for (int64_t b = threadIdx.x; b < a.nblk; b += 256) v += (double)a.parts[b * 3 * P + t];
         red[threadIdx.x] = v;
         __syncthreads();
         for (int h = 128; h >= 1; h >>= 1) {
@@ -141,16 +152,17 @@ __global__ __launch_bounds__(256) void k_pos_fold(PosFoldArgs a) {
         __syncthreads();
     }
     if (threadIdx.x != 0) return;
-    double dloss = 0.0, dscale = 0.0;
+    double dloss = 0.0, dscale = 0.0, dbias = 0.0;
     for (int p = 0; p < P; ++p) {
         const double dl = sums[p] * a.norm;  // change of L^p
         if (a.prefix_losses_out) a.prefix_losses_out[p] = (float)((double)a.prefix_losses_out[p] + dl);
         dloss += (double)a.wnorm[p] * dl;
         dscale -= (double)a.wnorm[p] * sums[P + p] * a.norm;
+        dbias -= (double)a.wnorm[p] * sums[2 * P + p] * a.norm;
     }
     *a.loss_out = (float)((double)*a.loss_out + dloss);
     if (a.dscale_out) *a.dscale_out = (float)((double)*a.dscale_out + dscale);
-    if (a.dbias_out) *a.dbias_out = (float)((double)*a.dbias_out - (double)a.npos * a.norm);
+    if (a.dbias_out) *a.dbias_out = (float)((double)*a.dbias_out + dbias);
 }
 
 }  // namespace

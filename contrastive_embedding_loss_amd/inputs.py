@@ -22,6 +22,7 @@ INFONCE = 0
 SIGLIP = 1
 INFONCE_ROWS = 2
 ONESET_SIGLIP = 3
+ONESET_SIGLIP_EDGES = 4
 
 DEFAULT_PREFIXES = (64, 128, 256, 512, 1024)
 
@@ -173,7 +174,8 @@ def random_positive_lists(R: int, N: int, row_offset: int, mean: float, seed: in
     one-set form its partner (row_offset + i) xor 1 and the row itself) is
     listed with probability mean / N; row ``dense_row`` (if given) lists every
     allowed column.  The one-set form draws over the whole set and keeps
-    (i, j) and (j, i) together, then returns the rows of the share.
+    (i, j) and (j, i) together (a dense row is listed by every other row as
+    well), then returns the rows of the share.
     """
     rng = np.random.default_rng(seed)
     Rs, off = (N, 0) if oneset else (R, row_offset)
@@ -181,19 +183,17 @@ def random_positive_lists(R: int, N: int, row_offset: int, mean: float, seed: in
     if oneset:
         pick = np.triu(pick, 1)
         pick = pick | pick.T
+    if dense_row is not None:
+        d = row_offset + dense_row if oneset else dense_row
+        pick[d] = True
+        if oneset:
+            pick[:, d] = True
     g = np.arange(Rs) + off
     own = g ^ 1 if oneset else g
     pick[np.arange(Rs), own] = False
     if oneset:
         pick[np.arange(Rs), g] = False
-    if oneset:
         pick = pick[row_offset:row_offset + R]
-        g, own = g[row_offset:row_offset + R], own[row_offset:row_offset + R]
-    if dense_row is not None:
-        pick[dense_row] = True
-        pick[dense_row, own[dense_row]] = False
-        if oneset:
-            pick[dense_row, g[dense_row]] = False
     counts = pick.sum(axis=1)
     row_ptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     return row_ptr, np.nonzero(pick)[1].astype(np.int32)
@@ -212,3 +212,28 @@ def workload_positives(w: Workload):
         return None
     row_ptr, col, _ = band_lists(w.R, w.extra["extra_pos"], w.extra["hard_neg"])
     return row_ptr, col
+
+
+def random_edge_lists(N: int, mean: float, seed: int, far: int = 0, lonely: int = 0):
+    """Seeded symmetric relation lists (CSR over all N rows of one set) for the one-set form with
+    listed relations ("UForm for Swift", section "Training": Edges(offsets, ids)).
+
+    Each unordered pair {i, j}, i != j, is an edge with probability mean / N; ``far`` extra edges
+    join rows far apart (i, i + N // 2); the first ``lonely`` rows have no edge at all.  Returns
+    (row_ptr int64 [N + 1], col int32): row g's partners, ascending.
+    """
+    rng = np.random.default_rng(seed)
+    pick = np.triu(rng.random((N, N)) < mean / N, 1)
+    for i in range(far):
+        pick[i, i + N // 2] = True
+    pick = pick | pick.T
+    pick[:lonely, :] = False
+    pick[:, :lonely] = False
+    counts = pick.sum(axis=1)
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int64), np.nonzero(pick)[1].astype(np.int32)
+
+
+def share_lists(lists, off: int, R: int):
+    """The CSR lists of rows off .. off + R - 1 of a whole set's lists."""
+    rp, col = lists
+    return (rp[off:off + R + 1] - rp[off]).astype(np.int64), col[rp[off]:rp[off + R]]

@@ -62,6 +62,7 @@ typedef enum {
     uform_contrastive_siglip_k = 1,       /* pairwise sigmoid, z = +1 at (i, off + i) */
     uform_contrastive_infonce_rows_k = 2, /* row CE of the R local rows + column PLSE */
     uform_contrastive_oneset_siglip_k = 3, /* one set scored against itself, sigmoid form (below) */
+    uform_contrastive_oneset_siglip_edges_k = 4, /* the same with every positive listed as a relation (below) */
 } uform_contrastive_kind_t;
 
 /* The one-set sigmoid form ("Scaling-Up Contrastive Learning over NVLink
@@ -74,7 +75,20 @@ typedef enum {
  * of softplus(-z_gj l_gj), z = +1 at j = g xor 1; a cell of a row with
  * itself is not scored.  dq is the gradient of the whole set's loss with
  * respect to the share's rows (both mirrored cells); dk must be NULL.  One
- * backward pass, over the share's rows. */
+ * backward pass, over the share's rows.
+ *
+ * The one-set form with listed relations (uform_contrastive_oneset_siglip_edges_k;
+ * "UForm for Swift", section "Training": a training step takes relations
+ * Relations(attract: Edges(offsets, ids)), CSR edge lists naming the items each
+ * item attracts): the same loss, share and gradient, but no cell is an
+ * implicit positive.  The options' pos_row_ptr / pos_col list the share's
+ * rows' relations (set indices, any rows of the set other than the row
+ * itself; a row may list none or several), and exactly the listed cells take
+ * z = +1.  N may be odd.  Mirrored cells carry one label, so the whole set's
+ * lists must be symmetric: a pair of two rows of the share listed one way only
+ * is invalid-argument (a partner outside the share cannot be checked).  No
+ * lists: every cell is a negative.  pos_logit_out must be NULL (a row has no
+ * single positive). */
 
 typedef enum {
     uform_status_success_k = 0,
@@ -102,7 +116,7 @@ typedef enum {
  *              1 <= n_prefixes <= 8.
  *  scale, bias finite; softmax kinds need |scale| <= 40 (else unsupported).
  *  kind        a uform_contrastive_kind_t; INFONCE needs R == N; the one-set
- *              form needs q inside k and dk = NULL (see above).
+ *              forms need q inside k and dk = NULL (see above).
  *  loss_out    device, 1 float: the weighted loss (written asynchronously).
  *  dq, dk      device FP32 [R][D] and [N][D], 16-byte aligned, overwritten;
  *              NULL skips that gradient.

@@ -10,6 +10,7 @@ in the seeded input generator, which holds none of the method's arithmetic.
 from .contrastive import (  # noqa: F401
     INFONCE,
     INFONCE_ROWS,
+    ONESET_EDGES,
     ONESET_SIGLIP,
     SIGLIP,
     KIND_NAMES,

@@ -44,7 +44,9 @@ INFONCE = 0
 SIGLIP = 1
 INFONCE_ROWS = 2
 ONESET_SIGLIP = 3
-KIND_NAMES = {INFONCE: "infonce", SIGLIP: "siglip", INFONCE_ROWS: "infonce_rows", ONESET_SIGLIP: "oneset_siglip"}
+ONESET_EDGES = 4
+KIND_NAMES = {INFONCE: "infonce", SIGLIP: "siglip", INFONCE_ROWS: "infonce_rows", ONESET_SIGLIP: "oneset_siglip",
+              ONESET_EDGES: "oneset_siglip_edges"}
 
 
 # --------------------------------------------------------------------------
@@ -85,11 +87,14 @@ def sigmoid(x: np.ndarray) -> np.ndarray:
 # the loss
 # --------------------------------------------------------------------------
 
-def _positive_mask(rows: np.ndarray, cols: np.ndarray, row_offset: int, oneset: bool = False) -> np.ndarray:
-    """E[a, b] = 1 where column cols[b] is the positive of row rows[a]: key row_offset + row for
-    the two-set kinds; for the one-set form, the other row of the row's pair, (row_offset + row) xor 1."""
+def _positive_mask(rows: np.ndarray, cols: np.ndarray, row_offset: int, kind: int) -> np.ndarray:
+    """E[a, b] = 1 where column cols[b] is the implicit positive of row rows[a]: key row_offset + row
+    for the two-set kinds; for the one-set form, the other row of the row's pair,
+    (row_offset + row) xor 1; none for the one-set form whose positives are all listed."""
     g = rows[:, None] + row_offset
-    return (cols[None, :] == (g ^ 1 if oneset else g)).astype(np.float64)
+    if kind == ONESET_EDGES:
+        return np.zeros((len(rows), len(cols)))
+    return (cols[None, :] == (g ^ 1 if kind == ONESET_SIGLIP else g)).astype(np.float64)
 
 
 def _listed_mask(rows: np.ndarray, cols: np.ndarray, positives) -> np.ndarray:
@@ -107,22 +112,30 @@ def _listed_mask(rows: np.ndarray, cols: np.ndarray, positives) -> np.ndarray:
     return E
 
 
-def check_positives(positives, R: int, N: int, row_offset: int, oneset: bool):
-    """Validate an extra-positive list and return it as (row_ptr int64 [R + 1], col int64 [nnz]).
+def check_positives(positives, R: int, N: int, row_offset: int, kind: int):
+    """Validate a positive list and return it as (row_ptr int64 [R + 1], col int64 [nnz]).
 
-    Row i's extra positives are col[row_ptr[i]:row_ptr[i + 1]]: strictly increasing key (set)
-    indices in [0, N), none of them the row's own positive (row_offset + i, or its pair partner
-    (row_offset + i) xor 1 in the one-set form) and, in the one-set form, not the row itself."""
+    Row i's listed positives are col[row_ptr[i]:row_ptr[i + 1]]: strictly increasing key (set)
+    indices in [0, N), none of them the row's implicit positive (row_offset + i, or its pair partner
+    (row_offset + i) xor 1 in the one-set form) and, in both one-set forms, not the row itself.  In
+    the one-set forms mirrored cells carry one label, so a listed pair of two rows of the share
+    must be listed both ways."""
     row_ptr = np.asarray(positives[0], dtype=np.int64)
     col = np.asarray(positives[1], dtype=np.int64)
     if row_ptr.shape != (R + 1,) or row_ptr[0] != 0 or np.any(np.diff(row_ptr) < 0) or row_ptr[-1] != len(col):
         raise ValueError("row_ptr must have R + 1 non-decreasing entries from 0 to len(col)")
+    oneset = kind in (ONESET_SIGLIP, ONESET_EDGES)
     for i in range(R):
         c = col[row_ptr[i]:row_ptr[i + 1]]
         g = row_offset + i
-        own = g ^ 1 if oneset else g
+        own = {SIGLIP: g, ONESET_SIGLIP: g ^ 1}.get(kind, -1)
         if np.any(c < 0) or np.any(c >= N) or np.any(np.diff(c) <= 0) or np.any(c == own) or (oneset and np.any(c == g)):
-            raise ValueError(f"row {i}: extra positives must be increasing, in [0, N), and not the row's own pair")
+            raise ValueError(f"row {i}: listed positives must be increasing, in [0, N), and not the row's own pair")
+    if oneset:
+        listed = set(zip(np.repeat(np.arange(R) + row_offset, np.diff(row_ptr)).tolist(), col.tolist()))
+        for g, j in listed:
+            if row_offset <= j < row_offset + R and (j, g) not in listed:
+                raise ValueError(f"rows {g} and {j} of the share: a one-set pair must be listed both ways")
     return row_ptr, col
 
 
@@ -154,6 +167,12 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
     (1/N) sum over local rows i and every j other than i itself of
     softplus(-z_ij l_ij), and ``dq`` is the gradient of the whole set's loss
     with respect to those rows (both mirrored cells), with no ``dk``.
+    ONESET_EDGES is the same one-set form with no implicit pairs: every
+    positive of the set is listed in ``positives`` (the relation edges of
+    "UForm for Swift", section "Training": an item attracts the items its
+    edge list names), a row may list none, several, or any other row of the
+    set, N may be odd, and there is no ``pos_logit``.  Mirrored cells carry one
+    label, so the whole set's lists are symmetric (checked within the share).
 
     ``positives`` (sigmoid kinds only) = (row_ptr, col) lists extra positive
     pairs in CSR form: each entry of the batch may carry several positives
@@ -187,13 +206,15 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
         raise ValueError("need 1 <= R <= N and row_offset + R <= N")
     if kind == INFONCE and (R != N or row_offset != 0):
         raise ValueError("symmetric InfoNCE needs R == N and row_offset == 0")
-    oneset = kind == ONESET_SIGLIP
-    if oneset and (N % 2 != 0 or not np.array_equal(q, k[row_offset:row_offset + R])):
-        raise ValueError("the one-set form needs an even set k and q = k[row_offset:row_offset + R]")
+    oneset = kind in (ONESET_SIGLIP, ONESET_EDGES)
+    if oneset and not np.array_equal(q, k[row_offset:row_offset + R]):
+        raise ValueError("the one-set forms need q = k[row_offset:row_offset + R]")
+    if kind == ONESET_SIGLIP and N % 2 != 0:
+        raise ValueError("the one-set form with pairs needs an even set (rows 2m and 2m + 1 pair up)")
     if positives is not None:
-        if kind not in (SIGLIP, ONESET_SIGLIP):
-            raise ValueError("extra positives are defined for the sigmoid kinds")
-        positives = check_positives(positives, R, N, row_offset, oneset)
+        if kind not in (SIGLIP, ONESET_SIGLIP, ONESET_EDGES):
+            raise ValueError("listed positives are defined for the sigmoid kinds")
+        positives = check_positives(positives, R, N, row_offset, kind)
     w = np.ones(P) if weights is None else np.asarray(weights, dtype=np.float64)
     W = float(np.sum(w))
     s = float(scale)
@@ -229,14 +250,14 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
                 pos = logits[rows - r0, pos_col[r0:r1]]
                 out = {"pos": pos}
                 if oneset:
-                    pos = logits[rows - r0, pos_col[r0:r1] ^ 1]
-                    out["pos"] = pos
-                    z = 2.0 * (_positive_mask(rows, all_cols, row_offset, True)
+                    if kind == ONESET_SIGLIP:
+                        out["pos"] = logits[rows - r0, pos_col[r0:r1] ^ 1]
+                    z = 2.0 * (_positive_mask(rows, all_cols, row_offset, kind)
                                + _listed_mask(rows, all_cols, positives)) - 1.0
                     keep = 1.0 - _self_mask(rows, all_cols, row_offset)
                     out["siglip_rows"] = np.sum(keep * softplus(-z * logits), axis=1)
                 elif kind == SIGLIP:
-                    z = 2.0 * (_positive_mask(rows, all_cols, row_offset)
+                    z = 2.0 * (_positive_mask(rows, all_cols, row_offset, kind)
                                + _listed_mask(rows, all_cols, positives)) - 1.0
                     out["siglip_rows"] = np.sum(softplus(-z * logits), axis=1)
                 else:
@@ -249,7 +270,7 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
             parts = list(pool.map(forward_rows, row_blocks))
             for (r0, r1), part in zip(row_blocks, parts):
                 pos_logit[p, r0:r1] = part["pos"]
-            if kind in (SIGLIP, ONESET_SIGLIP):
+            if kind in (SIGLIP, ONESET_SIGLIP, ONESET_EDGES):
                 siglip_rows = np.concatenate([part["siglip_rows"] for part in parts])
                 prefix_losses[p] = np.sum(siglip_rows) / N
             else:
@@ -276,9 +297,9 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
             # ---- residuals g_ij = dL^p / dl_ij on a slice of the grid
             def residual(logits, rows, cols):
                 if oneset:
-                    E = _positive_mask(rows, cols, row_offset, True) + _listed_mask(rows, cols, positives)
+                    E = _positive_mask(rows, cols, row_offset, kind) + _listed_mask(rows, cols, positives)
                     return (sigmoid(logits) - E) * (1.0 - _self_mask(rows, cols, row_offset)) / N
-                E = _positive_mask(rows, cols, row_offset)
+                E = _positive_mask(rows, cols, row_offset, kind)
                 if kind == SIGLIP:
                     E = E + _listed_mask(rows, cols, positives)
                     return (sigmoid(logits) - E) / N
@@ -323,8 +344,9 @@ def contrastive_fwd_bwd(q, k, prefixes, scale, bias, kind, weights=None, row_off
     result = {
         "loss": float(np.sum(w * prefix_losses) / W),
         "prefix_losses": prefix_losses,
-        "pos_logit": pos_logit,
     }
+    if kind != ONESET_EDGES:  # every other kind has one implicit positive per row
+        result["pos_logit"] = pos_logit
     if kind in (INFONCE, INFONCE_ROWS):
         result["row_lse"] = row_lse
         result["col_lse"] = col_lse

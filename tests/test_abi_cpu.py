@@ -86,7 +86,7 @@ def _call(q=0x10000, k=0x20000, R=256, N=256, D=1024, prefixes=PREFIXES, scale=1
 
 INVALID = [
     dict(q=0), dict(k=0), dict(loss=0), dict(q=0x10008), dict(dq=0x40004), dict(loss=0x30002),
-    dict(R=0), dict(N=0), dict(D=0), dict(R=300, N=256, kind=2), dict(kind=3), dict(kind=-1),
+    dict(R=0), dict(N=0), dict(D=0), dict(R=300, N=256, kind=2), dict(kind=3), dict(kind=-1), dict(kind=5),
     dict(R=128, N=256, kind=0), dict(prefixes=None), dict(prefixes=[64, 64, 1024]),
     dict(prefixes=[64, 48, 1024]), dict(prefixes=[100, 1024]), dict(prefixes=[64, 2048]),
     dict(prefixes=PREFIXES, n_prefixes=0), dict(prefixes=[32 * (i + 1) for i in range(9)]),
@@ -184,6 +184,9 @@ def test_other_ladders_need_the_forward_only(prefixes):
     (2, 2, 8, 0, [0, 1, 1], [3]),
     (3, 2, 8, 0, [0, 1, 1], [1]),           # one-set: row 0's pair partner
     (3, 2, 8, 0, [0, 0, 1], [1]),           # one-set: row 1 itself
+    (4, 3, 7, 0, [0, 1, 1, 1], [1]),        # one-set relations: row 0 lists row 1, row 1 not row 0
+    (4, 2, 7, 2, [0, 0, 1], [3]),           # one-set relations: row 3 (share row 1) lists itself
+    (4, 2, 7, 0, [0, 1, 1], [7]),           # one-set relations: past N
 ])
 def test_positive_list_checks(kind, R, N, off, row_ptr, col):
     rp = np.asarray(row_ptr, dtype=np.int64)
@@ -193,11 +196,11 @@ def test_positive_list_checks(kind, R, N, off, row_ptr, col):
     opt.pos_row_ptr = rp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
     opt.pos_col = pc.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     k = 0x20000
-    q = k + 2 * off * 1024 if kind == 3 else 0x10000
-    dk = 0 if kind == 3 else 0x50000
+    q = k + 2 * off * 1024 if kind in (3, 4) else 0x10000
+    dk = 0 if kind in (3, 4) else 0x50000
     assert _call(q=q, k=k, R=R, N=N, kind=kind, dk=dk, opt=opt) == 1, binding.last_error()
     msg = binding.last_error()
-    assert ("sigmoid" in msg) if kind in (0, 2) else ("pos_row_ptr" in msg or "row " in msg), msg
+    assert ("sigmoid" in msg) if kind in (0, 2) else ("pos_row_ptr" in msg or "row" in msg), msg
 
 
 def test_positive_list_needs_col_array():
@@ -241,3 +244,17 @@ def test_package_exports():
         assert getattr(pkg, name) is getattr(binding, name), name
     with pytest.raises(AttributeError):
         pkg.fwd_bwd_ex
+
+
+def test_oneset_relations_call_checks():
+    # the one-set form with listed relations: q inside k, no dk, no positive logit; an odd set and
+    # no lists at all are valid (checked with supported(), which touches no device)
+    k = 0x20000
+    assert _call(q=k, k=k, R=7, N=7, kind=4, dk=0x50000) == 1 and "dk" in binding.last_error()
+    assert _call(q=0x10000, k=k, R=7, N=7, kind=4, dk=0) == 1
+    opt = binding.Options()
+    opt.pos_logit_out = 0x70000
+    assert _call(q=k, k=k, R=7, N=7, kind=4, dk=0, opt=opt) == 1 and "positive logit" in binding.last_error()
+    assert binding.supported(1024, PREFIXES, 4) == 0
+    assert binding.workspace_bytes(7, 7, 1024, 5, 4) == binding.workspace_bytes(7, 7, 1024, 5, 3)
+    assert binding.workspace_bytes(7, 7, 1024, 5, 4, 10) > binding.workspace_bytes(7, 7, 1024, 5, 4)

@@ -145,9 +145,12 @@ def test_matches_torch_library_loss_and_autograd(rng, kind, R, N, off, prefixes,
     np.testing.assert_allclose(out["dk"], kt.grad.numpy(), rtol=1e-9, atol=1e-13)
     assert out["dscale"] == pytest.approx(st.grad.item(), rel=1e-9, abs=1e-14)
     assert out["dbias"] == pytest.approx(bt.grad.item(), rel=1e-9, abs=1e-14)
-    if kind == INFONCE_ROWS:
-        for p, width in enumerate(prefixes):
-            logits = s * F.normalize(qt[:, :width], dim=1) @ F.normalize(kt[:, :width], dim=1).T + b
+    for p, width in enumerate(prefixes):
+        logits = s * F.normalize(qt[:, :width], dim=1) @ F.normalize(kt[:, :width], dim=1).T + b
+        # the positive cell's logit of every kind, read off torch's grid at (i, off + i)
+        np.testing.assert_allclose(out["pos_logit"][p], logits[torch.arange(R), torch.arange(R) + off].detach().numpy(),
+                                   rtol=1e-12, atol=1e-14)
+        if kind == INFONCE_ROWS:
             np.testing.assert_allclose(out["col_lse"][p], torch.logsumexp(logits, 0).detach().numpy(),
                                        rtol=1e-12)
             np.testing.assert_allclose(out["row_lse"][p], torch.logsumexp(logits, 1).detach().numpy(),
@@ -338,6 +341,12 @@ def test_oneset_matches_torch_autograd_of_the_whole_set():
     assert out["dscale"] == pytest.approx(st.grad.item(), rel=1e-9)
     assert out["dbias"] == pytest.approx(bt.grad.item(), rel=1e-9)
     assert out["dk"] is None
+    # each row's positive logit is its cell with the pair partner g xor 1
+    for p, width in enumerate(prefixes):
+        xh = F.normalize(xt[:, :width], dim=1)
+        logits = (s * xh @ xh.T + b).detach()
+        np.testing.assert_allclose(out["pos_logit"][p], logits[torch.arange(N), torch.arange(N) ^ 1].numpy(),
+                                   rtol=1e-12, atol=1e-14)
 
 
 def test_oneset_central_differences_of_the_set():
@@ -472,3 +481,112 @@ def test_extra_positive_lists_are_checked(rng, kind, row_ptr, col, off):
     with pytest.raises(ValueError):
         contrastive_fwd_bwd(q, x, [32], 4.0, -1.0, kind, row_offset=off, grads=False,
                             positives=(np.array(row_ptr), np.array(col)))
+
+
+# ----------------------------------------------------------------------------- one set, listed relations only
+
+def _edges_csr(N, edges, rows):
+    """CSR lists of the given rows from undirected edges (both directions listed)."""
+    nb = {g: set() for g in range(N)}
+    for a, b in edges:
+        nb[a].add(b)
+        nb[b].add(a)
+    cols = [sorted(nb[g]) for g in rows]
+    rp = np.concatenate([[0], np.cumsum([len(c) for c in cols])]).astype(np.int64)
+    return rp, np.array([j for c in cols for j in c], dtype=np.int64)
+
+
+EDGES_9 = [(0, 5), (1, 2), (1, 7), (3, 4), (6, 8), (2, 7)]  # odd N; row 0's partner far away; several per row
+
+
+def test_oneset_edges_match_torch_autograd_of_the_whole_set():
+    from oracle import ONESET_EDGES
+    rng = np.random.default_rng(7)
+    N, D, prefixes, weights, s, b = 9, 48, [16, 48], [2, 1], 6.0, -2.5
+    x = rng.standard_normal((N, D))
+    for a, c in EDGES_9:
+        x[c] = x[a] + 0.5 * rng.standard_normal(D)
+    pos = _edges_csr(N, EDGES_9, range(N))
+    out = contrastive_fwd_bwd(x, x, prefixes, s, b, ONESET_EDGES, weights=weights, positives=pos)
+    xt = torch.tensor(x, requires_grad=True)
+    st = torch.tensor(s, dtype=torch.float64, requires_grad=True)
+    bt = torch.tensor(b, dtype=torch.float64, requires_grad=True)
+    z = -torch.ones(N, N, dtype=torch.float64)
+    for a, c in EDGES_9:
+        z[a, c] = z[c, a] = 1.0
+    keep = 1.0 - torch.eye(N, dtype=torch.float64)
+    total = 0.0
+    for p, width in enumerate(prefixes):
+        xh = F.normalize(xt[:, :width], dim=1)
+        total = total + weights[p] * (-(keep * F.logsigmoid(z * (st * xh @ xh.T + bt))).sum() / N)
+    total = total / sum(weights)
+    total.backward()
+    assert out["loss"] == pytest.approx(total.item(), rel=1e-12)
+    np.testing.assert_allclose(out["dq"], xt.grad.numpy(), rtol=1e-9, atol=1e-13)
+    assert out["dscale"] == pytest.approx(st.grad.item(), rel=1e-9)
+    assert out["dbias"] == pytest.approx(bt.grad.item(), rel=1e-9)
+    assert out["dk"] is None and "pos_logit" not in out
+
+
+def test_oneset_edges_of_the_pairs_equal_the_pairs_form():
+    # listing exactly the pairs (2m, 2m + 1) as relations gives the pairs form, rows and shares alike
+    from oracle import ONESET_EDGES
+    rng = np.random.default_rng(8)
+    N, D, R, off = 12, 64, 5, 3
+    x = rng.standard_normal((N, D))
+    x[1::2] = x[0::2] + 0.4 * rng.standard_normal((N // 2, D))
+    pos = _edges_csr(N, [(2 * m, 2 * m + 1) for m in range(N // 2)], range(off, off + R))
+    a = contrastive_fwd_bwd(x[off:off + R], x, [32, 64], 7.0, -3.0, ONESET_SIGLIP, row_offset=off)
+    e = contrastive_fwd_bwd(x[off:off + R], x, [32, 64], 7.0, -3.0, ONESET_EDGES, row_offset=off, positives=pos)
+    assert e["loss"] == pytest.approx(a["loss"], rel=1e-13)
+    np.testing.assert_allclose(e["dq"], a["dq"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(e["prefix_losses"], a["prefix_losses"], rtol=1e-13)
+    assert e["dscale"] == pytest.approx(a["dscale"], rel=1e-12)
+    assert e["dbias"] == pytest.approx(a["dbias"], rel=1e-12)
+
+
+def test_oneset_edges_identical_rows_closed_form():
+    # every cosine is 1: row g has m_g positives and N - 1 - m_g negatives, each with l = s + b
+    from oracle import ONESET_EDGES
+    N, D, s, b = 9, 64, 5.0, -1.0
+    x = np.tile(np.linspace(-1.0, 2.0, D), (N, 1))
+    pos = _edges_csr(N, EDGES_9, range(N))
+    m = np.diff(pos[0])
+    out = contrastive_fwd_bwd(x, x, [32, 64], s, b, ONESET_EDGES, positives=pos)
+    want = float(np.sum(m * _softplus(-(s + b)) + (N - 1 - m) * _softplus(s + b))) / N
+    assert out["loss"] == pytest.approx(want, rel=1e-12)
+    np.testing.assert_allclose(out["dq"], 0.0, atol=1e-12)
+    # no relations at all: every cell is a negative
+    none = (np.zeros(N + 1, dtype=np.int64), np.zeros(0, dtype=np.int64))
+    out0 = contrastive_fwd_bwd(x, x, [32, 64], s, b, ONESET_EDGES, positives=none)
+    assert out0["loss"] == pytest.approx((N - 1) * _softplus(s + b), rel=1e-12)
+
+
+def test_oneset_edges_shares_rebuild_the_set():
+    from oracle import ONESET_EDGES
+    rng = np.random.default_rng(9)
+    N, D = 9, 64
+    x = rng.standard_normal((N, D))
+    whole = contrastive_fwd_bwd(x, x, [32, 64], 6.0, -2.0, ONESET_EDGES, positives=_edges_csr(N, EDGES_9, range(N)))
+    loss, dq = 0.0, np.zeros((N, D))
+    for off, R in ((0, 4), (4, 1), (5, 4)):
+        part = contrastive_fwd_bwd(x[off:off + R], x, [32, 64], 6.0, -2.0, ONESET_EDGES, row_offset=off,
+                                   positives=_edges_csr(N, EDGES_9, range(off, off + R)))
+        loss += part["loss"]
+        dq[off:off + R] = part["dq"]
+    assert loss == pytest.approx(whole["loss"], rel=1e-13)
+    np.testing.assert_allclose(dq, whole["dq"], rtol=1e-12, atol=1e-15)
+
+
+def test_oneset_relations_must_be_symmetric_within_the_share():
+    from oracle import ONESET_EDGES
+    x = np.random.default_rng(10).standard_normal((6, 32))
+    one_way = (np.array([0, 1, 1, 1, 1, 1, 1]), np.array([3]))  # row 0 lists 3, row 3 does not list 0
+    with pytest.raises(ValueError):
+        contrastive_fwd_bwd(x, x, [32], 5.0, -1.0, ONESET_EDGES, positives=one_way)
+    self_edge = (np.array([0, 0, 1, 1, 1, 1, 1]), np.array([1]))  # row 1 lists itself
+    with pytest.raises(ValueError):
+        contrastive_fwd_bwd(x, x, [32], 5.0, -1.0, ONESET_EDGES, positives=self_edge)
+    # a partner outside the share cannot be checked from the share's lists, and is accepted
+    part = (np.array([0, 1]), np.array([5]))
+    contrastive_fwd_bwd(x[2:3], x, [32], 5.0, -1.0, ONESET_EDGES, row_offset=2, positives=part)

@@ -431,3 +431,166 @@ def test_positive_lists_other_ladders_and_finish(D, prefixes, one_split):
         assert (dq[:, prefixes[-1]:] == 0).all() and (dk[:, prefixes[-1]:] == 0).all()
     assert ex["dscale"].item() == pytest.approx(ref["dscale"], rel=1e-3, abs=1e-6)
     assert ex["dbias"].item() == pytest.approx(ref["dbias"], rel=1e-3, abs=1e-6)
+
+
+# ----------------------------------------------------------------------------- scale and bias regimes
+
+def _spread_inputs(R, N, D, seed, off=0):
+    """Rows near eight directions +-c_0 .. +-c_3, so cosines spread over [-1, 1]: with |s| = 40 the
+    logits span the whole range the fixed log-sum-exp shift must cover."""
+    rng = np.random.default_rng(seed)
+    C = rng.standard_normal((4, D))
+    dirs = np.concatenate([C, -C])
+    a = rng.integers(0, 8, size=N)
+    k = dirs[a] + 0.3 * rng.standard_normal((N, D))
+    q = k[off:off + R] + 0.2 * rng.standard_normal((R, D))
+    from contrastive_embedding_loss_amd.inputs import f32_to_bf16_bits
+    return f32_to_bf16_bits(q.astype(np.float32)), f32_to_bf16_bits(k.astype(np.float32))
+
+
+@pytest.mark.parametrize("case,kind,s,b", [
+    ("infonce-neg-scale", INFONCE, -14.0, 0.0),
+    ("siglip-neg-scale", SIGLIP, -10.0, -3.0),
+    ("infonce-scale-40", INFONCE, 40.0, 0.0),
+    ("infonce-scale-minus-40", INFONCE, -40.0, 0.0),
+    ("rows-scale-40", INFONCE_ROWS, 40.0, 0.0),
+    ("infonce-bias", INFONCE, 14.0, 0.5),
+    ("rows-bias", INFONCE_ROWS, 14.0, -1.5),
+    ("siglip-t30-b2", SIGLIP, 30.0, 2.0),
+    ("siglip-t30-b-25", SIGLIP, 30.0, -25.0),
+])
+def test_scale_and_bias_regimes(case, kind, s, b):
+    # every (scale, bias) the checks accept runs the same kernels: negative scales (the sign folded
+    # into the tables), the softmax scale limit |s| = 40 with cosines over [-1, 1], a softmax bias
+    # (it shifts the log-sum-exps and positive logits), and strongly positive or negative sigmoid biases
+    R, N, off = (160, 160, 0) if kind != INFONCE_ROWS else (96, 288, 64)
+    if "40" in case:
+        qb, kb = _spread_inputs(R, N, 1024, seed=191 + len(case), off=off)
+    else:
+        qb, kb = make_inputs(R, N, 1024, noise=0.5, seed=191 + len(case), row_offset=off)
+    got, ref = run_both(qb, kb, LADDER, s, b, kind, weights=(1, 1, 1, 1, 2), off=off, label=case)
+    check(got, ref, kind)
+    if "dscale" in got:
+        assert got["dscale"].item() == pytest.approx(ref["dscale"], rel=1e-3, abs=1e-6)
+        if kind == SIGLIP:
+            assert got["dbias"].item() == pytest.approx(ref["dbias"], rel=1e-3, abs=1e-6)
+
+
+# Listed positives the model already scores with confidence (sigma(l) close to 1): their residual
+# sigma(l) - 1 is small, and the dense passes leave them out so that it is formed in FP32.  With
+# t = 30 and b = -22 a near-duplicate positive has l ~ 8 (residual ~ 3.5e-4) while every negative
+# is negligible, so the listed cells carry most of the gradient.
+@pytest.mark.parametrize("t,b,kind", [(20.0, 0.0, SIGLIP), (30.0, -22.0, SIGLIP), (30.0, -22.0, "oneset")])
+def test_confident_listed_positives(t, b, kind):
+    from contrastive_embedding_loss_amd.inputs import ONESET_SIGLIP, make_band_inputs, random_positive_lists
+    if kind == "oneset":
+        # pairs of near-duplicates, and every listed cell a near-duplicate too: rows 4m .. 4m + 3 copy one draw
+        N, R, off = 256, 128, 64
+        rng = np.random.default_rng(201)
+        base = rng.standard_normal((N // 4, 1024))
+        x = np.repeat(base, 4, axis=0) + 0.05 * rng.standard_normal((N, 1024))
+        from contrastive_embedding_loss_amd.inputs import f32_to_bf16_bits
+        kb = f32_to_bf16_bits(x.astype(np.float32))
+        qb = kb[off:off + R]
+        g = np.arange(off, off + R)
+        cols = [np.array(sorted(set(range(4 * (r // 4), 4 * (r // 4) + 4)) - {r, r ^ 1}), dtype=np.int32)
+                for r in g]
+        rp = np.concatenate([[0], np.cumsum([len(c) for c in cols])]).astype(np.int64)
+        pos = (rp, np.concatenate(cols))
+        _pos_case(qb, kb, LADDER, t, b, ONESET_SIGLIP, off, pos, label=f"confident-oneset t={t} b={b}")
+    else:
+        qb, kb, rp, col = make_band_inputs(200, 1024, 2, 2, noise=0.05, hard_noise=1.0, seed=202)
+        _pos_case(qb, kb, LADDER, t, b, SIGLIP, 0, (rp, col), label=f"confident t={t} b={b}")
+
+
+# ----------------------------------------------------------------------------- one set, listed relations only
+
+@pytest.mark.parametrize("N,R,off,D,prefixes,one_split,far,lonely", [
+    (256, 256, 0, 1024, LADDER, False, 8, 3), (301, 96, 128, 1024, LADDER, False, 4, 0),
+    (300, 64, 33, 1024, LADDER, True, 0, 40), (193, 80, 7, 192, (64, 128), False, 3, 2),
+    (320, 320, 0, 320, (64, 128, 256), True, 5, 1)])
+def test_oneset_relations(N, R, off, D, prefixes, one_split, far, lonely):
+    # arbitrary symmetric relations: rows with none, several, partners far apart, odd sets
+    from contrastive_embedding_loss_amd.inputs import ONESET_SIGLIP_EDGES, random_edge_lists, share_lists
+    from oracle import ONESET_EDGES
+    qb, kb = make_inputs(R, N, D, recipe="gauss", noise=0.6, seed=211 + N, row_offset=off)
+    kb = kb.copy()
+    lists = random_edge_lists(N, 3.0, seed=212 + N, far=far, lonely=lonely)
+    rp, col = lists
+    # make every listed partner a noisy copy of its row's first partner-free ancestor: related rows look alike
+    x = bf16_bits_to_f32(kb).astype(np.float64)
+    rng = np.random.default_rng(213 + N)
+    for g in range(N):
+        for j in col[rp[g]:rp[g + 1]]:
+            if j > g:
+                x[j] = x[g] + 0.5 * rng.standard_normal(D)
+    from contrastive_embedding_loss_amd.inputs import f32_to_bf16_bits
+    kb = f32_to_bf16_bits(x.astype(np.float32))
+    qb = kb[off:off + R]
+    pos = share_lists(lists, off, R)
+    print(f"[case] oneset-relations N={N} R={R} off={off} D={D} listed={int(pos[0][-1])} one_split={one_split}",
+          flush=True)
+    k = to_dev(kb)
+    loss, dq, dk, ex = binding.fwd_bwd(k[off:off + R], k, prefixes, 10.0, -6.0, ONESET_SIGLIP_EDGES, row_offset=off,
+                                       extras=True, one_split=one_split, positives=pos)
+    torch.cuda.synchronize()
+    assert dk is None and "pos_logit" not in ex
+    ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), prefixes, 10.0, -6.0, ONESET_EDGES,
+                              row_offset=off, positives=pos)
+    assert abs(loss.item() - ref["loss"]) <= 1e-3 * abs(ref["loss"]), (loss.item(), ref["loss"])
+    assert np.abs(dq.cpu().numpy() - ref["dq"]).max() <= 2e-3 * np.abs(ref["dq"]).max()
+    np.testing.assert_allclose(ex["prefix_losses"].cpu().numpy(), ref["prefix_losses"], rtol=1e-3)
+    assert ex["dscale"].item() == pytest.approx(ref["dscale"], rel=1e-3, abs=1e-6)
+    assert ex["dbias"].item() == pytest.approx(ref["dbias"], rel=1e-3, abs=1e-6)
+
+
+def test_oneset_relations_of_the_pairs_match_the_pairs_form_and_no_relations():
+    from contrastive_embedding_loss_amd.inputs import ONESET_SIGLIP, ONESET_SIGLIP_EDGES
+    from oracle import ONESET_EDGES
+    N, R, off = 256, 96, 64
+    qb, kb = make_inputs(R, N, 1024, recipe="pairs", noise=0.6, seed=221, row_offset=off)
+    k = to_dev(kb)
+    g = np.arange(off, off + R)
+    pairs = (np.arange(R + 1, dtype=np.int64), (g ^ 1).astype(np.int32))
+    print("[case] oneset-relations: the pairs as relations; no relations", flush=True)
+    a = binding.fwd_bwd(k[off:off + R], k, LADDER, 10.0, -6.0, ONESET_SIGLIP, row_offset=off, extras=True)
+    e = binding.fwd_bwd(k[off:off + R], k, LADDER, 10.0, -6.0, ONESET_SIGLIP_EDGES, row_offset=off, extras=True,
+                        positives=pairs)
+    torch.cuda.synchronize()
+    assert abs(e[0].item() - a[0].item()) <= 1e-4 * abs(a[0].item())
+    assert (e[1] - a[1]).abs().max().item() <= 1e-3 * a[1].abs().max().item()
+    # no relations: every cell of the share's rows is a negative
+    n = binding.fwd_bwd(k[off:off + R], k, LADDER, 10.0, -6.0, ONESET_SIGLIP_EDGES, row_offset=off, extras=True)
+    torch.cuda.synchronize()
+    ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), LADDER, 10.0, -6.0, ONESET_EDGES,
+                              row_offset=off)
+    assert abs(n[0].item() - ref["loss"]) <= 1e-3 * abs(ref["loss"])
+    assert np.abs(n[1].cpu().numpy() - ref["dq"]).max() <= 2e-3 * np.abs(ref["dq"]).max()
+    assert n[3]["dbias"].item() == pytest.approx(ref["dbias"], rel=1e-3)
+
+
+def test_oneset_relations_confident():
+    # near-duplicate partners far apart in the set at t = 30, b = -22: the listed cells hold the gradient
+    from contrastive_embedding_loss_amd.inputs import ONESET_SIGLIP_EDGES, f32_to_bf16_bits, share_lists
+    from oracle import ONESET_EDGES
+    N, R, off, D = 240, 120, 60, 1024
+    rng = np.random.default_rng(231)
+    base = rng.standard_normal((N // 3, D))
+    x = np.concatenate([base, base, base]) + 0.05 * rng.standard_normal((N, D))  # rows g, g + 80, g + 160 alike
+    kb = f32_to_bf16_bits(x.astype(np.float32))
+    m = N // 3
+    cols = [sorted({(g % m) + t * m for t in range(3)} - {g}) for g in range(N)]
+    lists = (np.concatenate([[0], np.cumsum([len(c) for c in cols])]).astype(np.int64),
+             np.array([j for c in cols for j in c], dtype=np.int32))
+    pos = share_lists(lists, off, R)
+    print("[case] oneset-relations confident t=30 b=-22", flush=True)
+    k = to_dev(kb)
+    loss, dq, _, ex = binding.fwd_bwd(k[off:off + R], k, LADDER, 30.0, -22.0, ONESET_SIGLIP_EDGES, row_offset=off,
+                                      extras=True, positives=pos)
+    torch.cuda.synchronize()
+    ref = contrastive_fwd_bwd(bf16_bits_to_f64(kb[off:off + R]), bf16_bits_to_f64(kb), LADDER, 30.0, -22.0,
+                              ONESET_EDGES, row_offset=off, positives=pos)
+    assert abs(loss.item() - ref["loss"]) <= 1e-3 * abs(ref["loss"])
+    assert np.abs(dq.cpu().numpy() - ref["dq"]).max() <= 2e-3 * np.abs(ref["dq"]).max()
+    assert ex["dscale"].item() == pytest.approx(ref["dscale"], rel=1e-3, abs=1e-7)
+    assert ex["dbias"].item() == pytest.approx(ref["dbias"], rel=1e-3, abs=1e-7)

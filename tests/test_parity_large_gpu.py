@@ -1,7 +1,11 @@
 """GPU parity at the full workload sizes, in the launch configuration the bench times.
 
-``infonce_4096`` is compared with a live oracle run element by element.  The
-four large workloads are compared with the oracle's stored values
+``infonce_4096`` and every large workload are compared with a live oracle run
+on the host, element by element over whole tensors: the loss and every prefix
+loss (rel <= 1e-3), all of dq and dk against 2e-3 x max|grad| of the oracle's
+tensor, dL/dscale and dL/dbias (rel <= 1e-3), and every row/column
+log-sum-exp and positive logit (max-abs <= 1e-3).  The large workloads are
+also compared with the oracle's stored values
 (``tests/golden/<workload>.npz``, written by ``tests/golden/make_golden.py``
 from ``oracle/`` alone): the loss and every prefix loss (rel <= 1e-3), 16
 sampled rows of dq and dk against 2e-3 x max|grad| of the whole oracle
@@ -13,6 +17,7 @@ sum |x||dx|: a dropped radial term breaks it by O(1)).
 """
 
 import os
+import time
 
 import numpy as np
 import pytest
@@ -100,3 +105,39 @@ def test_large_workload_against_stored_oracle(name):
         assert np.abs(ex["row_lse"].cpu().numpy()[:, idx] - g["row_lse"]).max() <= 1e-3
         assert np.abs(ex["col_lse"].cpu().numpy()[:, g["col_idx"]] - g["col_lse"]).max() <= 1e-3
     check_properties(w, q, k, dq, dk)
+
+
+LARGE = ["siglip_16384", "rows_4096x65536", "infonce_32768", "oneset_16384x131072", "siglip_band_16384"]
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_large_workload_whole_tensors_against_live_oracle(name):
+    # the FP64 oracle on the host's cores (tens of seconds at these sizes) on the same BF16 arrays
+    w = WORKLOADS[name]
+    qb, kb, q, k, loss, dq, dk, ex = run_gpu(w)
+    t0 = time.time()
+    ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), w.prefixes, w.scale, w.bias, w.kind,
+                              weights=w.weights, row_offset=w.row_offset, positives=workload_positives(w))
+    print(f"[oracle] {name} in {time.time() - t0:.1f} s", flush=True)
+    rel = abs(loss - ref["loss"]) / abs(ref["loss"])
+    errs = {"loss_rel": rel}
+    assert rel <= 1e-3, (loss, ref["loss"])
+    np.testing.assert_allclose(ex["prefix_losses"].cpu().numpy(), ref["prefix_losses"], rtol=1e-3)
+    for gname, t in (("dq", dq), ("dk", dk)):
+        if t is None:
+            assert ref[gname] is None or w.kind == ONESET_SIGLIP
+            continue
+        got = t.cpu().numpy()
+        scale = np.abs(ref[gname]).max()
+        e = np.abs(got - ref[gname]).max()
+        errs[gname] = e / scale
+        assert e <= 2e-3 * scale, (gname, e, scale)
+        del got
+    assert ex["dscale"].item() == pytest.approx(ref["dscale"], rel=1e-3, abs=1e-6)
+    assert ex["dbias"].item() == pytest.approx(ref["dbias"], rel=1e-3, abs=1e-6)
+    names = ["pos_logit"] + (["row_lse", "col_lse"] if w.kind not in (SIGLIP, ONESET_SIGLIP) else [])
+    for n in names:
+        e = np.abs(ex[n].cpu().numpy() - ref[n]).max()
+        errs[n] = e
+        assert e <= 1e-3, (n, e)
+    print(f"[parity] {name} " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
