@@ -71,6 +71,8 @@ def library() -> ctypes.CDLL:
     lib.uform_contrastive_fwd_bwd.restype = ctypes.c_int
     lib.uform_contrastive_fwd_bwd_ex.argtypes = args + [ctypes.POINTER(Options)]
     lib.uform_contrastive_fwd_bwd_ex.restype = ctypes.c_int
+    lib.uform_contrastive_fwd_bwd_noalloc.argtypes = args + [ctypes.POINTER(Options)]
+    lib.uform_contrastive_fwd_bwd_noalloc.restype = ctypes.c_int
     lib.uform_contrastive_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                       ctypes.c_int32, ctypes.c_int32]
     lib.uform_contrastive_workspace_bytes.restype = ctypes.c_size_t
@@ -152,7 +154,7 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
             row_offset: int = 0, want_dq: bool = True, want_dk: bool = True, extras: bool = False,
             dq: torch.Tensor | None = None, dk: torch.Tensor | None = None, accumulate: bool = False,
             workspace: torch.Tensor | None = None, profile: bool = False, one_split: bool = False,
-            positives=None):
+            positives=None, noalloc: bool = False):
     """Loss and gradients of the Matryoshka contrastive loss on q's device.
 
     q [R, D] and k [N, D] are contiguous bfloat16 device tensors.  Returns
@@ -161,6 +163,8 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
     ``extras`` (and ``dscale``, ``dbias``: dL/dscale and dL/dbias, when a
     gradient is wanted).  Everything is enqueued on torch's current stream.  ``one_split`` runs each backward pass as
     one inner split (a diagnostic: the in-place finish that large problems take).
+    ``noalloc`` calls the allocation-free entry point (the library's fixed per-GPU
+    scratch instead of a workspace; outputs are still allocated here unless given).
     ``positives`` = (row_ptr, col), host integer arrays in CSR form, lists extra
     positive cells of the sigmoid kinds (row i: columns col[row_ptr[i]:row_ptr[i + 1]]).
     """
@@ -240,7 +244,8 @@ def fwd_bwd(q: torch.Tensor, k: torch.Tensor, prefixes, scale: float, bias: floa
         opt.workspace_bytes = workspace.numel() * workspace.element_size()
     opt.flags = (ACCUMULATE if accumulate else 0) | (PROFILE if profile else 0) | (ONE_SPLIT if one_split else 0)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    status = library().uform_contrastive_fwd_bwd_ex(
+    entry = library().uform_contrastive_fwd_bwd_noalloc if noalloc else library().uform_contrastive_fwd_bwd_ex
+    status = entry(
         _ptr(q), _ptr(k), R, N, D, pw, P, float(scale), float(bias), int(kind), _ptr(loss), _ptr(dq), _ptr(dk),
         ctypes.c_void_p(stream), ctypes.byref(opt))
     _check(status)

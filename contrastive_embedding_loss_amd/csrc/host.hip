@@ -432,6 +432,43 @@ struct ProfScope {
     } while (0)
 #define LAUNCH(expr) LAUNCH_NAMED(#expr, expr)
 
+// ---------------------------------------------------------------- allocation-free workspace
+// One fixed device array per GPU for the entry point that allocates nothing: the runtime
+// places a copy on every device the library's code is loaded on, and it stays until the
+// process ends.  Host code never uses the array's name as an address (on the host it names a
+// stand-in, not device memory): its device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+static __device__ __align__(256) unsigned char scratch[UFORM_CONTRASTIVE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::map<int, void *> g_scratch_ptr;  // device -> device address of that device's scratch
+
+uform_status_t scratch_address(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(uform_status_device_error_k, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it == g_scratch_ptr.end()) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return fail(uform_status_device_error_k, "hipGetSymbolAddress of the allocation-free scratch failed");
+        }
+        it = g_scratch_ptr.emplace(dev, ptr).first;
+    }
+    *out = it->second;
+    return uform_status_success_k;
+}
+
+// The workspace plan of a call (as run() lays it out).
+Plan call_plan(int64_t R, int64_t N, int64_t D, const int32_t *prefixes, int32_t P, int32_t kind_in, const float *dq,
+               const float *dk, const uform_contrastive_options_t *opt) {
+    const int32_t kind = (kind_in == kOneset || kind_in == kOnesetEdges) ? kSiglip : kind_in;
+    const int64_t npos = (opt && opt->pos_row_ptr) ? opt->pos_row_ptr[R] : -1;
+    return make_plan(R, N, D, prefixes, P, kind, opt ? opt->row_offset : 0, dq != nullptr, dk != nullptr,
+                     opt && (opt->flags & UFORM_CONTRASTIVE_ONE_SPLIT), npos);
+}
+
 uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t D, const int32_t *prefixes,
                    int32_t P, float scale, float bias, int32_t kind_in, float *loss_out, float *dq, float *dk,
                    hipStream_t s, const uform_contrastive_options_t *opt, const ProfCtx &prof) {
@@ -448,8 +485,7 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     const int64_t off = opt ? opt->row_offset : 0;
     const bool softmax = kind != kSiglip;
     const int64_t npos = (opt && opt->pos_row_ptr) ? opt->pos_row_ptr[R] : -1;
-    Plan pl = make_plan(R, N, D, prefixes, P, kind, off, dq != nullptr, dk != nullptr,
-                        opt && (opt->flags & UFORM_CONTRASTIVE_ONE_SPLIT), npos);
+    Plan pl = call_plan(R, N, D, prefixes, P, kind_in, dq, dk, opt);
 
     void *ws = nullptr;
     if (opt && opt->workspace) {
@@ -783,6 +819,37 @@ uform_status_t uform_contrastive_fwd_bwd_ex(const void *q, const void *k, int64_
     std::unique_lock<std::mutex> lock(g_prof_mu, std::defer_lock);
     if (prof.on) lock.lock();
     return run(q, k, R, N, D, prefixes, n_prefixes, scale, bias, kind, loss_out, dq, dk, stream, options, prof);
+}
+
+uform_status_t uform_contrastive_fwd_bwd_noalloc(const void *q, const void *k, int64_t R, int64_t N, int64_t D,
+                                                 const int32_t *prefixes, int32_t n_prefixes, float scale, float bias,
+                                                 int32_t kind, float *loss_out, float *dq, float *dk,
+                                                 hipStream_t stream, const uform_contrastive_options_t *options) {
+    uform_status_t st = validate(q, k, R, N, D, prefixes, n_prefixes, scale, bias, kind, loss_out, dq, dk, options);
+    if (st != uform_status_success_k) return st;
+    if (options && options->workspace)
+        return fail(uform_status_invalid_argument_k,
+                    "the allocation-free entry point uses its own scratch: pass workspace = NULL "
+                    "(uform_contrastive_fwd_bwd_ex takes a caller workspace)");
+    if (options && options->pos_row_ptr)
+        return fail(uform_status_unsupported_k,
+                    "the allocation-free entry point takes no positive lists (they are staged through pinned memory)");
+    if (options && (options->flags & UFORM_CONTRASTIVE_PROFILE))
+        return fail(uform_status_unsupported_k, "the allocation-free entry point does not profile (events are allocated)");
+    const size_t need = call_plan(R, N, D, prefixes, n_prefixes, kind, dq, dk, options).total;
+    if (need > (size_t)UFORM_CONTRASTIVE_NOALLOC_SCRATCH_BYTES)
+        return fail(uform_status_unsupported_k,
+                    "this call needs " + std::to_string(need) + " bytes of scratch; the allocation-free entry point holds " +
+                        std::to_string((size_t)UFORM_CONTRASTIVE_NOALLOC_SCRATCH_BYTES) +
+                        " (use uform_contrastive_fwd_bwd_ex with a workspace)");
+    void *ptr = nullptr;
+    st = scratch_address(&ptr);
+    if (st != uform_status_success_k) return st;
+    uform_contrastive_options_t opt{};
+    if (options) opt = *options;
+    opt.workspace = ptr;
+    opt.workspace_bytes = (size_t)UFORM_CONTRASTIVE_NOALLOC_SCRATCH_BYTES;
+    return run(q, k, R, N, D, prefixes, n_prefixes, scale, bias, kind, loss_out, dq, dk, stream, &opt, ProfCtx{});
 }
 
 int32_t uform_contrastive_profile(const char **names, float *ms, int32_t cap) {

@@ -203,6 +203,27 @@ uform_status_t uform_contrastive_fwd_bwd_ex(const void *q, const void *k, int64_
                                             float bias, int32_t kind, float *loss_out, float *dq, float *dk,
                                             hipStream_t stream, const uform_contrastive_options_t *options);
 
+/* For callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The same call as
+ * uform_contrastive_fwd_bwd_ex (same arguments, checks, results and stream
+ * order), but its workspace is a fixed device array of
+ * UFORM_CONTRASTIVE_NOALLOC_SCRATCH_BYTES bytes per GPU, held from the first use
+ * of the library on that GPU until the process ends; the call allocates
+ * nothing (no hipMalloc, no pinned or event allocation).  A call whose
+ * workspace would exceed the array (uform_contrastive_workspace_bytes > 128 MiB,
+ * e.g. 8192 x 8192 InfoNCE) returns unsupported; so does a call with positive
+ * lists or UFORM_CONTRASTIVE_PROFILE; options->workspace must be NULL
+ * (invalid-argument otherwise).  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race and give wrong results; order them
+ * on one stream.  The array keeps the last call's contents; each call writes
+ * every part of it that it reads. */
+#define UFORM_CONTRASTIVE_NOALLOC_SCRATCH_BYTES (128u << 20)
+uform_status_t uform_contrastive_fwd_bwd_noalloc(const void *q, const void *k, int64_t R, int64_t N, int64_t D,
+                                                 const int32_t *prefixes, int32_t n_prefixes, float scale,
+                                                 float bias, int32_t kind, float *loss_out, float *dq, float *dk,
+                                                 hipStream_t stream, const uform_contrastive_options_t *options);
+
 /* Device workspace a call of this shape needs, in bytes (gradients included);
  * 0 for arguments the call would reject.  The size of the caller-lent memory
  * of the options' workspace ("UForm for Swift", section "Arenas": the caller

@@ -1,0 +1,61 @@
+"""The allocation-free entry point against the workspace entry point it mirrors.
+
+``uform_contrastive_fwd_bwd_noalloc`` runs the same kernels on the library's
+fixed per-GPU scratch.  Two calls in a row (the second smaller, so the scratch
+holds the first call's contents when it starts) must each match
+``uform_contrastive_fwd_bwd_ex`` on the same inputs: the loss within 1e-3
+relative, dq and dk within 2e-3 x max|grad|, and, since the kernels and the
+launch configuration are the same, bitwise.  A call whose workspace would not
+fit the scratch is refused on the host.
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from contrastive_embedding_loss_amd import binding  # noqa: E402
+from contrastive_embedding_loss_amd.inputs import (  # noqa: E402
+    INFONCE, SIGLIP, bf16_bits_to_f32, make_inputs)
+
+pytestmark = pytest.mark.gpu
+LADDER = (64, 128, 256, 512, 1024)
+
+
+def _dev(bits):
+    return torch.from_numpy(bf16_bits_to_f32(bits)).to("cuda").to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("kind,s,b", [(INFONCE, 14.0, 0.0), (SIGLIP, 10.0, -10.0)])
+def test_noalloc_matches_workspace_entry_point_on_two_calls(kind, s, b):
+    for R in (1024, 300):  # the second call is smaller
+        print(f"[case] noalloc kind={kind} R=N={R}", flush=True)
+        qb, kb = make_inputs(R, R, 1024, noise=0.5, seed=241 + R)
+        q, k = _dev(qb), _dev(kb)
+        ref = binding.fwd_bwd(q, k, LADDER, s, b, kind, weights=(1, 1, 1, 1, 2), extras=True)
+        got = binding.fwd_bwd(q, k, LADDER, s, b, kind, weights=(1, 1, 1, 1, 2), extras=True, noalloc=True)
+        torch.cuda.synchronize()
+        assert abs(got[0].item() - ref[0].item()) <= 1e-3 * abs(ref[0].item())
+        for a, c in ((got[1], ref[1]), (got[2], ref[2])):
+            assert (a - c).abs().max().item() <= 2e-3 * c.abs().max().item()
+            assert torch.equal(a, c)
+        for name in ref[3]:
+            assert torch.equal(got[3][name], ref[3][name]), name
+
+
+def test_noalloc_refuses_what_it_cannot_hold():
+    qb, kb = make_inputs(64, 64, 1024, seed=251)
+    q, k = _dev(qb), _dev(kb)
+    # no caller workspace, no lists, no profiling
+    with pytest.raises(binding.UformError):
+        binding.fwd_bwd(q, k, LADDER, 14.0, 0.0, INFONCE, noalloc=True,
+                        workspace=torch.empty(1 << 20, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(binding.UformError):
+        binding.fwd_bwd(q, k, LADDER, 10.0, -10.0, SIGLIP, noalloc=True,
+                        positives=(np.zeros(65, dtype=np.int64), np.zeros(0, dtype=np.int32)))
+    # 8192 x 8192 InfoNCE needs more than the 128 MiB of scratch: refused before any launch
+    big = torch.zeros(8192, 1024, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(binding.UformError) as e:
+        binding.fwd_bwd(big, big, LADDER, 14.0, 0.0, INFONCE, noalloc=True)
+    assert e.value.status == 2 and "scratch" in e.value.message
+    torch.cuda.synchronize()
