@@ -14,7 +14,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 constexpr int kMaxP = 8;
-constexpr int kMaxD = 1024;
+constexpr int kMaxD = 2048;
+constexpr int kMaxSteps = kMaxD / 32;  // 32-wide steps of the widest row
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -81,6 +82,18 @@ struct ListEnt {
 constexpr int kListEntWords = (int)(sizeof(ListEnt) / 4);
 static_assert(sizeof(ListEnt) == 136, "ListEnt layout");
 
+// Tables of the generic backward (any prefix ladder): wave w of its workgroup owns the 32-wide
+// steps [w nq, (w + 1) nq) of the widest prefix.  S^p = the full partials of the waves below
+// wave_of[p] plus slot snap_slot[p] (wave_of[p]'s full partial when prefix p ends on its last
+// step, else a snapshot taken after step snap_at == snap_slot).
+struct GenTabs {
+    int8_t wave_of[kMaxP];
+    int8_t snap_slot[kMaxP];
+    int8_t snap_at[kMaxSteps];  // global step J: slot of the snapshot taken after J, or -1
+    int8_t band_of[kMaxSteps];  // global step J: the narrowest prefix covering it (P: none)
+    int32_t nslot;              // slots in use: 4 wave partials + snapshots
+};
+
 struct BwdArgs {
     const _Float16 *X16;  // outer rows scaled by their sig, FP16 [NO][D]
     const _Float16 *Y16;  // inner rows scaled by their sig, FP16 [NI][D]
@@ -116,6 +129,8 @@ struct BwdArgs {
     const float *diagA, *posdot, *invx, *gam;        // as in FinArgs
     int64_t R, pos_shift;
     int accumulate;
+    Prefixes pf;   // the prefix widths (generic backward)
+    GenTabs gt;    // generic backward: step and slot tables of the ladder
 };
 
 struct FinArgs {
@@ -156,6 +171,11 @@ hipError_t launch_colstats(const StatsArgs &a, hipStream_t s);
 hipError_t launch_siglip_tabs(const StatsArgs &a, hipStream_t s);
 bool bwd_mask_supported(uint32_t mask);
 hipError_t launch_bwd(const BwdArgs &a, uint32_t mask, bool sig, int64_t nsplit, hipStream_t s);
+// generic backward (any ladder, D <= 2048): nq = 32-wide steps per wave, a power of two <= 16
+constexpr int kGenOuter = 32;  // outer rows per generic backward workgroup
+int gen_max_slots(int nq);     // S slots its LDS holds at this nq
+int gen_max_bands(int nq);     // band operands (prefixes + 1) its LDS holds at this nq
+hipError_t launch_bwd_gen(const BwdArgs &a, int nq, bool sig, int64_t nsplit, hipStream_t s);
 hipError_t launch_maxes(const float *t0, const float *t1, const float *t2, const float *t3, int64_t n0, int64_t n1,
                         int64_t n2, int64_t n3, int P, float *gmax, hipStream_t s);
 hipError_t launch_finalize(const FinArgs &a, hipStream_t s);

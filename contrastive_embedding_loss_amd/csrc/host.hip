@@ -39,6 +39,8 @@ struct Plan {
     int kind;
     bool want_dq, want_dk;
     uint32_t mask;
+    bool gen;                          // the generic backward (ladders without a compiled kernel, D > 1024)
+    int gen_nq;                        // its 32-wide steps per wave
     int64_t nIt, nJt;                  // forward tiles
     int64_t nsplit_row, nsplit_col;    // backward inner splits
     int64_t bps_row, bps_col;          // inner blocks per split
@@ -99,8 +101,8 @@ void build_list_ents(int64_t NO, const int32_t *ptr, const int32_t *idx, int32_t
 }
 
 // Inner splits so that a pass launches enough workgroups for 256 CUs.
-void choose_split(int64_t NO, int64_t NI, int64_t &nsplit, int64_t &bps) {
-    const int64_t wgs = cdiv(NO, kBwdOuter);
+void choose_split(int64_t NO, int64_t NI, int64_t bo, int64_t &nsplit, int64_t &bps) {
+    const int64_t wgs = cdiv(NO, bo);
     const int64_t nblocks = cdiv(NI, kBwdInner);
     int64_t want = cdiv(256, wgs);  // one round of workgroups: one per CU (a workgroup fills its CU)
     if (want < 1) want = 1;
@@ -109,14 +111,60 @@ void choose_split(int64_t NO, int64_t NI, int64_t &nsplit, int64_t &bps) {
     nsplit = cdiv(nblocks, bps);
 }
 
+// Bit ds set: a prefix ends at 32 (ds + 1).  Ladders wider than 1024 have no compiled backward
+// (mask 0).
 uint32_t ladder_mask(const int32_t *pw, int32_t n) {
+    if (pw[n - 1] > 1024) return 0u;
     uint32_t m = 0;
     for (int32_t i = 0; i < n; ++i) m |= 1u << (pw[i] / 32 - 1);
     return m;
 }
 
+// 32-wide steps per wave of the generic backward: the least power of two with 4 waves covering
+// the widest prefix.
+int gen_nq_for(int32_t widest) {
+    const int steps = widest / 32;
+    int nq = 1;
+    while (4 * nq < steps) nq *= 2;
+    return nq;
+}
+
+GenTabs make_gen_tabs(const int32_t *pw, int32_t P, int nq) {
+    GenTabs t{};
+    for (int j = 0; j < kMaxSteps; ++j) {
+        t.snap_at[j] = -1;
+        int band = P;
+        for (int p = P - 1; p >= 0; --p)
+            if (pw[p] > 32 * j) band = p;
+        t.band_of[j] = (int8_t)band;
+    }
+    int interior = 0;
+    for (int p = 0; p < P; ++p) {
+        const int e = pw[p] / 32 - 1;  // the prefix's last step
+        t.wave_of[p] = (int8_t)(e / nq);
+        if ((e + 1) % nq == 0) {
+            t.snap_slot[p] = (int8_t)(e / nq);
+        } else {
+            t.snap_slot[p] = (int8_t)(4 + interior);
+            t.snap_at[e] = (int8_t)(4 + interior);
+            ++interior;
+        }
+    }
+    t.nslot = 4 + interior;
+    return t;
+}
+
+// Which backward a ladder takes: the compiled one (k_bwd), or the generic one if its tables fit.
+bool bwd_compiled(int64_t D, const int32_t *pw, int32_t P) {
+    return D <= 1024 && bwd_mask_supported(ladder_mask(pw, P));
+}
+bool bwd_generic_fits(const int32_t *pw, int32_t P) {
+    const int nq = gen_nq_for(pw[P - 1]);
+    return make_gen_tabs(pw, P, nq).nslot <= gen_max_slots(nq) && P + 1 <= gen_max_bands(nq);
+}
+
 Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, int kind, int64_t off, bool want_dq,
-               bool want_dk, bool one_split = false, int64_t npos = -1) {
+               bool want_dk, bool one_split = false, int64_t npos = -1, int force_gen = -1) {
     Plan p{};
     p.R = R;
     p.N = N;
@@ -127,11 +175,14 @@ Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, in
     p.want_dq = want_dq;
     p.want_dk = want_dk;
     p.mask = ladder_mask(pw, P);
+    p.gen = force_gen >= 0 ? force_gen != 0 : !bwd_compiled(D, pw, P);
+    p.gen_nq = gen_nq_for(pw[P - 1]);
+    const int64_t bo = p.gen ? kGenOuter : kBwdOuter;  // outer rows per backward workgroup
     const bool softmax = kind != kSiglip;
     p.nIt = cdiv(R, kFwdTile);
     p.nJt = cdiv(N, kFwdTile);
-    choose_split(R, N, p.nsplit_row, p.bps_row);
-    choose_split(N, R, p.nsplit_col, p.bps_col);
+    choose_split(R, N, bo, p.nsplit_row, p.bps_row);
+    choose_split(N, R, bo, p.nsplit_col, p.bps_col);
     if (one_split) {
         p.nsplit_row = p.nsplit_col = 1;
         p.bps_row = cdiv(N, kBwdInner);
@@ -144,7 +195,7 @@ Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, in
         p.slots_b = cdiv(N, kStatRows);
     } else {
         p.slots_a = cdiv(R + N, 256);
-        p.slots_b = cdiv(R, kBwdOuter) * p.nsplit_row;
+        p.slots_b = cdiv(R, bo) * p.nsplit_row;
     }
     p.nslots = p.slots_a + p.slots_b;
 
@@ -182,9 +233,10 @@ Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, in
     // forward partials: one per wave column (row partials) / wave row (column partials) of a tile
     p.o_rowpart = take(softmax ? sizeof(float) * 2 * p.nJt * P * R : 0);
     p.o_colpart = take(softmax ? sizeof(float) * 2 * p.nIt * P * N : 0);
-    // gradient partials only with inner splits (one split: the backward finishes the rows in place)
-    const size_t part_row = (want_dq && p.nsplit_row > 1) ? sizeof(float) * p.nsplit_row * R * D : 0;
-    const size_t part_col = (want_dk && p.nsplit_col > 1) ? sizeof(float) * p.nsplit_col * N * D : 0;
+    // gradient partials only with inner splits (one split: the backward finishes the rows in place;
+    // the generic backward always leaves its rows to k_finalize)
+    const size_t part_row = (want_dq && (p.nsplit_row > 1 || p.gen)) ? sizeof(float) * p.nsplit_row * R * D : 0;
+    const size_t part_col = (want_dk && (p.nsplit_col > 1 || p.gen)) ? sizeof(float) * p.nsplit_col * N * D : 0;
     p.o_part = take(part_row > part_col ? part_row : part_col);
     const size_t c_row = sizeof(float) * p.nsplit_row * P * R, c_col = sizeof(float) * p.nsplit_col * P * N;
     p.o_Cpart = take(c_row > c_col ? c_row : c_col);
@@ -290,12 +342,13 @@ uform_status_t validate(const void *q, const void *k, int64_t R, int64_t N, int6
                 }
         }
     }
-    if (D % 64 != 0 || D > kMaxD) return fail(uform_status_unsupported_k, "D must be a multiple of 64 and at most 1024");
+    if (D % 64 != 0 || D > kMaxD) return fail(uform_status_unsupported_k, "D must be a multiple of 64 and at most 2048");
     const bool sigmoid_kind = kind == kSiglip || oneset;
     if (!sigmoid_kind && std::fabs(scale) > UFORM_CONTRASTIVE_MAX_SOFTMAX_SCALE)
         return fail(uform_status_unsupported_k, "softmax kinds support |scale| <= 40");
-    if ((dq || dk || sigmoid_kind) && !bwd_mask_supported(ladder_mask(prefixes, n_prefixes)))
-        return fail(uform_status_unsupported_k, "this prefix ladder has no compiled backward kernel");
+    if ((dq || dk || sigmoid_kind) && !bwd_compiled(D, prefixes, n_prefixes) && !bwd_generic_fits(prefixes, n_prefixes))
+        return fail(uform_status_unsupported_k,
+                    "this prefix ladder needs more snapshot slots or bands than the backward's LDS holds at this width");
     if (N > (int64_t)1 << 31) return fail(uform_status_unsupported_k, "N must be below 2^31");
     return uform_status_success_k;
 }
@@ -689,7 +742,7 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
         float *const ts = (out && (rowpass || !dq)) ? tsum : nullptr;
         ba.tsum = ts;
         const int64_t nsplit = rowpass ? pl.nsplit_row : pl.nsplit_col;
-        const bool fuse = out && nsplit == 1;  // one split: the backward finishes the rows itself
+        const bool fuse = out && nsplit == 1 && !pl.gen;  // one split: the compiled backward finishes the rows itself
         if (fuse) {
             ba.fin_out = out;
             ba.finX = rowpass ? q : k;
@@ -702,7 +755,13 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
             ba.pos_shift = rowpass ? 0 : -off;
             ba.accumulate = (opt && (opt->flags & UFORM_CONTRASTIVE_ACCUMULATE)) ? 1 : 0;
         }
-        LAUNCH_NAMED("k_bwd", launch_bwd(ba, pl.mask, !softmax, nsplit, s));
+        if (pl.gen) {
+            ba.pf = pf;
+            ba.gt = make_gen_tabs(prefixes, P, pl.gen_nq);
+            LAUNCH_NAMED("k_bwd_gen", launch_bwd_gen(ba, pl.gen_nq, !softmax, nsplit, s));
+        } else {
+            LAUNCH_NAMED("k_bwd", launch_bwd(ba, pl.mask, !softmax, nsplit, s));
+        }
         if (out && !fuse) {
             FinArgs fa{};
             fa.X = rowpass ? q : k;
@@ -901,9 +960,14 @@ size_t uform_contrastive_workspace_bytes_ex(int64_t R, int64_t N, int64_t D, int
     int32_t pw[kMaxP];
     for (int32_t i = 0; i < n_prefixes; ++i) pw[i] = (int32_t)(D - 32 * (n_prefixes - 1 - i));  // any ladder ending at D
     const int64_t npos = n_positives < 0 ? -1 : n_positives;
-    if (kind == kOneset || kind == kOnesetEdges)
-        return make_plan(R, N, D, pw, n_prefixes, kSiglip, 0, true, false, false, npos).total;
-    return make_plan(R, N, D, pw, n_prefixes, kind, 0, true, true, false, npos).total;
+    // enough for either backward (the size depends on the ladder's count and width, not its steps)
+    const bool oneset = kind == kOneset || kind == kOnesetEdges;
+    size_t need = 0;
+    for (int g = 0; g < 2; ++g) {
+        const Plan pl = make_plan(R, N, D, pw, n_prefixes, oneset ? kSiglip : kind, 0, true, !oneset, false, npos, g);
+        need = pl.total > need ? pl.total : need;
+    }
+    return need;
 }
 
 uform_status_t uform_contrastive_supported(int64_t D, const int32_t *prefixes, int32_t n_prefixes, int32_t kind,
@@ -917,9 +981,11 @@ uform_status_t uform_contrastive_supported(int64_t D, const int32_t *prefixes, i
             return fail(uform_status_invalid_argument_k, "prefix widths must be increasing multiples of 32");
     }
     if (D < 1 || prefixes[n_prefixes - 1] > D) return fail(uform_status_invalid_argument_k, "the widest prefix exceeds D");
-    if (D % 64 != 0 || D > kMaxD) return fail(uform_status_unsupported_k, "D must be a multiple of 64 and at most 1024");
-    if ((with_gradients || kind == kSiglip || kind == kOneset || kind == kOnesetEdges) && !bwd_mask_supported(ladder_mask(prefixes, n_prefixes)))
-        return fail(uform_status_unsupported_k, "this prefix ladder has no compiled backward kernel");
+    if (D % 64 != 0 || D > kMaxD) return fail(uform_status_unsupported_k, "D must be a multiple of 64 and at most 2048");
+    if ((with_gradients || kind == kSiglip || kind == kOneset || kind == kOnesetEdges) &&
+        !bwd_compiled(D, prefixes, n_prefixes) && !bwd_generic_fits(prefixes, n_prefixes))
+        return fail(uform_status_unsupported_k,
+                    "this prefix ladder needs more snapshot slots or bands than the backward's LDS holds at this width");
     return uform_status_success_k;
 }
 

@@ -131,9 +131,9 @@ __device__ __forceinline__ void dma4_m0(const void *g, uint32_t m0v) {
 // per-row operand scale gam; for query rows also the prefix dot products
 // with their positive key.  A workgroup takes 4 RPW consecutive rows of the
 // list (query rows, then key rows), a wave RPW of them (16, 4 or 1: enough
-// workgroups to fill the GPU), one at a time with the next row's loads in flight.  Lane l holds the 16-byte chunks l and l + 64 of a
-// row (D <= 1024); prefix ends are multiples of 32, so no chunk straddles
-// one, and the sum over a prefix is an inclusive scan over the chunks read at
+// workgroups to fill the GPU), one at a time with the next row's loads in flight.  Lane l holds the 16-byte chunks
+// l, l + 64, ... of a row (NC of them: D <= 512 NC); prefix ends are multiples of 32, so no
+// chunk straddles one, and the sum over a prefix is an inclusive scan over the chunks read at
 // the prefix's last chunk.  Results go through LDS so that the tables are
 // written with consecutive rows on consecutive lanes.
 // ----------------------------------------------------------------------------
@@ -164,7 +164,7 @@ __device__ __forceinline__ float dot8(const uint4 &a, const uint4 &b) {
     return s;
 }
 
-template <int RPW>
+template <int RPW, int NC>
 __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
     constexpr int RB = 4 * RPW;  // rows per workgroup
     __shared__ float res[RB][2 * kMaxP + 1];  // per row: inv[P] | posdot[P] | sig
@@ -177,21 +177,23 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
 #pragma unroll
     for (int p = 0; p < kMaxP; ++p)
         if (p < P && lane == p) m = a.pf.w[p] / 8;
-    const bool c0 = lane < nch, c1 = lane + 64 < nch;
-    uint4 bx[2][2], by[2][2];
+    uint4 bx[2][NC], by[2][NC];
     auto fetch = [&](int j, int s) {
         const int64_t g = g0 + RPW * wave + j;
         const uint4 z = make_uint4(0, 0, 0, 0);
-        bx[s][0] = bx[s][1] = by[s][0] = by[s][1] = z;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) bx[s][c] = by[s][c] = z;
         if (g >= rows) return;
         const bool isq = g < a.R;
         const u16 *x = isq ? a.q + g * D : a.k + (g - a.R) * D;
-        if (c0) bx[s][0] = *(const uint4 *)(x + 8 * lane);
-        if (c1) bx[s][1] = *(const uint4 *)(x + 8 * (lane + 64));
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            if (lane + 64 * c < nch) bx[s][c] = *(const uint4 *)(x + 8 * (lane + 64 * c));
         if (isq) {
             const u16 *y = a.k + ((g + a.off) ^ a.pxor) * D;
-            if (c0) by[s][0] = *(const uint4 *)(y + 8 * lane);
-            if (c1) by[s][1] = *(const uint4 *)(y + 8 * (lane + 64));
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                if (lane + 64 * c < nch) by[s][c] = *(const uint4 *)(y + 8 * (lane + 64 * c));
         }
     };
     fetch(0, 0);
@@ -201,14 +203,18 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
         const int64_t g = g0 + RPW * wave + j;
         if (g >= rows) continue;  // wave-uniform
         const int s = j & 1;
-        const float S0 = wave_scan(sq8(bx[s][0]), lane), S1 = wave_scan(sq8(bx[s][1]), lane);
-        const float T0 = wave_scan(dot8(bx[s][0], by[s][0]), lane), T1 = wave_scan(dot8(bx[s][1], by[s][1]), lane);
-        // lane p < P: sums over prefix p's chunks (the first 64 chunks' total at lane 63).  Every
-        // lane takes part in every shuffle (a lane outside the exec mask supplies no value).
-        const int s1 = max(m - 65, 0);
-        const float a0 = __shfl(S0, min(m, 64) - 1), a1 = __shfl(S1, s1);
-        const float b0 = __shfl(T0, min(m, 64) - 1), b1 = __shfl(T1, s1);
-        const float ss = a0 + (m > 64 ? a1 : 0.f), dt = b0 + (m > 64 ? b1 : 0.f);
+        // lane p < P: sums over prefix p's chunks, group by group of 64 chunks (a group's total at
+        // lane 63).  Every lane takes part in every shuffle (a lane outside the exec mask supplies
+        // no value).
+        float ss = 0.f, dt = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const float Sc = wave_scan(sq8(bx[s][c]), lane), Tc = wave_scan(dot8(bx[s][c], by[s][c]), lane);
+            const int at = min(max(m - 64 * c, 1), 64) - 1;
+            const float av = __shfl(Sc, at), bv = __shfl(Tc, at);
+            ss += m > 64 * c ? av : 0.f;
+            dt += m > 64 * c ? bv : 0.f;
+        }
         const int r = RPW * wave + j;
         if (lane < P) {
             res[r][lane] = 1.0f / sqrtf(fmaxf(ss, 1.17549435e-38f));
@@ -1463,6 +1469,310 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// k_bwd_gen: one backward pass (row or column) for any prefix ladder and widths up to 2048.
+//
+// The arithmetic of k_bwd (recompute of S over an inner block, cell coefficients with every
+// scale folded in, band operands as running sums widest prefix first, dX += A_band . Y, the
+// positive cell and the radial term left to k_finalize), laid out for generality: 32 outer rows
+// per workgroup (a 2048-wide gradient quarter of 32 rows is 32 x 512 FP32 = 256 accumulators per
+// lane), 4 waves, wave w owning the 32-wide steps [w NQ, (w + 1) NQ) of the recompute and of the
+// update; prefix ends, snapshot slots and bands come from run-time tables; the phases of a block
+// run one after another (recompute, barrier, epilogue, barrier, update, barrier) while the copies
+// of the next block are in flight.  Lane l of the epilogue owns outer row l & 31 and inner rows
+// 4 w + 2 (l >> 5) + {0, 1}.  Split partials always go to k_finalize.
+// ----------------------------------------------------------------------------
+constexpr int GBO = kGenOuter;
+
+template <int NQ>
+struct GenLds {
+    static constexpr int YP = 4 * NQ * 32 + 8;                // FP16 per LDS row of an inner tile
+    static constexpr int RSL = BI * YP + 2 * kMaxP * BI * 2;  // FP16 per ring slot: the tile, then its tables
+    static constexpr int NSLOT = NQ >= 16 ? 7 : 12;           // S slots (4 wave partials + snapshots)
+    static constexpr int NBAND = NQ >= 16 ? 7 : kMaxP + 1;    // band operands (prefixes, then a zero band)
+};
+int gen_max_slots(int nq) { return nq >= 16 ? GenLds<16>::NSLOT : GenLds<8>::NSLOT; }
+int gen_max_bands(int nq) { return nq >= 16 ? GenLds<16>::NBAND : GenLds<8>::NBAND; }
+
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+
+template <int NQ, bool SIG, bool UPD>
+__global__ __launch_bounds__(256, 1) void k_bwd_gen(BwdArgs a) {
+    using G = GenLds<NQ>;
+    constexpr int YP = G::YP, RSL = G::RSL;
+    __shared__ __attribute__((aligned(16))) _Float16 Ys[2][RSL];
+    __shared__ __attribute__((aligned(16))) float Sl[G::NSLOT][GBO * SLOTP];
+    __shared__ __attribute__((aligned(16))) _Float16 At[G::NBAND][GBO * APITCH];
+    __shared__ float inv_sc[GBO];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4, l32 = lane & 31, h = lane >> 5;
+    const int NO = (int)a.NO, NI = (int)a.NI, D = a.D, P = a.pf.n;
+    const int o0 = (int)blockIdx.x * GBO;
+    const int o = o0 + l32;  // this lane's outer row in the epilogue
+    const bool ovalid = o < NO;
+    const int nblocks = (NI + BI - 1) / BI;
+    const int nb_begin = (int)blockIdx.y * (int)a.blocks_per_split;
+    const int nb_end = min(nb_begin + (int)a.blocks_per_split, nblocks);
+    const int dq0 = w * NQ * 32;  // first column of this wave's steps
+    const int dsh = (int)a.diag_shift, pxr = a.pxor;
+    const bool want_loss = SIG && a.want_loss != 0, want_bias = SIG && a.biasparts != nullptr;
+
+    // ---- this lane's outer-row terms (the static operand scale as in k_bwd)
+    float Ao[kMaxP], Co[kMaxP], Ro[kMaxP];
+    float csc = 1.0f;
+    {
+        const int64_t orow = ovalid ? o : 0;
+        float sc = 1.0f;
+        if (ovalid) {
+            const float ixP = a.oInv[(P - 1) * a.NO + orow];
+            float U = 0.f;
+            for (int p = 0; p < P; ++p) {
+                const float own = a.oNeg ? a.oNeg[p * a.NO + orow] : 0.f;
+                const float gt = a.gterm ? a.gterm[p] : a.gterm_val[p];
+                U += a.wnorm[p] * (a.oInv[p * a.NO + orow] / ixP) * a.iyrmax[p] * (own + gt);
+            }
+            if (U > 0.f) sc = ldexpf(1.0f, max(-126, min(126, 14 - (ilogbf(U) + 1))));
+        }
+        const float rsig = 1.0f / a.oSig[orow];  // exact: sig is a power of two
+#pragma unroll
+        for (int p = 0; p < kMaxP; ++p) {
+            const int pp = p < P ? p : 0;
+            Ao[p] = a.oA[pp * a.NO + orow] * rsig;
+            const float c = a.oC[pp * a.NO + orow];
+            Co[p] = SIG ? c * sc : c + log2f(sc);
+            Ro[p] = SIG ? 0.f : a.oRho[pp * a.NO + orow];
+        }
+        csc = rsig / sc;
+        if (w == 0 && h == 0) inv_sc[l32] = 1.0f / sc;
+    }
+
+    // ---- copies of inner block nb into ring slot sl: this wave's rows 4 w .. 4 w + 3 (the FP16
+    // inner matrix carries two zero blocks past its last row), their first DC columns (the steps
+    // of the four waves; later columns are never read) in 1 KB pieces, and one float of the
+    // block's tables [iI | iKap][p][row] per lane (rows past the end read the last row)
+    const int DC = min(D, 4 * NQ * 32);
+    const int npc = (DC * 2 + 1023) / 1024;
+    const int lastc = (DC * 2 - (npc - 1) * 1024) / 16;  // active lanes of the last piece
+    const uint32_t ys_lds = (uint32_t)(uintptr_t)&Ys[0][0];
+    const int te = 64 * w + lane;
+    const bool tact = te < 2 * P * BI;
+    const int tr = te % BI;
+    const float *tbase = tact ? ((te / (P * BI)) == 0 ? a.iI : a.iKap) + (int64_t)((te / BI) % P) * NI + tr : a.iI;
+    const int tlim = tact ? NI - 1 - tr : 0;
+    auto issue_block = [&](int nb, int sl) {
+        const _Float16 *gblk = a.Y16 + (int64_t)nb * BI * D;
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t voff = (uint32_t)(4 * w + k) * (uint32_t)D * 2u + 16u * (uint32_t)lane;
+            const uint32_t m0v = __builtin_amdgcn_readfirstlane(ys_lds + 2u * (uint32_t)(sl * RSL + (4 * w + k) * YP));
+            for (int pc = 0; pc < npc; ++pc)
+                if (pc + 1 < npc || lane < lastc) dma_row1(gblk, voff + 1024u * pc, m0v + 1024u * pc);
+        }
+        const uint32_t tb = __builtin_amdgcn_readfirstlane(ys_lds + 2u * (uint32_t)(sl * RSL + BI * YP) + 4u * (uint32_t)(64 * w));
+        dma4_m0(tbase + min(nb * BI, tlim), tb);
+    };
+
+    // zero the ring (tile columns past D stay zero) and the bands (band P stays zero)
+    for (int e = tid; e < 2 * RSL / 8; e += 256) *(uint4 *)&Ys[0][e * 8] = make_uint4(0, 0, 0, 0);
+    for (int e = tid; e < G::NBAND * GBO * APITCH / 8; e += 256) *(uint4 *)&At[0][e * 8] = make_uint4(0, 0, 0, 0);
+    lds_barrier();
+
+    // ---- outer rows' columns of this wave's steps as B operands (zero past NO or D)
+    f16x8 xr[2][NQ];
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob) {
+        const int orow = o0 + 16 * ob + l16;
+#pragma unroll
+        for (int ks = 0; ks < NQ; ++ks) {
+            const int d = dq0 + 32 * ks + 8 * g4;
+            f16x8 v = {};
+            if (orow < NO && d < D) v = *(const f16x8 *)(a.X16 + (int64_t)orow * D + d);
+            xr[ob][ks] = v;
+        }
+    }
+    f32x16 dacc[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dacc[j][r] = 0.f;
+    float Cacc[kMaxP], Lacc[kMaxP], Bacc[kMaxP];
+#pragma unroll
+    for (int p = 0; p < kMaxP; ++p) Cacc[p] = Lacc[p] = Bacc[p] = 0.f;
+
+    // listed cells: the entries of this workgroup's 64-row table block, sorted by nb
+    const int lob = (int)blockIdx.x >> 1, lbit = 32 * ((int)blockIdx.x & 1) + l32;
+    int lcur = 0, lend = 0;
+    if (a.lptr) {
+        lcur = a.lptr[lob];
+        lend = a.lptr[lob + 1];
+    }
+    int lnb = lcur < lend ? a.lent[lcur].nb : INT_MAX;
+    auto listed = [&](int nb) {
+        while (lnb < nb) {
+            ++lcur;
+            lnb = lcur < lend ? a.lent[lcur].nb : INT_MAX;
+        }
+        return lnb == nb;
+    };
+
+    // transposed reads of the inner tile for the update (per-lane part; slot and step added)
+    const _Float16 *ytr = &Ys[0][0] + (8 * (g4 >> 1) + (l16 >> 2)) * YP + 16 * (g4 & 1) + 4 * (lane & 3) + dq0;
+    const float *tabs0 = (const float *)&Ys[0][BI * YP];
+
+    if (nb_begin < nb_end) {
+        issue_block(nb_begin, 0);
+        wait_vm();
+        lds_barrier();
+    }
+    for (int nb = nb_begin; nb < nb_end; ++nb) {
+        const int cur = (nb - nb_begin) & 1;
+        issue_block(nb + 1, cur ^ 1);  // past the end: a zero block or the next split's rows, unused
+
+        // recompute: partial S^T (16 inner x 32 outer) over this wave's steps, and a snapshot
+        // after each step where a prefix ends inside them
+        {
+            const _Float16 *yrow = &Ys[cur][0] + l16 * YP + dq0 + 8 * g4;
+            f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            auto put = [&](int slot) {
+#pragma unroll
+                for (int ob = 0; ob < 2; ++ob) *(f32x4 *)&Sl[slot][(16 * ob + l16) * SLOTP + 4 * g4] = acc[ob];
+            };
+#pragma unroll
+            for (int ks = 0; ks < NQ; ++ks) {
+                const f16x8 yv = *(const f16x8 *)(yrow + 32 * ks);
+#pragma unroll
+                for (int ob = 0; ob < 2; ++ob)
+                    acc[ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(yv, xr[ob][ks], acc[ob], 0, 0, 0);
+                const int sl = a.gt.snap_at[w * NQ + ks];
+                if (sl >= 0) put(sl);
+            }
+            put(w);
+        }
+        lds_barrier();
+
+        // epilogue: coefficients of this lane's two cells for every prefix, widest first
+        {
+            const int nl = 4 * w + 2 * h;  // row of the first cell in the block
+            const float *tab = (const float *)((const char *)tabs0 + cur * RSL * 2);
+            bool ok[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int n = nb * BI + nl + t;
+                ok[t] = ovalid && n < NI && n != ((o + dsh) ^ pxr) && (pxr == 0 || n != o + dsh);
+            }
+            if (listed(nb)) {
+                const uint64_t *lm = a.lent[lcur].m + nl;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) ok[t] = ok[t] && ((lm[t] >> lbit) & 1ull) == 0ull;
+            }
+            float run[2] = {0.f, 0.f};
+#pragma unroll
+            for (int p = kMaxP - 1; p >= 0; --p) {
+                if (p >= P) continue;
+                const int wv = a.gt.wave_of[p];
+                f32x2 Sp = *(const f32x2 *)&Sl[a.gt.snap_slot[p]][l32 * SLOTP + nl];
+                for (int q = 0; q < wv; ++q) Sp += *(const f32x2 *)&Sl[q][l32 * SLOTP + nl];
+                float av[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const float iy = tab[p * BI + nl + t];
+                    const float e = Sp[t] * Ao[p];
+                    float c;
+                    if constexpr (!SIG) {
+                        c = __builtin_amdgcn_exp2f(fmaf(e, iy, Co[p])) * fmaf(Ro[p], iy, tab[(P + p) * BI + nl + t]);
+                    } else {
+                        const float uu = fmaf(e, iy, a.b2);
+                        const float tt = __builtin_amdgcn_exp2f(-fabsf(uu));
+                        const float wq = 1.f + tt;
+                        const float rr = __builtin_amdgcn_rcpf(wq);
+                        const float sg = uu >= 0.f ? rr : tt * rr;
+                        c = sg * Co[p] * iy;  // Co holds beta_o for the sigmoid form
+                        if (want_loss && ok[t]) {
+                            // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
+                            Lacc[p] += fmaxf(uu, 0.f) + __builtin_amdgcn_logf(wq) + (tt - (wq - 1.f)) * rr * kLog2e;
+                            if (want_bias) Bacc[p] += sg;
+                        }
+                    }
+                    av[t] = ok[t] ? c : 0.f;
+                    run[t] += av[t];
+                    Cacc[p] = fmaf(av[t], Sp[t], Cacc[p]);
+                }
+                uint32_t hpk;
+                asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(hpk) : "v"(run[0]), "v"(run[1]));
+                *(uint32_t *)&At[p][l32 * APITCH + nl] = hpk;
+            }
+        }
+        lds_barrier();
+
+        // update: dX[:, this wave's steps] += A_band . Y
+        if constexpr (UPD) {
+#pragma unroll
+            for (int jb = 0; jb < NQ; ++jb) {
+                const int band = a.gt.band_of[w * NQ + jb];
+                const f16x8 af = *(const f16x8 *)&At[band][l32 * APITCH + 8 * h];
+                const _Float16 *ysrc = ytr + cur * RSL + 32 * jb;
+                const f16x4 lo = ds_read_tr(ysrc);
+                const f16x4 hi = ds_read_tr(ysrc + 4 * YP);
+                const f16x8 bfv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                dacc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bfv, dacc[jb], 0, 0, 0);
+            }
+        }
+        wait_vm();      // the copies of block nb + 1 landed
+        lds_barrier();  // ... for every wave; the slots and bands of block nb are consumed
+    }
+
+    // ---- the raw gradient block (scale divided out) into this split's partial
+    const int64_t split = blockIdx.y;
+    if constexpr (UPD) {
+        float *dst = a.part + split * a.NO * D;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int orow = 8 * (r >> 2) + 4 * h + (r & 3);
+            const float sv = inv_sc[orow];
+            if (o0 + orow < NO) {
+                float *rowp = dst + (int64_t)(o0 + orow) * D + dq0 + l32;
+#pragma unroll
+                for (int jb = 0; jb < NQ; ++jb)
+                    if (dq0 + 32 * jb + l32 < D) rowp[32 * jb] = dacc[jb][r] * sv;
+            }
+        }
+    }
+    // radial sums over the eight (wave, half) parts of each row, and the sigmoid loss sums
+    float *red = &Sl[0][0];  // [8][kMaxP][GBO], then [4][kMaxP] twice
+#pragma unroll
+    for (int p = 0; p < kMaxP; ++p) red[((2 * w + h) * kMaxP + p) * GBO + l32] = Cacc[p];
+    if (want_loss) {
+#pragma unroll
+        for (int p = 0; p < kMaxP; ++p) {
+            const float v = wave_sum(Lacc[p]), u = wave_sum(Bacc[p]);
+            if (lane == 0) {
+                red[8 * kMaxP * GBO + w * kMaxP + p] = v;
+                red[8 * kMaxP * GBO + 4 * kMaxP + w * kMaxP + p] = u;
+            }
+        }
+    }
+    lds_barrier();
+    if (w == 0 && h == 0 && ovalid) {
+        for (int p = 0; p < P; ++p) {
+            float c = 0.f;
+            for (int k = 0; k < 8; ++k) c += red[(k * kMaxP + p) * GBO + l32];
+            a.Cpart[(split * P + p) * a.NO + o] = c * csc;
+        }
+    }
+    if (want_loss && tid < P) {
+        const float *lr = red + 8 * kMaxP * GBO;
+        const int64_t slot = (int64_t)a.loss_slot0 + split * gridDim.x + blockIdx.x;
+        a.lossparts[slot * P + tid] =
+            (((lr[0 * kMaxP + tid] + lr[1 * kMaxP + tid]) + lr[2 * kMaxP + tid]) + lr[3 * kMaxP + tid]) * kLn2;
+        if (want_bias) {
+            const float *br = lr + 4 * kMaxP;
+            a.biasparts[slot * P + tid] =
+                ((br[0 * kMaxP + tid] + br[1 * kMaxP + tid]) + br[2 * kMaxP + tid]) + br[3 * kMaxP + tid];
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
 // k_maxes: gmax[t][p] = max over the rows of table t, prefix p (one block each;
 // a fixed tree, so the result does not depend on scheduling).
 // ----------------------------------------------------------------------------
@@ -1622,13 +1932,19 @@ __global__ __launch_bounds__(256) void k_loss(LossArgs a) {
 // ----------------------------------------------------------------------------
 hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
     const int64_t rows = a.R + a.N;
-    // 16 rows per wave where that still gives 1024 workgroups, else 4, else 1
-    if (rows >= 1024 * kPrepRows)
-        hipLaunchKernelGGL(k_prep<16>, dim3((unsigned)((rows + 63) / 64)), dim3(256), 0, s, a);
-    else if (rows >= 1024 * 16)
-        hipLaunchKernelGGL(k_prep<4>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL(k_prep<1>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+    // 16 rows per wave where that still gives 1024 workgroups, else 4, else 1; rows wider than
+    // 1024 take four chunk groups per lane
+    const bool wide = a.D > 1024;
+    if (rows >= 1024 * kPrepRows) {
+        if (wide) hipLaunchKernelGGL((k_prep<16, 4>), dim3((unsigned)((rows + 63) / 64)), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_prep<16, 2>), dim3((unsigned)((rows + 63) / 64)), dim3(256), 0, s, a);
+    } else if (rows >= 1024 * 16) {
+        if (wide) hipLaunchKernelGGL((k_prep<4, 4>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_prep<4, 2>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
+    } else {
+        if (wide) hipLaunchKernelGGL((k_prep<1, 4>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_prep<1, 2>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -1655,8 +1971,9 @@ hipError_t launch_fwd(const u16 *q, const u16 *k, int64_t R, int64_t N, int D, c
                       const float *rowA, const float *colI, float cshift, float *rowpart, float *colpart,
                       hipStream_t s) {
     const int64_t nIt = (R + FB - 1) / FB, nJt = (N + FB - 1) / FB;
-    uint32_t mask = 0;
-    for (int p = 0; p < pf.n; ++p) mask |= 1u << (pf.w[p] / 32 - 1);
+    uint32_t mask = 0;  // compiled ladders end at or below 1024 (32 steps); wider lists run the run-time variant
+    for (int p = 0; p < pf.n; ++p) mask |= pf.w[p] <= 1024 ? 1u << (pf.w[p] / 32 - 1) : 0u;
+    if (pf.w[pf.n - 1] > 1024) mask = 0u;
     const dim3 grid((unsigned)(nIt * nJt));
 #define UFORM_CASE(m)                                                                                          \
     if (fwd_ladder(m) != 0u && mask == (m)) {                                                                  \
@@ -1726,6 +2043,29 @@ hipError_t launch_bwd(const BwdArgs &a, uint32_t mask, bool sig, int64_t nsplit,
     if (mask == (m)) return launch_bwd_mask<(m)>(a, sig, grid, s);
     UFORM_LADDERS(UFORM_CASE)
 #undef UFORM_CASE
+    return hipErrorInvalidValue;
+}
+
+template <int NQ>
+static hipError_t launch_bwd_gen_nq(const BwdArgs &a, bool sig, dim3 grid, hipStream_t s) {
+    if (!sig)
+        hipLaunchKernelGGL((k_bwd_gen<NQ, false, true>), grid, dim3(256), 0, s, a);
+    else if (a.do_update)
+        hipLaunchKernelGGL((k_bwd_gen<NQ, true, true>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_bwd_gen<NQ, true, false>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_gen(const BwdArgs &a, int nq, bool sig, int64_t nsplit, hipStream_t s) {
+    const dim3 grid((unsigned)((a.NO + GBO - 1) / GBO), (unsigned)nsplit);
+    switch (nq) {
+        case 1: return launch_bwd_gen_nq<1>(a, sig, grid, s);
+        case 2: return launch_bwd_gen_nq<2>(a, sig, grid, s);
+        case 4: return launch_bwd_gen_nq<4>(a, sig, grid, s);
+        case 8: return launch_bwd_gen_nq<8>(a, sig, grid, s);
+        case 16: return launch_bwd_gen_nq<16>(a, sig, grid, s);
+    }
     return hipErrorInvalidValue;
 }
 

@@ -43,17 +43,23 @@ __device__ __forceinline__ void load16(const u16 *p, float v[16]) {
     }
 }
 
-// Lane l holds elements 16 l .. 16 l + 15 of a row (D <= 1024); waves walk the outer rows
-// blockIdx.x * 4 + wave, stepping by the grid.
+// Lane l holds elements 16 l .. 16 l + 15 of each 1024-wide segment of a row (NSEG segments:
+// D <= 1024 NSEG); waves walk the outer rows blockIdx.x * 4 + wave, stepping by the grid.
+template <int NSEG>
 __global__ __launch_bounds__(256) void k_pos(PosArgs a) {
     __shared__ float red[4][3 * kMaxP];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int P = a.pf.n, D = a.D;
-    const int d0 = 16 * lane;
-    const bool act = d0 < D;
-    int pl = P;  // the narrowest prefix that covers this lane's elements (P: none)
-    for (int p = P - 1; p >= 0; --p)
-        if (d0 < a.pf.w[p]) pl = p;
+    int d0[NSEG], pl[NSEG];  // segment g: first element, narrowest prefix covering it (P: none)
+    bool act[NSEG];
+#pragma unroll
+    for (int g = 0; g < NSEG; ++g) {
+        d0[g] = 16 * lane + 1024 * g;
+        act[g] = d0[g] < D;
+        pl[g] = P;
+        for (int p = P - 1; p >= 0; --p)
+            if (d0[g] < a.pf.w[p]) pl[g] = p;
+    }
     // sums over this wave's cells (wave-uniform): softplus(-l^p), sigma(-l^p) cos^p, sigma(-l^p)
     float ls[kMaxP], cs[kMaxP], gs[kMaxP];
 #pragma unroll
@@ -62,30 +68,45 @@ __global__ __launch_bounds__(256) void k_pos(PosArgs a) {
     for (int64_t o = (int64_t)blockIdx.x * 4 + wave; o < a.NO; o += (int64_t)gridDim.x * 4) {
         const int e0 = a.ptr[o], e1 = a.ptr[o + 1];
         if (e0 >= e1) continue;
-        float xv[16];
-        if (act)
-            load16(a.x + o * D + d0, xv);
-        else
-            for (int c = 0; c < 16; ++c) xv[c] = 0.f;
+        float xv[NSEG][16];
+#pragma unroll
+        for (int g = 0; g < NSEG; ++g) {
+            if (act[g])
+                load16(a.x + o * D + d0[g], xv[g]);
+            else
+                for (int c = 0; c < 16; ++c) xv[g][c] = 0.f;
+        }
         float ix[kMaxP];
         for (int p = 0; p < P; ++p) ix[p] = a.invx[p * a.NO + o];
-        float acc[16];
+        float acc[NSEG][16];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) acc[c] = 0.f;
-        float xc = 0.f;  // sum over cells and covering prefixes of c_p cos^p |x^p|^-2
+        for (int g = 0; g < NSEG; ++g)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) acc[g][c] = 0.f;
+        float xc[NSEG];  // per segment: sum over cells and covering prefixes of c_p sigma(-l^p) cos^p |x^p|^-2
+#pragma unroll
+        for (int g = 0; g < NSEG; ++g) xc[g] = 0.f;
         for (int e = e0; e < e1; ++e) {
             const int64_t i = a.idx[e];
-            float yv[16];
-            if (act)
-                load16(a.y + i * D + d0, yv);
-            else
-                for (int c = 0; c < 16; ++c) yv[c] = 0.f;
-            float part = 0.f;
+            float yv[NSEG][16], part[NSEG];
 #pragma unroll
-            for (int c = 0; c < 16; ++c) part = fmaf(xv[c], yv[c], part);
-            float yc = 0.f;  // sum over covering prefixes of c_p sigma(-l^p) |x^p|^-1 |y^p|^-1
+            for (int g = 0; g < NSEG; ++g) {
+                if (act[g])
+                    load16(a.y + i * D + d0[g], yv[g]);
+                else
+                    for (int c = 0; c < 16; ++c) yv[g][c] = 0.f;
+                part[g] = 0.f;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) part[g] = fmaf(xv[g][c], yv[g][c], part[g]);
+            }
+            float yc[NSEG];  // per segment: sum over covering prefixes of c_p sigma(-l^p) |x^p|^-1 |y^p|^-1
+#pragma unroll
+            for (int g = 0; g < NSEG; ++g) yc[g] = 0.f;
             for (int p = 0; p < P; ++p) {
-                const float dot = wsum(d0 < a.pf.w[p] ? part : 0.f);
+                float mine = 0.f;
+#pragma unroll
+                for (int g = 0; g < NSEG; ++g) mine += d0[g] < a.pf.w[p] ? part[g] : 0.f;
+                const float dot = wsum(mine);
                 const float iy = a.invy[p * a.NI + i];
                 const float cosv = dot * ix[p] * iy;
                 const float l = fmaf(a.t, cosv, a.b);
@@ -94,25 +115,32 @@ __global__ __launch_bounds__(256) void k_pos(PosArgs a) {
                 ls[p] += fmaxf(-l, 0.f) + log1pf(expf(-fabsf(l)));
                 cs[p] = fmaf(sn, cosv, cs[p]);
                 gs[p] += sn;
-                if (p >= pl) {
-                    const float c = a.gc[p] * sn;
-                    yc = fmaf(c, ix[p] * iy, yc);
-                    xc = fmaf(c, cosv * ix[p] * ix[p], xc);
-                }
+                const float c = a.gc[p] * sn;
+#pragma unroll
+                for (int g = 0; g < NSEG; ++g)
+                    if (p >= pl[g]) {
+                        yc[g] = fmaf(c, ix[p] * iy, yc[g]);
+                        xc[g] = fmaf(c, cosv * ix[p] * ix[p], xc[g]);
+                    }
             }
 #pragma unroll
-            for (int c = 0; c < 16; ++c) acc[c] = fmaf(yc, yv[c], acc[c]);
-        }
-        if (a.out && act && pl < P) {
-            float4 *dst = (float4 *)(a.out + o * D + d0);
+            for (int g = 0; g < NSEG; ++g)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                float4 v = dst[c];
-                v.x += acc[4 * c] - xc * xv[4 * c];
-                v.y += acc[4 * c + 1] - xc * xv[4 * c + 1];
-                v.z += acc[4 * c + 2] - xc * xv[4 * c + 2];
-                v.w += acc[4 * c + 3] - xc * xv[4 * c + 3];
-                dst[c] = v;
+                for (int c = 0; c < 16; ++c) acc[g][c] = fmaf(yc[g], yv[g][c], acc[g][c]);
+        }
+#pragma unroll
+        for (int g = 0; g < NSEG; ++g) {
+            if (a.out && act[g] && pl[g] < P) {
+                float4 *dst = (float4 *)(a.out + o * D + d0[g]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    float4 v = dst[c];
+                    v.x += acc[g][4 * c] - xc[g] * xv[g][4 * c];
+                    v.y += acc[g][4 * c + 1] - xc[g] * xv[g][4 * c + 1];
+                    v.z += acc[g][4 * c + 2] - xc[g] * xv[g][4 * c + 2];
+                    v.w += acc[g][4 * c + 3] - xc[g] * xv[g][4 * c + 3];
+                    dst[c] = v;
+                }
             }
         }
     }
@@ -171,7 +199,10 @@ hipError_t launch_pos(const PosArgs &a, hipStream_t s, int64_t *blocks_out) {
     int64_t blocks = (a.NO + 3) / 4;
     if (blocks > kPosBlocks) blocks = kPosBlocks;
     if (blocks_out) *blocks_out = blocks;
-    hipLaunchKernelGGL(k_pos, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    if (a.D > 1024)
+        hipLaunchKernelGGL(k_pos<2>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_pos<1>, dim3((unsigned)blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

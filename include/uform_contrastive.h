@@ -100,7 +100,7 @@ typedef enum {
 
 /* Limits of the library. */
 #define UFORM_CONTRASTIVE_MAX_PREFIXES 8
-#define UFORM_CONTRASTIVE_MAX_DIM 1024
+#define UFORM_CONTRASTIVE_MAX_DIM 2048
 /* Softmax kinds use one fixed log-sum-exp shift per call, exact while
  * 2 * |scale| * log2(e) stays inside FP32's normal exponent range. */
 #define UFORM_CONTRASTIVE_MAX_SOFTMAX_SCALE 40.0f
@@ -110,7 +110,9 @@ typedef enum {
  *
  *  q, k        device, BF16 bit patterns, row-major [R][D] and [N][D] with
  *              leading dimension D, 16-byte aligned.
- *  R, N, D     1 <= R <= N; D % 64 == 0 and D <= 1024 (else unsupported).
+ *  R, N, D     1 <= R <= N; D % 64 == 0 and D <= 2048 (else unsupported):
+ *              the widths of the UForm README's tier table, whose Large and
+ *              XL tiers train the prefixes {64, ..., 1024, 2048}.
  *  prefixes    HOST array of n_prefixes widths, read during the call only:
  *              strictly increasing multiples of 32, last <= D;
  *              1 <= n_prefixes <= 8.
@@ -242,10 +244,15 @@ size_t uform_contrastive_workspace_bytes_ex(int64_t R, int64_t N, int64_t D, int
  * is in uform_contrastive_last_error()).  The ladders are the nested prefixes
  * of the UForm README's Matryoshka paragraph ({64, 128, 256, 512, 1024} and
  * the shorter ladders of the narrower tiers); the statuses those of "UForm
- * for Swift", section "Errors".  The backward is compiled for the
+ * for Swift", section "Errors".  The backward has kernels compiled for the
  * ladders {64,128,256,512,1024}, {64,128,256,512}, {64,128,256}, {64,128}
- * and the single widths {128}, {256}, {512}, {1024}; a softmax call without
- * gradients accepts any valid ladder. */
+ * and the single widths {128}, {256}, {512}, {1024} (the fast path); every
+ * other ladder, and every width above 1024 (the Large and XL tiers'
+ * {64, ..., 1024, 2048}), takes a generic backward that reads the ladder at
+ * run time.  Its LDS bounds the ladders it takes: above 1024 at most 6
+ * prefixes, at most 3 of them ending strictly inside a quarter of the widest
+ * (as 64, 128 and 256 do in {64, ..., 2048}); a ladder past that is
+ * unsupported.  A softmax call without gradients accepts any valid ladder. */
 uform_status_t uform_contrastive_supported(int64_t D, const int32_t *prefixes, int32_t n_prefixes, int32_t kind,
                                           int32_t with_gradients);
 

@@ -108,8 +108,11 @@ def test_invalid_arguments_are_rejected_on_the_host(kw):
 
 
 UNSUPPORTED = [
-    dict(D=1000, prefixes=[64, 992]), dict(D=2048, prefixes=[64, 2048]), dict(scale=50.0),
-    dict(prefixes=[96, 1024]),  # no compiled backward for this ladder
+    dict(D=1000, prefixes=[64, 992]), dict(D=4096, prefixes=[64, 4096]), dict(D=2112, prefixes=[64, 2112]),
+    dict(scale=50.0),
+    # the generic backward's LDS at widths above 1024: at most 6 prefixes, 3 of them inside a quarter
+    dict(D=2048, prefixes=[64, 128, 256, 384, 1024, 2048]),
+    dict(D=2048, prefixes=[64, 128, 256, 512, 1024, 1536, 2048]),
 ]
 
 
@@ -168,11 +171,15 @@ def test_compiled_ladders_are_supported(D, prefixes, kind):
     assert binding.supported(D, prefixes, kind) == 0, binding.last_error()
 
 
-@pytest.mark.parametrize("prefixes", [(96, 1024), (64, 256, 1024), (32, 64), (64, 128, 256, 512, 768)])
-def test_other_ladders_need_the_forward_only(prefixes):
-    assert binding.supported(1024, prefixes, 0) == 2
-    assert binding.supported(1024, prefixes, 1, with_gradients=False) == 2  # SigLIP's loss needs the backward
-    assert binding.supported(1024, prefixes, 0, with_gradients=False) == 0
+@pytest.mark.parametrize("D,prefixes", [
+    (1024, (96, 1024)), (1024, (64, 256, 1024)), (1024, (32, 64)), (1024, (64, 128, 256, 512, 768)),
+    (256, tuple(range(32, 257, 32))), (2048, (64, 128, 256, 512, 1024, 2048)), (2048, (2048,)),
+    (1536, (64, 128, 256, 512, 1024, 1536)), (2048, (512, 1024, 1536, 2048))])
+@pytest.mark.parametrize("kind", [0, 1, 2, 3, 4])
+def test_every_other_ladder_takes_the_generic_backward(D, prefixes, kind):
+    # ladders without a compiled backward, and the wide tiers' ladders, have gradients too
+    assert binding.supported(D, prefixes, kind) == 0, binding.last_error()
+    assert binding.supported(D, prefixes, kind, with_gradients=False) == 0
 
 
 @pytest.mark.parametrize("kind,R,N,off,row_ptr,col", [

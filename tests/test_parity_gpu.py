@@ -594,3 +594,86 @@ def test_oneset_relations_confident():
     assert np.abs(dq.cpu().numpy() - ref["dq"]).max() <= 2e-3 * np.abs(ref["dq"]).max()
     assert ex["dscale"].item() == pytest.approx(ref["dscale"], rel=1e-3, abs=1e-7)
     assert ex["dbias"].item() == pytest.approx(ref["dbias"], rel=1e-3, abs=1e-7)
+
+
+# ----------------------------------------------------------------------------- generic backward: wide rows, any ladder
+
+XL = (64, 128, 256, 512, 1024, 2048)  # the Large and XL tiers' prefixes
+
+
+@pytest.mark.parametrize("case", ["infonce", "siglip", "rows", "oneset", "relations", "band"])
+def test_wide_rows_2048(case):
+    # D = 2048 with the wide tiers' six prefixes, through the generic backward, every kind
+    from contrastive_embedding_loss_amd.inputs import ONESET_SIGLIP, ONESET_SIGLIP_EDGES, make_band_inputs, \
+        random_edge_lists, share_lists
+    from oracle import ONESET_EDGES
+    D, w = 2048, (1, 1, 1, 1, 1, 2)
+    if case == "infonce":
+        qb, kb = make_inputs(160, 160, D, noise=0.5, seed=261)
+        got, ref = run_both(qb, kb, XL, 1 / 0.07, 0.0, INFONCE, weights=w, label="wide")
+        check(got, ref, INFONCE)
+    elif case == "siglip":
+        qb, kb = make_inputs(200, 200, D, noise=0.5, seed=262)
+        got, ref = run_both(qb, kb, XL, 10.0, -10.0, SIGLIP, weights=w, label="wide")
+        check(got, ref, SIGLIP)
+    elif case == "rows":
+        qb, kb = make_inputs(96, 352, D, recipe="clustered", noise=0.2, seed=263, centroids=16, row_offset=128)
+        got, ref = run_both(qb, kb, XL, 1 / 0.07, 0.0, INFONCE_ROWS, weights=w, off=128, label="wide")
+        check(got, ref, INFONCE_ROWS)
+    elif case == "oneset":
+        from oracle import ONESET_SIGLIP as O3
+        qb, kb = make_inputs(96, 256, D, recipe="pairs", noise=0.6, seed=264, row_offset=64)
+        k = to_dev(kb)
+        loss, dq, _, ex = binding.fwd_bwd(k[64:160], k, XL, 10.0, -6.0, ONESET_SIGLIP, weights=w, row_offset=64,
+                                          extras=True)
+        torch.cuda.synchronize()
+        ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), XL, 10.0, -6.0, O3, weights=w,
+                                  row_offset=64)
+        assert abs(loss.item() - ref["loss"]) <= 1e-3 * abs(ref["loss"])
+        assert np.abs(dq.cpu().numpy() - ref["dq"]).max() <= 2e-3 * np.abs(ref["dq"]).max()
+        assert ex["dscale"].item() == pytest.approx(ref["dscale"], rel=1e-3, abs=1e-6)
+    elif case == "relations":
+        N, R, off = 257, 100, 90
+        qb, kb = make_inputs(R, N, D, noise=0.6, seed=265, row_offset=off)
+        lists = random_edge_lists(N, 3.0, seed=266, far=6, lonely=4)
+        pos = share_lists(lists, off, R)
+        k = to_dev(kb)
+        loss, dq, _, ex = binding.fwd_bwd(k[off:off + R], k, XL, 10.0, -6.0, ONESET_SIGLIP_EDGES, weights=w,
+                                          row_offset=off, extras=True, positives=pos)
+        torch.cuda.synchronize()
+        qb = kb[off:off + R]
+        ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), XL, 10.0, -6.0, ONESET_EDGES,
+                                  weights=w, row_offset=off, positives=pos)
+        assert abs(loss.item() - ref["loss"]) <= 1e-3 * abs(ref["loss"])
+        assert np.abs(dq.cpu().numpy() - ref["dq"]).max() <= 2e-3 * np.abs(ref["dq"]).max()
+        assert ex["dbias"].item() == pytest.approx(ref["dbias"], rel=1e-3, abs=1e-6)
+    else:
+        qb, kb, rp, col = make_band_inputs(120, D, 2, 2, noise=0.5, seed=267)
+        _pos_case(qb, kb, XL, 10.0, -10.0, SIGLIP, 0, (rp, col), label="wide band")
+
+
+@pytest.mark.parametrize("D,prefixes,kind", [
+    (1024, (96, 1024), INFONCE), (1024, (64, 256, 1024), SIGLIP), (64, (32, 64), INFONCE),
+    (768, (64, 128, 256, 512, 768), INFONCE_ROWS), (256, tuple(range(32, 257, 32)), INFONCE),
+    (1536, (64, 128, 256, 512, 1024, 1536), SIGLIP), (2048, (2048,), INFONCE), (2048, (512, 1024, 1536, 2048), SIGLIP),
+    (320, (32, 160, 288), SIGLIP)])
+def test_generic_backward_ladders(D, prefixes, kind):
+    # ladders without a compiled backward: prefix ends anywhere on 32-wide steps, up to 8 prefixes
+    R, N, off = (150, 150, 0) if kind != INFONCE_ROWS else (70, 230, 100)
+    qb, kb = make_inputs(R, N, D, noise=0.5, seed=271 + D + len(prefixes), row_offset=off)
+    got, ref = run_both(qb, kb, prefixes, 11.0, -3.0 if kind == SIGLIP else 0.0, kind, off=off, label="generic")
+    check(got, ref, kind)
+
+
+def test_generic_backward_one_split_and_accumulate():
+    # one inner split (the generic backward still finishes through k_finalize) and accumulate
+    qb, kb = make_inputs(130, 130, 2048, noise=0.5, seed=281)
+    q, k = to_dev(qb), to_dev(kb)
+    a = binding.fwd_bwd(q, k, XL, 12.0, 0.0, INFONCE)
+    b = binding.fwd_bwd(q, k, XL, 12.0, 0.0, INFONCE, one_split=True)
+    dq0 = torch.full_like(a[1], 0.5)
+    c = binding.fwd_bwd(q, k, XL, 12.0, 0.0, INFONCE, dq=dq0.clone(), accumulate=True, want_dk=False)
+    torch.cuda.synchronize()
+    scale = a[1].abs().max().item()
+    assert (a[1] - b[1]).abs().max().item() <= 1e-4 * scale and (a[2] - b[2]).abs().max().item() <= 1e-4 * scale
+    assert (c[1] - (a[1] + 0.5)).abs().max().item() <= 1e-4 * scale + 1e-6

@@ -141,3 +141,31 @@ def test_large_workload_whole_tensors_against_live_oracle(name):
         errs[n] = e
         assert e <= 1e-3, (n, e)
     print(f"[parity] {name} " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_wide_8192_against_live_oracle(kind):
+    # the wide tiers at a full batch: R = N = 8192 rows of 2048, prefixes {64, ..., 1024, 2048}
+    from contrastive_embedding_loss_amd.inputs import make_inputs
+    R, D, pf = 8192, 2048, (64, 128, 256, 512, 1024, 2048)
+    s, b = (1 / 0.07, 0.0) if kind == 0 else (10.0, -10.0)
+    print(f"[case] wide R=N={R} D={D} kind={kind}", flush=True)
+    qb, kb = make_inputs(R, R, D, noise=0.5, seed=291 + kind)
+    q = torch.from_numpy(bf16_bits_to_f32(qb)).to("cuda").to(torch.bfloat16)
+    k = torch.from_numpy(bf16_bits_to_f32(kb)).to("cuda").to(torch.bfloat16)
+    loss, dq, dk, ex = binding.fwd_bwd(q, k, pf, s, b, kind, extras=True)
+    torch.cuda.synchronize()
+    ref = contrastive_fwd_bwd(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), pf, s, b, kind)
+    assert abs(loss.item() - ref["loss"]) <= 1e-3 * abs(ref["loss"]), (loss.item(), ref["loss"])
+    np.testing.assert_allclose(ex["prefix_losses"].cpu().numpy(), ref["prefix_losses"], rtol=1e-3)
+    errs = {}
+    for name, g in (("dq", dq), ("dk", dk)):
+        e = np.abs(g.cpu().numpy() - ref[name]).max() / np.abs(ref[name]).max()
+        errs[name] = e
+        assert e <= 2e-3, (name, e)
+    assert np.abs(ex["pos_logit"].cpu().numpy() - ref["pos_logit"]).max() <= 1e-3
+    if kind == 0:
+        assert np.abs(ex["row_lse"].cpu().numpy() - ref["row_lse"]).max() <= 1e-3
+        assert np.abs(ex["col_lse"].cpu().numpy() - ref["col_lse"]).max() <= 1e-3
+    print(f"[parity] wide 8192 kind={kind} " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+    check_properties(type("W", (), {"prefixes": pf, "D": D})(), q, k, dq, dk)
