@@ -40,7 +40,7 @@ def measured_traffic(workload: str):
     for line in open(path):
         if line.startswith("traffic-record "):
             kv = dict(f.split("=", 1) for f in line.split()[1:])
-            if kv.get("kernel") == "k_bwd" and kv.get("source_sha256_16") == sha:
+            if kv.get("kernel") in ("k_bwd", "k_bwd_gen") and kv.get("source_sha256_16") == sha:
                 return int(kv["read_bytes"]) + int(kv["write_bytes"])
     return None
 
@@ -142,10 +142,13 @@ def main():
     # Algorithmic MFMA work credited to one launch: 3 R N D = its gradient contraction 2 R N D
     # plus half of the single logit recompute 2 R N D that the step's count includes (each
     # launch actually executes a full recompute, 4 R N D in all; the extra is not credited).
+    # (the compiled backward k_bwd, or the generic one for ladders without a compiled kernel and rows
+    # wider than 1024)
     launches = 1 if oneset else 2
-    bwd_ms = kern_per_step.get("k_bwd", float("nan")) / launches
+    bwd_name = "k_bwd" if "k_bwd" in kern_per_step else "k_bwd_gen"
+    bwd_ms = kern_per_step.get(bwd_name, float("nan")) / launches
     bwd_tflops = (4.0 if oneset else 3.0) * R * N * D / (bwd_ms * 1e-3) / 1e12
-    roofline = {"kernel": "k_bwd", "bound": "mfma", "achieved": round(bwd_tflops, 1),
+    roofline = {"kernel": bwd_name, "bound": "mfma", "achieved": round(bwd_tflops, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(w.name), "avg_launch_ms": round(bwd_ms, 4),
                 "executed_tflops": round(4.0 * R * N * D / (bwd_ms * 1e-3) / 1e12, 1)}

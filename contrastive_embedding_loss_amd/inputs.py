@@ -206,6 +206,13 @@ WORKLOADS["siglip_band_16384"] = Workload(
     noise=0.5, seed=6, extra={"extra_pos": 2, "hard_neg": 2, "hard_noise": 1.0})
 
 
+# The Large and XL tiers' width: 8192 x 8192 rows of 2048 with prefixes {64, ..., 1024, 2048}
+# (UForm README, tier table and Matryoshka paragraph), the last prefix weighted 2.
+WORKLOADS["infonce_8192_d2048"] = Workload(
+    "infonce_8192_d2048", INFONCE, 8192, 8192, D=2048, prefixes=(64, 128, 256, 512, 1024, 2048),
+    weights=(1, 1, 1, 1, 1, 2), noise=0.5, seed=7)
+
+
 def workload_positives(w: Workload):
     """The extra-positive lists of a workload (band recipe), else None."""
     if w.recipe != "band":

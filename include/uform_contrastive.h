@@ -226,8 +226,9 @@ uform_status_t uform_contrastive_fwd_bwd_noalloc(const void *q, const void *k, i
                                                  float bias, int32_t kind, float *loss_out, float *dq, float *dk,
                                                  hipStream_t stream, const uform_contrastive_options_t *options);
 
-/* Device workspace a call of this shape needs, in bytes (gradients included);
- * 0 for arguments the call would reject.  The size of the caller-lent memory
+/* Device workspace a call of this shape needs, in bytes (gradients included,
+ * enough for any prefix ladder of this count up to D); 0 for arguments the call
+ * would reject.  The size of the caller-lent memory
  * of the options' workspace ("UForm for Swift", section "Arenas": the caller
  * sizes the memory a call lands in, and a loop that reuses it allocates once). */
 size_t uform_contrastive_workspace_bytes(int64_t R, int64_t N, int64_t D, int32_t n_prefixes, int32_t kind);

@@ -369,9 +369,11 @@ def test_positive_list_edge_cases():
     own = binding.fwd_bwd(q, k, LADDER, 10.0, -10.0, SIGLIP, row_offset=30, positives=pos, workspace=ws)
     for a, b in zip(full, own):
         assert torch.equal(a, b)
-    # a list one byte short of its workspace is refused before any launch
+    # a workspace too small for the call (here one without room for the lists' tables) is refused
+    # before any launch
     with pytest.raises(binding.UformError):
-        binding.fwd_bwd(q, k, LADDER, 10.0, -10.0, SIGLIP, row_offset=30, positives=pos, workspace=ws[:nbytes - 512])
+        binding.fwd_bwd(q, k, LADDER, 10.0, -10.0, SIGLIP, row_offset=30, positives=pos,
+                        workspace=ws[:binding.workspace_bytes(100, 160, 1024, len(LADDER), SIGLIP) // 4])
     torch.cuda.synchronize()
 
 
