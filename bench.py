@@ -157,8 +157,8 @@ def main():
     n_jt, n_it = -(-N // 128), -(-R // 128)
     stage_bytes = {
         "k_prep": (R + N) * D * 2 + 4 * ((R + N) * (3 * P + 2) + R * P),
-        "k_rowstats": 4 * R * P * (2 * n_jt + 9),
-        "k_colstats": 4 * N * P * (2 * n_it + 9),
+        "k_rowstats": 4 * R * P * (n_jt + 9),
+        "k_colstats": 4 * N * P * (n_it + 9),
     }
     hbm_stages = {}
     for name, nbytes in stage_bytes.items():

@@ -230,9 +230,9 @@ Plan make_plan(int64_t R, int64_t N, int64_t D, const int32_t *pw, int32_t P, in
     const bool bwd = want_dq || want_dk || !softmax;  // some backward pass runs
     p.o_qH = take(bwd ? sizeof(u16) * bwd_padded_rows(R) * D : 0);
     p.o_kH = take(bwd ? sizeof(u16) * bwd_padded_rows(N) * D : 0);
-    // forward partials: one per wave column (row partials) / wave row (column partials) of a tile
-    p.o_rowpart = take(softmax ? sizeof(float) * 2 * p.nJt * P * R : 0);
-    p.o_colpart = take(softmax ? sizeof(float) * 2 * p.nIt * P * N : 0);
+    // forward partials: one per tile (row partials per column tile, column partials per row tile)
+    p.o_rowpart = take(softmax ? sizeof(float) * p.nJt * P * R : 0);
+    p.o_colpart = take(softmax ? sizeof(float) * p.nIt * P * N : 0);
     // gradient partials only with inner splits (one split: the backward finishes the rows in place;
     // the generic backward always leaves its rows to k_finalize)
     const size_t part_row = (want_dq && (p.nsplit_row > 1 || p.gen)) ? sizeof(float) * p.nsplit_row * R * D : 0;
@@ -640,8 +640,8 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     sa.pxor = pxor;
     sa.nopos = nopos ? 1 : 0;
     sa.mirror = mirror;
-    sa.nJt = 2 * pl.nJt;  // partials per row: two per column tile
-    sa.nIt = 2 * pl.nIt;
+    sa.nJt = pl.nJt;  // partials per row: one per column tile
+    sa.nIt = pl.nIt;
     sa.pf = pf;
     sa.kind = kind;
     sa.scale = scale;

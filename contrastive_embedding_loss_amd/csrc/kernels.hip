@@ -279,17 +279,27 @@ __global__ __launch_bounds__(256) void k_half_copy(const u16 *__restrict__ x, co
 // FP32 accumulators are read in place ("snapshotted") and each cell's
 // e = 2^(S a_i ik_j + c) is added to a row partial and a column partial; the
 // positive cell is left out of both (the statistics kernel adds it back from
-// an exact FP32 dot product).  Writes rowpart[jt][p][i] and colpart[it][p][j].
+// an exact FP32 dot product).  Each wave keeps its reduced partials (one row
+// and one column value per lane and prefix) until the sweep ends; then the two
+// waves that share a row (a column) add theirs through LDS and the tile writes
+// one partial per row and per column: rowpart[jt][p][i], colpart[it][p][j].
 // ----------------------------------------------------------------------------
 constexpr int FB = 128;
 constexpr int FK = 64;
+
+// A snapshot of prefix p: this lane's row sum (row fwd_lane_row(wi, lane) of the tile, over the
+// wave's 64 columns) into rkeep[p] and its column sum (column 64 wj + lane, over the wave's 64
+// rows) into ckeep[p].
+__device__ __forceinline__ int fwd_lane_row(int wi, int lane) {
+    const int v = lane & 31, bi = v >> 4, r = v & 15;
+    return wi * 64 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
 
 template <bool MASKED>
 __device__ __forceinline__ void fwd_snapshot(const f32x16 (&acc)[2][2], int p, int wi, int wj, int lane, int tid,
                                              int64_t i0, int64_t j0, int64_t R, int64_t N, int64_t off, int P,
                                              float cshift, const float (*fA)[FB], const float (*fI)[FB],
-                                             int64_t it, int64_t jt,
-                                             float *__restrict__ rowpart, float *__restrict__ colpart) {
+                                             float (&rkeep)[kMaxP], float (&ckeep)[kMaxP]) {
     float rs[32];
     float cs[2];
     float Ij[2];
@@ -322,19 +332,37 @@ __device__ __forceinline__ void fwd_snapshot(const f32x16 (&acc)[2][2], int p, i
     }
     // row sums: lane (lane & 31) of each half ends up with row index v = lane & 31
     const float rv = reduce_scatter32(rs, lane);
-    {
-        // row partial of this wave's 64 columns: rowpart[2 jt + wj][p][row]
-        const int v = lane & 31, bi = v >> 4, r = v & 15;
-        const int il = wi * 64 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t gi = i0 + il;
-        if (gi < R) rowpart[((2 * jt + wj) * P + p) * R + gi] = rv;
-    }
-    {
-        // column partial of this wave's 64 rows: lanes 0..31 column block 0, 32..63 block 1
-        const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(cs[0]), __float_as_uint(cs[1]), false, false);
-        const float cv = __uint_as_float(c[0]) + __uint_as_float(c[1]);
-        const int64_t g = j0 + wj * 64 + lane;
-        if (g < N) colpart[((2 * it + wi) * P + p) * N + g] = cv;
+    // column sums of this wave's 64 rows: lanes 0..31 column block 0, 32..63 block 1
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(cs[0]), __float_as_uint(cs[1]), false, false);
+    const float cv = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+#pragma unroll
+    for (int q = 0; q < kMaxP; ++q)
+        if (q == p) {
+            rkeep[q] = rv;
+            ckeep[q] = cv;
+        }
+}
+
+// The tile's partials: the two waves of a row (of a column) add theirs in LDS (the operand ring,
+// free after the sweep), and the tile writes one partial per row and per column.
+__device__ __forceinline__ void fwd_write_partials(float *lds, const float (&rkeep)[kMaxP], const float (&ckeep)[kMaxP],
+                                                   int wi, int wj, int lane, int tid, int P, int64_t i0, int64_t j0,
+                                                   int64_t R, int64_t N, int64_t it, int64_t jt,
+                                                   float *__restrict__ rowpart, float *__restrict__ colpart) {
+    float *rl = lds, *cl = lds + 2 * kMaxP * FB;  // [2][kMaxP][FB] each
+    lds_barrier();  // every wave is done with the ring
+    const int il = fwd_lane_row(wi, lane);
+#pragma unroll
+    for (int p = 0; p < kMaxP; ++p)
+        if (p < P) {
+            rl[(wj * kMaxP + p) * FB + il] = rkeep[p];
+            cl[(wi * kMaxP + p) * FB + wj * 64 + lane] = ckeep[p];
+        }
+    lds_barrier();
+    for (int e = tid; e < P * FB; e += 256) {
+        const int p = e / FB, x = e % FB;
+        if (i0 + x < R) rowpart[(jt * P + p) * R + i0 + x] = rl[p * FB + x] + rl[(kMaxP + p) * FB + x];
+        if (j0 + x < N) colpart[(it * P + p) * N + j0 + x] = cl[p * FB + x] + cl[(kMaxP + p) * FB + x];
     }
 }
 
@@ -427,6 +455,9 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    float rkeep[kMaxP], ckeep[kMaxP];  // this lane's row and column partial of every prefix
+#pragma unroll
+    for (int q = 0; q < kMaxP; ++q) rkeep[q] = ckeep[q] = 0.f;
 
     if constexpr (MASK != 0u) {
         // Prefix ladder known at compile time: no branch inside a slice.  The ring holds four
@@ -533,11 +564,9 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
                 slice(std::true_type{});
             }
             if (masked)
-                fwd_snapshot<true>(acc, p, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, it, jt, rowpart,
-                                   colpart);
+                fwd_snapshot<true>(acc, p, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, rkeep, ckeep);
             else
-                fwd_snapshot<false>(acc, p, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, it, jt, rowpart,
-                                    colpart);
+                fwd_snapshot<false>(acc, p, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, rkeep, ckeep);
         });
     } else {
     const int nst = (Dsw + FK - 1) / FK;
@@ -572,17 +601,19 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
                         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
                 if (pnext < P && dk + 16 == pf.w[pnext]) {
                     if (masked)
-                        fwd_snapshot<true>(acc, pnext, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, it,
-                                           jt, rowpart, colpart);
+                        fwd_snapshot<true>(acc, pnext, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, rkeep,
+                                           ckeep);
                     else
-                        fwd_snapshot<false>(acc, pnext, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, it,
-                                            jt, rowpart, colpart);
+                        fwd_snapshot<false>(acc, pnext, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, rkeep,
+                                            ckeep);
                     ++pnext;
                 }
             }
         }
     }
     }
+    fwd_write_partials(reinterpret_cast<float *>(&Ring[0][0][0]), rkeep, ckeep, wi, wj, lane, tid, P, i0, j0, R, N,
+                       it, jt, rowpart, colpart);
 }
 
 // ----------------------------------------------------------------------------

@@ -212,8 +212,7 @@ uform_status_t uform_contrastive_fwd_bwd_ex(const void *q, const void *k, int64_
  * UFORM_CONTRASTIVE_NOALLOC_SCRATCH_BYTES bytes per GPU, held from the first use
  * of the library on that GPU until the process ends; the call allocates
  * nothing (no hipMalloc, no pinned or event allocation).  A call whose
- * workspace would exceed the array (uform_contrastive_workspace_bytes > 128 MiB,
- * e.g. 8192 x 8192 InfoNCE) returns unsupported; so does a call with positive
+ * workspace would exceed the array (e.g. 16384 x 16384 InfoNCE) returns unsupported; so does a call with positive
  * lists or UFORM_CONTRASTIVE_PROFILE; options->workspace must be NULL
  * (invalid-argument otherwise).  Every call on one GPU shares that GPU's
  * array: calls that overlap on one GPU (on different streams, or from

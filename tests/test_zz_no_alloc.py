@@ -53,8 +53,8 @@ def test_noalloc_refuses_what_it_cannot_hold():
     with pytest.raises(binding.UformError):
         binding.fwd_bwd(q, k, LADDER, 10.0, -10.0, SIGLIP, noalloc=True,
                         positives=(np.zeros(65, dtype=np.int64), np.zeros(0, dtype=np.int32)))
-    # 8192 x 8192 InfoNCE needs more than the 128 MiB of scratch: refused before any launch
-    big = torch.zeros(8192, 1024, dtype=torch.bfloat16, device="cuda")
+    # 16384 x 16384 InfoNCE needs more than the 128 MiB of scratch: refused before any launch
+    big = torch.zeros(16384, 1024, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(binding.UformError) as e:
         binding.fwd_bwd(big, big, LADDER, 14.0, 0.0, INFONCE, noalloc=True)
     assert e.value.status == 2 and "scratch" in e.value.message
