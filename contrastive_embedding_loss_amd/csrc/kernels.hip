@@ -646,15 +646,19 @@ __device__ __forceinline__ float fold_partials(const float *part, int64_t ntiles
     const int g = threadIdx.x / kStatRows, rl = threadIdx.x % kStatRows;
     float v = 0.f;
     if (ok) {
-        // four independent running sums (loads in flight), added in a fixed order
+        // eight independent running sums (eight loads in flight per lane), added in a fixed order
         const int W = (int)(blockDim.x / 64);
-        float u[4] = {0.f, 0.f, 0.f, 0.f};
+        float u[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         int64_t t = g;
-        for (; t + 3 * W < ntiles; t += 4 * W)
+        for (; t + 7 * W < ntiles; t += 8 * W) {
+            float x[8];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) u[k] += part[((t + W * k) * P + p) * len + r];
+            for (int k = 0; k < 8; ++k) x[k] = part[((t + W * k) * P + p) * len + r];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) u[k] += x[k];
+        }
         for (; t < ntiles; t += W) u[0] += part[(t * P + p) * len + r];
-        v = (u[0] + u[1]) + (u[2] + u[3]);
+        v = ((u[0] + u[1]) + (u[2] + u[3])) + ((u[4] + u[5]) + (u[6] + u[7]));
     }
     fold[g][rl] = v;
     __syncthreads();
