@@ -139,13 +139,20 @@ __device__ __forceinline__ void dma4_m0(const void *g, uint32_t m0v) {
 // ----------------------------------------------------------------------------
 constexpr int kPrepRows = 64;  // most rows per workgroup
 
-// inclusive prefix sum over the 64 lanes
-__device__ __forceinline__ float wave_scan(float v, int lane) {
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) {
-        const float u = __shfl_up(v, k);
-        v += lane >= k ? u : 0.f;
-    }
+// inclusive prefix sum over the 64 lanes, in DPP moves (no LDS round trips): shifts by 1, 2, 4, 8
+// inside each row of 16 lanes (lanes shifted in from outside the row read 0), then lane 15 of
+// each row added to the row after it and lane 31 to rows 2 and 3
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_in(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, true));
+}
+__device__ __forceinline__ float wave_scan(float v, int) {
+    v += dpp_in<0x111, 0xf>(v);  // row_shr:1
+    v += dpp_in<0x112, 0xf>(v);  // row_shr:2
+    v += dpp_in<0x114, 0xf>(v);  // row_shr:4
+    v += dpp_in<0x118, 0xf>(v);  // row_shr:8
+    v += dpp_in<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_in<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
 
