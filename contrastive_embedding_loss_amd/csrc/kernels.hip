@@ -684,20 +684,32 @@ __device__ __forceinline__ void lead_sum_write(float v, float *dst) {
     }
 }
 
-__global__ __launch_bounds__(64 * kStatWaves) void k_rowstats(StatsArgs a) {
+// The lead threads (one per row) read every prefix's table entries of their row into LDS before
+// the folds, so that those reads are in flight during the folds rather than after each of them
+// (each lead thread reads back only what it wrote: no barrier).
+__global__ __launch_bounds__(64 * kStatWaves, 8) void k_rowstats(StatsArgs a) {  // two blocks per CU
     __shared__ float fold[kStatWaves][kStatRows];
-    const int64_t i = (int64_t)blockIdx.x * kStatRows + threadIdx.x % kStatRows;
+    __shared__ float tab[5][kMaxP][kStatRows];  // inv_q, inv_k of the positive, posdot, qA, qIYR
+    const int rl = threadIdx.x % kStatRows;
+    const int64_t i = (int64_t)blockIdx.x * kStatRows + rl;
     const bool lead = threadIdx.x < kStatRows;
+    const bool mine = lead && i < a.R;
     const int P = a.pf.n;
+    if (mine)
+        for (int p = 0; p < P; ++p) {
+            tab[0][p][rl] = a.invq[p * a.R + i];
+            tab[1][p][rl] = a.invk[p * a.N + ((i + a.off) ^ a.pxor)];
+            tab[2][p][rl] = a.posdot[p * a.R + i];
+            tab[3][p][rl] = a.qA[p * a.R + i];
+            tab[4][p][rl] = a.qIYR[p * a.R + i];
+        }
     for (int p = 0; p < P; ++p) {
         float ce = 0.f;
         const float negsum = fold_partials(a.rowpart, a.nJt, P, p, a.R, i, i < a.R, fold);
-        if (lead && i < a.R) {
+        if (mine) {
             const float neg = negsum;
-            const float iq = a.invq[p * a.R + i], ik = a.invk[p * a.N + ((i + a.off) ^ a.pxor)];
-            const float S = a.posdot[p * a.R + i];
-            const float A = a.qA[p * a.R + i];
-            const float x = fmaf(S * A, ik, a.cshift);
+            const float iq = tab[0][p][rl], ik = tab[1][p][rl], S = tab[2][p][rl], iqP = tab[0][P - 1][rl];
+            const float x = fmaf(S * tab[3][p][rl], ik, a.cshift);
             const float epos = __builtin_amdgcn_exp2f(x);
             const float Z = neg + epos;
             ce = ce_from(neg, epos, x, Z);
@@ -706,47 +718,57 @@ __global__ __launch_bounds__(64 * kStatWaves) void k_rowstats(StatsArgs a) {
             const float invZ = 1.0f / Z;
             a.negfrac[p * a.R + i] = neg * invZ;
             // band-operand scale: beta_p / gam = sgn w_p inv_p / inv_P (folded into the exponent)
-            const float iqP = a.invq[(P - 1) * a.R + i];
             a.qC[p * a.R + i] = a.cshift + log2f(a.wnorm[p] * iq / iqP);
             a.qRho[p * a.R + i] = a.sgn * invZ;
-            a.qKap[p * a.R + i] = a.sgn * invZ * a.qIYR[p * a.R + i];
+            a.qKap[p * a.R + i] = a.sgn * invZ * tab[4][p][rl];
             if (a.kind == kRows) a.diagA[p * a.R + i] = -a.wnorm[p] * a.scale * (neg * invZ) * a.inv_den * iq * ik;
         }
         lead_sum_write(ce, &a.lossparts[((int64_t)a.slot0 + blockIdx.x) * P + p]);
     }
 }
 
-__global__ __launch_bounds__(64 * kStatWaves) void k_colstats(StatsArgs a) {
+__global__ __launch_bounds__(64 * kStatWaves, 8) void k_colstats(StatsArgs a) {  // two blocks per CU
     __shared__ float fold[kStatWaves][kStatRows];
-    const int64_t j = (int64_t)blockIdx.x * kStatRows + threadIdx.x % kStatRows;
+    __shared__ float tab[5][kMaxP][kStatRows];  // inv_k, kIYR, inv_q and posdot * qA of the positive, row negfrac
+    const int rl = threadIdx.x % kStatRows;
+    const int64_t j = (int64_t)blockIdx.x * kStatRows + rl;
     const bool lead = threadIdx.x < kStatRows;
+    const bool mine = lead && j < a.N;
     const int P = a.pf.n;
+    const int64_t i = j - a.off;  // the query row whose positive is column j, if any
+    const bool haspos = mine && i >= 0 && i < a.R;
+    const bool sym = a.kind == kInfonce;
+    if (mine)
+        for (int p = 0; p < P; ++p) {
+            tab[0][p][rl] = a.invk[p * a.N + j];
+            tab[1][p][rl] = a.kIYR[p * a.N + j];
+            tab[2][p][rl] = haspos ? a.invq[p * a.R + i] : 0.f;
+            tab[3][p][rl] = haspos ? a.posdot[p * a.R + i] * a.qA[p * a.R + i] : 0.f;
+            tab[4][p][rl] = sym ? a.negfrac[p * a.R + j] : 0.f;
+        }
     for (int p = 0; p < P; ++p) {
         float ce = 0.f;
         const float negsum = fold_partials(a.colpart, a.nIt, P, p, a.N, j, j < a.N, fold);
-        if (lead && j < a.N) {
+        if (mine) {
             const float neg = negsum;
-            const float ik = a.invk[p * a.N + j];
-            const int64_t i = j - a.off;
-            float epos = 0.f, x = 0.f, iq = 0.f;
-            if (i >= 0 && i < a.R) {
-                iq = a.invq[p * a.R + i];
-                x = fmaf(a.posdot[p * a.R + i] * a.qA[p * a.R + i], ik, a.cshift);
+            const float ik = tab[0][p][rl], ikP = tab[0][P - 1][rl];
+            float epos = 0.f, x = 0.f;
+            if (haspos) {
+                x = fmaf(tab[3][p][rl], ik, a.cshift);
                 epos = __builtin_amdgcn_exp2f(x);
             }
             const float Z = neg + epos;
             if (a.col_lse_out) a.col_lse_out[p * a.N + j] = logf(Z) + a.lse_offset;
-            const float ikP = a.invk[(P - 1) * a.N + j];
             a.kC[p * a.N + j] = a.cshift + log2f(a.wnorm[p] * ik / ikP);
-            if (a.kind == kInfonce) {
+            if (sym) {
                 const float invZ = 1.0f / Z;
                 ce = ce_from(neg, epos, x, Z);
                 a.kNegfrac[p * a.N + j] = neg * invZ;
                 a.kRho[p * a.N + j] = a.sgn * invZ;
-                a.kKap[p * a.N + j] = a.sgn * invZ * a.kIYR[p * a.N + j];
+                a.kKap[p * a.N + j] = a.sgn * invZ * tab[1][p][rl];
                 // positive cell (j, j): g = -(neg_r / Z_r + neg_c / Z_c) / 2N
                 a.diagA[p * a.R + j] =
-                    -a.wnorm[p] * a.scale * (a.negfrac[p * a.R + j] + neg * invZ) * a.inv_den * iq * ik;
+                    -a.wnorm[p] * a.scale * (tab[4][p][rl] + neg * invZ) * a.inv_den * tab[2][p][rl] * ik;
             } else {
                 a.kRho[p * a.N + j] = 0.f;
                 a.kKap[p * a.N + j] = 0.f;
