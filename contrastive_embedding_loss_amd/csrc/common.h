@@ -39,6 +39,7 @@ struct PrepArgs {
     const u16 *q, *k;
     int64_t R, N, off;
     int pxor;  // positive of local row i: key (off + i) ^ pxor (1: the one-set form's pairs)
+    int want_pos;  // 1: the positive dot products (posdot) are formed here; 0: the forward writes them
     int D;
     Prefixes pf;
     float a_scale, gam_scale;
@@ -163,9 +164,10 @@ struct LossArgs {
 // launchers (kernels.hip)
 hipError_t launch_prep(const PrepArgs &a, hipStream_t s);
 hipError_t launch_half_copy(const u16 *x, const float *sig, int64_t rows, int D, _Float16 *xh, hipStream_t s);
+// (the forward also writes posdot[p][i], the prefix dot product of row i with its positive off + i)
 hipError_t launch_fwd(const u16 *q, const u16 *k, int64_t R, int64_t N, int D, const Prefixes &pf, int64_t off,
                       const float *rowA, const float *colI, float cshift, float *rowpart, float *colpart,
-                      hipStream_t s);
+                      float *posdot, hipStream_t s);
 hipError_t launch_rowstats(const StatsArgs &a, hipStream_t s);
 hipError_t launch_colstats(const StatsArgs &a, hipStream_t s);
 hipError_t launch_siglip_tabs(const StatsArgs &a, hipStream_t s);

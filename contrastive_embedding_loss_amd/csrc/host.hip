@@ -615,6 +615,7 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     pa.a_scale = scale * kLog2e;
     pa.gam_scale = (float)(mirror * abs_s / den);
     pa.pxor = pxor;
+    pa.want_pos = softmax ? 0 : 1;  // the softmax kinds' forward writes posdot from its diagonal tiles
     pa.invq = invq;
     pa.invk = invk;
     pa.qA = qA;
@@ -679,7 +680,7 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
 
     if (softmax) {
         LAUNCH_NAMED("k_fwd", launch_fwd(q, k, R, N, Di, pf, off, qA, invk, cshift, F(pl.o_rowpart),
-                                         F(pl.o_colpart), s));
+                                         F(pl.o_colpart), posdot, s));
         sa.slot0 = 0;
         LAUNCH_NAMED("k_rowstats", launch_rowstats(sa, s));
         sa.slot0 = pl.slots_a;

@@ -128,8 +128,9 @@ __device__ __forceinline__ void dma4_m0(const void *g, uint32_t m0v) {
 // ----------------------------------------------------------------------------
 // k_prep: per-prefix inverse L2 norms of every row (and s log2(e) times
 // them), the exact power-of-two row scale sig ~ 1/|row| and the backward's
-// per-row operand scale gam; for query rows also the prefix dot products
-// with their positive key.  A workgroup takes 4 RPW consecutive rows of the
+// per-row operand scale gam; for query rows of the sigmoid kinds also the prefix dot products
+// with their positive key (the softmax kinds' forward takes them from its diagonal tiles, so
+// that each row is read once here).  A workgroup takes 4 RPW consecutive rows of the
 // list (query rows, then key rows), a wave RPW of them (16, 4 or 1: enough
 // workgroups to fill the GPU), one at a time with the next row's loads in flight.  Lane l holds the 16-byte chunks
 // l, l + 64, ... of a row (NC of them: D <= 512 NC); prefix ends are multiples of 32, so no
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
 #pragma unroll
         for (int c = 0; c < NC; ++c)
             if (lane + 64 * c < nch) bx[s][c] = *(const uint4 *)(x + 8 * (lane + 64 * c));
-        if (isq) {
+        if (isq && a.want_pos) {
             const u16 *y = a.k + ((g + a.off) ^ a.pxor) * D;
 #pragma unroll
             for (int c = 0; c < NC; ++c)
@@ -216,7 +217,8 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
         float ss = 0.f, dt = 0.f;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const float Sc = wave_scan(sq8(bx[s][c]), lane), Tc = wave_scan(dot8(bx[s][c], by[s][c]), lane);
+            const float Sc = wave_scan(sq8(bx[s][c]), lane);
+            const float Tc = a.want_pos ? wave_scan(dot8(bx[s][c], by[s][c]), lane) : 0.f;
             const int at = min(max(m - 64 * c, 1), 64) - 1;
             const float av = __shfl(Sc, at), bv = __shfl(Tc, at);
             ss += m > 64 * c ? av : 0.f;
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
             (isq ? a.invq : a.invk)[p * nr + i] = inv;
             (isq ? a.qA : a.kA)[p * nr + i] = a.a_scale * inv;
             (isq ? a.qIYR : a.kIYR)[p * nr + i] = inv / sig;
-            if (isq) a.posdot[p * a.R + i] = res[r][kMaxP + p];
+            if (isq && a.want_pos) a.posdot[p * a.R + i] = res[r][kMaxP + p];
         } else {
             (isq ? a.sigq : a.sigk)[i] = sig;
             (isq ? a.gamq : a.gamk)[i] = a.gam_scale * res[r][P - 1];
@@ -306,7 +308,7 @@ template <bool MASKED>
 __device__ __forceinline__ void fwd_snapshot(const f32x16 (&acc)[2][2], int p, int wi, int wj, int lane, int tid,
                                              int64_t i0, int64_t j0, int64_t R, int64_t N, int64_t off, int P,
                                              float cshift, const float (*fA)[FB], const float (*fI)[FB],
-                                             float (&rkeep)[kMaxP], float (&ckeep)[kMaxP]) {
+                                             float (&rkeep)[kMaxP], float (&ckeep)[kMaxP], float *posdot) {
     float rs[32];
     float cs[2];
     float Ij[2];
@@ -331,6 +333,9 @@ __device__ __forceinline__ void fwd_snapshot(const f32x16 (&acc)[2][2], int p, i
                     const int64_t gi = i0 + il;
                     const bool ok = (gi < R) & (gj[bj] < N) & (gj[bj] != gi + off);
                     e[bj] = ok ? e[bj] : 0.f;
+                    // the positive cell (gi, off + gi) is in a masked tile: its prefix dot product, as the
+                    // MFMAs summed it, is the positive's logit input for the statistics and the backward
+                    if ((gi < R) & (gj[bj] == gi + off)) posdot[p * R + gi] = acc[bi][bj][r];
                 }
                 cs[bj] = (bi == 0 && r == 0) ? e[bj] : cs[bj] + e[bj];  // no addition of a zero start
             }
@@ -386,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
                                                 int64_t N, int D, Prefixes pf, int64_t off,
                                                 const float *__restrict__ rowA, const float *__restrict__ colI,
                                                 float cshift, float *__restrict__ rowpart,
-                                                float *__restrict__ colpart) {
+                                                float *__restrict__ colpart, float *__restrict__ posdot) {
     // Operand slices (128 rows x 64 bf16, 128 bytes per row) in a ring of two, copied
     // global -> LDS directly one slice ahead.  Rows are unpadded; the 16-byte chunk c of
     // row r sits at position c ^ ((r >> 1) & 7), so the MFMA operand reads (16 rows,
@@ -571,9 +576,9 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
                 slice(std::true_type{});
             }
             if (masked)
-                fwd_snapshot<true>(acc, p, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, rkeep, ckeep);
+                fwd_snapshot<true>(acc, p, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, rkeep, ckeep, posdot);
             else
-                fwd_snapshot<false>(acc, p, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, rkeep, ckeep);
+                fwd_snapshot<false>(acc, p, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, rkeep, ckeep, posdot);
         });
     } else {
     const int nst = (Dsw + FK - 1) / FK;
@@ -609,10 +614,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
                 if (pnext < P && dk + 16 == pf.w[pnext]) {
                     if (masked)
                         fwd_snapshot<true>(acc, pnext, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, rkeep,
-                                           ckeep);
+                                           ckeep, posdot);
                     else
                         fwd_snapshot<false>(acc, pnext, wi, wj, lane, tid, i0, j0, R, N, off, P, cshift, fA, fI, rkeep,
-                                            ckeep);
+                                            ckeep, posdot);
                     ++pnext;
                 }
             }
@@ -2033,7 +2038,7 @@ hipError_t launch_half_copy(const u16 *x, const float *sig, int64_t rows, int D,
 
 hipError_t launch_fwd(const u16 *q, const u16 *k, int64_t R, int64_t N, int D, const Prefixes &pf, int64_t off,
                       const float *rowA, const float *colI, float cshift, float *rowpart, float *colpart,
-                      hipStream_t s) {
+                      float *posdot, hipStream_t s) {
     const int64_t nIt = (R + FB - 1) / FB, nJt = (N + FB - 1) / FB;
     uint32_t mask = 0;  // compiled ladders end at or below 1024 (32 steps); wider lists run the run-time variant
     for (int p = 0; p < pf.n; ++p) mask |= pf.w[p] <= 1024 ? 1u << (pf.w[p] / 32 - 1) : 0u;
@@ -2042,13 +2047,13 @@ hipError_t launch_fwd(const u16 *q, const u16 *k, int64_t R, int64_t N, int D, c
 #define UFORM_CASE(m)                                                                                          \
     if (fwd_ladder(m) != 0u && mask == (m)) {                                                                  \
         hipLaunchKernelGGL(k_fwd<fwd_ladder(m)>, grid, dim3(256), 0, s, q, k, R, N, D, pf, off, rowA, colI, cshift, \
-                           rowpart, colpart);                                                                  \
+                           rowpart, colpart, posdot);                                                          \
         return hipGetLastError();                                                                              \
     }
     UFORM_LADDERS(UFORM_CASE)
 #undef UFORM_CASE
     hipLaunchKernelGGL(k_fwd<0u>, grid, dim3(256), 0, s, q, k, R, N, D, pf, off, rowA, colI, cshift, rowpart,
-                       colpart);
+                       colpart, posdot);
     return hipGetLastError();
 }
 
