@@ -86,6 +86,17 @@ def test_rows_clustered_with_offset():
     check(got, ref, INFONCE_ROWS)
 
 
+# Row shares whose positives (off + i) cross forward tiles at an unaligned offset: the forward takes
+# the positive cells' prefix dot products from its diagonal tiles, here split over two row tiles and
+# three column tiles, for the compiled ladder and for a ladder the forward runs with run-time ends.
+@pytest.mark.parametrize("R,N,off,D,prefixes", [
+    (200, 700, 333, 1024, LADDER), (150, 500, 77, 320, (96, 160, 320)), (1, 300, 299, 1024, LADDER)])
+def test_rows_unaligned_offset(R, N, off, D, prefixes):
+    qb, kb = make_inputs(R, N, D, noise=0.5, seed=61 + off, row_offset=off)
+    got, ref = run_both(qb, kb, prefixes, 1 / 0.07, 0.0, INFONCE_ROWS, off=off, label="rows-unaligned")
+    check(got, ref, INFONCE_ROWS)
+
+
 @pytest.mark.parametrize("D,prefixes,kind", [
     (512, (64, 128, 256, 512), INFONCE), (256, (256,), SIGLIP), (256, (64, 128, 256), INFONCE_ROWS),
     (128, (64, 128), INFONCE), (1024, (1024,), INFONCE), (512, (512,), SIGLIP), (128, (128,), INFONCE),
