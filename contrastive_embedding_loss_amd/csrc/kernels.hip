@@ -287,8 +287,9 @@ __global__ __launch_bounds__(256) void k_half_copy(const u16 *__restrict__ x, co
 // workgroups per CU; one barrier per slice).  At every prefix boundary the
 // FP32 accumulators are read in place ("snapshotted") and each cell's
 // e = 2^(S a_i ik_j + c) is added to a row partial and a column partial; the
-// positive cell is left out of both (the statistics kernel adds it back from
-// an exact FP32 dot product).  Each wave keeps its reduced partials (one row
+// positive cell is left out of both, and the masked tiles (which hold every
+// positive cell) write its raw prefix dot product to posdot, from which the
+// statistics kernels add it back in FP32.  Each wave keeps its reduced partials (one row
 // and one column value per lane and prefix) until the sweep ends; then the two
 // waves that share a row (a column) add theirs through LDS and the tile writes
 // one partial per row and per column: rowpart[jt][p][i], colpart[it][p][j].
