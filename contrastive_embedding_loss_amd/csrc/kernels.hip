@@ -1259,7 +1259,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
                     st.e[t] = sg * Co[p] * tb.iy[t];  // Co holds beta_o for the sigmoid form
                 }
             } else {
-                // the unmasked coefficient sigma(l) beta_o iy
+                // the unmasked coefficient sigma(l) beta_o iy, and the loss: softplus(l) / ln 2 =
+                // max(u, 0) + log2(1 + tt) per cell, the four cells' log2(1 + tt) taken as one
+                // log2 of the product of their (1 + tt) (each in (1, 2]), each with log1p's rounding
+                // corrected to first order
+                float prod = 1.f, lsum = 0.f;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const float uu = fmaf(st.e[t], tb.iy[t], a.b2);
@@ -1269,14 +1273,14 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
                     const float sg = uu >= 0.f ? rr : tt * rr;
                     st.e[t] = sg * Co[p] * tb.iy[t];  // Co holds beta_o for the sigmoid form
                     if constexpr (LOSS) {
-                        // softplus(l) / ln 2 = max(u, 0) + log2(1 + tt), with log1p's rounding corrected
                         const float corr = (tt - (wq - 1.f)) * rr * kLog2e;
-                        const float lt = fmaxf(uu, 0.f) + __builtin_amdgcn_logf(wq) + corr;
                         const bool in = !MK || __builtin_amdgcn_inverse_ballot_w64(mk[t]);
-                        Lacc[p] += in ? lt : 0.f;
-                        if constexpr (BIAS) Bacc[p] += in ? (uu >= 0.f ? rr : tt * rr) : 0.f;  // sigma(l), unscaled
+                        prod *= in ? wq : 1.f;
+                        lsum += in ? fmaxf(uu, 0.f) + corr : 0.f;
+                        if constexpr (BIAS) Bacc[p] += in ? sg : 0.f;  // sigma(l), unscaled
                     }
                 }
+                if constexpr (LOSS) Lacc[p] += __builtin_amdgcn_logf(prod) + lsum;
             }
         } else if constexpr (k == 2) {
             // a^p = e (Rho_o iy + Kap) (softmax) or e (sigmoid), masked
