@@ -26,10 +26,22 @@
 namespace uform {
 namespace {
 
+// Sum over the wave, in every lane, without LDS round trips: quad permutes (lanes 1 and 2 apart),
+// the half-row and row mirrors (the other quad, the other half-row), then the 16-lane and 32-lane
+// swaps add the partner row and the partner half-wave.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float wsum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
+    v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v += dpp_mov<0x141>(v);  // row_half_mirror
+    v += dpp_mov<0x140>(v);  // row_mirror
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(h[0]) + __uint_as_float(h[1]);
 }
 
 // 16 BF16 values (32 bytes, 16-byte aligned) widened to FP32.
