@@ -35,12 +35,6 @@ __device__ __forceinline__ void static_for(F &&f) {
 // small helpers
 // ----------------------------------------------------------------------------
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
-}
-
 __device__ __forceinline__ float bf16_lo(unsigned int v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned int v) { return __uint_as_float(v & 0xffff0000u); }
 
@@ -82,6 +76,19 @@ __device__ __forceinline__ float reduce_scatter32(float (&v)[32], int lane) {
     stage(std::integral_constant<int, 2>{}, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
     stage(std::integral_constant<int, 1>{}, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
     return v[0];
+}
+// Sum over the wave, in every lane, without LDS round trips: quad permutes (lanes 1 and 2 apart),
+// the half-row and row mirrors, then the 16-lane and 32-lane swaps add the partner row and the
+// partner half-wave.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v += dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x140>(v);  // row_mirror
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(h[0]) + __uint_as_float(h[1]);
 }
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
