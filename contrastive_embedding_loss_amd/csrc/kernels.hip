@@ -1892,16 +1892,41 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs a) {
     __shared__ float Cs[kMaxP];
     const int64_t o = blockIdx.x;
     const int P = a.pf.n;
+    const int D = a.D;
+    const int Dw = a.pf.w[P - 1];
     const int64_t ipos = o + a.pos_shift;  // index of the positive's query row in diagA/posdot
     const bool has_pos = ipos >= 0 && ipos < a.R;
     const int64_t ypos = (o + a.diag_shift) ^ a.pxor;  // positive's row in Y
+    // This thread's columns: groups of four, 4 (tid + 256 g) (prefix ends are multiples of 32,
+    // so a group lies in one band).  Their split partials and row values are loaded first, so
+    // that those loads are in flight during the table work below.
+    constexpr int GMAX = kMaxD / 1024;
+    float4 pv[GMAX];
+    uint2 xw[GMAX], yw[GMAX];
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+        const int d0 = 4 * ((int)threadIdx.x + 256 * g);
+        pv[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+        xw[g] = yw[g] = make_uint2(0u, 0u);
+        if (d0 < Dw) {
+            for (int64_t sp = 0; sp < a.nsplit; ++sp) {
+                const float4 u = *(const float4 *)(a.part + (sp * a.NO + o) * D + d0);
+                pv[g].x += u.x;
+                pv[g].y += u.y;
+                pv[g].z += u.z;
+                pv[g].w += u.w;
+            }
+            xw[g] = *(const uint2 *)(a.X + o * D + d0);
+            if (has_pos) yw[g] = *(const uint2 *)(a.Y + ypos * D + d0);
+        }
+    }
     // radial sums over the splits: wave p adds prefix p's partials (a fixed order per lane,
     // then a fixed tree across the lanes)
     {
         const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
         for (int p = wv; p < P; p += 4) {
             float c = 0.f;
-            for (int64_t s = ln; s < a.nsplit; s += 64) c += a.Cpart[(s * P + p) * a.NO + o];
+            for (int64_t sp = ln; sp < a.nsplit; sp += 64) c += a.Cpart[(sp * P + p) * a.NO + o];
             c = wave_sum(c);
             if (ln == 0) Cs[p] = c;
         }
@@ -1928,21 +1953,35 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs a) {
         if (a.tsum) a.tsum[o] = ts;
     }
     __syncthreads();
-    const int D = a.D;
-    const int Dw = a.pf.w[P - 1];
+    const float gm = a.gam[o];
     float *dst = a.out + o * D;
-    for (int d = threadIdx.x; d < D; d += 256) {
-        float v = 0.f;
-        if (d < Dw) {
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+        const int d0 = 4 * ((int)threadIdx.x + 256 * g);
+        if (d0 >= D) break;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (d0 < Dw) {
             int b = 0;
-            while (d >= a.pf.w[b]) ++b;
-            for (int s = 0; s < a.nsplit; ++s) v += a.part[((int64_t)s * a.NO + o) * D + d];
-            v *= a.gam[o];
-            const float xv = __uint_as_float((unsigned int)a.X[o * D + d] << 16);
-            const float yv = has_pos ? __uint_as_float((unsigned int)a.Y[ypos * D + d] << 16) : 0.f;
-            v = fmaf(DG[b], yv, fmaf(-RD[b], xv, v));
+            while (d0 >= a.pf.w[b]) ++b;
+            const float dgb = DG[b], rdb = RD[b];
+            const float p4[4] = {pv[g].x, pv[g].y, pv[g].z, pv[g].w};
+            const unsigned int xu[2] = {xw[g].x, xw[g].y}, yu[2] = {yw[g].x, yw[g].y};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float xv = (e & 1) ? bf16_hi(xu[e >> 1]) : bf16_lo(xu[e >> 1]);
+                const float yv = (e & 1) ? bf16_hi(yu[e >> 1]) : bf16_lo(yu[e >> 1]);
+                v[e] = fmaf(dgb, yv, fmaf(-rdb, xv, p4[e] * gm));
+            }
         }
-        dst[d] = a.accumulate ? dst[d] + v : v;
+        float4 *dp = (float4 *)(dst + d0);
+        if (a.accumulate) {
+            const float4 old = *dp;
+            v[0] += old.x;
+            v[1] += old.y;
+            v[2] += old.z;
+            v[3] += old.w;
+        }
+        *dp = make_float4(v[0], v[1], v[2], v[3]);
     }
 }
 
