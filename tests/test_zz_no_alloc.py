@@ -16,7 +16,7 @@ torch = pytest.importorskip("torch")
 
 from contrastive_embedding_loss_amd import binding  # noqa: E402
 from contrastive_embedding_loss_amd.inputs import (  # noqa: E402
-    INFONCE, SIGLIP, bf16_bits_to_f32, make_inputs)
+    INFONCE, INFONCE_ROWS, ONESET_SIGLIP, SIGLIP, bf16_bits_to_f32, make_inputs)
 
 pytestmark = pytest.mark.gpu
 LADDER = (64, 128, 256, 512, 1024)
@@ -37,6 +37,32 @@ def test_noalloc_matches_workspace_entry_point_on_two_calls(kind, s, b):
         torch.cuda.synchronize()
         assert abs(got[0].item() - ref[0].item()) <= 1e-3 * abs(ref[0].item())
         for a, c in ((got[1], ref[1]), (got[2], ref[2])):
+            assert (a - c).abs().max().item() <= 2e-3 * c.abs().max().item()
+            assert torch.equal(a, c)
+        for name in ref[3]:
+            assert torch.equal(got[3][name], ref[3][name]), name
+
+
+@pytest.mark.parametrize("kind", [INFONCE_ROWS, ONESET_SIGLIP])
+def test_noalloc_shares_on_two_calls(kind):
+    # a share of rows at an offset: inner splits, their partials and k_finalize in the scratch
+    # (the row kind), and the one-set form's single pass over its share
+    for R, N, off in ((256, 1024, 64), (100, 300, 33)):
+        print(f"[case] noalloc share kind={kind} R={R} N={N} off={off}", flush=True)
+        oneset = kind == ONESET_SIGLIP
+        qb, kb = make_inputs(R, N, 1024, recipe="pairs" if oneset else "gauss", noise=0.5, seed=261 + R,
+                             row_offset=off)
+        k = _dev(kb)
+        q = k[off:off + R] if oneset else _dev(qb)
+        s, b = (10.0, -6.0) if oneset else (14.0, 0.0)
+        ref = binding.fwd_bwd(q, k, LADDER, s, b, kind, row_offset=off, extras=True)
+        got = binding.fwd_bwd(q, k, LADDER, s, b, kind, row_offset=off, extras=True, noalloc=True)
+        torch.cuda.synchronize()
+        assert abs(got[0].item() - ref[0].item()) <= 1e-3 * abs(ref[0].item())
+        for a, c in ((got[1], ref[1]), (got[2], ref[2])):
+            if c is None:
+                assert a is None
+                continue
             assert (a - c).abs().max().item() <= 2e-3 * c.abs().max().item()
             assert torch.equal(a, c)
         for name in ref[3]:
