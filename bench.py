@@ -156,7 +156,10 @@ def main():
     # HBM-bound stages: algorithmic bytes (rows read once, tables and partials as laid out) per launch
     n_jt, n_it = -(-N // 128), -(-R // 128)
     stage_bytes = {
-        "k_prep": (R + N) * D * 2 + 4 * ((R + N) * (3 * P + 2) + R * P),
+        # rows read once, the tables, and the sig-scaled FP16 copies of both row sets (with the two zero
+        # blocks past each last row) that k_prep writes for the backward
+        "k_prep": (R + N) * D * 2 + 4 * ((R + N) * (3 * P + 2) + R * P)
+                  + ((-(-R // 16) + 2) * 16 + (-(-N // 16) + 2) * 16) * D * 2,
         "k_rowstats": 4 * R * P * (n_jt + 9),
         "k_colstats": 4 * N * P * (n_it + 9),
     }

@@ -45,6 +45,10 @@ struct PrepArgs {
     float a_scale, gam_scale;
     float *invq, *invk, *qA, *kA, *qIYR, *kIYR, *posdot, *sigq, *sigk, *gamq, *gamk;
     float *gmax;  // [4][P], zeroed here for k_maxes
+    // sig-scaled FP16 copies of the rows for the backward (nullptr: no backward runs), with their
+    // zero rows up to Rpad and Npad (the backward's copies run past the last block)
+    _Float16 *qH, *kH;
+    int64_t Rpad, Npad;
 };
 
 // Statistics / coefficient-table kernels.  "q" tables are [P][R], "k" tables [P][N].
@@ -163,7 +167,6 @@ struct LossArgs {
 
 // launchers (kernels.hip)
 hipError_t launch_prep(const PrepArgs &a, hipStream_t s);
-hipError_t launch_half_copy(const u16 *x, const float *sig, int64_t rows, int D, _Float16 *xh, hipStream_t s);
 // (the forward also writes posdot[p][i], the prefix dot product of row i with its positive off + i)
 hipError_t launch_fwd(const u16 *q, const u16 *k, int64_t R, int64_t N, int D, const Prefixes &pf, int64_t off,
                       const float *rowA, const float *colI, float cshift, float *rowpart, float *colpart,

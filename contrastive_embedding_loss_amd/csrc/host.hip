@@ -628,11 +628,12 @@ uform_status_t run(const void *q_, const void *k_, int64_t R, int64_t N, int64_t
     pa.gamq = gamq;
     pa.gamk = gamk;
     pa.gmax = F(pl.o_gmax);
+    const bool half = dq || dk || !softmax;  // some backward pass runs: k_prep writes its FP16 copies
+    pa.qH = half ? qH : nullptr;
+    pa.kH = half ? kH : nullptr;
+    pa.Rpad = bwd_padded_rows(R);
+    pa.Npad = bwd_padded_rows(N);
     LAUNCH_NAMED("k_prep", launch_prep(pa, s));
-    if (dq || dk || !softmax) {
-        LAUNCH_NAMED("k_half_copy", launch_half_copy(q, sigq, R, Di, qH, s));
-        LAUNCH_NAMED("k_half_copy", launch_half_copy(k, sigk, N, Di, kH, s));
-    }
 
     StatsArgs sa{};
     sa.R = R;

@@ -236,11 +236,39 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
             res[r][lane] = 1.0f / sqrtf(fmaxf(ss, 1.17549435e-38f));
             res[r][kMaxP + lane] = dt;
         }
-        if (lane == P - 1) {
-            const float norm = sqrtf(ss);
-            res[r][2 * kMaxP] = norm > 0.f ? ldexpf(1.0f, -ilogbf(norm)) : 1.0f;
+        // the row scale sig = 2^-floor(log2 |row[:P_n]|), formed by every lane from lane P - 1's sum
+        const float ssP = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ss), P - 1));
+        const float normP = sqrtf(ssP);
+        const float sig = normP > 0.f ? ldexpf(1.0f, -ilogbf(normP)) : 1.0f;
+        if (lane == 0) res[r][2 * kMaxP] = sig;
+        if (a.qH) {
+            // the backward's FP16 copy of the row, times sig (exact: a power of two, and a BF16 value
+            // times it fits FP16 above FP16's subnormal range)
+            const bool isq = g < a.R;
+            _Float16 *xh = isq ? a.qH + g * D : a.kH + (g - a.R) * D;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                if (lane + 64 * c < nch) {
+                    const unsigned int in[4] = {bx[s][c].x, bx[s][c].y, bx[s][c].z, bx[s][c].w};
+                    f16x8 h;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        h[2 * i] = (_Float16)(bf16_lo(in[i]) * sig);
+                        h[2 * i + 1] = (_Float16)(bf16_hi(in[i]) * sig);
+                    }
+                    *(f16x8 *)(xh + 8 * (lane + 64 * c)) = h;
+                }
         }
     }
+    // zero rows past the last row of each copy (block 0: q's; k's by block 1, or by block 0 in a
+    // grid of one block)
+    if (a.qH)
+        for (int which = 0; which < 2; ++which) {
+            if ((int)blockIdx.x != (gridDim.x > 1 ? which : 0)) continue;
+            _Float16 *xh = which == 0 ? a.qH : a.kH;
+            const int64_t e0 = (which == 0 ? a.R : a.N) * D, e1 = (which == 0 ? a.Rpad : a.Npad) * D;
+            for (int64_t e = e0 + 8 * (int64_t)threadIdx.x; e < e1; e += 8 * 256) *(f16x8 *)(xh + e) = f16x8{};
+        }
     __syncthreads();
     // tables [p][row]: consecutive rows on consecutive lanes (two runs where the block holds both kinds)
     for (int e = threadIdx.x; e < RB * (P + 1); e += 256) {
@@ -261,30 +289,6 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
             (isq ? a.gamq : a.gamk)[i] = a.gam_scale * res[r][P - 1];
         }
     }
-}
-
-// ----------------------------------------------------------------------------
-// k_half_copy: xh[r][d] = x[r][d] * sig_r in FP16.  sig is a power of two
-// that brings the row norm into [1, 2), so the BF16 -> FP16 conversion is exact
-// for every element above FP16's subnormal range.  Rows rows .. rows_pad - 1 are
-// zeros (the backward streams whole blocks past the last row).  8 elements per thread.
-// ----------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_half_copy(const u16 *__restrict__ x, const float *__restrict__ sig,
-                                                   int64_t rows, int64_t rows_pad, int D, _Float16 *__restrict__ xh) {
-    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-    if (e >= rows_pad * D) return;
-    f16x8 h = {};
-    if (e < rows * D) {
-        const float sc = sig[e / D];
-        const uint4 v = *(const uint4 *)(x + e);
-        const unsigned int in[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            h[2 * i] = (_Float16)(bf16_lo(in[i]) * sc);
-            h[2 * i + 1] = (_Float16)(bf16_hi(in[i]) * sc);
-        }
-    }
-    *(f16x8 *)(xh + e) = h;
 }
 
 // ----------------------------------------------------------------------------
@@ -2065,14 +2069,6 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
         if (wide) hipLaunchKernelGGL((k_prep<1, 4>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
         else hipLaunchKernelGGL((k_prep<1, 2>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_half_copy(const u16 *x, const float *sig, int64_t rows, int D, _Float16 *xh, hipStream_t s) {
-    const int64_t rows_pad = bwd_padded_rows(rows);
-    const int64_t chunks = rows_pad * D / 8;  // D is a multiple of 64
-    hipLaunchKernelGGL(k_half_copy, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, x, sig, rows, rows_pad,
-                       D, xh);
     return hipGetLastError();
 }
 
