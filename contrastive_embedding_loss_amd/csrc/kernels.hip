@@ -1580,7 +1580,31 @@ int gen_max_bands(int nq) { return nq >= 16 ? GenLds<16>::NBAND : GenLds<8>::NBA
 
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 
-template <int NQ, bool SIG, bool UPD>
+// A ladder the generic backward can also take at compile time (LM: bit e set where a prefix ends at
+// 32 (e + 1)), with the same slots as the host's tables: a prefix ending on its wave's last step
+// uses that wave's partial, the others snapshot slots 4, 5, ... in prefix order.
+template <uint64_t LM, int NQ>
+struct GenLadder {
+    static constexpr int P = __builtin_popcountll(LM);
+    static constexpr int end_step(int p) {
+        int c = -1;
+        for (int e = 0; e < 64; ++e)
+            if (((LM >> e) & 1ull) != 0ull && ++c == p) return e;
+        return 0;
+    }
+    static constexpr int wave_of(int p) { return end_step(p) / NQ; }
+    static constexpr int snap_slot(int p) {
+        if ((end_step(p) + 1) % NQ == 0) return end_step(p) / NQ;
+        int interior = 0;
+        for (int q = 0; q < p; ++q)
+            if ((end_step(q) + 1) % NQ != 0) ++interior;
+        return 4 + interior;
+    }
+};
+// the Large and XL tiers' ladder {64, 128, 256, 512, 1024, 2048}
+constexpr uint64_t kLadder2048 = (1ull << 1) | (1ull << 3) | (1ull << 7) | (1ull << 15) | (1ull << 31) | (1ull << 63);
+
+template <int NQ, bool SIG, bool UPD, uint64_t LM = 0>
 __global__ __launch_bounds__(256, 1) void k_bwd_gen(BwdArgs a) {
     using G = GenLds<NQ>;
     constexpr int YP = G::YP, RSL = G::RSL;
@@ -1751,12 +1775,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_gen(BwdArgs a) {
                 for (int t = 0; t < 2; ++t) ok[t] = ok[t] && ((lm[t] >> lbit) & 1ull) == 0ull;
             }
             float run[2] = {0.f, 0.f};
-#pragma unroll
-            for (int p = kMaxP - 1; p >= 0; --p) {
-                if (p >= P) continue;
-                const int wv = a.gt.wave_of[p];
-                f32x2 Sp = *(const f32x2 *)&Sl[a.gt.snap_slot[p]][l32 * SLOTP + nl];
-                for (int q = 0; q < wv; ++q) Sp += *(const f32x2 *)&Sl[q][l32 * SLOTP + nl];
+            // the unit of prefix p (a compile-time index, so that the per-prefix registers stay
+            // registers), given S^p: the full partials of the waves below the one where p ends, plus
+            // p's snapshot slot
+            auto unit = [&](auto pc, f32x2 Sp) {
+                constexpr int p = decltype(pc)::value;
                 float av[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
@@ -1785,6 +1808,26 @@ __global__ __launch_bounds__(256, 1) void k_bwd_gen(BwdArgs a) {
                 uint32_t hpk;
                 asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(hpk) : "v"(run[0]), "v"(run[1]));
                 *(uint32_t *)&At[p][l32 * APITCH + nl] = hpk;
+            };
+            if constexpr (LM != 0) {  // the ladder known at compile time: fixed slots, no loops
+                using GL = GenLadder<LM, NQ>;
+                static_for<0, GL::P>([&](auto ic) {
+                    constexpr int p = GL::P - 1 - decltype(ic)::value;
+                    constexpr int slot = GL::snap_slot(p), wv = GL::wave_of(p);
+                    f32x2 Sp = *(const f32x2 *)&Sl[slot][l32 * SLOTP + nl];
+                    static_for<0, wv>(
+                        [&](auto qc) { Sp += *(const f32x2 *)&Sl[decltype(qc)::value][l32 * SLOTP + nl]; });
+                    unit(std::integral_constant<int, p>{}, Sp);
+                });
+            } else {
+                static_for<0, kMaxP>([&](auto ic) {
+                    constexpr int p = kMaxP - 1 - decltype(ic)::value;
+                    if (p >= P) return;
+                    const int wv = a.gt.wave_of[p];
+                    f32x2 Sp = *(const f32x2 *)&Sl[a.gt.snap_slot[p]][l32 * SLOTP + nl];
+                    for (int q = 0; q < wv; ++q) Sp += *(const f32x2 *)&Sl[q][l32 * SLOTP + nl];
+                    unit(std::integral_constant<int, p>{}, Sp);
+                });
             }
         }
         lds_barrier();
@@ -2164,6 +2207,19 @@ hipError_t launch_bwd(const BwdArgs &a, uint32_t mask, bool sig, int64_t nsplit,
 
 template <int NQ>
 static hipError_t launch_bwd_gen_nq(const BwdArgs &a, bool sig, dim3 grid, hipStream_t s) {
+    uint64_t lm = 0;  // the ladder as a 64-bit mask (prefix ends at multiples of 32 up to 2048)
+    for (int p = 0; p < a.pf.n; ++p) lm |= 1ull << (a.pf.w[p] / 32 - 1);
+    if constexpr (NQ == 16) {
+        if (lm == kLadder2048) {  // compiled with the ladder's slots
+            if (!sig)
+                hipLaunchKernelGGL((k_bwd_gen<NQ, false, true, kLadder2048>), grid, dim3(256), 0, s, a);
+            else if (a.do_update)
+                hipLaunchKernelGGL((k_bwd_gen<NQ, true, true, kLadder2048>), grid, dim3(256), 0, s, a);
+            else
+                hipLaunchKernelGGL((k_bwd_gen<NQ, true, false, kLadder2048>), grid, dim3(256), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     if (!sig)
         hipLaunchKernelGGL((k_bwd_gen<NQ, false, true>), grid, dim3(256), 0, s, a);
     else if (a.do_update)
