@@ -1568,9 +1568,18 @@ __global__ __launch_bounds__(256, 1) void k_bwd(BwdArgs a) {
 // ----------------------------------------------------------------------------
 constexpr int GBO = kGenOuter;
 
-template <int NQ>
+// Tile rows of a swizzled ring (SWZ) are unpadded and hold 16-byte chunk c of inner row r at
+// chunk c ^ gen_swz(r): with this map both the recompute's 16-byte row reads and the update's
+// transposed reads are free of bank conflicts (the padded pitch + 16 halves leaves the
+// transposed reads at about 1.5x their conflict-free time).  It permutes chunks inside aligned
+// groups of 16, so a swizzled ring needs rows whose copied width is a multiple of 128 halves.
+__device__ __forceinline__ int gen_swz(int r) { return ((5 * (r & 3)) ^ (8 * ((r >> 2) & 1))) & 15; }
+
+template <int NQ, bool SWZ = false>
 struct GenLds {
-    static constexpr int YP = 4 * NQ * 32 + 8;                // FP16 per LDS row of an inner tile
+    // FP16 per LDS row of an inner tile (unswizzled: + 16 keeps the recompute's 16-byte row reads
+    // free of bank conflicts, + 8 left them and the transposed reads 2-way)
+    static constexpr int YP = 4 * NQ * 32 + (SWZ ? 0 : 16);
     static constexpr int RSL = BI * YP + 2 * kMaxP * BI * 2;  // FP16 per ring slot: the tile, then its tables
     static constexpr int NSLOT = NQ >= 16 ? 7 : 12;           // S slots (4 wave partials + snapshots)
     static constexpr int NBAND = NQ >= 16 ? 7 : kMaxP + 1;    // band operands (prefixes, then a zero band)
@@ -1600,13 +1609,43 @@ struct GenLadder {
             if ((end_step(q) + 1) % NQ != 0) ++interior;
         return 4 + interior;
     }
+    // the snapshot slot written after step e (a prefix ending there, not on its wave's last
+    // step), or -1
+    static constexpr int snap_at(int e) {
+        for (int p = 0; p < P; ++p)
+            if (end_step(p) == e && (e + 1) % NQ != 0) return snap_slot(p);
+        return -1;
+    }
+    // bit W set: wave W writes a snapshot after its step ks
+    static constexpr uint32_t snap_waves(int ks) {
+        uint32_t m = 0;
+        for (int W = 0; W < 4; ++W)
+            if (snap_at(W * NQ + ks) >= 0) m |= 1u << W;
+        return m;
+    }
+    // the band operand of step j: the narrowest prefix that reaches past it (P: none, zero band)
+    static constexpr int band_of(int j) {
+        for (int p = 0; p < P; ++p)
+            if (end_step(p) >= j) return p;
+        return P;
+    }
+    // wave W's bands, 4 bits per step (NQ <= 16)
+    static constexpr uint64_t bands(int W) {
+        uint64_t m = 0;
+        for (int jb = 0; jb < NQ; ++jb) m |= (uint64_t)band_of(W * NQ + jb) << (4 * jb);
+        return m;
+    }
 };
 // the Large and XL tiers' ladder {64, 128, 256, 512, 1024, 2048}
 constexpr uint64_t kLadder2048 = (1ull << 1) | (1ull << 3) | (1ull << 7) | (1ull << 15) | (1ull << 31) | (1ull << 63);
 
 template <int NQ, bool SIG, bool UPD, uint64_t LM = 0>
 __global__ __launch_bounds__(256, 1) void k_bwd_gen(BwdArgs a) {
-    using G = GenLds<NQ>;
+    // the compiled ladder (widest prefix 2048 = D) takes the swizzled ring, and its per-prefix
+    // registers only for its own prefixes
+    constexpr bool SWZ = LM != 0;
+    constexpr int NPV = LM != 0 ? __builtin_popcountll(LM) : kMaxP;
+    using G = GenLds<NQ, SWZ>;
     constexpr int YP = G::YP, RSL = G::RSL;
     __shared__ __attribute__((aligned(16))) _Float16 Ys[2][RSL];
     __shared__ __attribute__((aligned(16))) float Sl[G::NSLOT][GBO * SLOTP];
@@ -1628,7 +1667,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_gen(BwdArgs a) {
     const bool want_loss = SIG && a.want_loss != 0, want_bias = SIG && a.biasparts != nullptr;
 
     // ---- this lane's outer-row terms (the static operand scale as in k_bwd)
-    float Ao[kMaxP], Co[kMaxP], Ro[kMaxP];
+    float Ao[NPV], Co[NPV], Ro[NPV];
     float csc = 1.0f;
     {
         const int64_t orow = ovalid ? o : 0;
@@ -1645,7 +1684,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_gen(BwdArgs a) {
         }
         const float rsig = 1.0f / a.oSig[orow];  // exact: sig is a power of two
 #pragma unroll
-        for (int p = 0; p < kMaxP; ++p) {
+        for (int p = 0; p < NPV; ++p) {
             const int pp = p < P ? p : 0;
             Ao[p] = a.oA[pp * a.NO + orow] * rsig;
             const float c = a.oC[pp * a.NO + orow];
@@ -1672,7 +1711,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_gen(BwdArgs a) {
     auto issue_block = [&](int nb, int sl) {
         const _Float16 *gblk = a.Y16 + (int64_t)nb * BI * D;
         for (int k = 0; k < 4; ++k) {
-            const uint32_t voff = (uint32_t)(4 * w + k) * (uint32_t)D * 2u + 16u * (uint32_t)lane;
+            // swizzled: lane i of a 1 KB piece fetches the chunk that belongs at chunk i (every piece full)
+            const int src_lane = SWZ ? (lane ^ gen_swz(4 * w + k)) : lane;
+            const uint32_t voff = (uint32_t)(4 * w + k) * (uint32_t)D * 2u + 16u * (uint32_t)src_lane;
             const uint32_t m0v = __builtin_amdgcn_readfirstlane(ys_lds + 2u * (uint32_t)(sl * RSL + (4 * w + k) * YP));
             for (int pc = 0; pc < npc; ++pc)
                 if (pc + 1 < npc || lane < lastc) dma_row1(gblk, voff + 1024u * pc, m0v + 1024u * pc);
@@ -1704,9 +1745,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_gen(BwdArgs a) {
     for (int j = 0; j < NQ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dacc[j][r] = 0.f;
-    float Cacc[kMaxP], Lacc[kMaxP], Bacc[kMaxP];
+    float Cacc[NPV], Lacc[NPV], Bacc[NPV];
 #pragma unroll
-    for (int p = 0; p < kMaxP; ++p) Cacc[p] = Lacc[p] = Bacc[p] = 0.f;
+    for (int p = 0; p < NPV; ++p) Cacc[p] = Lacc[p] = Bacc[p] = 0.f;
 
     // listed cells: the entries of this workgroup's 64-row table block, sorted by nb
     const int lob = (int)blockIdx.x >> 1, lbit = 32 * ((int)blockIdx.x & 1) + l32;
@@ -1728,6 +1769,15 @@ __global__ __launch_bounds__(256, 1) void k_bwd_gen(BwdArgs a) {
     const _Float16 *ytr = &Ys[0][0] + (8 * (g4 >> 1) + (l16 >> 2)) * YP + 16 * (g4 & 1) + 4 * (lane & 3) + dq0;
     const float *tabs0 = (const float *)&Ys[0][BI * YP];
 
+    uint64_t wbands = 0;  // the compiled ladder's bands of this wave's steps
+    if constexpr (LM != 0) {
+        using GL = GenLadder<LM, NQ>;
+        constexpr uint64_t b0 = GL::bands(0), b1 = GL::bands(1), b2 = GL::bands(2), b3 = GL::bands(3);
+        wbands = w == 0 ? b0 : w == 1 ? b1 : w == 2 ? b2 : b3;
+        wbands = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(wbands >> 32)) << 32) |
+                 (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)wbands);
+    }
+
     if (nb_begin < nb_end) {
         issue_block(nb_begin, 0);
         wait_vm();
@@ -1746,14 +1796,46 @@ __global__ __launch_bounds__(256, 1) void k_bwd_gen(BwdArgs a) {
 #pragma unroll
                 for (int ob = 0; ob < 2; ++ob) *(f32x4 *)&Sl[slot][(16 * ob + l16) * SLOTP + 4 * g4] = acc[ob];
             };
+            if constexpr (LM != 0) {
+                // the ladder's snapshots are known per step: straight-line steps with the tile
+                // reads RD steps ahead
+                using GL = GenLadder<LM, NQ>;
+                constexpr int RD = NQ < 4 ? NQ : (SIG ? 2 : 4);  // the sigmoid form has fewer registers to spare
+                // step ks reads logical chunk 4 ks + g4 of row l16, stored at 4 (ks ^ (sw >> 2)) + (g4 ^ (sw & 3))
+                const int sw = gen_swz(l16);
+                const _Float16 *yr0 = &Ys[cur][0] + l16 * YP + dq0 + 8 * (g4 ^ (sw & 3));
+                const _Float16 *yrm[4] = {yr0 + 32 * (0 ^ (sw >> 2)), yr0 + 32 * (1 ^ (sw >> 2)), yr0 + 32 * (2 ^ (sw >> 2)),
+                                          yr0 + 32 * (3 ^ (sw >> 2))};
+                auto yat = [&](int ks) { return (const f16x8 *)(yrm[ks & 3] + 32 * (ks & ~3)); };
+                f16x8 yb[RD];
+                static_for<0, RD>([&](auto kc) { yb[decltype(kc)::value] = *yat(decltype(kc)::value); });
+                static_for<0, NQ>([&](auto kc) {
+                    constexpr int ks = decltype(kc)::value;
+                    const f16x8 yv = yb[ks % RD];
+                    if constexpr (ks + RD < NQ) yb[ks % RD] = *yat(ks + RD);
 #pragma unroll
-            for (int ks = 0; ks < NQ; ++ks) {
-                const f16x8 yv = *(const f16x8 *)(yrow + 32 * ks);
+                    for (int ob = 0; ob < 2; ++ob)
+                        acc[ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(yv, xr[ob][ks], acc[ob], 0, 0, 0);
+                    constexpr uint32_t wm = GL::snap_waves(ks);
+                    if constexpr (wm != 0u) {
+                        static_for<0, 4>([&](auto Wc) {
+                            constexpr int W = decltype(Wc)::value;
+                            constexpr int slot = GL::snap_at(W * NQ + ks);
+                            if constexpr (slot >= 0)
+                                if (w == W) put(slot);
+                        });
+                    }
+                });
+            } else {
 #pragma unroll
-                for (int ob = 0; ob < 2; ++ob)
-                    acc[ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(yv, xr[ob][ks], acc[ob], 0, 0, 0);
-                const int sl = a.gt.snap_at[w * NQ + ks];
-                if (sl >= 0) put(sl);
+                for (int ks = 0; ks < NQ; ++ks) {
+                    const f16x8 yv = *(const f16x8 *)(yrow + 32 * ks);
+#pragma unroll
+                    for (int ob = 0; ob < 2; ++ob)
+                        acc[ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(yv, xr[ob][ks], acc[ob], 0, 0, 0);
+                    const int sl = a.gt.snap_at[w * NQ + ks];
+                    if (sl >= 0) put(sl);
+                }
             }
             put(w);
         }
@@ -1833,7 +1915,37 @@ __global__ __launch_bounds__(256, 1) void k_bwd_gen(BwdArgs a) {
         lds_barrier();
 
         // update: dX[:, this wave's steps] += A_band . Y
-        if constexpr (UPD) {
+        if constexpr (UPD && LM != 0) {
+            // the bands of every wave's steps are known (4 bits per step, this wave's sequence in
+            // scalar registers); the band and tile reads run RD steps ahead of the products
+            using GL = GenLadder<LM, NQ>;
+            constexpr int RD = NQ < 3 ? NQ : (SIG ? 2 : 3);
+            // row ru = 8 (g4 >> 1) + (l16 >> 2) (and ru + 4, whose swizzle is sw ^ 8) at logical
+            // chunk 4 jb + t, t = 2 (g4 & 1) + ((lane & 3) >> 1), half lane & 1 of it
+            const int ru = 8 * (g4 >> 1) + (l16 >> 2), sw = gen_swz(ru);
+            const _Float16 *yu0 = &Ys[cur][0] + ru * YP + dq0 + 8 * ((2 * (g4 & 1) + ((lane & 3) >> 1)) ^ (sw & 3)) +
+                                  4 * (lane & 1);
+            const _Float16 *yum[4] = {yu0 + 32 * (0 ^ (sw >> 2)), yu0 + 32 * (1 ^ (sw >> 2)), yu0 + 32 * (2 ^ (sw >> 2)),
+                                      yu0 + 32 * (3 ^ (sw >> 2))};
+            const _Float16 *asrc = &At[0][0] + l32 * APITCH + 8 * h;
+            f16x8 ab[RD];
+            f16x4 ylo[RD], yhi[RD];
+            auto rd = [&](auto jc) {
+                constexpr int jb = decltype(jc)::value;
+                const int band = (int)((wbands >> (4 * jb)) & 15u);
+                ab[jb % RD] = *(const f16x8 *)(asrc + band * (GBO * APITCH));
+                ylo[jb % RD] = ds_read_tr(yum[jb & 3] + 32 * (jb & ~3));
+                yhi[jb % RD] = ds_read_tr(yum[(jb & 3) ^ 2] + 32 * (jb & ~3) + 4 * YP);
+            };
+            static_for<0, RD>(rd);
+            static_for<0, NQ>([&](auto jc) {
+                constexpr int jb = decltype(jc)::value;
+                const f16x8 af = ab[jb % RD];
+                const f16x8 bfv = __builtin_shufflevector(ylo[jb % RD], yhi[jb % RD], 0, 1, 2, 3, 4, 5, 6, 7);
+                if constexpr (jb + RD < NQ) rd(std::integral_constant<int, jb + RD>{});
+                dacc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bfv, dacc[jb], 0, 0, 0);
+            });
+        } else if constexpr (UPD) {
 #pragma unroll
             for (int jb = 0; jb < NQ; ++jb) {
                 const int band = a.gt.band_of[w * NQ + jb];
@@ -1868,10 +1980,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_gen(BwdArgs a) {
     // radial sums over the eight (wave, half) parts of each row, and the sigmoid loss sums
     float *red = &Sl[0][0];  // [8][kMaxP][GBO], then [4][kMaxP] twice
 #pragma unroll
-    for (int p = 0; p < kMaxP; ++p) red[((2 * w + h) * kMaxP + p) * GBO + l32] = Cacc[p];
+    for (int p = 0; p < NPV; ++p) red[((2 * w + h) * kMaxP + p) * GBO + l32] = Cacc[p];
     if (want_loss) {
 #pragma unroll
-        for (int p = 0; p < kMaxP; ++p) {
+        for (int p = 0; p < NPV; ++p) {
             const float v = wave_sum(Lacc[p]), u = wave_sum(Bacc[p]);
             if (lane == 0) {
                 red[8 * kMaxP * GBO + w * kMaxP + p] = v;
@@ -2210,7 +2322,7 @@ static hipError_t launch_bwd_gen_nq(const BwdArgs &a, bool sig, dim3 grid, hipSt
     uint64_t lm = 0;  // the ladder as a 64-bit mask (prefix ends at multiples of 32 up to 2048)
     for (int p = 0; p < a.pf.n; ++p) lm |= 1ull << (a.pf.w[p] / 32 - 1);
     if constexpr (NQ == 16) {
-        if (lm == kLadder2048) {  // compiled with the ladder's slots
+        if (lm == kLadder2048 && a.D == 2048) {  // compiled with the ladder's slots and a swizzled ring
             if (!sig)
                 hipLaunchKernelGGL((k_bwd_gen<NQ, false, true, kLadder2048>), grid, dim3(256), 0, s, a);
             else if (a.do_update)
