@@ -133,6 +133,10 @@ def main():
     flops = (4.0 if oneset else 8.0) * R * N * D
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     pair_scores = float(R) * N * P / (ms_per_step * 1e-3)
+    # for comparison with implementations counted without the logit recompute: two-set 6RND
+    # (forward, dQ, dK), one-set 4RND (logits, dX); and cells (pairs scored once) per second
+    tflops_no_recompute = (4.0 if oneset else 6.0) * R * N * D / (ms_per_step * 1e-3) / 1e12
+    cells = float(R) * N / (ms_per_step * 1e-3)
     kern_per_step = {n: t / args.steps for n, t in kern.items()}
     print(f"[bench] {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s; kernels (ms/step): "
           + ", ".join(f"{n}={t:.3f}" for n, t in sorted(kern_per_step.items(), key=lambda x: -x[1])),
@@ -253,6 +257,8 @@ def main():
                    "weights": list(w.weights) if w.weights else None, "recipe": w.recipe,
                    **({"extra_positives": int(positives[0][-1])} if positives is not None else {})},
         "pair_scores_per_s": pair_scores,
+        "cells_per_s": cells,
+        "tflops_no_recompute": round(tflops_no_recompute, 2),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "pct_of_gemm_ceiling": round(100.0 * tflops / gemm["tflops"], 2) if gemm else None,
         "gemm_ceiling": gemm,
