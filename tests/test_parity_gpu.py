@@ -614,6 +614,32 @@ def test_oneset_relations_confident():
 XL = (64, 128, 256, 512, 1024, 2048)  # the Large and XL tiers' prefixes
 
 
+@pytest.mark.parametrize("case,kind,s,b", [
+    ("infonce-neg-scale", INFONCE, -14.0, 0.0),
+    ("infonce-scale-40", INFONCE, 40.0, 0.0),
+    ("infonce-bias", INFONCE, 14.0, 0.5),
+    ("rows-bias", INFONCE_ROWS, 14.0, -1.5),
+    ("siglip-neg-scale", SIGLIP, -10.0, -3.0),
+    ("siglip-t30-b2", SIGLIP, 30.0, 2.0),
+    ("siglip-t30-b-25", SIGLIP, 30.0, -25.0),
+])
+def test_scale_and_bias_regimes_2048(case, kind, s, b):
+    # the same regimes at D = 2048 with the wide tiers' ladder, whose backward is the generic
+    # kernel compiled for that ladder (its own epilogue, sigmoid loss and band operands)
+    D, w = 2048, (1, 1, 1, 1, 1, 2)
+    R, N, off = (160, 160, 0) if kind != INFONCE_ROWS else (96, 288, 64)
+    if "40" in case:
+        qb, kb = _spread_inputs(R, N, D, seed=271 + len(case), off=off)
+    else:
+        qb, kb = make_inputs(R, N, D, noise=0.5, seed=271 + len(case), row_offset=off)
+    got, ref = run_both(qb, kb, XL, s, b, kind, weights=w, off=off, label=case + "-2048")
+    check(got, ref, kind)
+    if "dscale" in got:
+        assert got["dscale"].item() == pytest.approx(ref["dscale"], rel=1e-3, abs=1e-6)
+        if kind == SIGLIP:
+            assert got["dbias"].item() == pytest.approx(ref["dbias"], rel=1e-3, abs=1e-6)
+
+
 @pytest.mark.parametrize("case", ["infonce", "siglip", "rows", "oneset", "relations", "band"])
 def test_wide_rows_2048(case):
     # D = 2048 with the wide tiers' six prefixes, through the generic backward, every kind
