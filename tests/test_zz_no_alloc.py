@@ -69,6 +69,26 @@ def test_noalloc_shares_on_two_calls(kind):
             assert torch.equal(got[3][name], ref[3][name]), name
 
 
+@pytest.mark.parametrize("kind,s,b", [(INFONCE, 14.0, 0.0), (SIGLIP, 10.0, -10.0)])
+def test_noalloc_wide_rows_on_two_calls(kind, s, b):
+    # D = 2048 with the wide tiers' ladder: the generic backward's split partials and k_finalize in
+    # the scratch
+    xl, w = (64, 128, 256, 512, 1024, 2048), (1, 1, 1, 1, 1, 2)
+    for R in (384, 200):
+        print(f"[case] noalloc wide kind={kind} R=N={R}", flush=True)
+        qb, kb = make_inputs(R, R, 2048, noise=0.5, seed=281 + R)
+        q, k = _dev(qb), _dev(kb)
+        ref = binding.fwd_bwd(q, k, xl, s, b, kind, weights=w, extras=True)
+        got = binding.fwd_bwd(q, k, xl, s, b, kind, weights=w, extras=True, noalloc=True)
+        torch.cuda.synchronize()
+        assert abs(got[0].item() - ref[0].item()) <= 1e-3 * abs(ref[0].item())
+        for a, c in ((got[1], ref[1]), (got[2], ref[2])):
+            assert (a - c).abs().max().item() <= 2e-3 * c.abs().max().item()
+            assert torch.equal(a, c)
+        for name in ref[3]:
+            assert torch.equal(got[3][name], ref[3][name]), name
+
+
 def test_noalloc_refuses_what_it_cannot_hold():
     qb, kb = make_inputs(64, 64, 1024, seed=251)
     q, k = _dev(qb), _dev(kb)
