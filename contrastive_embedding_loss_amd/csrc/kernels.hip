@@ -392,13 +392,13 @@ __device__ __forceinline__ void fwd_write_partials(float *lds, const float (&rke
 
 // Slices (64 wide) covered by the prefixes of ladder MASK (bit ds: a prefix ends at 32 (ds + 1)),
 // for ladders whose prefixes all end on a slice boundary; 0 otherwise.
-constexpr int fwd_ladder_slices(uint32_t mask) {
-    if (mask == 0u || (mask & 0x55555555u) != 0u) return 0;
-    return (32 - __builtin_clz(mask)) / 2;
+constexpr int fwd_ladder_slices(uint64_t mask) {
+    if (mask == 0ull || (mask & 0x5555555555555555ull) != 0ull) return 0;
+    return (64 - __builtin_clzll(mask)) / 2;
 }
-constexpr uint32_t fwd_ladder(uint32_t mask) { return fwd_ladder_slices(mask) > 0 ? mask : 0u; }
+constexpr uint64_t fwd_ladder(uint64_t mask) { return fwd_ladder_slices(mask) > 0 ? mask : 0ull; }
 
-template <uint32_t MASK>
+template <uint64_t MASK>
 __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const u16 *__restrict__ k, int64_t R,
                                                 int64_t N, int D, Prefixes pf, int64_t off,
                                                 const float *__restrict__ rowA, const float *__restrict__ colI,
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
 #pragma unroll
     for (int q = 0; q < kMaxP; ++q) rkeep[q] = ckeep[q] = 0.f;
 
-    if constexpr (MASK != 0u) {
+    if constexpr (MASK != 0ull) {
         // Prefix ladder known at compile time: no branch inside a slice.  The ring holds four
         // 32-wide slices (rows of 64 bytes; the 16-byte chunk c of row r at position
         // c ^ ((r >> 2) & 3), so the operand reads of 16 rows meet 64 different banks).  Per slice
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
         constexpr int SLB2 = FB * FK2 * 2;  // bytes per operand slice
         constexpr int NSL = 2 * fwd_ladder_slices(MASK);
         static_assert(NSL >= 2, "every prefix must end on a 64-wide boundary");
-        constexpr int NPm = __builtin_popcount(MASK);
+        constexpr int NPm = __builtin_popcountll(MASK);
         // copies: this wave moves pieces 2 wave, 2 wave + 1 (16 rows x 64 bytes each) of both operands
         uint32_t cq[2], ck[2];
 #pragma unroll
@@ -576,8 +576,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const u16 *__restrict__ q, const
             // 32-wide slices up to the end of prefix p
             constexpr int endsl = [] {
                 int c = -1;
-                for (int ds = 0; ds < 32; ++ds)
-                    if (MASK & (1u << ds))
+                for (int ds = 0; ds < 64; ++ds)
+                    if (MASK & (1ull << ds))
                         if (++c == p) return ds + 1;
                 return 0;
             }();
@@ -2242,19 +2242,23 @@ hipError_t launch_fwd(const u16 *q, const u16 *k, int64_t R, int64_t N, int D, c
                       const float *rowA, const float *colI, float cshift, float *rowpart, float *colpart,
                       float *posdot, hipStream_t s) {
     const int64_t nIt = (R + FB - 1) / FB, nJt = (N + FB - 1) / FB;
-    uint32_t mask = 0;  // compiled ladders end at or below 1024 (32 steps); wider lists run the run-time variant
-    for (int p = 0; p < pf.n; ++p) mask |= pf.w[p] <= 1024 ? 1u << (pf.w[p] / 32 - 1) : 0u;
-    if (pf.w[pf.n - 1] > 1024) mask = 0u;
+    uint64_t mask = 0;  // bit e: a prefix ends at 32 (e + 1) (widths up to 2048)
+    for (int p = 0; p < pf.n; ++p) mask |= 1ull << (pf.w[p] / 32 - 1);
     const dim3 grid((unsigned)(nIt * nJt));
+    if (mask == kLadder2048) {  // the Large and XL tiers' ladder
+        hipLaunchKernelGGL(k_fwd<fwd_ladder(kLadder2048)>, grid, dim3(256), 0, s, q, k, R, N, D, pf, off, rowA, colI,
+                           cshift, rowpart, colpart, posdot);
+        return hipGetLastError();
+    }
 #define UFORM_CASE(m)                                                                                          \
-    if (fwd_ladder(m) != 0u && mask == (m)) {                                                                  \
+    if (fwd_ladder(m) != 0ull && mask == (m)) {                                                                \
         hipLaunchKernelGGL(k_fwd<fwd_ladder(m)>, grid, dim3(256), 0, s, q, k, R, N, D, pf, off, rowA, colI, cshift, \
                            rowpart, colpart, posdot);                                                          \
         return hipGetLastError();                                                                              \
     }
     UFORM_LADDERS(UFORM_CASE)
 #undef UFORM_CASE
-    hipLaunchKernelGGL(k_fwd<0u>, grid, dim3(256), 0, s, q, k, R, N, D, pf, off, rowA, colI, cshift, rowpart,
+    hipLaunchKernelGGL(k_fwd<0ull>, grid, dim3(256), 0, s, q, k, R, N, D, pf, off, rowA, colI, cshift, rowpart,
                        colpart, posdot);
     return hipGetLastError();
 }
