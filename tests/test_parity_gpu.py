@@ -110,8 +110,29 @@ def test_other_ladders(D, prefixes, kind):
 
 # One inner split per backward pass: the backward kernel applies the finalize terms in place
 # (the path every pass takes once the outer rows alone fill the GPU, e.g. 32768 x 32768).
-@pytest.mark.parametrize("case", ["infonce", "siglip", "rows", "siglip-tail", "infonce-tail"])
+@pytest.mark.parametrize("case", ["infonce", "siglip", "rows", "siglip-tail", "infonce-tail", "wide", "wide-siglip",
+                                  "generic-tail"])
 def test_one_split_finish(case):
+    # (wide, generic-tail: one split of the generic backward, finished by k_finalize; the run-time
+    # ladder's widest prefix, 384, leaves zero columns inside the waves' steps and past them)
+    if case == "wide":
+        qb, kb = make_inputs(160, 160, 2048, noise=0.5, seed=77)
+        args, kw = ((64, 128, 256, 512, 1024, 2048), 1 / 0.07, 0.0, INFONCE), dict(weights=(1, 1, 1, 1, 1, 2))
+        got, ref = run_both(qb, kb, *args, label="one-split-" + case, one_split=True, **kw)
+        check(got, ref, args[3])
+        return
+    if case == "wide-siglip":
+        qb, kb = make_inputs(200, 200, 2048, noise=0.5, seed=78)
+        args = ((64, 128, 256, 512, 1024, 2048), 10.0, -10.0, SIGLIP)
+        got, ref = run_both(qb, kb, *args, label="one-split-" + case, one_split=True)
+        check(got, ref, args[3])
+        return
+    if case == "generic-tail":
+        qb, kb = make_inputs(160, 160, 1024, noise=0.4, seed=79)
+        args = ((96, 192, 384), 12.0, -2.0, SIGLIP)
+        got, ref = run_both(qb, kb, *args, label="one-split-" + case, one_split=True)
+        check(got, ref, args[3])
+        return
     if case == "infonce":
         qb, kb = make_inputs(300, 300, 1024, noise=0.5, seed=71)
         args = (LADDER, 1 / 0.07, 0.0, INFONCE)
@@ -145,6 +166,22 @@ def test_one_split_accumulate_matches_split_path():
     assert (dq1 - (a[1] + 0.5)).abs().max().item() <= 1e-4 * scale + 1e-6
     assert (dk1 - (a[2] - 0.25)).abs().max().item() <= 1e-4 * scale + 1e-6
     assert (dq1[:, 256:] == 0.5).all() and (dk1[:, 256:] == -0.25).all()
+
+
+def test_one_split_accumulate_generic_matches_split_path():
+    # one split of the generic backward with accumulate: a run-time ladder narrower than D
+    qb, kb = make_inputs(192, 192, 1024, noise=0.5, seed=80)
+    q, k = to_dev(qb), to_dev(kb)
+    pf = (96, 192, 384)
+    a = binding.fwd_bwd(q, k, pf, 14.0, 0.0, INFONCE)
+    dq0 = torch.full_like(a[1], 0.5)
+    dk0 = torch.full_like(a[2], -0.25)
+    _, dq1, dk1 = binding.fwd_bwd(q, k, pf, 14.0, 0.0, INFONCE, dq=dq0.clone(), dk=dk0.clone(), accumulate=True,
+                                  one_split=True)
+    scale = max(a[1].abs().max().item(), a[2].abs().max().item())
+    assert (dq1 - (a[1] + 0.5)).abs().max().item() <= 1e-4 * scale + 1e-6
+    assert (dk1 - (a[2] - 0.25)).abs().max().item() <= 1e-4 * scale + 1e-6
+    assert (dq1[:, 384:] == 0.5).all() and (dk1[:, 384:] == -0.25).all()
 
 
 def test_single_pair_infonce_is_zero():
