@@ -247,9 +247,9 @@ size_t uform_contrastive_workspace_bytes_ex(int64_t R, int64_t N, int64_t D, int
  * for Swift", section "Errors".  The backward has kernels compiled for the
  * ladders {64,128,256,512,1024}, {64,128,256,512}, {64,128,256}, {64,128}
  * and the single widths {128}, {256}, {512}, {1024} (the fast path); every
- * other ladder, and every width above 1024 (the Large and XL tiers'
- * {64, ..., 1024, 2048}), takes a generic backward that reads the ladder at
- * run time.  Its LDS bounds the ladders it takes: above 1024 at most 6
+ * other ladder, and every width above 1024, takes a generic backward, compiled
+ * for the Large and XL tiers' {64, ..., 1024, 2048} and reading any other
+ * ladder at run time.  Its LDS bounds the ladders it takes: above 1024 at most 6
  * prefixes, at most 3 of them ending strictly inside a quarter of the widest
  * (as 64, 128 and 256 do in {64, ..., 2048}); a ladder past that is
  * unsupported.  A softmax call without gradients accepts any valid ladder. */
