@@ -677,6 +677,26 @@ def test_scale_and_bias_regimes_2048(case, kind, s, b):
             assert got["dbias"].item() == pytest.approx(ref["dbias"], rel=1e-3, abs=1e-6)
 
 
+@pytest.mark.parametrize("case", ["rows-one-row", "infonce-one-pair", "siglip-ragged"])
+def test_wide_rows_2048_edges(case):
+    # the 2048-wide ladder's kernels on degenerate and ragged shapes: one row of a share scored
+    # at the last key, a single pair (loss and gradients exactly zero), and sizes far from a tile
+    D, w = 2048, (1, 1, 1, 1, 1, 2)
+    if case == "rows-one-row":
+        qb, kb = make_inputs(1, 200, D, noise=0.5, seed=291, row_offset=199)
+        got, ref = run_both(qb, kb, XL, 1 / 0.07, 0.0, INFONCE_ROWS, weights=w, off=199, label="wide-" + case)
+        check(got, ref, INFONCE_ROWS)
+    elif case == "infonce-one-pair":
+        qb, kb = make_inputs(1, 1, D, seed=292)
+        got, ref = run_both(qb, kb, XL, 14.0, 0.0, INFONCE, weights=w, label="wide-" + case)
+        assert abs(got["loss"]) <= 1e-6
+        assert np.abs(got["dq"]).max() <= 1e-6 and np.abs(got["dk"]).max() <= 1e-6
+    else:
+        qb, kb = make_inputs(33, 77, D, noise=0.5, seed=293)
+        got, ref = run_both(qb, kb, XL, 10.0, -10.0, SIGLIP, weights=w, label="wide-" + case)
+        check(got, ref, SIGLIP)
+
+
 @pytest.mark.parametrize("case", ["infonce", "siglip", "rows", "oneset", "relations", "band"])
 def test_wide_rows_2048(case):
     # D = 2048 with the wide tiers' six prefixes, through the generic backward, every kind
