@@ -51,9 +51,12 @@ __device__ __forceinline__ f16x8 pack_f16x8(const float (&v)[8]) {
 // lane i with 15 - i and 7 - i (DPP row mirror and half mirror), stages 2 and
 // 1 use quad permutes.  Each stage pairs lanes that differ in the stage's bit
 // and agree on the bits of the stages before, so lane l keeps slot l & 31.
+// A lane permutation within rows of 16 (every source lane exists, so the zero that bound_ctrl
+// gives a missing source never appears); in this form the compiler folds it into the add that
+// consumes it (v_add_f32 with a DPP operand instead of a move and an add).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 __device__ __forceinline__ float reduce_scatter32(float (&v)[32], int lane) {
 #pragma unroll
